@@ -1,0 +1,418 @@
+"""Plain, slow, fp64 CPU oracle of the speculative-decoding verify step.
+
+TEST INFRASTRUCTURE ONLY -- imported by the tests, the smoke check and the
+bench's cpu_baseline leg, never by the GPU library.  It shares no code with the
+GPU path: it decodes bf16 itself, rounds stage outputs itself and reads only
+host numpy arrays.
+
+Sources (web pages; cited by title and section):
+  [SW]  "SwitchSD는 LLM 내부 표현으로 추측 디코딩의 복사 모드를 판별한다"
+        (onedev.kr/papers/87): sections "어떻게 동작하나" (how it works) and
+        "무엇과 다른가" (how it differs).
+  [SD]  "LLM 투기적 디코딩(Speculative Decoding) 해부 ..." (blog.huny.dev):
+        section 2 (pipeline: drafting, parallel verification, rejection sampler,
+        bonus token) and section 3 (equations for alpha(x), p'(x), P_final).
+  [EX]  "추측 디코딩은 왜 빨라지면서 답은 바뀌지 않나" (jl917.github.io):
+        step 2 (batch verify, cut at the first mismatch).
+  [SL]  "SlimSpec: Low-Rank Draft LM-Head for Accelerated Speculative Decoding"
+        (gist.science/ko/paper/2605.10453): "방법론 / 아키텍처", z = W_up W_down h.
+
+Every function below is the plain definition of its step; the readings taken
+where the pages are silent or garbled are listed next to the code that uses them.
+Parity pins: every function here is pinned by tests that do not call it to
+produce the expected value (brute force, closed forms, library routines,
+hand-derived values); see tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Flag bits, shared in meaning (not in code) with the GPU library's header.
+FLAG_PROBE_TIE = 1          # |score - tau| < 1e-5
+FLAG_ACCEPT_TIE = 2         # a decisive acceptance test is a near tie
+FLAG_CDF_TIE = 4            # the categorical draw lands within eps of a CDF step
+FLAG_DEGENERATE = 8         # residual mass <= 0: fell back to the target distribution
+FLAG_NO_CANDIDATE = 16      # no candidate (gate closed or nothing found): root sample only
+FLAG_BAD_PAGE = 32          # page-table entry or prefix length out of range
+FLAG_BAD_CTX = 64           # context offsets out of range
+FLAG_BAD_TOKEN = 128        # candidate token id outside [0, V)
+
+PROBE_TIE_EPS = 1e-5
+ACCEPT_TIE_REL = 1e-4
+CDF_TIE_EPS = 1e-8
+
+
+# ----------------------------------------------------------------------------------
+# number formats (own implementation; the GPU library has its own)
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the 16 bits are the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def round_f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value (ties to even), returned as fp64.
+    bf16 keeps 7 explicit mantissa bits; fp64 has 52, so the rounding point is bit 45."""
+    u = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = (u + lsb + np.uint64((1 << 44) - 1)) >> np.uint64(45) << np.uint64(45)
+    return r.view(np.float64)
+
+
+def round_stage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a stage output to the ABI dtype (bf16 RNE, or fp32)."""
+    if dtype == "bf16":
+        return round_f64_to_bf16(x)
+    return x.astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------
+# a1: copy-candidate retrieval  [SW, "무엇과 다른가"]
+
+def copy_match(ctx: np.ndarray, ctx_off: np.ndarray, kappa: int, W: int, D: int):
+    """For each sequence (context ctx[off[b]:off[b+1]], current token t = L-1):
+    the key is the kappa-gram ending at t.  Every earlier end position j
+    (kappa-1 <= j <= t-1) whose kappa-gram equals the key is an occurrence;
+    occurrences may overlap.  Up to W occurrences are kept, most recent (largest j)
+    first; candidate i continues the context after its occurrence:
+    ctx[j+1 .. j+len], len = min(D, t-j) (readings: exact id equality, truncation
+    at the end of the context, no de-duplication).  Missing candidates have len 0
+    and position -1; token slots past len hold -1."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    off = np.asarray(ctx_off, dtype=np.int64)
+    B = len(off) - 1
+    cand_tok = np.full((B, W, D), -1, dtype=np.int32)
+    cand_len = np.zeros((B, W), dtype=np.int32)
+    cand_pos = np.full((B, W), -1, dtype=np.int32)
+    n_found = np.zeros(B, dtype=np.int32)
+    flags = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        lo, hi = off[b], off[b + 1]
+        if not (0 <= lo <= hi <= len(ctx)):
+            flags[b] |= FLAG_BAD_CTX
+            continue
+        c = ctx[lo:hi]
+        L = len(c)
+        t = L - 1
+        if L < kappa + 1:
+            continue
+        key = c[t - kappa + 1:t + 1]
+        i = 0
+        for j in range(t - 1, kappa - 2, -1):
+            if i == W:
+                break
+            if np.array_equal(c[j - kappa + 1:j + 1], key):
+                ln = min(D, t - j)
+                cand_pos[b, i] = j
+                cand_len[b, i] = ln
+                cand_tok[b, i, :ln] = c[j + 1:j + 1 + ln]
+                i += 1
+        n_found[b] = i
+    return dict(cand_tok=cand_tok, cand_len=cand_len, cand_pos=cand_pos,
+                n_found=n_found, flags=flags)
+
+
+# ----------------------------------------------------------------------------------
+# a2: probe gate  [SW, "어떻게 동작하나" (bias-free probe) and "무엇과 다른가" (dual gate)]
+
+def probe_gate(h: np.ndarray, w: np.ndarray, tau: float, n_found=None):
+    """score = sigma(w . h) with no bias; the probe fires when score >= tau
+    ("tau or above"); the copy path opens when the probe fires AND the kappa-gram
+    has a prior occurrence (n_found >= 1).  h: [B, d] fp64 values, w: [d]."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    x = h @ w
+    score = 1.0 / (1.0 + np.exp(-x))
+    probe = score >= tau
+    if n_found is None:
+        gate = probe
+    else:
+        gate = probe & (np.asarray(n_found) >= 1)
+    flags = np.where(np.abs(score - tau) < PROBE_TIE_EPS, FLAG_PROBE_TIE, 0).astype(np.int32)
+    return dict(score=score, probe=probe.astype(np.int32), gate=gate.astype(np.int32),
+                flags=flags)
+
+
+# ----------------------------------------------------------------------------------
+# a3: block-triangular verify attention  [SW, "무엇과 다른가"]
+
+def gather_prefix(pool: np.ndarray, page_table: np.ndarray, b: int, P: int, page: int):
+    """Rows 0..P-1 of sequence b's prefix from a paged pool [n_pages, page, Hkv, hd].
+    Returns (rows [P, Hkv, hd], valid mask [P]) -- rows of out-of-range pages are
+    marked invalid."""
+    n_pages = pool.shape[0]
+    rows = np.zeros((P,) + pool.shape[2:], dtype=pool.dtype)
+    valid = np.zeros(P, dtype=bool)
+    for pos in range(0, P, page):
+        pg = int(page_table[b, pos // page])
+        n = min(page, P - pos)
+        if 0 <= pg < n_pages:
+            rows[pos:pos + n] = pool[pg, :n]
+            valid[pos:pos + n] = True
+    return rows, valid
+
+
+def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len,
+                     B, W, D, Hq, Hkv, scale=None, page=16, out_dtype="bf16"):
+    """Attention of every candidate row over the prefix and its own candidate.
+
+    Row r = i*D + o of sequence b holds candidate token (i, o).  Its query head hq
+    (KV head hq // (Hq/Hkv)) attends to every prefix key 0..P_b-1 and to the keys
+    of its own candidate at offsets 0..o (itself included); keys of other candidates
+    are invisible.  Scores are (q . k) * scale with scale = 1/sqrt(hd); weights are
+    the softmax of the visible scores; the output is the weighted sum of values.
+
+    Inputs are fp64 arrays (decoded): q [B*M, Hq, hd], k_cand/v_cand [B*M, Hkv, hd],
+    pools [n_pages, page, Hkv, hd].  Returns (O exact fp64, O rounded to out_dtype,
+    flags [B])."""
+    M = W * D
+    hd = q.shape[-1]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    O = np.zeros(q.shape, dtype=np.float64)
+    flags = np.zeros(B, dtype=np.int32)
+    max_keys = page_table.shape[1] * page
+    for b in range(B):
+        P = int(prefix_len[b])
+        if P < 0 or P > max_keys:
+            flags[b] |= FLAG_BAD_PAGE
+            P = min(max(P, 0), max_keys)
+        kp, valid = gather_prefix(k_pool, page_table, b, P, page)
+        vp, _ = gather_prefix(v_pool, page_table, b, P, page)
+        if not valid.all():
+            flags[b] |= FLAG_BAD_PAGE
+        for i in range(W):
+            rows = slice(b * M + i * D, b * M + (i + 1) * D)
+            for hq in range(Hq):
+                kv = hq // g
+                keys = np.concatenate([kp[:, kv, :], k_cand[rows, kv, :]], axis=0)   # [P+D, hd]
+                vals = np.concatenate([vp[:, kv, :], v_cand[rows, kv, :]], axis=0)
+                s = (q[rows, hq, :] @ keys.T) * scale                                  # [D, P+D]
+                vis = np.zeros((D, P + D), dtype=bool)
+                vis[:, :P] = valid[None, :]
+                for o in range(D):
+                    vis[o, P:P + o + 1] = True
+                s = np.where(vis, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.where(vis, np.exp(s - m), 0.0)
+                a = e / e.sum(axis=1, keepdims=True)
+                O[rows, hq, :] = a @ vals
+    return O, round_stage(O, out_dtype), flags
+
+
+# ----------------------------------------------------------------------------------
+# a4/a5: vocabulary projection  [SL, "방법론 / 아키텍처"]; softmax rows [SD, section 3]
+
+def _logsumexp_rows(z: np.ndarray) -> np.ndarray:
+    m = z.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def lm_head_full(H: np.ndarray, W_full, temperature: float = 1.0, dtype: str = "bf16",
+                 block: int = 8192):
+    """Full-rank head z = W_full h for every row h of H (z[r, v] = sum_k W[v,k] H[r,k]).
+    W_full may be bf16 bits (decoded here block by block).  Logits are stored as
+    fp32 (stage boundary); lse[r] = log sum_v exp(z[r,v]/T) is taken in fp64 from
+    the stored fp32 logits.  Returns (logits fp32 [M, V], lse fp64 [M])."""
+    H = np.asarray(H, dtype=np.float64)
+    V = W_full.shape[0]
+    z = np.empty((H.shape[0], V), dtype=np.float32)
+    for s in range(0, V, block):
+        Wb = as_f64(W_full[s:s + block], dtype)
+        z[:, s:s + block] = (H @ Wb.T).astype(np.float32)
+    lse = _logsumexp_rows(z.astype(np.float64) / temperature)
+    return z, lse
+
+
+def lm_head_lowrank(H: np.ndarray, W_down, W_up, temperature: float = 1.0,
+                    dtype: str = "bf16", block: int = 16384):
+    """SlimSpec head z = W_up (W_down h): the rank-r intermediate t = W_down h is kept
+    unrounded, then projected to the vocabulary.  Returns (logits fp32, lse fp64, t)."""
+    H = np.asarray(H, dtype=np.float64)
+    Wd = as_f64(W_down, dtype)
+    t = H @ Wd.T                                      # [M, r]
+    V = W_up.shape[0]
+    z = np.empty((H.shape[0], V), dtype=np.float32)
+    for s in range(0, V, block):
+        Wu = as_f64(W_up[s:s + block], dtype)
+        z[:, s:s + block] = (t @ Wu.T).astype(np.float32)
+    lse = _logsumexp_rows(z.astype(np.float64) / temperature)
+    return z, lse, t
+
+
+def head_softmax(logits: np.ndarray, lse: np.ndarray, temperature: float = 1.0):
+    """Row softmax exp(z/T - lse) in fp64 (the head's probability output)."""
+    return np.exp(logits.astype(np.float64) / temperature - lse[:, None])
+
+
+# ----------------------------------------------------------------------------------
+# a6: rejection sampling  [SD, sections 2-3]; longest verified continuation [SW]
+
+def _draw(r: np.ndarray, u: float):
+    """Categorical draw by inverse CDF over ascending token id:
+    k = min{k : C_k > u * S}, with C the running sum of r and S its total.
+    Returns (k, tie) where tie marks u*S within CDF_TIE_EPS*S of a CDF step."""
+    C = np.cumsum(r)
+    S = C[-1]
+    x = u * S
+    k = int(np.searchsorted(C, x, side="right"))
+    k = min(k, len(r) - 1)
+    lo = C[k - 1] if k > 0 else 0.0
+    tie = (abs(x - lo) < CDF_TIE_EPS * S) or (abs(C[k] - x) < CDF_TIE_EPS * S)
+    return k, tie
+
+
+def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
+                  temperature: float = 1.0, gate=None):
+    """Leviathan/Chen acceptance over W independent candidate chains, keeping the
+    longest accepted run.
+
+    p at a position is softmax(z/T) of the row that precedes it: the root logits for
+    offset 0, row (i, o-1) of the verify pass otherwise (row (i, o) holds token
+    (i, o) and judges token (i, o+1)).  Draft token x at (i, o) is accepted iff
+    u_acc[i,o] * Q < p(x), with Q = q[(i,o)][x] (dense drafts) or 1 (q is None:
+    deterministic copy drafts, a point mass on x).  This is alpha = min(1, p/q) of
+    section 3, written so that p >= q always accepts.  The chain stops at the first
+    rejection.  a_i = accepted length of candidate i; the chosen candidate is the
+    one with the longest run, ties to the smallest index.  After its a accepted
+    tokens one more token is drawn:
+      rejection at offset a: residual max(0, P - Qd), Qd the draft distribution at
+                             (i*, a) (a point mass on the draft token for copy drafts)
+      all accepted:          the bonus distribution softmax(row (i*, len-1))
+    by inverse CDF with u_res[i*].  Uniforms are indexed by position, not consumed.
+    Returns a dict of per-sequence results."""
+    root_logits = np.asarray(root_logits, dtype=np.float32)
+    logits = np.asarray(logits, dtype=np.float32)
+    B, W, D = cand_tok.shape
+    V = root_logits.shape[1]
+    M = W * D
+    T = float(temperature)
+    z_root = root_logits.astype(np.float64) / T
+    lse_root = _logsumexp_rows(z_root)
+    out = dict(
+        n_acc=np.zeros(B, dtype=np.int32), best=np.full(B, -1, dtype=np.int32),
+        out_tok=np.full((B, D + 1), -1, dtype=np.int32), n_out=np.zeros(B, dtype=np.int32),
+        acc_per_cand=np.zeros((B, W), dtype=np.int32), flags=np.zeros(B, dtype=np.int32),
+        abs_tie=np.zeros(B, dtype=bool),
+    )
+    lse_cache = {}
+
+    def row_p(b, prow):
+        """Target distribution (fp64) at the row that judges the next token."""
+        if prow < 0:
+            return np.exp(z_root[b] - lse_root[b])
+        r = b * M + prow
+        if r not in lse_cache:
+            zz = logits[r].astype(np.float64) / T
+            m = zz.max()
+            lse_cache[r] = (zz, m + np.log(np.exp(zz - m).sum()))
+        zz, l = lse_cache[r]
+        return np.exp(zz - l)
+
+    for b in range(B):
+        flags = 0
+        lens = np.asarray(cand_len[b]).copy()
+        if gate is not None and not gate[b]:
+            lens[:] = 0
+        a = np.zeros(W, dtype=np.int64)
+        for i in range(W):
+            if lens[i] < 1:
+                continue
+            a[i] = lens[i]
+            for o in range(lens[i]):
+                x = int(cand_tok[b, i, o])
+                prow = -1 if o == 0 else i * D + o - 1
+                if 0 <= x < V:
+                    p = row_p(b, prow)[x]
+                    Q = 1.0 if q is None else float(q[b * M + i * D + o, x])
+                else:
+                    flags |= FLAG_BAD_TOKEN
+                    p, Q = 0.0, 1.0
+                lhs = u_acc[b, i, o] * Q
+                if abs(lhs - p) < ACCEPT_TIE_REL * max(p, lhs):
+                    flags |= FLAG_ACCEPT_TIE
+                if abs(lhs - p) < 1e-4:
+                    out["abs_tie"][b] = True
+                if not (lhs < p):
+                    a[i] = o
+                    break
+        out["acc_per_cand"][b] = a
+        have = np.nonzero(lens >= 1)[0]
+        if len(have) == 0:
+            # no candidate: one token from the target distribution at the current token
+            r = row_p(b, -1)
+            y, tie = _draw(r, u_res[b, 0])
+            out["out_tok"][b, 0] = y
+            out["n_out"][b] = 1
+            out["n_acc"][b] = 0
+            out["best"][b] = -1
+            out["flags"][b] = flags | FLAG_NO_CANDIDATE | (FLAG_CDF_TIE if tie else 0)
+            continue
+        best = int(have[np.argmax(a[have])])          # argmax returns the first maximum
+        ab = int(a[best])
+        out["best"][b] = best
+        out["n_acc"][b] = ab
+        out["out_tok"][b, :ab] = cand_tok[b, best, :ab]
+        prow = -1 if ab == 0 else best * D + ab - 1
+        P = row_p(b, prow)
+        if ab < lens[best]:
+            x = int(cand_tok[b, best, ab])
+            if q is None:
+                Qd = np.zeros(V)
+                if 0 <= x < V:
+                    Qd[x] = 1.0
+            else:
+                Qd = q[b * M + best * D + ab].astype(np.float64)
+            r = np.maximum(0.0, P - Qd)
+        else:
+            r = P
+        if not (r.sum() > 0.0):
+            r = P
+            flags |= FLAG_DEGENERATE
+        y, tie = _draw(r, u_res[b, best])
+        if tie:
+            flags |= FLAG_CDF_TIE
+        out["out_tok"][b, ab] = y
+        out["n_out"][b] = ab + 1
+        out["flags"][b] = flags
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# a7: the whole verify step
+
+def verify_step(case_arrays: dict, shape, drafts=None, q_override=None):
+    """copy_match -> probe_gate -> verify_attention -> lm_head -> reject_sample on one
+    batch.  `drafts` = (cand_tok, cand_len) for the neural-draft path (copy retrieval
+    skipped, gate open).  Returns every stage's outputs."""
+    A = case_arrays
+    sh = shape
+    res = {}
+    if drafts is None:
+        cm = copy_match(A["ctx"], A["ctx_off"], sh.kappa, sh.W, sh.D)
+        pg = probe_gate(as_f64(A["probe_h"], sh.dtype), A["probe_w"], sh.tau, cm["n_found"])
+        cand_tok, cand_len, gate = cm["cand_tok"], cm["cand_len"], pg["gate"]
+        res.update(copy=cm, probe=pg)
+    else:
+        cand_tok, cand_len = drafts
+        gate = np.ones(sh.B, dtype=np.int32)
+    O, O_r, aflags = verify_attention(
+        as_f64(A["q"], sh.dtype), as_f64(A["k_cand"], sh.dtype), as_f64(A["v_cand"], sh.dtype),
+        as_f64(A["k_pool"], sh.dtype), as_f64(A["v_pool"], sh.dtype), A["page_table"],
+        A["prefix_len"], sh.B, sh.W, sh.D, sh.Hq, sh.Hkv, out_dtype=sh.dtype)
+    H = O_r.reshape(O_r.shape[0], -1)
+    logits, lse = lm_head_full(H, A["w_full"], sh.temperature, sh.dtype)
+    q = q_override if q_override is not None else A.get("q_draft")
+    rs = reject_sample(A["root_logits"], logits, q, cand_tok, cand_len, A["u_acc"],
+                       A["u_res"], sh.temperature, gate)
+    res.update(attn=O_r, attn_exact=O, attn_flags=aflags, logits=logits, lse=lse, sample=rs,
+               cand_tok=cand_tok, cand_len=cand_len, gate=gate)
+    return res

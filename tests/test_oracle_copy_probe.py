@@ -1,0 +1,156 @@
+"""Pins for the oracle's copy retrieval and probe gate (CPU only).
+
+copy retrieval: SwitchSD summary (onedev.kr/papers/87), 'How it differs'.
+probe: same page, 'How it works' (bias-free linear probe sigma(w.h)) and
+'How it differs' (copy path opens iff score >= tau and the kappa-gram recurs).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from verification_step_amd import workloads as wl
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _csr(seqs):
+    ctx = np.concatenate([np.asarray(s, dtype=np.int32) for s in seqs]) if seqs else np.zeros(0, np.int32)
+    off = np.concatenate([[0], np.cumsum([len(s) for s in seqs])]).astype(np.int32)
+    return ctx, off
+
+
+def brute_occurrences(c, kappa):
+    """All earlier end positions of the trailing kappa-gram, found by comparing
+    Python tuples of every window (independent of the oracle's scan)."""
+    L = len(c)
+    if L < kappa + 1:
+        return []
+    key = tuple(c[L - kappa:])
+    windows = {j: tuple(c[j - kappa + 1:j + 1]) for j in range(kappa - 1, L - 1)}
+    return sorted([j for j, w in windows.items() if w == key], reverse=True)
+
+
+def test_golden_cases():
+    d = json.load(open(os.path.join(GOLD, "copy_match_cases.json")))
+    for case in d["cases"]:
+        ctx, off = _csr([case["ctx"]])
+        r = oracle.copy_match(ctx, off, case["kappa"], case["W"], case["D"])
+        assert r["cand_pos"][0].tolist() == case["cand_pos"], case["name"]
+        assert r["cand_len"][0].tolist() == case["cand_len"], case["name"]
+        assert r["cand_tok"][0].tolist() == case["cand_tok"], case["name"]
+        assert int(r["n_found"][0]) == case["n_found"], case["name"]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_small_alphabet(seed):
+    """Random contexts over a 3-letter alphabet (many overlapping matches)."""
+    rng = np.random.default_rng(seed)
+    kappa = int(rng.integers(1, 6))
+    W = int(rng.integers(1, 6))
+    D = int(rng.integers(1, 7))
+    seqs = [rng.integers(0, 3, size=int(rng.integers(0, 60))) for _ in range(4)]
+    ctx, off = _csr(seqs)
+    r = oracle.copy_match(ctx, off, kappa, W, D)
+    for b, c in enumerate(seqs):
+        occ = brute_occurrences(list(c), kappa)[:W]
+        t = len(c) - 1
+        assert int(r["n_found"][b]) == len(occ)
+        for i in range(W):
+            if i < len(occ):
+                j = occ[i]
+                ln = min(D, t - j)
+                assert r["cand_pos"][b, i] == j
+                assert r["cand_len"][b, i] == ln
+                assert r["cand_tok"][b, i, :ln].tolist() == list(c[j + 1:j + 1 + ln])
+                assert (r["cand_tok"][b, i, ln:] == -1).all()
+            else:
+                assert r["cand_pos"][b, i] == -1 and r["cand_len"][b, i] == 0
+                assert (r["cand_tok"][b, i] == -1).all()
+
+
+def test_invariants_on_generated_context():
+    """Llama-8B-shaped context with planted repeats and the forced trailing plant:
+    the planted end positions (known by construction) are returned first, in order,
+    with full-length continuations; every returned window equals the key."""
+    sh = wl.config(2)
+    case = wl.make_case(sh, 2000, "measure", with_head=False, with_q=False)
+    A = case.arrays
+    r = oracle.copy_match(A["ctx"], A["ctx_off"], sh.kappa, sh.W, sh.D)
+    ends = case.meta["forced_ends"][0]
+    assert len(ends) == sh.W
+    c = A["ctx"]
+    t = len(c) - 1
+    key = c[t - 4:t + 1]
+    pos = r["cand_pos"][0]
+    assert (np.diff(pos) < 0).all()
+    for j in pos:
+        assert (c[j - 4:j + 1] == key).all()
+    # nothing more recent than the last returned position was skipped
+    for j in range(int(pos[-1]) + 1, t):
+        if j not in pos:
+            assert not (c[j - 4:j + 1] == key).all()
+    assert pos.tolist() == ends                      # planted occurrences are the most recent
+    assert (r["cand_len"][0] == sh.D).all()
+
+
+def test_tiny_config_plant():
+    sh = wl.config(1)
+    case = wl.make_case(sh, 1000)
+    A = case.arrays
+    r = oracle.copy_match(A["ctx"], A["ctx_off"], sh.kappa, sh.W, sh.D)
+    occ = brute_occurrences(list(A["ctx"]), sh.kappa)
+    assert case.meta["forced_ends"][0][0] in occ
+    assert int(r["n_found"][0]) == min(len(occ), sh.W) >= 1
+
+
+def test_bad_offsets_flagged():
+    ctx = np.arange(10, dtype=np.int32)
+    off = np.array([0, 12], dtype=np.int32)
+    r = oracle.copy_match(ctx, off, 5, 2, 2)
+    assert r["flags"][0] & oracle.FLAG_BAD_CTX and r["n_found"][0] == 0
+
+
+# ---------------------------------------------------------------------------- probe
+
+def test_probe_against_library_sigmoid():
+    rng = np.random.default_rng(3)
+    B, d = 6, 96
+    h = rng.standard_normal((B, d))
+    w = rng.standard_normal(d) / math.sqrt(d)
+    r = oracle.probe_gate(h, w, 0.4, np.array([1, 0, 2, 1, 0, 3]))
+    for b in range(B):
+        x = math.fsum(float(h[b, k]) * float(w[k]) for k in range(d))
+        s = float(scipy.special.expit(x))
+        assert abs(r["score"][b] - s) < 1e-14
+        assert r["probe"][b] == (s >= 0.4)
+        assert r["gate"][b] == ((s >= 0.4) and b not in (1, 4))
+
+
+def test_probe_closed_forms():
+    h = np.zeros((3, 8))
+    w = np.ones(8)
+    r = oracle.probe_gate(h, w, 0.4, np.array([1, 0, 5]))
+    assert np.all(r["score"] == 0.5)               # sigma(0) = 1/2
+    assert r["gate"].tolist() == [1, 0, 1]          # 1/2 >= 0.4; n_found gates
+    r = oracle.probe_gate(h, w, 0.5, np.array([1, 1, 1]))
+    assert r["probe"].tolist() == [1, 1, 1]        # "tau or above" is inclusive
+    assert (r["flags"] & oracle.FLAG_PROBE_TIE).all()
+    # a large negative projection closes the probe
+    r = oracle.probe_gate(-np.ones((1, 8)), w, 0.4, np.array([3]))
+    assert r["probe"][0] == 0 and abs(r["score"][0] - 1 / (1 + math.e ** 8)) < 1e-15
+
+
+def test_forced_open_recipe_fires_probe():
+    for c in (1, 2, 4, 5):
+        sh = wl.config(c)
+        if c == 5:
+            sh = sh.with_(B=4, P=sh.P[:4])
+        case = wl.make_case(sh.with_(V=min(sh.V, 1024)), 77, "measure", with_head=False, with_q=False)
+        A = case.arrays
+        r = oracle.probe_gate(oracle.as_f64(A["probe_h"], sh.dtype), A["probe_w"], sh.tau)
+        assert (r["probe"] == 1).all()

@@ -1,0 +1,276 @@
+"""Pins for the oracle's rejection sampler (CPU only).
+
+Rejection-sampling blog (blog.huny.dev), sections 2-3: accept draft x with
+probability alpha = min(1, p(x)/q(x)); on rejection draw from
+p' = max(0, p-q)/sum max(0, p-q); all drafts accepted -> a bonus token from the
+next position's p; identity P_final = min(p,q) + max(0,p-q) = p (lossless).
+Section 5's five checks are mirrored with our own values (the page's numbers
+were lost in extraction).  SwitchSD summary, 'How it differs': among W
+candidates keep the longest verified continuation.
+
+The exact-law pins compute the law of the oracle *implementation's* output by
+locating, by bisection on the oracle itself, the thresholds in each uniform at
+which its decision changes; the law is then compared with the closed form.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _logits_of(p):
+    return np.log(np.asarray(p, dtype=np.float64)).astype(np.float32)
+
+
+def _stored_p(p):
+    """Target probabilities as the sampler sees them: softmax of the fp32 logits."""
+    z = _logits_of(p).astype(np.float64)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def run(root_p, rows_p, q, toks, lens, u_acc, u_res, W, D):
+    V = len(root_p)
+    root = _logits_of(root_p)[None, :]
+    logits = np.stack([_logits_of(r) for r in rows_p]) if rows_p else np.zeros((W * D, V), np.float32)
+    return oracle.reject_sample(root, logits, q, np.asarray(toks, np.int32).reshape(1, W, D),
+                                np.asarray(lens, np.int32).reshape(1, W),
+                                np.asarray(u_acc, np.float64).reshape(1, W, D),
+                                np.asarray(u_res, np.float64).reshape(1, W))
+
+
+# ----------------------------------------------------------------- section 5 cases
+
+def test_case1_target_dominates_always_accepts():
+    p = [0.1, 0.6, 0.3]
+    q = np.array([[0.3, 0.4, 0.3]], dtype=np.float32)      # p(1)=0.6 >= q(1)=0.4
+    for u in (0.01, 0.25, 0.5, 0.75, 0.9999):
+        r = run(p, [p], q, [1], [1], [u], [0.5], 1, 1)
+        assert r["n_acc"][0] == 1 and r["out_tok"][0, 0] == 1
+
+
+def test_case2_threshold():
+    g = json.load(open(os.path.join(GOLD, "sampler_cases.json")))["threshold_case"]
+    p = [g["p_x"], 1 - g["p_x"]]
+    q = np.array([[g["q_x"], 1 - g["q_x"]]], dtype=np.float32)
+    ra = run(p, [p], q, [0], [1], [g["u_accept"]], [0.5], 1, 1)
+    rr = run(p, [p], q, [0], [1], [g["u_reject"]], [0.5], 1, 1)
+    assert ra["n_acc"][0] == 1 and rr["n_acc"][0] == 0
+
+
+def test_case3_residual_normalised_and_zero_where_draft_overproposes():
+    p = np.array([0.1, 0.2, 0.3, 0.4])
+    qd = np.array([0.4, 0.3, 0.2, 0.1])
+    q = qd.astype(np.float32)[None, :]
+    # rejection of token 0 (q > p there); scan the residual draw over u_res
+    emitted = []
+    for u in np.linspace(0.0005, 0.9995, 2000):
+        r = run(p, [p], q, [0], [1], [0.999], [u], 1, 1)
+        assert r["n_acc"][0] == 0
+        emitted.append(int(r["out_tok"][0, 0]))
+    emitted = np.array(emitted)
+    freq = np.bincount(emitted, minlength=4) / len(emitted)
+    resid = np.maximum(0.0, _stored_p(p) - qd.astype(np.float32))
+    resid /= resid.sum()
+    assert freq[0] == 0 and freq[1] == 0                  # over-proposed tokens get nothing
+    assert np.abs(freq - resid).max() < 2e-3              # grid resolution 1/2000
+    assert abs(resid.sum() - 1) < 1e-15
+
+
+def test_case4_all_accepted_gives_bonus_from_last_row():
+    V, K = 5, 3
+    toks = [2, 0, 4]
+    near_one = lambda k: [0.996 if j == k else 0.001 for j in range(V)]
+    rows = [near_one(0), near_one(4), near_one(3)]          # rows judge toks[1], toks[2], bonus
+    q = np.full((K, V), 0.2, dtype=np.float32)
+    r = run(near_one(2), rows, q, toks, [K], [0.5] * K, [0.5], 1, K)
+    assert r["n_acc"][0] == 3 and r["n_out"][0] == 4
+    assert r["out_tok"][0].tolist() == [2, 0, 4, 3]         # bonus = argmax of row K-1
+
+
+# ----------------------------------------------------------------- exact laws
+
+def _threshold(f, lo=0.0, hi=1.0, it=64):
+    """sup{u in [lo,hi): f(u)} for a predicate true on [lo, theta) and false after."""
+    if not f(lo):
+        return lo
+    if f(np.nextafter(hi, 0)):
+        return hi
+    for _ in range(it):
+        mid = 0.5 * (lo + hi)
+        if f(mid):
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def exact_law(root_p, rows_p, qrows, D, V, W=1):
+    """Law of (first token, second token | n_out >= 2) of the oracle's output with
+    drafts x_o ~ q_o independently, for W=1.  Uses bisection on the oracle only."""
+    first = np.zeros(V)
+    second = np.zeros(V)
+    p_second_mass = 0.0
+    q = np.asarray(qrows, dtype=np.float32)
+    for path in itertools.product(range(V), repeat=D):
+        w_path = float(np.prod([float(q[o, path[o]]) for o in range(D)]))
+        if w_path == 0.0:
+            continue
+        # threshold of each acceptance test (earlier tests forced to accept with u=0)
+        th = []
+        for o in range(D):
+            def acc(u, o=o):
+                ua = [0.0] * D
+                ua[o] = u
+                if o + 1 < D:
+                    ua[o + 1] = np.nextafter(1.0, 0)
+                r = run(root_p, rows_p, q, list(path), [D], ua, [0.5], 1, D)
+                return r["n_acc"][0] >= o + 1
+            th.append(_threshold(acc))
+        for a in range(D + 1):
+            pa = np.prod(th[:a]) * ((1 - th[a]) if a < D else 1.0)
+            if pa == 0.0:
+                continue
+            ua = [t * 0.5 for t in th[:a]] + ([(1 + th[a]) * 0.5] if a < D else [])
+            ua = (ua + [0.5] * D)[:D]
+
+            def tok_le(k, u):
+                r = run(root_p, rows_p, q, list(path), [D], ua, [u], 1, D)
+                assert r["n_acc"][0] == a
+                return r["out_tok"][0, a] <= k
+            F = [_threshold(lambda u, k=k: tok_le(k, u)) for k in range(V)]
+            law_y = np.diff(np.concatenate([[0.0], F]))
+            if a == 0:
+                first += w_path * pa * law_y
+            else:
+                first[path[0]] += w_path * pa
+                p_second_mass += w_path * pa
+                if a == 1:
+                    second += w_path * pa * law_y
+                else:
+                    second[path[1]] += w_path * pa
+    return first, second / max(p_second_mass, 1e-300), p_second_mass
+
+
+def _dyadic(p, bits=20):
+    """Probabilities k/2^bits summing to exactly one (exact in fp32), so the draft
+    law sums to one in the exact arithmetic of the identity."""
+    k = np.floor(np.asarray(p) * 2 ** bits).astype(np.int64)
+    k[np.argmax(k)] += 2 ** bits - k.sum()
+    return k / 2.0 ** bits
+
+
+@pytest.mark.parametrize("seed,V,D", [(0, 3, 1), (1, 4, 1), (2, 5, 1), (3, 3, 2), (4, 4, 2)])
+def test_emitted_law_equals_target_exactly(seed, V, D):
+    """Identity P_final = p: the first emitted token follows the root target
+    distribution, and given a second token it follows row 0's distribution."""
+    rng = np.random.default_rng(seed)
+    root_p = rng.dirichlet(np.ones(V))
+    rows_p = [rng.dirichlet(np.ones(V)) for _ in range(D)]
+    qrows = [_dyadic(rng.dirichlet(np.ones(V))) for _ in range(D)]
+    first, second, m2 = exact_law(root_p, rows_p, qrows, D, V)
+    assert np.abs(first - _stored_p(root_p)).max() < 1e-9
+    assert np.abs(second - _stored_p(rows_p[0])).max() < 1e-9
+    # acceptance law: P(a >= 1) = beta_0 = sum_x min(p_0(x), q_0(x))
+    beta0 = np.minimum(_stored_p(root_p), np.asarray(qrows[0], np.float32)).sum()
+    assert abs(m2 - beta0) < 1e-9
+
+
+def test_monte_carlo_50k_within_4_sigma():
+    """Section 5, case 5: 50,000 trials with strongly mismatched p and q."""
+    rng = np.random.default_rng(11)
+    V, N = 4, 50000
+    p = np.array([0.7, 0.1, 0.1, 0.1])
+    qd = np.array([0.05, 0.05, 0.1, 0.8], dtype=np.float32)
+    root = _logits_of(p)[None, :]
+    row = _logits_of(np.full(V, 0.25))[None, :]
+    counts = np.zeros(V)
+    xs = rng.choice(V, size=N, p=qd.astype(np.float64) / qd.sum())
+    ua = rng.random(N)
+    ur = rng.random(N)
+    for n in range(N):
+        r = oracle.reject_sample(root, row, qd[None, :], np.array([[[xs[n]]]], np.int32),
+                                 np.array([[1]], np.int32), np.array([[[ua[n]]]]),
+                                 np.array([[ur[n]]]))
+        counts[r["out_tok"][0, 0]] += 1
+    f = counts / N
+    ps = _stored_p(p)
+    assert (np.abs(f - ps) <= 4 * np.sqrt(ps * (1 - ps) / N)).all()
+
+
+def test_greedy_limit_any_W():
+    """One-hot target rows: the result is the longest prefix agreeing with the
+    argmax chain, then the argmax, for any number of candidates."""
+    V, W, D = 6, 3, 3
+    hot = lambda k: [1 - 1e-30 * (V - 1) if j == k else 1e-30 for j in range(V)]
+    greedy = [4, 1, 5, 2]                        # argmax at root, rows (.,0), (.,1), (.,2)
+    toks = [[4, 1, 0], [4, 1, 5], [3, 1, 5]]
+    rows = []
+    for i in range(W):
+        rows += [hot(greedy[1]), hot(greedy[2]), hot(greedy[3])]
+    q = np.full((W * D, V), 1.0 / V, dtype=np.float32)
+    r = run(hot(greedy[0]), rows, q, toks, [D] * W, [0.3] * (W * D), [0.7] * W, W, D)
+    assert r["acc_per_cand"][0].tolist() == [2, 3, 0]
+    assert r["best"][0] == 1 and r["out_tok"][0].tolist() == greedy
+
+
+def test_multi_candidate_counterexample_law():
+    g = json.load(open(os.path.join(GOLD, "sampler_cases.json")))["multi_candidate_counterexample"]
+    p = np.array(g["p"])
+    # enumerate the 2 acceptance uniforms on thresholds and the residual uniform
+    law = np.zeros(2)
+    q = np.array([g["q"], g["q"]], dtype=np.float32)
+    for ua0, w0 in ((0.25, 0.5), (0.75, 0.5)):
+        for ua1, w1 in ((0.25, 0.5), (0.75, 0.5)):
+            for ur, wr in ((0.25, 0.5), (0.75, 0.5)):
+                r = run(p, [p, p], q, [0, 0], [1, 1], [ua0, ua1], [ur, ur], 2, 1)
+                law[r["out_tok"][0, 0]] += w0 * w1 * wr
+    assert np.allclose(law, g["first_token_law"], atol=1e-12)
+
+
+def test_point_mass_drafts():
+    g = json.load(open(os.path.join(GOLD, "sampler_cases.json")))["point_mass_case"]
+    p = g["p"]
+    x = g["x"]
+    th = _threshold(lambda u: run(p, [p], None, [x], [1], [u], [0.5], 1, 1)["n_acc"][0] == 1)
+    assert abs(th - g["accept_prob"]) < 1e-7
+    law = np.zeros(3)
+    F = [_threshold(lambda u, k=k: run(p, [p], None, [x], [1], [0.99], [u], 1, 1)["out_tok"][0, 0] <= k)
+         for k in range(3)]
+    law = np.diff(np.concatenate([[0.0], F]))
+    assert np.allclose(law, g["replacement_law"], atol=1e-7)
+
+
+def test_no_candidate_samples_root_and_flags():
+    p = [0.25, 0.5, 0.25]
+    r = run(p, [p, p], None, [0, 1], [0, 0], [0.1, 0.1], [0.6, 0.1], 2, 1)
+    assert r["n_out"][0] == 1 and r["best"][0] == -1 and r["out_tok"][0, 0] == 1
+    assert r["flags"][0] & oracle.FLAG_NO_CANDIDATE
+    # closed gate behaves the same even with candidates present
+    root = _logits_of(p)[None, :]
+    rr = oracle.reject_sample(root, np.stack([_logits_of(p)] * 2), None,
+                              np.array([[[0], [1]]], np.int32), np.array([[1, 1]], np.int32),
+                              np.array([[[0.1], [0.1]]]), np.array([[0.6, 0.1]]), gate=[0])
+    assert rr["n_out"][0] == 1 and rr["flags"][0] & oracle.FLAG_NO_CANDIDATE
+
+
+def test_degenerate_residual_falls_back_to_target():
+    p = [0.5, 0.5]
+    q = np.array([[0.9, 0.6]], dtype=np.float32)           # q >= p everywhere (unnormalised input)
+    r = run(p, [p], q, [0], [1], [0.99], [0.75], 1, 1)
+    assert r["n_acc"][0] == 0 and r["flags"][0] & oracle.FLAG_DEGENERATE
+    assert r["out_tok"][0, 0] == 1
+
+
+def test_ties_choose_smallest_candidate_and_bad_token_rejects():
+    p = [0.5, 0.5]
+    r = run(p, [p, p], None, [0, 1], [1, 1], [0.1, 0.1], [0.3, 0.3], 2, 1)
+    assert r["acc_per_cand"][0].tolist() == [1, 1] and r["best"][0] == 0
+    r = run(p, [p], None, [7], [1], [0.0], [0.3], 1, 1)
+    assert r["n_acc"][0] == 0 and r["flags"][0] & oracle.FLAG_BAD_TOKEN

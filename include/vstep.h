@@ -1,0 +1,241 @@
+/* vstep.h -- C ABI of the speculative-decoding verify step for AMD MI355X (gfx950).
+ *
+ * The verify step of speculative decoding, on one GPU:
+ *   copy retrieval  -> probe gate -> block-triangular verify attention
+ *   -> vocabulary projection (full or low-rank) -> rejection sampling.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SW] "SwitchSD는 LLM 내부 표현으로 추측 디코딩의 복사 모드를 판별한다" (onedev.kr/papers/87),
+ *        sections "어떻게 동작하나" (how it works) and "무엇과 다른가" (how it differs).
+ *   [SD] "LLM 투기적 디코딩(Speculative Decoding) 해부 ..." (blog.huny.dev), section 2
+ *        (draft / parallel verify / rejection sampler / bonus token) and section 3
+ *        (alpha(x) = min(1, p/q), residual p'(x), P_final identity).
+ *   [SL] "SlimSpec: Low-Rank Draft LM-Head for Accelerated Speculative Decoding"
+ *        (gist.science/ko/paper/2605.10453), "방법론 / 아키텍처": z = W_up W_down h.
+ *
+ * Conventions (every entry point):
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates or frees memory and keeps no state between calls other than
+ *     its loaded code object.
+ *   - Every call only ENQUEUES work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns at once; outputs are valid after the stream is synchronised.
+ *   - The return value reports host-side validation (checked before anything is
+ *     launched: nothing is enqueued when a call fails validation) and launch errors.
+ *     Conditions that only the device can see (bad page index, bad token id, near
+ *     ties) come back in per-sequence `flags` outputs (VS_FLAG_*).
+ *   - Workspace: calls that take `workspace` need at least the size reported by the
+ *     matching vs_*_workspace_bytes function.  The workspace must be filled with
+ *     zeros before its first use; every call leaves its counters at zero again, so a
+ *     workspace can be reused by later calls on the same stream.  Calls that share a
+ *     workspace must not run concurrently (on different streams).
+ *   - Thread-safe and re-entrant as long as concurrent calls use distinct outputs and
+ *     workspaces.  No C++ exception crosses this interface.
+ *   - Layouts are row-major (C order).  "bf16" is the 16-bit brain float (top half of
+ *     an IEEE fp32), rounded to nearest-even wherever the library writes it.
+ */
+#ifndef VSTEP_H
+#define VSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VS_ABI_VERSION 1
+
+typedef enum {
+    VS_OK = 0,
+    VS_ERR_INVALID_ARG = -1,   /* null required pointer, non-positive or inconsistent size */
+    VS_ERR_UNSUPPORTED = -2,   /* valid request outside what the kernels implement */
+    VS_ERR_WORKSPACE = -3,     /* workspace null or smaller than required */
+    VS_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} vs_status;
+
+typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
+
+/* Per-sequence device flags (bitwise OR). */
+enum {
+    VS_FLAG_PROBE_TIE = 1,            /* |score - tau| < 1e-5: probe decision is a near tie */
+    VS_FLAG_ACCEPT_TIE = 2,           /* a decisive acceptance test has |u*Q - p| < 1e-4*max(p, u*Q) */
+    VS_FLAG_CDF_TIE = 4,              /* the final draw lies within 1e-8*S of a CDF step */
+    VS_FLAG_DEGENERATE_RESIDUAL = 8,  /* residual mass <= 0: drew from the target p instead */
+    VS_FLAG_NO_CANDIDATE = 16,        /* gate closed or no candidate: one token from the root p */
+    VS_FLAG_BAD_PAGE = 32,            /* page index outside the pool, or prefix_len out of range */
+    VS_FLAG_BAD_CTX = 64,             /* context offsets outside [0, ctx_total] or decreasing */
+    VS_FLAG_BAD_TOKEN = 128           /* candidate token id outside [0, V): treated as rejected */
+};
+
+int         vs_abi_version(void);
+const char *vs_status_str(int status);
+
+/* ---------------------------------------------------------------------------------
+ * Copy-candidate retrieval [SW "무엇과 다른가"].
+ * For each sequence b, the context is ctx[ctx_off[b] .. ctx_off[b+1]) (token ids),
+ * its last token is the current token t.  The key is the kappa-gram ending at t.
+ * Every earlier end position j (kappa-1 <= j <= t-1) whose kappa ids equal the key
+ * is an occurrence (overlaps allowed).  The W largest j are kept, most recent
+ * first; candidate i is ctx[j+1 .. j+len], len = min(D, t-j).
+ *   ctx       int32 [ctx_total]
+ *   ctx_off   int32 [B+1]     (device; checked on the device: bad offsets -> VS_FLAG_BAD_CTX)
+ *   cand_tok  int32 [B, W, D] out: candidate ids, -1 past len
+ *   cand_len  int32 [B, W]    out: 0 for missing candidates
+ *   cand_pos  int32 [B, W]    out: end position j of the occurrence, or -1
+ *   n_found   int32 [B]       out: number of candidates returned (<= W)
+ *   flags     int32 [B]       out (may be NULL)
+ * Limits: 1 <= kappa <= 16, 1 <= W, 1 <= D, W*D <= 1024, B >= 1.  Bit-exact. */
+int vs_copy_match(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B,
+                  int kappa, int W, int D, int32_t *cand_tok, int32_t *cand_len,
+                  int32_t *cand_pos, int32_t *n_found, int32_t *flags, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Probe gate [SW "어떻게 동작하나": bias-free linear probe; "무엇과 다른가": dual gate].
+ * score[b] = sigmoid(sum_k w[k] h[b,k]) (fp32 products and accumulation, sigmoid in
+ * fp64, stored fp32); gate[b] = (score >= tau) && (n_found == NULL || n_found[b] >= 1).
+ *   h      [B, d] of h_dtype (VS_F32 or VS_BF16)
+ *   w      fp32 [d]
+ *   n_found int32 [B] or NULL
+ *   score  fp32 [B] out;  gate int32 [B] out;  flags int32 [B] out or NULL (VS_FLAG_PROBE_TIE) */
+int vs_probe_gate(const void *h, int h_dtype, const float *w, int B, int d, float tau,
+                  const int32_t *n_found, float *score, int32_t *gate, int32_t *flags,
+                  void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Block-triangular verify attention [SW "무엇과 다른가"].
+ * Row r = i*D + o of sequence b holds candidate token (i, o).  For query head hq
+ * (KV head hq / (Hq/Hkv)), the row attends to prefix keys 0..prefix_len[b]-1 and to
+ * the keys of its own candidate at offsets 0..o (itself included); other candidates
+ * are invisible.  softmax(scale * q.k) over the visible keys, weighted sum of values.
+ *   q             [B*W*D, Hq, hd]   dtype
+ *   k_cand/v_cand [B*W*D, Hkv, hd]  dtype (the candidates' own keys/values)
+ *   k_pool/v_pool [n_pool_pages, page_size, Hkv, hd] dtype (paged prefix cache)
+ *   page_table    int32 [B, max_pages]: page of prefix positions 16p..16p+15
+ *   prefix_len    int32 [B]
+ *   out           [B*W*D, Hq, hd] dtype (bf16 rounded to nearest even, or fp32)
+ *   flags         int32 [B] out or NULL (VS_FLAG_BAD_PAGE: keys of a bad page are skipped)
+ * Supported: VS_BF16 with head_dim 128 (MFMA path); VS_F32 with head_dim 16, 32 or 64.
+ * page_size must be 16.  scale <= 0 selects 1/sqrt(head_dim).  Accumulation in fp32. */
+typedef struct {
+    int32_t B, W, D, Hq, Hkv, head_dim, page_size, max_pages, n_pool_pages;
+    int32_t dtype;          /* vs_dtype */
+    float scale;
+} vs_attn_desc;
+
+size_t vs_attention_workspace_bytes(const vs_attn_desc *desc);
+int vs_verify_attention(const vs_attn_desc *desc, const void *q, const void *k_cand,
+                        const void *v_cand, const void *k_pool, const void *v_pool,
+                        const int32_t *page_table, const int32_t *prefix_len, void *out,
+                        int32_t *flags, void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Vocabulary projection [SL "방법론 / 아키텍처"].
+ *   rank == 0: z = W_full h            (w_full [V, d] dtype)
+ *   rank  > 0: z = W_up (W_down h)     (w_down [rank, d], w_up [V, rank]; the rank-r
+ *              intermediate is kept in fp32, not rounded to dtype)
+ * for every row h of `h` [M, d] (dtype).  Outputs:
+ *   logits  fp32 [M, V] (required)
+ *   row_lse fp64 [M]    (required): log sum_v exp(z[r,v] / temperature), from the fp32 logits
+ *   probs   fp32 [M, V] or NULL: exp(z/temperature - lse) when write_probs != 0
+ * Supported: VS_BF16 (MFMA path, d % 32 == 0, rank % 32 == 0) and VS_F32 (any d). */
+typedef struct {
+    int32_t M, d, V, rank;  /* rank 0 = full-rank head */
+    int32_t dtype;          /* vs_dtype */
+    float temperature;      /* > 0 */
+    int32_t write_probs;
+} vs_head_desc;
+
+size_t vs_head_workspace_bytes(const vs_head_desc *desc);
+int vs_lm_head(const vs_head_desc *desc, const void *h, const void *w_full,
+               const void *w_down, const void *w_up, float *logits, double *row_lse,
+               float *probs, void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Rejection sampling [SD sections 2-3] keeping the longest verified run [SW].
+ * Candidate i of sequence b is judged token by token: draft x at offset o is
+ * accepted iff u_acc[b,i,o] * Q < p(x), where p = softmax(z/T) of the preceding row
+ * (root_logits[b] for o = 0, row (b, i, o-1) of `logits` otherwise) and
+ * Q = q[(b,i,o)][x] (dense drafts) or 1 (q == NULL: copy drafts, a point mass on x).
+ * The scan stops at the first rejection; a_i = accepted length.  The candidate
+ * with the largest a_i wins (ties: smallest i).  Its a tokens are emitted, then one
+ * more token drawn by inverse CDF over ascending ids with u_res[b, best]:
+ *   rejection at offset a -> residual max(0, p - Qd) (Qd = q row (b,i,a), or the
+ *                            point mass on the draft token);
+ *   all accepted          -> bonus softmax(row (b, i, len-1)/T).
+ * No candidate (all cand_len 0, or gate[b] == 0): one token from softmax(root/T)
+ * drawn with u_res[b, 0], VS_FLAG_NO_CANDIDATE.  All sampler arithmetic is fp64.
+ *   root_logits fp32 [B, V]; logits fp32 [B*W*D, V]; row_lse fp64 [B*W*D] (from vs_lm_head)
+ *   q fp32 [B*W*D, V] or NULL; cand_tok int32 [B,W,D]; cand_len int32 [B,W]
+ *   u_acc fp64 [B,W,D]; u_res fp64 [B,W]  (uniforms in [0,1), indexed by position)
+ *   gate int32 [B] or NULL (NULL = open)
+ * Outputs: n_acc [B], best [B] (-1 if none), out_tok [B, D+1] (-1 padded),
+ *   n_out [B] (= n_acc + 1), acc_per_cand [B, W], flags [B] (may be NULL). */
+typedef struct {
+    int32_t B, W, D, V;
+    float temperature;
+} vs_sample_desc;
+
+size_t vs_sample_workspace_bytes(const vs_sample_desc *desc);
+int vs_reject_sample(const vs_sample_desc *desc, const float *root_logits,
+                     const float *logits, const double *row_lse, const float *q,
+                     const int32_t *cand_tok, const int32_t *cand_len, const double *u_acc,
+                     const double *u_res, const int32_t *gate, int32_t *n_acc, int32_t *best,
+                     int32_t *out_tok, int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * The whole verify step, enqueued on one stream with no host synchronisation:
+ *   copy_match + probe_gate (one fused launch; skipped when external_drafts != 0, in
+ *   which case cand_tok/cand_len are INPUTS from a neural drafter and the gate is open)
+ *   -> verify_attention -> lm_head (full rank, head input = attention output viewed
+ *   as [B*W*D, Hq*hd], so d must equal Hq*head_dim) -> reject_sample.
+ * stage_events: NULL, or 6 hipEvent_t handles recorded on `stream` before stage 1
+ * and after each of the 5 stages (retrieval+gate, attention, head GEMM, head
+ * normaliser, sampler) -- for timing only. */
+typedef struct {
+    int32_t B, W, D, kappa;
+    int32_t Hq, Hkv, head_dim, page_size, max_pages, n_pool_pages;
+    int32_t d, V;
+    int32_t dtype;            /* vs_dtype of q/k/v/pools/head/probe h/attention output */
+    float scale;              /* <= 0: 1/sqrt(head_dim) */
+    float tau;                /* probe threshold */
+    float temperature;
+    int32_t external_drafts;
+    int64_t ctx_total;
+} vs_step_desc;
+
+typedef struct {
+    /* copy retrieval and gate (unused when external_drafts) */
+    const int32_t *ctx, *ctx_off;
+    const void *probe_h;        /* [B, d] dtype */
+    const float *probe_w;       /* [d] */
+    /* attention */
+    const void *q, *k_cand, *v_cand, *k_pool, *v_pool;
+    const int32_t *page_table, *prefix_len;
+    /* head */
+    const void *w_full;         /* [V, d] */
+    /* sampler */
+    const float *root_logits;   /* [B, V] */
+    const float *q_draft;       /* [B*W*D, V] or NULL (copy drafts: point mass) */
+    const double *u_acc, *u_res;
+    /* retrieval outputs (inputs when external_drafts) */
+    int32_t *cand_tok, *cand_len;
+    int32_t *cand_pos, *n_found;            /* may be NULL when external_drafts */
+    float *score; int32_t *gate;            /* may be NULL when external_drafts */
+    /* stage outputs */
+    void *attn_out;                         /* [B*W*D, Hq, hd] dtype */
+    float *logits;                          /* [B*W*D, V] */
+    double *row_lse;                        /* [B*W*D] */
+    int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand;
+    int32_t *flags;                         /* [B]: OR of every stage's flags */
+    void **stage_events;                    /* NULL or 6 hipEvent_t */
+} vs_step_io;
+
+size_t vs_step_workspace_bytes(const vs_step_desc *desc);
+int vs_verify_step(const vs_step_desc *desc, const vs_step_io *io, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSTEP_H */

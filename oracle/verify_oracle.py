@@ -259,15 +259,17 @@ def head_softmax(logits: np.ndarray, lse: np.ndarray, temperature: float = 1.0):
 def _draw(r: np.ndarray, u: float):
     """Categorical draw by inverse CDF over ascending token id:
     k = min{k : C_k > u * S}, with C the running sum of r and S its total.
-    Returns (k, tie) where tie marks u*S within CDF_TIE_EPS*S of a CDF step."""
+    Returns (k, tie, margin): tie marks u*S within CDF_TIE_EPS*S of a CDF step;
+    margin is the distance to the nearest step as a fraction of S."""
     C = np.cumsum(r)
     S = C[-1]
     x = u * S
     k = int(np.searchsorted(C, x, side="right"))
     k = min(k, len(r) - 1)
     lo = C[k - 1] if k > 0 else 0.0
-    tie = (abs(x - lo) < CDF_TIE_EPS * S) or (abs(C[k] - x) < CDF_TIE_EPS * S)
-    return k, tie
+    margin = min(abs(x - lo), abs(C[k] - x)) / S
+    tie = margin < CDF_TIE_EPS
+    return k, tie, margin
 
 
 def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
@@ -302,6 +304,9 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
         out_tok=np.full((B, D + 1), -1, dtype=np.int32), n_out=np.zeros(B, dtype=np.int32),
         acc_per_cand=np.zeros((B, W), dtype=np.int32), flags=np.zeros(B, dtype=np.int32),
         abs_tie=np.zeros(B, dtype=bool),
+        # diagnostics: smallest relative distance of a decisive acceptance test from its
+        # threshold, and of the final draw from the nearest CDF step (fraction of S)
+        accept_margin=np.full(B, np.inf), cdf_margin=np.full(B, np.inf),
     )
     lse_cache = {}
 
@@ -337,6 +342,9 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
                     flags |= FLAG_BAD_TOKEN
                     p, Q = 0.0, 1.0
                 lhs = u_acc[b, i, o] * Q
+                if max(p, lhs) > 0:
+                    out["accept_margin"][b] = min(out["accept_margin"][b],
+                                                  abs(lhs - p) / max(p, lhs))
                 if abs(lhs - p) < ACCEPT_TIE_REL * max(p, lhs):
                     flags |= FLAG_ACCEPT_TIE
                 if abs(lhs - p) < 1e-4:
@@ -349,7 +357,7 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
         if len(have) == 0:
             # no candidate: one token from the target distribution at the current token
             r = row_p(b, -1)
-            y, tie = _draw(r, u_res[b, 0])
+            y, tie, out["cdf_margin"][b] = _draw(r, u_res[b, 0])
             out["out_tok"][b, 0] = y
             out["n_out"][b] = 1
             out["n_acc"][b] = 0
@@ -377,7 +385,7 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
         if not (r.sum() > 0.0):
             r = P
             flags |= FLAG_DEGENERATE
-        y, tie = _draw(r, u_res[b, best])
+        y, tie, out["cdf_margin"][b] = _draw(r, u_res[b, best])
         if tie:
             flags |= FLAG_CDF_TIE
         out["out_tok"][b, ab] = y

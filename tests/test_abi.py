@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/vstep.h, and rejects bad arguments on the host before
+anything is launched (a failing call enqueues nothing, so these calls never
+touch a device)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from verification_step_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vstep.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libvstep.so is not built (run `python -m verification_step_amd.build`)")
+    return L.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vs_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_calls():
+    names = declared_functions()
+    for n in ("vs_copy_match", "vs_probe_gate", "vs_verify_attention", "vs_lm_head",
+              "vs_reject_sample", "vs_verify_step"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(vs_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.vs_abi_version() == 1
+    assert lib.vs_status_str(0) == b"ok"
+    assert b"workspace" in lib.vs_status_str(-3)
+    assert lib.vs_status_str(99) == b"unknown status"
+
+
+def test_struct_layouts_match_header():
+    # int32 fields then int64 ctx_total at its natural alignment
+    assert C.sizeof(L.StepDesc) == 80
+    assert L.StepDesc.ctx_total.offset == 72
+    assert C.sizeof(L.StepIO) == 32 * 8
+    assert C.sizeof(L.AttnDesc) == 44
+    assert C.sizeof(L.HeadDesc) == 28
+    assert C.sizeof(L.SampleDesc) == 20
+
+
+def test_copy_match_validation(lib):
+    nul = None
+    fake = C.c_void_p(16)   # never dereferenced: validation fails first
+    # null outputs
+    assert lib.vs_copy_match(fake, 10, fake, 1, 5, 2, 2, nul, fake, fake, fake, nul, nul) == -1
+    # kappa outside 1..16
+    assert lib.vs_copy_match(fake, 10, fake, 1, 17, 2, 2, fake, fake, fake, fake, nul, nul) == -2
+    assert lib.vs_copy_match(fake, 10, fake, 1, 0, 2, 2, fake, fake, fake, fake, nul, nul) == -2
+    # W*D beyond 1024 rows, B <= 0
+    assert lib.vs_copy_match(fake, 10, fake, 1, 5, 64, 17, fake, fake, fake, fake, nul, nul) == -1
+    assert lib.vs_copy_match(fake, 10, fake, 0, 5, 2, 2, fake, fake, fake, fake, nul, nul) == -1
+
+
+def test_probe_validation(lib):
+    fake = C.c_void_p(16)
+    assert lib.vs_probe_gate(None, 1, fake, 1, 8, 0.4, None, fake, fake, None, None) == -1
+    assert lib.vs_probe_gate(fake, 7, fake, 1, 8, 0.4, None, fake, fake, None, None) == -2
+    assert lib.vs_probe_gate(fake, 1, fake, 1, 8, float("nan"), None, fake, fake, None, None) == -1
+
+
+def test_attention_validation(lib):
+    fake = C.c_void_p(16)
+    ok = dict(B=1, W=4, D=20, Hq=32, Hkv=8, head_dim=128, page_size=16, max_pages=256,
+              n_pool_pages=256, dtype=1, scale=0.0)
+
+    def call(**over):
+        d = L.AttnDesc(**{**ok, **over})
+        return lib.vs_verify_attention(C.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                                       None, fake, 0, None)
+
+    assert call(Hq=30) == -1                 # Hq % Hkv != 0
+    assert call(head_dim=64) == -2           # bf16 path is head_dim 128
+    assert call(dtype=0, head_dim=128) == -2
+    assert call(page_size=32) == -2
+    assert call(W=0) == -1
+    assert call(W=64, D=20) == -1            # more than 1024 rows per sequence
+    assert call() == -3                      # workspace too small
+    d = L.AttnDesc(**ok)
+    assert lib.vs_attention_workspace_bytes(C.byref(d)) > 0
+    assert lib.vs_verify_attention(C.byref(d), None, fake, fake, fake, fake, fake, fake, fake,
+                                   None, fake, 1 << 30, None) == -1
+
+
+def test_head_validation(lib):
+    fake = C.c_void_p(16)
+    ok = dict(M=80, d=4096, V=128256, rank=0, dtype=1, temperature=1.0, write_probs=0)
+
+    def call(w_full=fake, w_down=None, w_up=None, probs=None, ws=fake, nbytes=1 << 30, **over):
+        d = L.HeadDesc(**{**ok, **over})
+        return lib.vs_lm_head(C.byref(d), fake, w_full, w_down, w_up, fake, fake, probs, ws,
+                              nbytes, None)
+
+    assert call(d=4001) == -2                # bf16 needs d % 32 == 0
+    assert call(temperature=0.0) == -1
+    assert call(w_full=None) == -1
+    assert call(rank=512, w_down=fake, w_up=fake) == -1   # both heads given
+    assert call(rank=500, w_full=None, w_down=fake, w_up=fake) == -2
+    assert call(write_probs=1) == -1         # probs requested but null
+    assert call(nbytes=16) == -3
+    d = L.HeadDesc(**ok)
+    assert lib.vs_head_workspace_bytes(C.byref(d)) >= 80 * 1002 * 8     # (max, sum) per row and 128-row tile
+
+
+def test_sample_validation(lib):
+    fake = C.c_void_p(16)
+    d = L.SampleDesc(1, 4, 20, 128256, 1.0)
+    args = [fake] * 15
+    assert lib.vs_reject_sample(C.byref(L.SampleDesc(1, 4, 20, 128256, -1.0)), *args, None, 0,
+                                None) == -1
+    assert lib.vs_reject_sample(C.byref(L.SampleDesc(1, 4, 20, 1 << 20, 1.0)), *args, None, 0,
+                                None) == -2
+    bad = list(args)
+    bad[0] = None
+    assert lib.vs_reject_sample(C.byref(d), *bad, None, 0, None) == -1
+
+
+def test_step_validation(lib):
+    fake = C.c_void_p(16)
+    base = dict(B=1, W=4, D=20, kappa=5, Hq=32, Hkv=8, head_dim=128, page_size=16, max_pages=256,
+                n_pool_pages=256, d=4096, V=128256, dtype=1, scale=0.0, tau=0.4, temperature=1.0,
+                external_drafts=0, ctx_total=4096)
+    d = L.StepDesc(**base)
+    assert lib.vs_step_workspace_bytes(C.byref(d)) > 0
+    io = L.StepIO()
+    assert lib.vs_verify_step(C.byref(d), C.byref(io), fake, 1 << 40, None) == -1
+    for f in io._fields_:
+        if f[0] != "stage_events":
+            setattr(io, f[0], 16)
+    assert lib.vs_verify_step(C.byref(d), C.byref(io), fake, 16, None) == -3
+    d2 = L.StepDesc(**{**base, "d": 4000})
+    assert lib.vs_verify_step(C.byref(d2), C.byref(io), fake, 1 << 40, None) == -1
+    d3 = L.StepDesc(**{**base, "kappa": 20})
+    assert lib.vs_verify_step(C.byref(d3), C.byref(io), fake, 1 << 40, None) == -2

@@ -1,0 +1,415 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Matching rules: integer outputs (retrieval, gate, accepted lengths, chosen
+candidate, emitted tokens) bit-exact except sequences where either side flags a
+near tie; attention outputs and logits within 1e-2 of the oracle in the
+elementwise relative error with an RMS floor (max |x-y| / max(|y|, rms(y))).
+Shapes span several tiles with ragged tails; the full-size workloads run in the
+configuration the bench times.
+"""
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from gpu_util import (case_to_dev, compare_sampler, rel_err, require_gpu, say, tensor_np,
+                      to_dev)
+from verification_step_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _api():
+    from verification_step_amd import api
+    return api
+
+
+_cache = {}
+
+
+def get_case(key, maker):
+    if key not in _cache:
+        _cache[key] = maker()
+    return _cache[key]
+
+
+def small_shape(**kw):
+    base = dict(name="small", dtype="bf16", B=2, W=3, D=7, Hq=8, Hkv=2, hd=128, d=1024, V=1000,
+                P=(300, 777), paged_random=True)
+    base.update(kw)
+    return wl.Shape(**base)
+
+
+# =============================================================================== copy + probe
+
+@pytest.mark.parametrize("c,variant", [(1, "measure"), (2, "measure"), (2, "natural"),
+                                       (4, "measure"), (5, "measure"), (5, "natural")])
+def test_copy_match_workloads(c, variant):
+    api = _api()
+    sh = wl.config(c)
+    case = wl.make_case(sh.with_(V=min(sh.V, 4096)) if c != 1 else sh, 100 + c, variant,
+                        with_head=False, with_q=False)
+    A = case.arrays
+    say("copy_match", c, variant)
+    g = api.copy_match(to_dev(A["ctx"]), to_dev(A["ctx_off"]), sh.kappa, sh.W, sh.D)
+    o = oracle.copy_match(A["ctx"], A["ctx_off"], sh.kappa, sh.W, sh.D)
+    for k in ("cand_tok", "cand_len", "cand_pos", "n_found", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), k
+
+
+def test_copy_match_random_batches():
+    api = _api()
+    for seed in range(6):
+        rng = np.random.default_rng(seed)
+        kappa = int(rng.integers(1, 9))
+        W = int(rng.integers(1, 9))
+        D = int(rng.integers(1, 21))
+        lens = rng.integers(0, 400, size=64)
+        lens[:3] = [0, kappa, kappa + 1]
+        seqs = [rng.integers(0, 3, size=int(n)).astype(np.int32) for n in lens]
+        ctx = np.concatenate(seqs).astype(np.int32)
+        off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        say("copy_match random", seed, kappa, W, D)
+        g = api.copy_match(to_dev(ctx), to_dev(off), kappa, W, D)
+        o = oracle.copy_match(ctx, off, kappa, W, D)
+        for k in ("cand_tok", "cand_len", "cand_pos", "n_found", "flags"):
+            assert np.array_equal(tensor_np(g[k]), o[k]), (seed, k)
+
+
+def test_copy_match_long_contexts_and_bad_offsets():
+    """Occurrences far from the current token (several LDS segments), none at all,
+    one straddling a segment boundary, and invalid offsets."""
+    api = _api()
+    rng = np.random.default_rng(9)
+    L = 20000
+    seqs = []
+    a = rng.integers(10, 1000, size=L).astype(np.int32)
+    a[-5:] = [1, 2, 3, 4, 5]
+    a[3:8] = [1, 2, 3, 4, 5]
+    seqs.append(a)                                            # only match near the start
+    b = rng.integers(10, 1000, size=L).astype(np.int32)
+    seqs.append(b)                                            # no match
+    c = rng.integers(10, 1000, size=L).astype(np.int32)
+    c[-5:] = [7, 7, 8, 8, 9]
+    j = L - 2 - 8192 + 2                                      # window crosses a segment edge
+    c[j - 4:j + 1] = [7, 7, 8, 8, 9]
+    seqs.append(c)
+    ctx = np.concatenate(seqs).astype(np.int32)
+    off = np.array([0, L, 2 * L, 3 * L], dtype=np.int32)
+    say("copy_match long")
+    g = api.copy_match(to_dev(ctx), to_dev(off), 5, 4, 20)
+    o = oracle.copy_match(ctx, off, 5, 4, 20)
+    for k in ("cand_tok", "cand_len", "cand_pos", "n_found", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), k
+    assert tensor_np(g["n_found"]).tolist() == [1, 0, 1]
+    bad = np.array([0, 50, 40, 3 * L + 5], dtype=np.int32)   # decreasing, past the end
+    g = api.copy_match(to_dev(ctx), to_dev(bad), 5, 2, 4)
+    o = oracle.copy_match(ctx, bad, 5, 2, 4)
+    for k in ("cand_tok", "cand_len", "cand_pos", "n_found", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), k
+    assert (tensor_np(g["flags"])[1:] & oracle.FLAG_BAD_CTX).all()
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "f32"), (4096, "bf16"), (8192, "bf16")])
+def test_probe_gate(d, dtype):
+    api = _api()
+    rng = np.random.default_rng(d)
+    B = 64
+    w = (rng.standard_normal(d) / np.sqrt(d)).astype(np.float32)
+    h32 = rng.standard_normal((B, d)).astype(np.float32)
+    h = wl.f32_to_bf16_bits(h32) if dtype == "bf16" else h32
+    n_found = rng.integers(0, 3, size=B).astype(np.int32)
+    say("probe", d, dtype)
+    g = api.probe_gate(to_dev(h, dtype == "bf16"), to_dev(w), 0.4, to_dev(n_found))
+    o = oracle.probe_gate(oracle.as_f64(h, dtype), w, 0.4, n_found)
+    score = tensor_np(g["score"])
+    assert np.abs(score - o["score"]).max() < 1e-5
+    ok = o["flags"] == 0
+    assert ok.sum() >= B - 2
+    assert np.array_equal(tensor_np(g["gate"])[ok], o["gate"][ok])
+    assert np.array_equal(tensor_np(g["flags"])[ok], o["flags"][ok])
+
+
+# =============================================================================== attention
+
+def _run_attention(case):
+    api = _api()
+    sh = case.shape
+    T = case_to_dev(case, {"q", "k_cand", "v_cand", "k_pool", "v_pool", "page_table",
+                           "prefix_len"})
+    out, flags = api.verify_attention(T["q"], T["k_cand"], T["v_cand"], T["k_pool"],
+                                      T["v_pool"], T["page_table"], T["prefix_len"], sh.W, sh.D)
+    return tensor_np(out), tensor_np(flags)
+
+
+def _oracle_attention(case, seqs=None):
+    sh = case.shape
+    A = case.arrays
+    f = lambda k: oracle.as_f64(A[k], sh.dtype)
+    return oracle.verify_attention(f("q"), f("k_cand"), f("v_cand"), f("k_pool"), f("v_pool"),
+                                   A["page_table"], A["prefix_len"], sh.B, sh.W, sh.D, sh.Hq,
+                                   sh.Hkv, out_dtype=sh.dtype)
+
+
+@pytest.mark.parametrize("shape", [
+    small_shape(),
+    small_shape(B=3, P=(0, 16, 1000), W=2, D=5, Hq=16, Hkv=4),    # empty prefix, one page
+    small_shape(B=1, P=(4096,), W=4, D=20, Hq=32, Hkv=8, d=4096),  # Llama-8B attention shape
+    small_shape(B=2, P=(513, 2047), W=1, D=7, Hq=4, Hkv=4, d=512), # MHA, gamma=7 drafts
+    small_shape(B=1, P=(100,), W=8, D=20, Hq=64, Hkv=8, d=8192),   # 70B rows, short prefix
+], ids=["small", "edge_prefixes", "llama8b_attn", "mha_w1", "70b_rows"])
+def test_attention_bf16(shape):
+    case = wl.make_case(shape, 7, with_head=False, with_q=False)
+    say("attention", shape)
+    g, gf = _run_attention(case)
+    _, o_r, of = _oracle_attention(case)
+    assert np.array_equal(gf, of)
+    assert rel_err(g, o_r) <= TOL
+
+
+def test_attention_f32_tiny():
+    case = wl.make_case(wl.config(1), 1000, with_head=False, with_q=False)
+    say("attention tiny f32")
+    g, gf = _run_attention(case)
+    O, _, of = _oracle_attention(case)
+    assert rel_err(g, O) < 1e-5 and np.array_equal(gf, of)
+
+
+def test_attention_bad_page_flagged():
+    sh = small_shape(B=2, P=(64, 64), paged_random=False)
+    case = wl.make_case(sh, 3, with_head=False, with_q=False)
+    case.arrays["page_table"][1, 2] = 10 ** 6            # out of the pool: skipped and flagged
+    say("attention bad page")
+    g, gf = _run_attention(case)
+    _, o_r, of = _oracle_attention(case)
+    assert gf.tolist() == of.tolist() and (gf[1] & oracle.FLAG_BAD_PAGE) and gf[0] == 0
+    assert rel_err(g, o_r) <= TOL
+
+
+@pytest.mark.parametrize("c", [2, 4, 5])
+def test_attention_full_size(c):
+    sh = wl.config(c)
+    case = get_case(("attn", c), lambda: wl.make_case(sh.with_(V=1024), 1000 * c, with_head=False,
+                                                       with_q=False))
+    say("attention full", c)
+    g, gf = _run_attention(case)
+    _, o_r, of = _oracle_attention(case)
+    assert np.array_equal(gf, of)
+    assert rel_err(g, o_r) <= TOL
+
+
+# =============================================================================== head
+
+def _head_case(M, d, V, dtype="bf16", rank=0, seed=0):
+    rng = np.random.default_rng(seed)
+    h32 = rng.standard_normal((M, d)).astype(np.float32) * 0.05
+    if rank == 0:
+        w32 = (rng.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32)
+        ws = dict(w_full=w32)
+    else:
+        ws = dict(w_down=(rng.standard_normal((rank, d)) / np.sqrt(d)).astype(np.float32),
+                  w_up=(rng.standard_normal((V, rank)) / np.sqrt(rank)).astype(np.float32))
+        h32 = rng.standard_normal((M, d)).astype(np.float32)
+    if dtype == "bf16":
+        h = wl.f32_to_bf16_bits(h32)
+        ws = {k: wl.f32_to_bf16_bits(v) for k, v in ws.items()}
+    else:
+        h = h32
+    return h, ws
+
+
+@pytest.mark.parametrize("M,d,V,dtype,T", [
+    (37, 256, 1000, "bf16", 1.0), (100, 512, 2000, "bf16", 0.7), (8, 64, 512, "f32", 1.0),
+    (160, 1024, 777, "bf16", 1.0), (1024, 256, 300, "bf16", 1.0)])
+def test_head_full(M, d, V, dtype, T):
+    api = _api()
+    h, ws = _head_case(M, d, V, dtype, seed=M + V)
+    bf = dtype == "bf16"
+    say("head", M, d, V, dtype)
+    lg, lse, _ = api.lm_head(to_dev(h, bf), w_full=to_dev(ws["w_full"], bf), temperature=T)
+    z, l = oracle.lm_head_full(oracle.as_f64(h, dtype), ws["w_full"], T, dtype)
+    assert rel_err(tensor_np(lg), z) <= (TOL if bf else 1e-5)
+    assert np.abs(tensor_np(lse) - l).max() < 1e-5
+
+
+@pytest.mark.parametrize("M,d,r,V", [(7, 256, 64, 1000), (5, 512, 32, 3000)])
+def test_head_lowrank_small(M, d, r, V):
+    api = _api()
+    h, ws = _head_case(M, d, V, "bf16", rank=r, seed=r)
+    say("head lowrank", M, d, r, V)
+    lg, lse, pr = api.lm_head(to_dev(h, True), w_down=to_dev(ws["w_down"], True),
+                              w_up=to_dev(ws["w_up"], True), write_probs=True)
+    z, l, _ = oracle.lm_head_lowrank(oracle.as_f64(h, "bf16"), ws["w_down"], ws["w_up"], 1.0,
+                                     "bf16")
+    assert rel_err(tensor_np(lg), z) <= TOL
+    assert np.abs(tensor_np(lse) - l).max() < 1e-5
+    p = oracle.head_softmax(z, l)
+    assert rel_err(tensor_np(pr), p) <= TOL
+    assert np.abs(tensor_np(pr).astype(np.float64).sum(axis=1) - 1).max() < 1e-4
+
+
+def test_head_lowrank_slimspec_full():
+    """SlimSpec draft head at r = d/8 = 512 over the full vocabulary; also checked
+    against the dense product (W_up W_down) h on sampled vocabulary rows."""
+    api = _api()
+    sh = wl.config(3)
+    case = get_case(("slim",), lambda: wl.make_case(sh, 3000, with_head=False, with_q=False))
+    A = case.arrays
+    say("head lowrank slimspec full")
+    lg, lse, pr = api.lm_head(to_dev(A["draft_h"], True), w_down=to_dev(A["w_down"], True),
+                              w_up=to_dev(A["w_up"], True), write_probs=True)
+    z, l, t = oracle.lm_head_lowrank(oracle.as_f64(A["draft_h"], "bf16"), A["w_down"], A["w_up"])
+    g = tensor_np(lg)
+    assert rel_err(g, z) <= TOL
+    assert np.abs(tensor_np(lse) - l).max() < 1e-5
+    assert rel_err(tensor_np(pr), oracle.head_softmax(z, l)) <= TOL
+    rows = np.random.default_rng(0).choice(sh.V, 8192, replace=False)
+    dense = oracle.bf16_bits_to_f64(A["w_up"][rows]) @ oracle.bf16_bits_to_f64(A["w_down"])
+    zd = oracle.as_f64(A["draft_h"], "bf16") @ dense.T
+    assert rel_err(g[:, rows], zd) <= TOL
+
+
+# =============================================================================== sampler
+
+@pytest.mark.parametrize("qmode,T", [("dense", 1.0), ("point", 1.0), ("dense", 0.6)])
+def test_reject_sample_synthetic(qmode, T):
+    """Sampler alone on generator-made logits; its row normaliser input is scipy's
+    logsumexp of those logits."""
+    api = _api()
+    rng = np.random.default_rng(5)
+    B, W, D, V = 64, 3, 5, 1000
+    M = W * D
+    root = (rng.standard_normal((B, V)) * 1.5).astype(np.float32)
+    logits = (rng.standard_normal((B * M, V)) * 1.5).astype(np.float32)
+    lse = scipy.special.logsumexp(logits.astype(np.float64) / T, axis=1)
+    q = wl.draft_probs_from_logits(rng, (B * M, V), 1.5) if qmode == "dense" else None
+    # drafts: mostly high-probability tokens so that runs are long and varied
+    cand = rng.integers(0, 20, size=(B, W, D)).astype(np.int32)
+    clen = rng.integers(0, D + 1, size=(B, W)).astype(np.int32)
+    clen[0] = 0                                   # no candidate
+    for b in range(B):
+        for i in range(W):
+            cand[b, i, clen[b, i]:] = -1
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    gate = np.ones(B, dtype=np.int32)
+    gate[1] = 0                                   # closed gate
+    say("reject_sample", qmode, T)
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse),
+                          to_dev(q) if q is not None else None, to_dev(cand), to_dev(clen),
+                          to_dev(ua), to_dev(ur), T, to_dev(gate))
+    o = oracle.reject_sample(root, logits, q, cand, clen, ua, ur, T, gate)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    assert n_exc <= 2 and n_cmp >= B - 2
+    assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
+
+
+# =============================================================================== whole step
+
+def _step_inputs(case, T, external=None):
+    sh = case.shape
+    keys = {"ctx", "ctx_off", "probe_h", "probe_w", "q", "k_cand", "v_cand", "k_pool", "v_pool",
+            "page_table", "prefix_len", "w_full", "root_logits", "q_draft", "u_acc", "u_res"}
+    I = case_to_dev(case, keys)
+    if external is not None:
+        I["cand_tok"] = to_dev(external[0])
+        I["cand_len"] = to_dev(external[1])
+    return I
+
+
+def _check_step(case, g, o, external=False):
+    sh = case.shape
+    if not external:
+        for k in ("cand_tok", "cand_len", "cand_pos", "n_found"):
+            assert np.array_equal(tensor_np(g[k]), o["copy"][k]), k
+        ok = o["probe"]["flags"] == 0
+        assert np.array_equal(tensor_np(g["gate"])[ok], o["gate"][ok])
+    assert rel_err(tensor_np(g["attn_out"]), o["attn"].reshape(tensor_np(g["attn_out"]).shape)) <= TOL
+    assert rel_err(tensor_np(g["logits"]), o["logits"]) <= TOL
+    assert np.abs(tensor_np(g["row_lse"]) - o["lse"]).max() < 1e-3
+    n_cmp, n_exc = compare_sampler({k: g[k] for k in ("n_acc", "best", "out_tok", "n_out",
+                                                      "acc_per_cand", "flags")},
+                                   o["sample"], sh.B)
+    return n_cmp, n_exc
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "llama8b", "ragged"])
+def test_verify_step_end_to_end(name):
+    api = _api()
+    if name == "tiny":
+        sh, seed = wl.config(1), 1000
+    elif name == "small":
+        sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
+    elif name == "llama8b":
+        sh, seed = wl.config(2), 2000
+    else:
+        sh, seed = wl.config(5), 5000
+    case = get_case(("step", name), lambda: wl.make_case(sh, seed))
+    I = _step_inputs(case, sh.temperature)
+    say("verify_step", name)
+    step = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa)
+    g = step()
+    o = oracle.verify_step(case.arrays, sh)
+    n_cmp, n_exc = _check_step(case, g, o)
+    assert n_exc <= max(1, sh.B // 16), (n_cmp, n_exc)
+
+
+def test_verify_step_external_drafts_slimspec():
+    """Neural-draft path: the SlimSpec low-rank head makes q for gamma=7 drafts, the
+    drafts are sampled from the oracle's q by inverse CDF (the drafter's job), then
+    the step verifies them with W=1."""
+    api = _api()
+    sh = wl.config(3)
+    case = get_case(("slim_step",), lambda: wl.make_case(sh, 3000))
+    A = case.arrays
+    z, l, _ = oracle.lm_head_lowrank(oracle.as_f64(A["draft_h"], "bf16"), A["w_down"], A["w_up"])
+    q = oracle.head_softmax(z, l).astype(np.float32)              # [gamma, V]
+    drafts = np.zeros((1, 1, sh.D), dtype=np.int32)
+    for o_ in range(sh.D):
+        c = np.cumsum(q[o_].astype(np.float64))
+        drafts[0, 0, o_] = min(int(np.searchsorted(c, A["u_draft"][0, 0, o_] * c[-1], "right")),
+                               sh.V - 1)
+    lens = np.array([[sh.D]], dtype=np.int32)
+    A2 = dict(A)
+    A2["q_draft"] = q
+    case.arrays = A2
+    I = _step_inputs(case, 1.0, external=(drafts, lens))
+    say("verify_step slimspec external drafts")
+    step = api.VerifyStep(I, B=1, W=1, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          external_drafts=True)
+    g = step()
+    o = oracle.verify_step(A2, sh, drafts=(drafts, lens))
+    _check_step(case, g, o, external=True)
+
+
+def test_verify_step_equals_its_calls():
+    """The fused step gives the same bits as its five calls made one by one."""
+    api = _api()
+    sh = small_shape(B=3, P=(300, 777, 64))
+    case = get_case(("step", "small"), lambda: wl.make_case(sh, 11))
+    I = _step_inputs(case, 1.0)
+    say("verify_step vs calls")
+    g = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V)()
+    cm = api.copy_match(I["ctx"], I["ctx_off"], 5, sh.W, sh.D)
+    pg = api.probe_gate(I["probe_h"], I["probe_w"], 0.4, cm["n_found"])
+    att, _ = api.verify_attention(I["q"], I["k_cand"], I["v_cand"], I["k_pool"], I["v_pool"],
+                                  I["page_table"], I["prefix_len"], sh.W, sh.D)
+    lg, lse, _ = api.lm_head(att.reshape(att.shape[0], -1), w_full=I["w_full"])
+    rs = api.reject_sample(I["root_logits"], lg, lse, I["q_draft"], cm["cand_tok"],
+                           cm["cand_len"], I["u_acc"], I["u_res"], 1.0, pg["gate"])
+    for k in ("cand_tok", "cand_len", "cand_pos", "n_found"):
+        assert np.array_equal(tensor_np(g[k]), tensor_np(cm[k])), k
+    assert np.array_equal(tensor_np(g["gate"]), tensor_np(pg["gate"]))
+    assert np.array_equal(tensor_np(g["attn_out"]), tensor_np(att))
+    assert np.array_equal(tensor_np(g["logits"]), tensor_np(lg))
+    assert np.array_equal(tensor_np(g["row_lse"]), tensor_np(lse))
+    for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand"):
+        assert np.array_equal(tensor_np(g[k]), tensor_np(rs[k])), k

@@ -1,0 +1,106 @@
+"""ctypes view of libvstep.so (the C ABI declared in include/vstep.h).
+
+Loading fails loudly when the library has not been built: there is no other
+implementation of these calls in this package.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvstep.so")
+
+VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = 0, -1, -2, -3, -4
+VS_F32, VS_BF16 = 0, 1
+
+FLAG_PROBE_TIE = 1
+FLAG_ACCEPT_TIE = 2
+FLAG_CDF_TIE = 4
+FLAG_DEGENERATE_RESIDUAL = 8
+FLAG_NO_CANDIDATE = 16
+FLAG_BAD_PAGE = 32
+FLAG_BAD_CTX = 64
+FLAG_BAD_TOKEN = 128
+
+EXPORTED = [
+    "vs_abi_version", "vs_status_str", "vs_copy_match", "vs_probe_gate",
+    "vs_attention_workspace_bytes", "vs_verify_attention", "vs_head_workspace_bytes",
+    "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
+    "vs_step_workspace_bytes", "vs_verify_step",
+]
+
+P = C.c_void_p
+I32 = C.c_int32
+
+
+class AttnDesc(C.Structure):
+    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("Hq", I32), ("Hkv", I32),
+                ("head_dim", I32), ("page_size", I32), ("max_pages", I32),
+                ("n_pool_pages", I32), ("dtype", I32), ("scale", C.c_float)]
+
+
+class HeadDesc(C.Structure):
+    _fields_ = [("M", I32), ("d", I32), ("V", I32), ("rank", I32), ("dtype", I32),
+                ("temperature", C.c_float), ("write_probs", I32)]
+
+
+class SampleDesc(C.Structure):
+    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("V", I32), ("temperature", C.c_float)]
+
+
+class StepDesc(C.Structure):
+    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("kappa", I32), ("Hq", I32), ("Hkv", I32),
+                ("head_dim", I32), ("page_size", I32), ("max_pages", I32),
+                ("n_pool_pages", I32), ("d", I32), ("V", I32), ("dtype", I32),
+                ("scale", C.c_float), ("tau", C.c_float), ("temperature", C.c_float),
+                ("external_drafts", I32), ("ctx_total", C.c_int64)]
+
+
+class StepIO(C.Structure):
+    _fields_ = [(n, P) for n in (
+        "ctx", "ctx_off", "probe_h", "probe_w",
+        "q", "k_cand", "v_cand", "k_pool", "v_pool", "page_table", "prefix_len",
+        "w_full", "root_logits", "q_draft", "u_acc", "u_res",
+        "cand_tok", "cand_len", "cand_pos", "n_found", "score", "gate",
+        "attn_out", "logits", "row_lse",
+        "n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags", "stage_events")]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libvstep.so once; raise if it is missing (build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libvstep.so not found at {path}: build it with "
+            "`python -m verification_step_amd.build` (hipcc, gfx950)")
+    lib = C.CDLL(path)
+    lib.vs_abi_version.restype = C.c_int
+    lib.vs_status_str.restype = C.c_char_p
+    lib.vs_status_str.argtypes = [C.c_int]
+    lib.vs_copy_match.argtypes = [P, C.c_int64, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P,
+                                  P, P, P]
+    lib.vs_probe_gate.argtypes = [P, C.c_int, P, C.c_int, C.c_int, C.c_float, P, P, P, P, P]
+    lib.vs_attention_workspace_bytes.restype = C.c_size_t
+    lib.vs_attention_workspace_bytes.argtypes = [C.POINTER(AttnDesc)]
+    lib.vs_verify_attention.argtypes = [C.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, P,
+                                        C.c_size_t, P]
+    lib.vs_head_workspace_bytes.restype = C.c_size_t
+    lib.vs_head_workspace_bytes.argtypes = [C.POINTER(HeadDesc)]
+    lib.vs_lm_head.argtypes = [C.POINTER(HeadDesc), P, P, P, P, P, P, P, P, C.c_size_t, P]
+    lib.vs_sample_workspace_bytes.restype = C.c_size_t
+    lib.vs_sample_workspace_bytes.argtypes = [C.POINTER(SampleDesc)]
+    lib.vs_reject_sample.argtypes = [C.POINTER(SampleDesc)] + [P] * 16 + [C.c_size_t, P]
+    lib.vs_step_workspace_bytes.restype = C.c_size_t
+    lib.vs_step_workspace_bytes.argtypes = [C.POINTER(StepDesc)]
+    lib.vs_verify_step.argtypes = [C.POINTER(StepDesc), C.POINTER(StepIO), P, C.c_size_t, P]
+    for fn in EXPORTED:
+        if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
+            getattr(lib, fn).restype = C.c_int
+    _lib = lib
+    return lib

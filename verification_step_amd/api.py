@@ -1,0 +1,285 @@
+"""Python binding of libvstep: argument marshalling only.
+
+Each function checks dtype, device and contiguity, allocates its outputs as torch
+tensors (torch owns the memory), and passes raw device pointers plus torch's
+current HIP stream to the C ABI.  Every step of the verify path runs in the HIP
+kernels of libvstep; nothing is computed here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+class VstepError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = L.load()
+        super().__init__(f"{where}: {lib.vs_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, dtype, name, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _vs_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.VS_BF16
+    if t.dtype == torch.float32:
+        return L.VS_F32
+    raise TypeError(f"model tensors must be bf16 or fp32, got {t.dtype}")
+
+
+def _raise(st, where):
+    if st != L.VS_OK:
+        raise VstepError(st, where)
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device=None, key: str = "default") -> torch.Tensor:
+    """A zero-initialised device workspace of at least nbytes, cached per device/key."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    k = (dev.index, key)
+    ws = _ws_cache.get(k)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[k] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------------
+
+def copy_match(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int, W: int, D: int):
+    lib = L.load()
+    _check(ctx, torch.int32, "ctx")
+    _check(ctx_off, torch.int32, "ctx_off")
+    B = ctx_off.numel() - 1
+    dev = ctx_off.device
+    out = dict(
+        cand_tok=torch.empty((B, W, D), dtype=torch.int32, device=dev),
+        cand_len=torch.empty((B, W), dtype=torch.int32, device=dev),
+        cand_pos=torch.empty((B, W), dtype=torch.int32, device=dev),
+        n_found=torch.empty((B,), dtype=torch.int32, device=dev),
+        flags=torch.empty((B,), dtype=torch.int32, device=dev),
+    )
+    st = lib.vs_copy_match(_ptr(ctx), ctx.numel(), _ptr(ctx_off), B, kappa, W, D,
+                           _ptr(out["cand_tok"]), _ptr(out["cand_len"]), _ptr(out["cand_pos"]),
+                           _ptr(out["n_found"]), _ptr(out["flags"]), _stream())
+    _raise(st, "copy_match")
+    return out
+
+
+def probe_gate(h: torch.Tensor, w: torch.Tensor, tau: float, n_found: Optional[torch.Tensor] = None):
+    lib = L.load()
+    if h.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("h must be bf16 or fp32")
+    _check(h, h.dtype, "h")
+    _check(w, torch.float32, "w")
+    _check(n_found, torch.int32, "n_found")
+    B, d = h.shape
+    dev = h.device
+    out = dict(score=torch.empty(B, dtype=torch.float32, device=dev),
+               gate=torch.empty(B, dtype=torch.int32, device=dev),
+               flags=torch.empty(B, dtype=torch.int32, device=dev))
+    st = lib.vs_probe_gate(_ptr(h), _vs_dtype(h), _ptr(w), B, d, float(tau), _ptr(n_found),
+                           _ptr(out["score"]), _ptr(out["gate"]), _ptr(out["flags"]), _stream())
+    _raise(st, "probe_gate")
+    return out
+
+
+def attn_desc(B, W, D, Hq, Hkv, hd, max_pages, n_pool_pages, dtype, scale=0.0):
+    return L.AttnDesc(B, W, D, Hq, Hkv, hd, 16, max_pages, n_pool_pages, dtype, scale)
+
+
+def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, W: int, D: int,
+                     scale: float = 0.0, out: Optional[torch.Tensor] = None):
+    lib = L.load()
+    dt = q.dtype
+    for name, t in (("q", q), ("k_cand", k_cand), ("v_cand", v_cand), ("k_pool", k_pool),
+                    ("v_pool", v_pool)):
+        _check(t, dt, name)
+    _check(page_table, torch.int32, "page_table")
+    _check(prefix_len, torch.int32, "prefix_len")
+    BM, Hq, hd = q.shape
+    B = prefix_len.numel()
+    Hkv = k_cand.shape[1]
+    if BM != B * W * D:
+        raise ValueError("q rows must equal B*W*D")
+    desc = attn_desc(B, W, D, Hq, Hkv, hd, page_table.shape[1], k_pool.shape[0], _vs_dtype(q),
+                     scale)
+    if out is None:
+        out = torch.empty_like(q)
+    flags = torch.empty(B, dtype=torch.int32, device=q.device)
+    nbytes = lib.vs_attention_workspace_bytes(C.byref(desc))
+    ws = workspace(nbytes, q.device)
+    st = lib.vs_verify_attention(C.byref(desc), _ptr(q), _ptr(k_cand), _ptr(v_cand), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(page_table), _ptr(prefix_len), _ptr(out),
+                                 _ptr(flags), _ptr(ws), ws.numel(), _stream())
+    _raise(st, "verify_attention")
+    return out, flags
+
+
+def lm_head(h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
+            write_probs: bool = False):
+    lib = L.load()
+    dt = h.dtype
+    _check(h, dt, "h")
+    for name, t in (("w_full", w_full), ("w_down", w_down), ("w_up", w_up)):
+        _check(t, dt, name)
+    M, d = h.shape
+    rank = 0 if w_down is None else w_down.shape[0]
+    V = (w_full if rank == 0 else w_up).shape[0]
+    desc = L.HeadDesc(M, d, V, rank, _vs_dtype(h), float(temperature), int(write_probs))
+    dev = h.device
+    logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    row_lse = torch.empty(M, dtype=torch.float64, device=dev)
+    probs = torch.empty((M, V), dtype=torch.float32, device=dev) if write_probs else None
+    nbytes = lib.vs_head_workspace_bytes(C.byref(desc))
+    ws = workspace(nbytes, dev, "head")
+    st = lib.vs_lm_head(C.byref(desc), _ptr(h), _ptr(w_full), _ptr(w_down), _ptr(w_up),
+                        _ptr(logits), _ptr(row_lse), _ptr(probs), _ptr(ws), ws.numel(), _stream())
+    _raise(st, "lm_head")
+    return logits, row_lse, probs
+
+
+def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_res,
+                  temperature: float = 1.0, gate=None):
+    lib = L.load()
+    _check(root_logits, torch.float32, "root_logits")
+    _check(logits, torch.float32, "logits")
+    _check(row_lse, torch.float64, "row_lse")
+    _check(q, torch.float32, "q")
+    _check(cand_tok, torch.int32, "cand_tok")
+    _check(cand_len, torch.int32, "cand_len")
+    _check(u_acc, torch.float64, "u_acc")
+    _check(u_res, torch.float64, "u_res")
+    _check(gate, torch.int32, "gate")
+    B, W, D = cand_tok.shape
+    V = root_logits.shape[1]
+    dev = root_logits.device
+    desc = L.SampleDesc(B, W, D, V, float(temperature))
+    out = dict(n_acc=torch.empty(B, dtype=torch.int32, device=dev),
+               best=torch.empty(B, dtype=torch.int32, device=dev),
+               out_tok=torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+               n_out=torch.empty(B, dtype=torch.int32, device=dev),
+               acc_per_cand=torch.empty((B, W), dtype=torch.int32, device=dev),
+               flags=torch.empty(B, dtype=torch.int32, device=dev))
+    nbytes = lib.vs_sample_workspace_bytes(C.byref(desc))
+    ws = workspace(nbytes, dev, "sample")
+    st = lib.vs_reject_sample(C.byref(desc), _ptr(root_logits), _ptr(logits), _ptr(row_lse),
+                              _ptr(q), _ptr(cand_tok), _ptr(cand_len), _ptr(u_acc), _ptr(u_res),
+                              _ptr(gate), _ptr(out["n_acc"]), _ptr(out["best"]),
+                              _ptr(out["out_tok"]), _ptr(out["n_out"]), _ptr(out["acc_per_cand"]),
+                              _ptr(out["flags"]), _ptr(ws), ws.numel(), _stream())
+    _raise(st, "reject_sample")
+    return out
+
+
+# ---------------------------------------------------------------------------------
+
+class VerifyStep:
+    """One verify step bound to fixed device buffers, so that repeated calls (timing,
+    a decode loop) enqueue the step without any host-side allocation."""
+
+    def __init__(self, inputs: dict, B: int, W: int, D: int, Hq: int, Hkv: int, hd: int,
+                 V: int, tau: float = 0.4, temperature: float = 1.0, kappa: int = 5,
+                 external_drafts: bool = False, scale: float = 0.0):
+        self.lib = L.load()
+        I = inputs
+        dt = I["q"].dtype
+        dev = I["q"].device
+        self.dtype = dt
+        self.inputs = I
+        d = Hq * hd
+        M = B * W * D
+        self.desc = L.StepDesc(B, W, D, kappa, Hq, Hkv, hd, 16, I["page_table"].shape[1],
+                               I["k_pool"].shape[0], d, V, _vs_dtype(I["q"]), float(scale),
+                               float(tau), float(temperature), int(external_drafts),
+                               I["ctx"].numel() if not external_drafts else 0)
+        self.out = dict(
+            cand_tok=I["cand_tok"] if external_drafts else torch.empty((B, W, D), dtype=torch.int32, device=dev),
+            cand_len=I["cand_len"] if external_drafts else torch.empty((B, W), dtype=torch.int32, device=dev),
+            cand_pos=torch.empty((B, W), dtype=torch.int32, device=dev),
+            n_found=torch.empty(B, dtype=torch.int32, device=dev),
+            score=torch.empty(B, dtype=torch.float32, device=dev),
+            gate=torch.empty(B, dtype=torch.int32, device=dev),
+            attn_out=torch.empty((M, Hq, hd), dtype=dt, device=dev),
+            logits=torch.empty((M, V), dtype=torch.float32, device=dev),
+            row_lse=torch.empty(M, dtype=torch.float64, device=dev),
+            n_acc=torch.empty(B, dtype=torch.int32, device=dev),
+            best=torch.empty(B, dtype=torch.int32, device=dev),
+            out_tok=torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+            n_out=torch.empty(B, dtype=torch.int32, device=dev),
+            acc_per_cand=torch.empty((B, W), dtype=torch.int32, device=dev),
+            flags=torch.empty(B, dtype=torch.int32, device=dev),
+        )
+        nbytes = self.lib.vs_step_workspace_bytes(C.byref(self.desc))
+        if nbytes == 0:
+            raise VstepError(L.VS_ERR_INVALID_ARG, "verify_step (descriptor rejected)")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.io = L.StepIO()
+        self.bind(I)
+
+    def bind(self, I: dict):
+        """(Re)point the step at a set of input tensors of the same shapes."""
+        io = self.io
+        o = self.out
+        for name in ("ctx", "ctx_off", "probe_h", "probe_w", "q", "k_cand", "v_cand", "k_pool",
+                     "v_pool", "page_table", "prefix_len", "w_full", "root_logits", "q_draft",
+                     "u_acc", "u_res"):
+            t = I.get(name)
+            setattr(io, name, None if t is None else t.data_ptr())
+        for name, t in o.items():
+            setattr(io, name, t.data_ptr())
+        self.inputs = I
+
+    def event_array(self, events):
+        """Pointer to a C array of the 6 hipEvent_t behind `events` (torch.cuda.Event with
+        timing), recorded once here so that the handles exist.  Keep the result alive."""
+        for e in events:
+            e.record()
+        torch.cuda.synchronize()
+        arr = (C.c_void_p * 6)(*[e.cuda_event for e in events])
+        self._keep = getattr(self, "_keep", [])
+        self._keep.append((events, arr))
+        return C.cast(arr, C.c_void_p).value
+
+    def use_events(self, ptr):
+        """Record stage events of the following calls into the array at `ptr` (or stop)."""
+        self.io.stage_events = ptr
+
+    def __call__(self):
+        st = self.lib.vs_verify_step(C.byref(self.desc), C.byref(self.io), _ptr(self.ws),
+                                     self.ws.numel(), _stream())
+        _raise(st, "verify_step")
+        return self.out
+
+
+def verify_step(inputs: dict, **kw):
+    """One-shot verify step (allocates its outputs and workspace)."""
+    return VerifyStep(inputs, **kw)()

@@ -1,0 +1,485 @@
+// Block-triangular verify attention (SwitchSD summary, onedev.kr/papers/87,
+// "무엇과 다른가"): every candidate row attends to the whole prefix and to the rows
+// of its own candidate up to itself; other candidates are masked out.  The mask is
+// evaluated from (candidate, offset) indices, never materialised.
+//
+// bf16 path (head_dim 128), per workgroup = (sequence b, KV head, row block, key split):
+//   * the g*M query rows that share a KV head (GQA) are ordered r = m*g + h_local
+//     and cut into blocks of NW waves x RT tiles x 16 rows;
+//   * prefix keys are split in ranges of `split_keys` (paged KV, 16-token pages);
+//     the candidates' own keys form one extra split;
+//   * each 32-key block is staged in LDS: K row-major, V transposed (key-contiguous)
+//     so that it can be the A operand of the PV product;
+//   * S^T = K Q^T with MFMA 16x16x32 bf16: a lane holds 4 keys x 1 query row, so
+//     the row max needs two cross-lane exchanges and the probabilities P^T feed the
+//     next MFMA (O^T += V^T P^T) straight from registers;
+//   * online softmax in fp32 (exp2 domain); partial (max, sum, O) per split go to the
+//     workspace and a combine kernel merges them in a fixed order.
+// fp32 path (head_dim 16/32/64): one thread per (query row, head), plain loops.
+
+#include "vs_internal.hpp"
+
+namespace vs {
+
+namespace {
+
+constexpr int kHD = 128;
+constexpr int kKB = 32;            // keys per block
+constexpr int kKsStride = kHD + 8; // bf16 elements per staged K row (pad: no bank conflicts)
+constexpr int kVtStride = kKB + 8; // bf16 elements per staged V^T row
+constexpr int kPage = 16;
+
+struct AttnArgs {
+  const bf16_t *q, *k_cand, *v_cand, *k_pool, *v_pool;
+  const int32_t *page_table, *prefix_len;
+  bf16_t *out;
+  float *part_o;   // [B*Hkv][n_rb][n_splits+1][rows_per_block][hd]
+  float *part_ml;  // [B*Hkv][n_rb][n_splits+1][rows_per_block][2]
+  int32_t *flags;
+  int B, W, D, M, Hq, Hkv, g, max_pages, n_pool_pages;
+  int rows_per_kv, n_rb, rows_per_block, split_keys, n_splits;
+  float scale_log2;
+};
+
+__device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
+  if (P < 0 || P > max_keys) {
+    *bad = true;
+    return P < 0 ? 0 : max_keys;
+  }
+  return P;
+}
+
+template <int RT>
+__global__ void __launch_bounds__(512)
+attn_mfma_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[kKB * kKsStride];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[kHD * kVtStride];
+  __shared__ int kvalid[kKB];
+
+  const int nthreads = blockDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+
+  const int n_sp = a.n_splits + 1;
+  const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
+  const int bid = xcd_remap(blockIdx.x, nblocks);
+  const int rb = bid % a.n_rb;
+  const int s = (bid / a.n_rb) % n_sp;
+  const int z = bid / (a.n_rb * n_sp);
+  const int b = z / a.Hkv;
+  const int kvh = z % a.Hkv;
+
+  bool badP = false;
+  const int P = clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
+  const int n_pref = (P + a.split_keys - 1) / a.split_keys;
+  const int n_active = n_pref + 1;
+  const bool is_cand = (s == a.n_splits);
+  if (!is_cand && s >= n_pref) return;
+  if (badP && is_cand && rb == 0 && kvh == 0 && tid == 0 && a.flags)
+    atomicOr(&a.flags[b], FLAG_BAD_PAGE);
+
+  const int k_begin = is_cand ? 0 : s * a.split_keys;
+  const int k_end = is_cand ? a.M : min(P, (s + 1) * a.split_keys);
+
+  // ---- this lane's query rows and fragments
+  int rr[RT], mrow[RT];
+  bf16x8 qf[RT][4];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    rr[t] = rb * a.rows_per_block + (wv * RT + t) * 16 + l16;
+    const bool ok = rr[t] < a.rows_per_kv;
+    mrow[t] = ok ? rr[t] / a.g : a.M;   // a.M marks a padding row
+    const int hq = kvh * a.g + (ok ? rr[t] % a.g : 0);
+    const bf16_t *qp = a.q + (((int64_t)b * a.M + (ok ? mrow[t] : 0)) * a.Hq + hq) * kHD;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      if (ok) {
+        qf[t][s4] = *(const bf16x8 *)(qp + 32 * s4 + 8 * lg);
+      } else {
+        qf[t][s4] = bf16x8{};
+      }
+    }
+  }
+
+  f32x4 O[RT][8];
+  float m_run[RT], l_part[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    m_run[t] = -INFINITY;
+    l_part[t] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+
+  for (int kb = k_begin; kb < k_end; kb += kKB) {
+    // ---- stage 32 keys: K row-major, V transposed
+    for (int c = tid; c < kKB * 16; c += nthreads) {
+      const int key = c >> 4;
+      const int ch = c & 15;
+      const int pos = kb + key;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      bool valid = pos < k_end;
+      if (valid) {
+        const bf16_t *kp, *vp;
+        if (is_cand) {
+          const int64_t off = (((int64_t)b * a.M + pos) * a.Hkv + kvh) * kHD + 8 * ch;
+          kp = a.k_cand + off;
+          vp = a.v_cand + off;
+        } else {
+          const int pg = ptab[pos / kPage];
+          if (pg < 0 || pg >= a.n_pool_pages) {
+            valid = false;
+            if (ch == 0 && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
+          }
+          const int64_t off =
+              (((int64_t)(valid ? pg : 0) * kPage + pos % kPage) * a.Hkv + kvh) * kHD + 8 * ch;
+          kp = a.k_pool + off;
+          vp = a.v_pool + off;
+        }
+        if (valid) {
+          kv = *(const u32x4 *)kp;
+          vv = *(const u32x4 *)vp;
+        }
+      }
+      *(u32x4 *)(&Ks[key * kKsStride + 8 * ch]) = kv;
+      const bf16_t *ve = (const bf16_t *)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(8 * ch + e) * kVtStride + key] = ve[e];
+      if (ch == 0) kvalid[key] = valid;
+    }
+    __syncthreads();
+
+    bf16x8 ka[4], kb2[4], vf[8];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      ka[s4] = *(const bf16x8 *)&Ks[l16 * kKsStride + 32 * s4 + 8 * lg];
+      kb2[s4] = *(const bf16x8 *)&Ks[(16 + l16) * kKsStride + 32 * s4 + 8 * lg];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const bf16_t *row = &Vt[(16 * tt + l16) * kVtStride];
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+      const bf16x4 lo = *(const bf16x4 *)(row + 4 * lg);
+      const bf16x4 hi = *(const bf16x4 *)(row + 16 + 4 * lg);
+      vf[tt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    bool vis_a[4], vis_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vis_a[j] = kvalid[4 * lg + j];
+      vis_b[j] = kvalid[16 + 4 * lg + j];
+    }
+
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        sa = mfma16x16x32(ka[s4], qf[t][s4], sa);
+        sb = mfma16x16x32(kb2[s4], qf[t][s4], sb);
+      }
+      float xa[4], xb[4];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bool va = vis_a[j], vb = vis_b[j];
+        if (is_cand) {
+          const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
+          const int m = mrow[t];
+          va = va && m < a.M && ka_i / a.D == m / a.D && ka_i <= m;
+          vb = vb && m < a.M && kb_i / a.D == m / a.D && kb_i <= m;
+        }
+        xa[j] = va ? sa[j] * a.scale_log2 : -INFINITY;
+        xb[j] = vb ? sb[j] * a.scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, fmaxf(xa[j], xb[j]));
+      }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const float mnew = fmaxf(m_run[t], bmax);
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      const float corr = exp2f(m_run[t] - mref);
+      float pa[4], pb[4], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pa[j] = exp2f(xa[j] - mref);
+        pb[j] = exp2f(xb[j] - mref);
+        psum += pa[j] + pb[j];
+      }
+      l_part[t] = l_part[t] * corr + psum;
+      m_run[t] = mnew;
+      uint32_t pk[4] = {pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]),
+                        pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])};
+      const bf16x8 pfrag = *(const bf16x8 *)pk;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        O[t][tt] *= corr;
+        O[t][tt] = mfma16x16x32(vf[tt], pfrag, O[t][tt]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- finish: row sums over the 4 lane groups, then final output or partials
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float l = l_part[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const bool ok = rr[t] < a.rows_per_kv;
+    if (!ok) continue;
+    const int row_in_block = (wv * RT + t) * 16 + l16;
+    if (n_active == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int hq = kvh * a.g + rr[t] % a.g;
+      bf16_t *op = a.out + (((int64_t)b * a.M + mrow[t]) * a.Hq + hq) * kHD;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        uint32_t w0 = pack_bf16x2(O[t][tt][0] * inv, O[t][tt][1] * inv);
+        uint32_t w1 = pack_bf16x2(O[t][tt][2] * inv, O[t][tt][3] * inv);
+        *(uint2 *)(op + 16 * tt + 4 * lg) = make_uint2(w0, w1);
+      }
+    } else {
+      const int64_t slot =
+          (((int64_t)z * a.n_rb + rb) * n_sp + s) * a.rows_per_block + row_in_block;
+      float *po = a.part_o + slot * kHD;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) *(f32x4 *)(po + 16 * tt + 4 * lg) = O[t][tt];
+      if (lg == 0) {
+        a.part_ml[slot * 2 + 0] = m_run[t];
+        a.part_ml[slot * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge the split partials of every row in a fixed order (prefix splits ascending,
+// then the candidate split).  One thread per (row, 4 head-dim values).
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(AttnArgs a) {
+  const int n_sp = a.n_splits + 1;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total_rows = (int64_t)a.B * a.Hkv * a.n_rb * a.rows_per_block;
+  const int64_t row = gid / 32;
+  const int c4 = (int)(gid % 32) * 4;
+  if (row >= total_rows) return;
+  const int row_in_block = (int)(row % a.rows_per_block);
+  const int rb = (int)((row / a.rows_per_block) % a.n_rb);
+  const int z = (int)(row / ((int64_t)a.rows_per_block * a.n_rb));
+  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const int rr = rb * a.rows_per_block + row_in_block;
+  if (rr >= a.rows_per_kv) return;
+  bool badP = false;
+  const int P = clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
+  const int n_pref = (P + a.split_keys - 1) / a.split_keys;
+  if (n_pref == 0) return;  // the candidate split alone wrote the output
+  const int64_t base = ((int64_t)z * a.n_rb + rb) * n_sp;
+  float mx = -INFINITY;
+  for (int k = 0; k <= n_pref; ++k) {
+    const int sp = (k == n_pref) ? a.n_splits : k;
+    mx = fmaxf(mx, a.part_ml[((base + sp) * a.rows_per_block + row_in_block) * 2]);
+  }
+  const float mref = (mx == -INFINITY) ? 0.f : mx;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k <= n_pref; ++k) {
+    const int sp = (k == n_pref) ? a.n_splits : k;
+    const int64_t slot = (base + sp) * a.rows_per_block + row_in_block;
+    const float w = exp2f(a.part_ml[slot * 2] - mref);
+    l += w * a.part_ml[slot * 2 + 1];
+    const f32x4 o = *(const f32x4 *)(a.part_o + slot * kHD + c4);
+    acc += w * o;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int m = rr / a.g;
+  const int hq = kvh * a.g + rr % a.g;
+  bf16_t *op = a.out + (((int64_t)b * a.M + m) * a.Hq + hq) * kHD + c4;
+  *(uint2 *)op = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                            pack_bf16x2(acc[2] * inv, acc[3] * inv));
+}
+
+// ---------------------------------------------------------------------------- fp32 path
+template <int HD>
+__global__ void __launch_bounds__(256)
+attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const float *k_pool,
+                const float *v_pool, const int32_t *page_table, const int32_t *prefix_len,
+                float *out, int32_t *flags, int B, int W, int D, int Hq, int Hkv, int max_pages,
+                int n_pool_pages, float scale) {
+  const int M = W * D;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)B * M * Hq) return;
+  const int hq = (int)(gid % Hq);
+  const int r = (int)((gid / Hq) % M);
+  const int b = (int)(gid / ((int64_t)Hq * M));
+  const int kvh = hq / (Hq / Hkv);
+  bool badP = false;
+  const int P = clamp_prefix(prefix_len[b], max_pages * kPage, &badP);
+  if (badP && flags && r == 0 && hq == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
+  float qv[HD], acc[HD];
+  const float *qp = q + (((int64_t)b * M + r) * Hq + hq) * HD;
+  for (int e = 0; e < HD; ++e) {
+    qv[e] = qp[e];
+    acc[e] = 0.f;
+  }
+  float mx = -INFINITY, l = 0.f;
+  const int i = r / D, o = r % D;
+  const int nkeys = P + o + 1;
+  for (int k = 0; k < nkeys; ++k) {
+    const float *kp, *vp;
+    if (k < P) {
+      const int pg = page_table[(int64_t)b * max_pages + k / kPage];
+      if (pg < 0 || pg >= n_pool_pages) {
+        if (flags && (k % kPage) == 0 && hq == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
+        continue;
+      }
+      const int64_t off = (((int64_t)pg * kPage + k % kPage) * Hkv + kvh) * HD;
+      kp = k_pool + off;
+      vp = v_pool + off;
+    } else {
+      const int64_t off = (((int64_t)b * M + i * D + (k - P)) * Hkv + kvh) * HD;
+      kp = k_cand + off;
+      vp = v_cand + off;
+    }
+    float sdot = 0.f;
+    for (int e = 0; e < HD; ++e) sdot = fmaf(qv[e], kp[e], sdot);
+    sdot *= scale;
+    const float mnew = fmaxf(mx, sdot);
+    const float corr = expf(mx - mnew);
+    const float p = expf(sdot - mnew);
+    l = l * corr + p;
+    for (int e = 0; e < HD; ++e) acc[e] = acc[e] * corr + p * vp[e];
+    mx = mnew;
+  }
+  float *op = out + (((int64_t)b * M + r) * Hq + hq) * HD;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  for (int e = 0; e < HD; ++e) op[e] = acc[e] * inv;
+}
+
+__global__ void zero_i32_kernel(int32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page) {
+  AttnPlan p{};
+  const int M = W * D;
+  const int g = Hq / Hkv;
+  p.rows_per_kv = g * M;
+  const int tiles = (p.rows_per_kv + 15) / 16;
+  // row block: fewest padded rows, then the largest block (fewer re-reads of K/V)
+  int best_waste = 1 << 30, best_rows = 0;
+  for (int rt = 1; rt <= 2; ++rt) {
+    for (int nw = 1; nw <= 8; ++nw) {
+      const int tpb = rt * nw;
+      const int nrb = (tiles + tpb - 1) / tpb;
+      const int waste = nrb * tpb - tiles;
+      const int rows = tpb * 16;
+      if (tpb > tiles && nw > 1) continue;
+      if (waste < best_waste || (waste == best_waste && rows > best_rows)) {
+        best_waste = waste;
+        best_rows = rows;
+        p.rt = rt;
+        p.nw = nw;
+      }
+    }
+  }
+  p.rows_per_block = p.rt * p.nw * 16;
+  p.n_rb = (tiles + p.rt * p.nw - 1) / (p.rt * p.nw);
+  // key splits: about 256 workgroups of prefix work for the longest sequence's share
+  const int max_keys = max_pages * page;
+  const int groups = B * Hkv * p.n_rb;
+  int want = (256 + groups - 1) / groups;
+  if (want < 1) want = 1;
+  int sk = (max_keys + want - 1) / want;
+  sk = ((sk + kKB - 1) / kKB) * kKB;
+  if (sk < 256) sk = 256;
+  p.split_keys = sk;
+  p.n_splits = (max_keys + sk - 1) / sk;
+  if (p.n_splits < 1) p.n_splits = 1;
+  return p;
+}
+
+size_t attn_workspace_bytes(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages, int page,
+                            int dtype) {
+  if (dtype != 1) return 0;
+  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, page);
+  const size_t slots = (size_t)B * Hkv * p.n_rb * (p.n_splits + 1) * p.rows_per_block;
+  return slots * (size_t)(kHD + 2) * sizeof(float) + 256;
+}
+
+hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages,
+                            int n_pool_pages, int dtype, float scale, const void *q,
+                            const void *k_cand, const void *v_cand, const void *k_pool,
+                            const void *v_pool, const int32_t *page_table,
+                            const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
+                            hipStream_t st) {
+  const int M = W * D;
+  if (dtype == 0) {
+    const int64_t n = (int64_t)B * M * Hq;
+    const int blocks = (int)((n + 255) / 256);
+#define VS_F32_ATTN(HDV)                                                                       \
+  hipLaunchKernelGGL(attn_f32_kernel<HDV>, dim3(blocks), dim3(256), 0, st, (const float *)q,   \
+                     (const float *)k_cand, (const float *)v_cand, (const float *)k_pool,      \
+                     (const float *)v_pool, page_table, prefix_len, (float *)out, flags, B, W, \
+                     D, Hq, Hkv, max_pages, n_pool_pages, scale)
+    if (hd == 16) VS_F32_ATTN(16);
+    else if (hd == 32) VS_F32_ATTN(32);
+    else VS_F32_ATTN(64);
+#undef VS_F32_ATTN
+    return hipGetLastError();
+  }
+  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, kPage);
+  AttnArgs a;
+  a.q = (const bf16_t *)q;
+  a.k_cand = (const bf16_t *)k_cand;
+  a.v_cand = (const bf16_t *)v_cand;
+  a.k_pool = (const bf16_t *)k_pool;
+  a.v_pool = (const bf16_t *)v_pool;
+  a.page_table = page_table;
+  a.prefix_len = prefix_len;
+  a.out = (bf16_t *)out;
+  const size_t slots = (size_t)B * Hkv * p.n_rb * (p.n_splits + 1) * p.rows_per_block;
+  a.part_o = (float *)ws;
+  a.part_ml = a.part_o + slots * kHD;
+  a.flags = flags;
+  a.B = B;
+  a.W = W;
+  a.D = D;
+  a.M = M;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = Hq / Hkv;
+  a.max_pages = max_pages;
+  a.n_pool_pages = n_pool_pages;
+  a.rows_per_kv = p.rows_per_kv;
+  a.n_rb = p.n_rb;
+  a.rows_per_block = p.rows_per_block;
+  a.split_keys = p.split_keys;
+  a.n_splits = p.n_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int nblocks = p.n_rb * (p.n_splits + 1) * B * Hkv;
+  if (p.rt == 1)
+    hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3(nblocks), dim3(64 * p.nw), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_mfma_kernel<2>, dim3(nblocks), dim3(64 * p.nw), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)B * Hkv * p.n_rb * p.rows_per_block * 32;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st) {
+  if (n <= 0 || p == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace vs

@@ -1,0 +1,277 @@
+// C ABI of libvstep: argument validation (before anything is enqueued), workspace
+// sizing and the verify-step orchestration.  See include/vstep.h for the contract.
+
+#include "../../include/vstep.h"
+#include "vs_internal.hpp"
+
+#include <math.h>
+
+namespace vs {
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
+}
+
+namespace {
+
+constexpr int kMaxRows = 1024;      // W*D per sequence
+constexpr int kMaxVocabSampler = 1024 * 512;
+
+inline hipStream_t S(void *s) { return (hipStream_t)s; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? VS_OK : VS_ERR_HIP; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_attn(const vs_attn_desc *d) {
+  if (!d) return VS_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->W <= 0 || d->D <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->head_dim <= 0 ||
+      d->max_pages < 0 || d->n_pool_pages < 0)
+    return VS_ERR_INVALID_ARG;
+  if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
+  if (d->Hq % d->Hkv != 0) return VS_ERR_INVALID_ARG;
+  if (d->page_size != 16) return VS_ERR_UNSUPPORTED;
+  if (d->dtype == VS_BF16) {
+    if (d->head_dim != 128) return VS_ERR_UNSUPPORTED;
+  } else if (d->dtype == VS_F32) {
+    if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64) return VS_ERR_UNSUPPORTED;
+  } else {
+    return VS_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)d->max_pages * 16 > (1 << 28)) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+int check_head(const vs_head_desc *d) {
+  if (!d) return VS_ERR_INVALID_ARG;
+  if (d->M <= 0 || d->d <= 0 || d->V <= 0 || d->rank < 0) return VS_ERR_INVALID_ARG;
+  if (!(d->temperature > 0.f) || !isfinite(d->temperature)) return VS_ERR_INVALID_ARG;
+  if (d->dtype == VS_BF16) {
+    if (d->d % 32 != 0 || d->rank % 32 != 0) return VS_ERR_UNSUPPORTED;
+  } else if (d->dtype != VS_F32) {
+    return VS_ERR_UNSUPPORTED;
+  }
+  return VS_OK;
+}
+
+int check_sample(const vs_sample_desc *d) {
+  if (!d) return VS_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->W <= 0 || d->D <= 0 || d->V <= 0) return VS_ERR_INVALID_ARG;
+  if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
+  if (!(d->temperature > 0.f) || !isfinite(d->temperature)) return VS_ERR_INVALID_ARG;
+  if (d->V > kMaxVocabSampler) return VS_ERR_UNSUPPORTED;
+  return VS_OK;
+}
+
+float attn_scale(float scale, int hd) { return scale > 0.f ? scale : 1.0f / sqrtf((float)hd); }
+
+struct StepLayout {
+  size_t attn, head, total;
+};
+
+StepLayout step_layout(const vs_step_desc *d) {
+  StepLayout L;
+  L.attn = 0;
+  const size_t a = vs::attn_workspace_bytes(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim,
+                                            d->max_pages, 16, d->dtype);
+  L.head = align256(a);
+  const size_t h = vs::head_workspace_bytes(d->B * d->W * d->D, d->d, d->V, 0, d->dtype);
+  L.total = align256(L.head + h);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vs_abi_version(void) { return VS_ABI_VERSION; }
+
+const char *vs_status_str(int s) {
+  switch (s) {
+    case VS_OK: return "ok";
+    case VS_ERR_INVALID_ARG: return "invalid argument";
+    case VS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VS_ERR_WORKSPACE: return "workspace missing or too small";
+    case VS_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int vs_copy_match(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B, int kappa,
+                  int W, int D, int32_t *cand_tok, int32_t *cand_len, int32_t *cand_pos,
+                  int32_t *n_found, int32_t *flags, void *stream) {
+  if (!ctx_off || !cand_tok || !cand_len || !cand_pos || !n_found) return VS_ERR_INVALID_ARG;
+  if (ctx_total < 0 || (ctx_total > 0 && !ctx)) return VS_ERR_INVALID_ARG;
+  if (B <= 0 || W <= 0 || D <= 0 || (int64_t)W * D > kMaxRows) return VS_ERR_INVALID_ARG;
+  if (kappa < 1 || kappa > 16) return VS_ERR_UNSUPPORTED;
+  return hip_status(vs::launch_copy_match(ctx, ctx_total, ctx_off, B, kappa, W, D, cand_tok,
+                                          cand_len, cand_pos, n_found, flags, nullptr, 0, nullptr,
+                                          0, 0.f, nullptr, nullptr, S(stream)));
+}
+
+int vs_probe_gate(const void *h, int h_dtype, const float *w, int B, int d, float tau,
+                  const int32_t *n_found, float *score, int32_t *gate, int32_t *flags,
+                  void *stream) {
+  if (!h || !w || !score || !gate) return VS_ERR_INVALID_ARG;
+  if (B <= 0 || d <= 0 || !isfinite(tau)) return VS_ERR_INVALID_ARG;
+  if (h_dtype != VS_F32 && h_dtype != VS_BF16) return VS_ERR_UNSUPPORTED;
+  return hip_status(vs::launch_probe_gate(h, h_dtype == VS_BF16, w, B, d, tau, n_found, score,
+                                          gate, flags, S(stream)));
+}
+
+size_t vs_attention_workspace_bytes(const vs_attn_desc *d) {
+  if (check_attn(d) != VS_OK) return 0;
+  return vs::attn_workspace_bytes(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->max_pages,
+                                  d->page_size, d->dtype);
+}
+
+int vs_verify_attention(const vs_attn_desc *d, const void *q, const void *k_cand,
+                        const void *v_cand, const void *k_pool, const void *v_pool,
+                        const int32_t *page_table, const int32_t *prefix_len, void *out,
+                        int32_t *flags, void *workspace, size_t ws_bytes, void *stream) {
+  int st = check_attn(d);
+  if (st != VS_OK) return st;
+  if (!q || !k_cand || !v_cand || !prefix_len || !out) return VS_ERR_INVALID_ARG;
+  if (d->max_pages > 0 && (!k_pool || !v_pool || !page_table)) return VS_ERR_INVALID_ARG;
+  const size_t need = vs_attention_workspace_bytes(d);
+  if (need > 0 && (!workspace || ws_bytes < need)) return VS_ERR_WORKSPACE;
+  if (flags) {
+    hipError_t e = vs::launch_zero_i32(flags, d->B, S(stream));
+    if (e != hipSuccess) return VS_ERR_HIP;
+  }
+  return hip_status(vs::launch_attention(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim,
+                                         d->max_pages, d->n_pool_pages, d->dtype,
+                                         attn_scale(d->scale, d->head_dim), q, k_cand, v_cand,
+                                         k_pool, v_pool, page_table, prefix_len, out, flags,
+                                         workspace, S(stream)));
+}
+
+size_t vs_head_workspace_bytes(const vs_head_desc *d) {
+  if (check_head(d) != VS_OK) return 0;
+  return vs::head_workspace_bytes(d->M, d->d, d->V, d->rank, d->dtype);
+}
+
+int vs_lm_head(const vs_head_desc *d, const void *h, const void *w_full, const void *w_down,
+               const void *w_up, float *logits, double *row_lse, float *probs, void *workspace,
+               size_t ws_bytes, void *stream) {
+  int st = check_head(d);
+  if (st != VS_OK) return st;
+  if (!h || !logits || !row_lse) return VS_ERR_INVALID_ARG;
+  if (d->rank == 0 && !w_full) return VS_ERR_INVALID_ARG;
+  if (d->rank > 0 && (!w_down || !w_up || w_full)) return VS_ERR_INVALID_ARG;
+  if (d->write_probs && !probs) return VS_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < vs_head_workspace_bytes(d)) return VS_ERR_WORKSPACE;
+  hipError_t e = vs::launch_head_gemm(d->M, d->d, d->V, d->rank, d->dtype, d->temperature, h,
+                                      w_full, w_down, w_up, logits, workspace, S(stream));
+  if (e != hipSuccess) return VS_ERR_HIP;
+  return hip_status(vs::launch_head_finish(d->M, d->d, d->V, d->rank, d->dtype, d->temperature,
+                                           logits, row_lse, d->write_probs ? probs : nullptr,
+                                           workspace, S(stream)));
+}
+
+size_t vs_sample_workspace_bytes(const vs_sample_desc *d) {
+  if (check_sample(d) != VS_OK) return 0;
+  return vs::sample_workspace_bytes(d->B, d->W, d->D, d->V);
+}
+
+int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const float *logits,
+                     const double *row_lse, const float *q, const int32_t *cand_tok,
+                     const int32_t *cand_len, const double *u_acc, const double *u_res,
+                     const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
+                     int32_t *n_out, int32_t *acc_per_cand, int32_t *flags, void *workspace,
+                     size_t ws_bytes, void *stream) {
+  int st = check_sample(d);
+  if (st != VS_OK) return st;
+  if (!root_logits || !logits || !row_lse || !cand_tok || !cand_len || !u_acc || !u_res ||
+      !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
+    return VS_ERR_INVALID_ARG;
+  const size_t need = vs_sample_workspace_bytes(d);
+  if (need > 0 && (!workspace || ws_bytes < need)) return VS_ERR_WORKSPACE;
+  return hip_status(vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, root_logits, logits,
+                                       row_lse, q, cand_tok, cand_len, u_acc, u_res, gate, n_acc,
+                                       best, out_tok, n_out, acc_per_cand, flags, 0, workspace,
+                                       S(stream)));
+}
+
+static int check_step(const vs_step_desc *d) {
+  if (!d) return VS_ERR_INVALID_ARG;
+  vs_attn_desc ad = {d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->page_size, d->max_pages,
+                     d->n_pool_pages, d->dtype, d->scale};
+  int st = check_attn(&ad);
+  if (st != VS_OK) return st;
+  vs_head_desc hd = {d->B * d->W * d->D, d->d, d->V, 0, d->dtype, d->temperature, 0};
+  if ((st = check_head(&hd)) != VS_OK) return st;
+  vs_sample_desc sd = {d->B, d->W, d->D, d->V, d->temperature};
+  if ((st = check_sample(&sd)) != VS_OK) return st;
+  if (d->d != d->Hq * d->head_dim) return VS_ERR_INVALID_ARG;
+  if (!d->external_drafts) {
+    if (d->kappa < 1 || d->kappa > 16) return VS_ERR_UNSUPPORTED;
+    if (d->ctx_total < 0 || !isfinite(d->tau)) return VS_ERR_INVALID_ARG;
+  }
+  return VS_OK;
+}
+
+size_t vs_step_workspace_bytes(const vs_step_desc *d) {
+  if (check_step(d) != VS_OK) return 0;
+  return step_layout(d).total;
+}
+
+int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  int st = check_step(d);
+  if (st != VS_OK) return st;
+  if (!io) return VS_ERR_INVALID_ARG;
+  if (!io->q || !io->k_cand || !io->v_cand || !io->prefix_len || !io->w_full ||
+      !io->root_logits || !io->u_acc || !io->u_res || !io->cand_tok || !io->cand_len ||
+      !io->attn_out || !io->logits || !io->row_lse || !io->n_acc || !io->best || !io->out_tok ||
+      !io->n_out || !io->acc_per_cand || !io->flags)
+    return VS_ERR_INVALID_ARG;
+  if (d->max_pages > 0 && (!io->k_pool || !io->v_pool || !io->page_table))
+    return VS_ERR_INVALID_ARG;
+  if (!d->external_drafts) {
+    if (!io->ctx_off || (d->ctx_total > 0 && !io->ctx) || !io->probe_h || !io->probe_w ||
+        !io->cand_pos || !io->n_found || !io->score || !io->gate)
+      return VS_ERR_INVALID_ARG;
+  }
+  const StepLayout L = step_layout(d);
+  if (!workspace || ws_bytes < L.total) return VS_ERR_WORKSPACE;
+  hipStream_t s = S(stream);
+  hipEvent_t *ev = (hipEvent_t *)io->stage_events;
+  auto mark = [&](int i) -> bool {
+    return ev == nullptr || hipEventRecord(ev[i], s) == hipSuccess;
+  };
+  const int M = d->B * d->W * d->D;
+  char *ws = (char *)workspace;
+  hipError_t e;
+  if (!mark(0)) return VS_ERR_HIP;
+  // 1. copy retrieval + probe gate (one launch), or external drafts
+  if (!d->external_drafts) {
+    e = vs::launch_copy_match(io->ctx, d->ctx_total, io->ctx_off, d->B, d->kappa, d->W, d->D,
+                              io->cand_tok, io->cand_len, io->cand_pos, io->n_found, io->flags,
+                              io->probe_h, d->dtype == VS_BF16, io->probe_w, d->d, d->tau,
+                              io->score, io->gate, s);
+  } else {
+    e = vs::launch_zero_i32(io->flags, d->B, s);
+  }
+  if (e != hipSuccess || !mark(1)) return VS_ERR_HIP;
+  // 2. verify attention
+  e = vs::launch_attention(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->max_pages,
+                           d->n_pool_pages, d->dtype, attn_scale(d->scale, d->head_dim), io->q,
+                           io->k_cand, io->v_cand, io->k_pool, io->v_pool, io->page_table,
+                           io->prefix_len, io->attn_out, io->flags, ws + L.attn, s);
+  if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
+  // 3. head: GEMM + tile statistics, then the row normaliser
+  e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,
+                           nullptr, nullptr, io->logits, ws + L.head, s);
+  if (e != hipSuccess || !mark(3)) return VS_ERR_HIP;
+  e = vs::launch_head_finish(M, d->d, d->V, 0, d->dtype, d->temperature, io->logits, io->row_lse,
+                             nullptr, ws + L.head, s);
+  if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
+  // 4. rejection sampling
+  e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
+                         io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_acc,
+                         io->u_res, d->external_drafts ? nullptr : io->gate, io->n_acc, io->best,
+                         io->out_tok, io->n_out, io->acc_per_cand, io->flags, 1, nullptr, s);
+  if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
+  return VS_OK;
+}
+
+}  // extern "C"

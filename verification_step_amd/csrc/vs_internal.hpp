@@ -1,0 +1,105 @@
+// Internal declarations shared by the HIP translation units of libvstep.
+// Kernels are written for gfx950 (CDNA4): wave64, MFMA bf16 16x16x32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vs {
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+// flag bits (same values as the public header)
+enum : int {
+  FLAG_PROBE_TIE = 1, FLAG_ACCEPT_TIE = 2, FLAG_CDF_TIE = 4, FLAG_DEGENERATE = 8,
+  FLAG_NO_CANDIDATE = 16, FLAG_BAD_PAGE = 32, FLAG_BAD_CTX = 64, FLAG_BAD_TOKEN = 128
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs here are finite)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
+
+// Bijection of a 1-D workgroup index so that consecutive logical tiles land on the
+// same XCD (workgroups are dealt round-robin over the 8 XCDs of an MI355X), letting
+// tiles that share operands share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks / 8;
+  if (bid >= 8 * q) return bid;
+  return (bid % 8) * q + bid / 8;
+}
+
+// ---------------------------------------------------------------------------- launchers
+struct AttnPlan {
+  int rt;           // row tiles (16 rows) per wave
+  int nw;           // waves per workgroup
+  int rows_per_kv;  // g * M
+  int n_rb;         // row blocks per (sequence, kv head)
+  int rows_per_block;
+  int split_keys;   // prefix keys per split (multiple of 32)
+  int n_splits;     // prefix splits (a candidate split is added after them)
+};
+
+AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page);
+size_t attn_workspace_bytes(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages, int page,
+                            int dtype);
+
+hipError_t launch_copy_match(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B,
+                             int kappa, int W, int D, int32_t *cand_tok, int32_t *cand_len,
+                             int32_t *cand_pos, int32_t *n_found, int32_t *flags,
+                             // fused probe (h == nullptr: retrieval only)
+                             const void *h, int h_bf16, const float *w, int d, float tau,
+                             float *score, int32_t *gate, hipStream_t st);
+
+hipError_t launch_probe_gate(const void *h, int h_bf16, const float *w, int B, int d, float tau,
+                             const int32_t *n_found, float *score, int32_t *gate, int32_t *flags,
+                             hipStream_t st);
+
+hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages,
+                            int n_pool_pages, int dtype, float scale, const void *q,
+                            const void *k_cand, const void *v_cand, const void *k_pool,
+                            const void *v_pool, const int32_t *page_table,
+                            const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
+                            hipStream_t st);
+
+size_t head_workspace_bytes(int M, int d, int V, int rank, int dtype);
+// Two phases so that the step can time them separately: the GEMM (+ per-tile row
+// statistics), then the row normaliser (+ optional probabilities).
+hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temperature,
+                            const void *h, const void *w_full, const void *w_down,
+                            const void *w_up, float *logits, void *ws, hipStream_t st);
+hipError_t launch_head_finish(int M, int d, int V, int rank, int dtype, float temperature,
+                              const float *logits, double *row_lse, float *probs, void *ws,
+                              hipStream_t st);
+
+size_t sample_workspace_bytes(int B, int W, int D, int V);
+hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
+                          const float *logits, const double *row_lse, const float *q,
+                          const int32_t *cand_tok, const int32_t *cand_len, const double *u_acc,
+                          const double *u_res, const int32_t *gate, int32_t *n_acc, int32_t *best,
+                          int32_t *out_tok, int32_t *n_out, int32_t *acc_per_cand,
+                          int32_t *flags, int flags_accumulate, void *ws, hipStream_t st);
+
+}  // namespace vs

@@ -143,10 +143,18 @@ def probe_gate(h: np.ndarray, w: np.ndarray, tau: float, n_found=None):
 # ----------------------------------------------------------------------------------
 # a3: block-triangular verify attention  [SW, "무엇과 다른가"]
 
+def token_major(pool: np.ndarray, kind: str) -> np.ndarray:
+    """View a paged pool as [n_pages, page, Hkv, hd].  K pages are stored
+    [n_pages, Hkv, page, hd]; V pages transposed, [n_pages, Hkv, hd, page]."""
+    if kind == "k":
+        return np.transpose(pool, (0, 2, 1, 3))
+    return np.transpose(pool, (0, 3, 1, 2))
+
+
 def gather_prefix(pool: np.ndarray, page_table: np.ndarray, b: int, P: int, page: int):
-    """Rows 0..P-1 of sequence b's prefix from a paged pool [n_pages, page, Hkv, hd].
-    Returns (rows [P, Hkv, hd], valid mask [P]) -- rows of out-of-range pages are
-    marked invalid."""
+    """Rows 0..P-1 of sequence b's prefix from a token-major paged view
+    [n_pages, page, Hkv, hd].  Returns (rows [P, Hkv, hd], valid mask [P]) -- rows of
+    out-of-range pages are marked invalid."""
     n_pages = pool.shape[0]
     rows = np.zeros((P,) + pool.shape[2:], dtype=pool.dtype)
     valid = np.zeros(P, dtype=bool)
@@ -170,7 +178,7 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len,
     the softmax of the visible scores; the output is the weighted sum of values.
 
     Inputs are fp64 arrays (decoded): q [B*M, Hq, hd], k_cand/v_cand [B*M, Hkv, hd],
-    pools [n_pages, page, Hkv, hd].  Returns (O exact fp64, O rounded to out_dtype,
+    k_pool [n_pages, Hkv, page, hd], v_pool [n_pages, Hkv, hd, page].  Returns (O exact fp64, O rounded to out_dtype,
     flags [B])."""
     M = W * D
     hd = q.shape[-1]
@@ -185,8 +193,8 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len,
         if P < 0 or P > max_keys:
             flags[b] |= FLAG_BAD_PAGE
             P = min(max(P, 0), max_keys)
-        kp, valid = gather_prefix(k_pool, page_table, b, P, page)
-        vp, _ = gather_prefix(v_pool, page_table, b, P, page)
+        kp, valid = gather_prefix(token_major(k_pool, "k"), page_table, b, P, page)
+        vp, _ = gather_prefix(token_major(v_pool, "v"), page_table, b, P, page)
         if not valid.all():
             flags[b] |= FLAG_BAD_PAGE
         for i in range(W):

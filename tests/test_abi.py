@@ -122,7 +122,7 @@ def test_head_validation(lib):
     assert call(write_probs=1) == -1         # probs requested but null
     assert call(nbytes=16) == -3
     d = L.HeadDesc(**ok)
-    assert lib.vs_head_workspace_bytes(C.byref(d)) >= 80 * 1002 * 8     # (max, sum) per row and 128-row tile
+    assert lib.vs_head_workspace_bytes(C.byref(d)) >= 80 * 501 * 8      # (max, sum) per row and 256-row tile
 
 
 def test_sample_validation(lib):

@@ -23,8 +23,8 @@ def _rand_case(rng, B, W, D, Hq, Hkv, hd, P, page=16, shuffle=True):
     q = rng.standard_normal((B * M, Hq, hd))
     kc = rng.standard_normal((B * M, Hkv, hd))
     vc = rng.standard_normal((B * M, Hkv, hd))
-    kp = rng.standard_normal((n_pages, page, Hkv, hd))
-    vp = rng.standard_normal((n_pages, page, Hkv, hd))
+    kp = rng.standard_normal((n_pages, Hkv, page, hd))          # K pages: token rows
+    vp = rng.standard_normal((n_pages, Hkv, hd, page))          # V pages: transposed
     perm = rng.permutation(n_pages) if shuffle else np.arange(n_pages)
     pt = np.full((B, max(maxp, 1)), -1, dtype=np.int32)
     o = 0
@@ -34,9 +34,16 @@ def _rand_case(rng, B, W, D, Hq, Hkv, hd, P, page=16, shuffle=True):
     return q, kc, vc, kp, vp, pt, np.asarray(P, dtype=np.int32)
 
 
-def _contiguous_prefix(pool, pt, b, P, page=16):
-    rows = [pool[pt[b, pos // page], pos % page] for pos in range(P)]
-    return np.stack(rows) if rows else np.zeros((0,) + pool.shape[2:])
+def _contiguous_prefix(pool, pt, b, P, page=16, kind="k"):
+    """Prefix rows [P, Hkv, hd] read element by element from the paged layout."""
+    Hkv = pool.shape[1]
+    hd = pool.shape[3] if kind == "k" else pool.shape[2]
+    out = np.zeros((P, Hkv, hd))
+    for pos in range(P):
+        pg, off = pt[b, pos // page], pos % page
+        for h in range(Hkv):
+            out[pos, h] = pool[pg, h, off, :] if kind == "k" else pool[pg, h, :, off]
+    return out
 
 
 def causal_per_candidate(q, kc, vc, kp, vp, pt, plen, B, W, D, Hq, Hkv):
@@ -48,8 +55,8 @@ def causal_per_candidate(q, kc, vc, kp, vp, pt, plen, B, W, D, Hq, Hkv):
     out = np.zeros_like(q)
     for b in range(B):
         P = int(plen[b])
-        Kp = _contiguous_prefix(kp, pt, b, P)
-        Vp = _contiguous_prefix(vp, pt, b, P)
+        Kp = _contiguous_prefix(kp, pt, b, P, kind="k")
+        Vp = _contiguous_prefix(vp, pt, b, P, kind="v")
         for i in range(W):
             rows = slice(b * M + i * D, b * M + (i + 1) * D)
             K = np.concatenate([Kp, kc[rows]], axis=0)            # [P+D, Hkv, hd]
@@ -88,7 +95,7 @@ def test_zero_query_gives_mean_of_visible_values():
     q, kc, vc, kp, vp, pt, plen = _rand_case(rng, B, W, D, Hq, Hkv, hd, P)
     q[:] = 0.0
     O, _, _ = oracle.verify_attention(q, kc, vc, kp, vp, pt, plen, B, W, D, Hq, Hkv)
-    Vp = _contiguous_prefix(vp, pt, 0, 21)[:, 0, :]
+    Vp = _contiguous_prefix(vp, pt, 0, 21, kind="v")[:, 0, :]
     for i in range(W):
         for o in range(D):
             vis = np.concatenate([Vp, vc[i * D:i * D + o + 1, 0, :]])
@@ -101,7 +108,7 @@ def test_constant_values_pass_through():
     q, kc, vc, kp, vp, pt, plen = _rand_case(rng, B, W, D, Hq, Hkv, hd, P)
     c = rng.standard_normal(hd)
     vc[:] = c
-    vp[:] = c
+    vp[:] = c[None, None, :, None]                          # V pages hold hd on axis 2
     O, _, _ = oracle.verify_attention(q, kc, vc, kp, vp, pt, plen, B, W, D, Hq, Hkv)
     assert np.abs(O - c).max() < 1e-13
 
@@ -124,8 +131,8 @@ def test_single_token_candidates_are_decode_attention():
     W, hd, P = 3, 8, (30,)
     q, kc, vc, kp, vp, pt, plen = _rand_case(rng, 1, W, 1, 2, 1, hd, P)
     O, _, _ = oracle.verify_attention(q, kc, vc, kp, vp, pt, plen, 1, W, 1, 2, 1)
-    Kp = _contiguous_prefix(kp, pt, 0, 30)[:, 0, :]
-    Vp = _contiguous_prefix(vp, pt, 0, 30)[:, 0, :]
+    Kp = _contiguous_prefix(kp, pt, 0, 30, kind="k")[:, 0, :]
+    Vp = _contiguous_prefix(vp, pt, 0, 30, kind="v")[:, 0, :]
     for i in range(W):
         K = np.concatenate([Kp, kc[i:i + 1, 0, :]])
         Vv = np.concatenate([Vp, vc[i:i + 1, 0, :]])

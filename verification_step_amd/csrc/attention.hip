@@ -8,16 +8,24 @@
 //     and cut into blocks of NW waves x RT tiles x 16 rows;
 //   * prefix keys are split in ranges of `split_keys` (paged KV, 16-token pages);
 //     the candidates' own keys form one extra split;
-//   * each 32-key block is staged in LDS: K row-major, V transposed (key-contiguous)
-//     so that it can be the A operand of the PV product;
+//   * the paged cache is head-major per page: K [page][kv head][16 tokens][hd] and
+//     V transposed within a page, [page][kv head][hd][16 tokens], so a 32-key block
+//     of either is a few contiguous 4 KB runs; the next block is loaded into
+//     registers while the current one (double-buffered in LDS) is multiplied;
+//   * K sits in LDS row-major and V key-contiguous, the A operand of the PV product;
 //   * S^T = K Q^T with MFMA 16x16x32 bf16: a lane holds 4 keys x 1 query row, so
 //     the row max needs two cross-lane exchanges and the probabilities P^T feed the
 //     next MFMA (O^T += V^T P^T) straight from registers;
-//   * online softmax in fp32 (exp2 domain); partial (max, sum, O) per split go to the
-//     workspace and a combine kernel merges them in a fixed order.
+//   * online softmax in fp32 (exp2 domain); P enters the PV product as bf16 hi + lo
+//     (two MFMAs), which keeps the output error at the bf16 rounding of O itself;
+//   * partial (max, sum, O) per split go to the workspace and a combine kernel
+//     merges them in a fixed order.
 // fp32 path (head_dim 16/32/64): one thread per (query row, head), plain loops.
 
 #include "vs_internal.hpp"
+
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace vs {
 
@@ -49,12 +57,22 @@ __device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
   return P;
 }
 
+// One 32-key block of prefix keys (two 16-token pages) as 16-byte chunks: 512 chunks
+// of K (page, key, 8 head-dim values) and 512 chunks of V^T (page, head-dim row,
+// 8 keys).  Each thread owns chunks tid, tid + nthreads, ...
+constexpr int kChunksPerBlock = 1024;
+constexpr int kMaxChunksPerThread = 8;    // workgroups have >= 2 waves
+
+struct BlockRegs {
+  u32x4 c[kMaxChunksPerThread];
+};
+
 template <int RT>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(RT == 1 ? 512 : 256)
 attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kKB * kKsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kHD * kVtStride];
-  __shared__ int kvalid[kKB];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kKB * kKsStride];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][kHD * kVtStride];
+  __shared__ int kvalid[2][kKB];
 
   const int nthreads = blockDim.x;
   const int tid = threadIdx.x;
@@ -62,6 +80,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int wv = tid >> 6;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  const int nchunk = (kChunksPerBlock + nthreads - 1) / nthreads;
 
   const int n_sp = a.n_splits + 1;
   const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
@@ -95,13 +114,7 @@ attn_mfma_kernel(AttnArgs a) {
     const int hq = kvh * a.g + (ok ? rr[t] % a.g : 0);
     const bf16_t *qp = a.q + (((int64_t)b * a.M + (ok ? mrow[t] : 0)) * a.Hq + hq) * kHD;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      if (ok) {
-        qf[t][s4] = *(const bf16x8 *)(qp + 32 * s4 + 8 * lg);
-      } else {
-        qf[t][s4] = bf16x8{};
-      }
-    }
+    for (int s4 = 0; s4 < 4; ++s4) qf[t][s4] = ok ? *(const bf16x8 *)(qp + 32 * s4 + 8 * lg) : bf16x8{};
   }
 
   f32x4 O[RT][8];
@@ -116,53 +129,90 @@ attn_mfma_kernel(AttnArgs a) {
 
   const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
 
-  for (int kb = k_begin; kb < k_end; kb += kKB) {
-    // ---- stage 32 keys: K row-major, V transposed
+  // ---- prefix blocks: global -> registers (next block) while this block is used
+  BlockRegs regs;
+  int pg_cur[2] = {-1, -1};
+  auto fetch_prefix = [&](int kb) {
+    int pg[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int pos = kb + 16 * p;
+      pg[p] = -1;
+      if (pos < k_end) {
+        const int v = ptab[pos / kPage];
+        if (v >= 0 && v < a.n_pool_pages) pg[p] = v;
+        else if (tid == 0 && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
+      }
+      pg_cur[p] = pg[p];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxChunksPerThread; ++j) {
+      if (j >= nchunk) break;
+      const int c = tid + j * nthreads;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c < 512) {
+        const int p = c >> 8, key = (c & 255) >> 4, ch = c & 15;
+        if (pg[p] >= 0 && kb + 16 * p + key < k_end)
+          v = *(const u32x4 *)(a.k_pool + (((int64_t)pg[p] * a.Hkv + kvh) * kPage + key) * kHD +
+                               8 * ch);
+      } else if (c < 1024) {
+        const int c2 = c - 512;
+        const int p = c2 >> 8, hd = (c2 & 255) >> 1, half = c2 & 1;
+        if (pg[p] >= 0)
+          v = *(const u32x4 *)(a.v_pool + (((int64_t)pg[p] * a.Hkv + kvh) * kHD + hd) * kPage +
+                               8 * half);
+      }
+      regs.c[j] = v;
+    }
+  };
+  auto store_prefix = [&](int buf, int kb) {
+#pragma unroll
+    for (int j = 0; j < kMaxChunksPerThread; ++j) {
+      if (j >= nchunk) break;
+      const int c = tid + j * nthreads;
+      if (c < 512) {
+        const int p = c >> 8, key = (c & 255) >> 4, ch = c & 15;
+        *(u32x4 *)&Ks[buf][(16 * p + key) * kKsStride + 8 * ch] = regs.c[j];
+      } else if (c < 1024) {
+        const int c2 = c - 512;
+        const int p = c2 >> 8, hd = (c2 & 255) >> 1, half = c2 & 1;
+        *(u32x4 *)&Vt[buf][hd * kVtStride + 16 * p + 8 * half] = regs.c[j];
+      }
+    }
+    if (tid < kKB) {
+      const int p = tid >> 4;
+      kvalid[buf][tid] = (pg_cur[p] >= 0) && (kb + tid < k_end);
+    }
+  };
+  // candidate keys (row-major [B*M, Hkv, hd]): staged directly, V transposed on the way
+  auto stage_cand = [&](int buf, int kb) {
     for (int c = tid; c < kKB * 16; c += nthreads) {
-      const int key = c >> 4;
-      const int ch = c & 15;
+      const int key = c >> 4, ch = c & 15;
       const int pos = kb + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      bool valid = pos < k_end;
-      if (valid) {
-        const bf16_t *kp, *vp;
-        if (is_cand) {
-          const int64_t off = (((int64_t)b * a.M + pos) * a.Hkv + kvh) * kHD + 8 * ch;
-          kp = a.k_cand + off;
-          vp = a.v_cand + off;
-        } else {
-          const int pg = ptab[pos / kPage];
-          if (pg < 0 || pg >= a.n_pool_pages) {
-            valid = false;
-            if (ch == 0 && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
-          }
-          const int64_t off =
-              (((int64_t)(valid ? pg : 0) * kPage + pos % kPage) * a.Hkv + kvh) * kHD + 8 * ch;
-          kp = a.k_pool + off;
-          vp = a.v_pool + off;
-        }
-        if (valid) {
-          kv = *(const u32x4 *)kp;
-          vv = *(const u32x4 *)vp;
-        }
+      if (pos < k_end) {
+        const int64_t off = (((int64_t)b * a.M + pos) * a.Hkv + kvh) * kHD + 8 * ch;
+        kv = *(const u32x4 *)(a.k_cand + off);
+        vv = *(const u32x4 *)(a.v_cand + off);
       }
-      *(u32x4 *)(&Ks[key * kKsStride + 8 * ch]) = kv;
+      *(u32x4 *)&Ks[buf][key * kKsStride + 8 * ch] = kv;
       const bf16_t *ve = (const bf16_t *)&vv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(8 * ch + e) * kVtStride + key] = ve[e];
-      if (ch == 0) kvalid[key] = valid;
+      for (int e = 0; e < 8; ++e) Vt[buf][(8 * ch + e) * kVtStride + key] = ve[e];
+      if (ch == 0) kvalid[buf][key] = pos < k_end;
     }
-    __syncthreads();
+  };
 
+  auto compute = [&](int buf, int kb) {
     bf16x8 ka[4], kb2[4], vf[8];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      ka[s4] = *(const bf16x8 *)&Ks[l16 * kKsStride + 32 * s4 + 8 * lg];
-      kb2[s4] = *(const bf16x8 *)&Ks[(16 + l16) * kKsStride + 32 * s4 + 8 * lg];
+      ka[s4] = *(const bf16x8 *)&Ks[buf][l16 * kKsStride + 32 * s4 + 8 * lg];
+      kb2[s4] = *(const bf16x8 *)&Ks[buf][(16 + l16) * kKsStride + 32 * s4 + 8 * lg];
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const bf16_t *row = &Vt[(16 * tt + l16) * kVtStride];
+      const bf16_t *row = &Vt[buf][(16 * tt + l16) * kVtStride];
       typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
       const bf16x4 lo = *(const bf16x4 *)(row + 4 * lg);
       const bf16x4 hi = *(const bf16x4 *)(row + 16 + 4 * lg);
@@ -171,10 +221,9 @@ attn_mfma_kernel(AttnArgs a) {
     bool vis_a[4], vis_b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vis_a[j] = kvalid[4 * lg + j];
-      vis_b[j] = kvalid[16 + 4 * lg + j];
+      vis_a[j] = kvalid[buf][4 * lg + j];
+      vis_b[j] = kvalid[buf][16 + 4 * lg + j];
     }
-
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -212,16 +261,46 @@ attn_mfma_kernel(AttnArgs a) {
       }
       l_part[t] = l_part[t] * corr + psum;
       m_run[t] = mnew;
-      uint32_t pk[4] = {pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]),
-                        pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])};
-      const bf16x8 pfrag = *(const bf16x8 *)pk;
+      // P = hi + lo, both bf16: the PV product keeps ~16 significant bits of P
+      uint32_t hk[4], lk[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16_t h0 = f32_to_bf16(pa[2 * j]), h1 = f32_to_bf16(pa[2 * j + 1]);
+        const bf16_t g0 = f32_to_bf16(pb[2 * j]), g1 = f32_to_bf16(pb[2 * j + 1]);
+        hk[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        hk[2 + j] = (uint32_t)g0 | ((uint32_t)g1 << 16);
+        lk[j] = pack_bf16x2(pa[2 * j] - bf16_to_f32(h0), pa[2 * j + 1] - bf16_to_f32(h1));
+        lk[2 + j] = pack_bf16x2(pb[2 * j] - bf16_to_f32(g0), pb[2 * j + 1] - bf16_to_f32(g1));
+      }
+      const bf16x8 phi = *(const bf16x8 *)hk;
+      const bf16x8 plo = *(const bf16x8 *)lk;
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         O[t][tt] *= corr;
-        O[t][tt] = mfma16x16x32(vf[tt], pfrag, O[t][tt]);
+        O[t][tt] = mfma16x16x32(vf[tt], phi, O[t][tt]);
+        O[t][tt] = mfma16x16x32(vf[tt], plo, O[t][tt]);
       }
     }
-    __syncthreads();
+  };
+
+  if (is_cand) {
+    int buf = 0;
+    for (int kb = k_begin; kb < k_end; kb += kKB) {
+      stage_cand(buf, kb);
+      __syncthreads();
+      compute(buf, kb);
+      buf ^= 1;
+    }
+  } else {
+    if (k_begin < k_end) fetch_prefix(k_begin);
+    int buf = 0;
+    for (int kb = k_begin; kb < k_end; kb += kKB) {
+      store_prefix(buf, kb);
+      __syncthreads();
+      if (kb + kKB < k_end) fetch_prefix(kb + kKB);
+      compute(buf, kb);
+      buf ^= 1;
+    }
   }
 
   // ---- finish: row sums over the 4 lane groups, then final output or partials
@@ -330,15 +409,16 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
   const int nkeys = P + o + 1;
   for (int k = 0; k < nkeys; ++k) {
     const float *kp, *vp;
+    int vstride = 1;
     if (k < P) {
       const int pg = page_table[(int64_t)b * max_pages + k / kPage];
       if (pg < 0 || pg >= n_pool_pages) {
         if (flags && (k % kPage) == 0 && hq == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
         continue;
       }
-      const int64_t off = (((int64_t)pg * kPage + k % kPage) * Hkv + kvh) * HD;
-      kp = k_pool + off;
-      vp = v_pool + off;
+      kp = k_pool + (((int64_t)pg * Hkv + kvh) * kPage + k % kPage) * HD;
+      vp = v_pool + ((int64_t)pg * Hkv + kvh) * HD * kPage + k % kPage;
+      vstride = kPage;
     } else {
       const int64_t off = (((int64_t)b * M + i * D + (k - P)) * Hkv + kvh) * HD;
       kp = k_cand + off;
@@ -351,7 +431,7 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
     const float corr = expf(mx - mnew);
     const float p = expf(sdot - mnew);
     l = l * corr + p;
-    for (int e = 0; e < HD; ++e) acc[e] = acc[e] * corr + p * vp[e];
+    for (int e = 0; e < HD; ++e) acc[e] = acc[e] * corr + p * vp[e * vstride];
     mx = mnew;
   }
   float *op = out + (((int64_t)b * M + r) * Hq + hq) * HD;
@@ -375,12 +455,11 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   // row block: fewest padded rows, then the largest block (fewer re-reads of K/V)
   int best_waste = 1 << 30, best_rows = 0;
   for (int rt = 1; rt <= 2; ++rt) {
-    for (int nw = 1; nw <= 8; ++nw) {
+    for (int nw = 2; nw <= (rt == 1 ? 8 : 4); ++nw) {
       const int tpb = rt * nw;
       const int nrb = (tiles + tpb - 1) / tpb;
       const int waste = nrb * tpb - tiles;
       const int rows = tpb * 16;
-      if (tpb > tiles && nw > 1) continue;
       if (waste < best_waste || (waste == best_waste && rows > best_rows)) {
         best_waste = waste;
         best_rows = rows;
@@ -389,18 +468,33 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
       }
     }
   }
-  p.rows_per_block = p.rt * p.nw * 16;
-  p.n_rb = (tiles + p.rt * p.nw - 1) / (p.rt * p.nw);
   // key splits: about 256 workgroups of prefix work for the longest sequence's share
   const int max_keys = max_pages * page;
-  const int groups = B * Hkv * p.n_rb;
-  int want = (256 + groups - 1) / groups;
-  if (want < 1) want = 1;
-  int sk = (max_keys + want - 1) / want;
-  sk = ((sk + kKB - 1) / kKB) * kKB;
-  if (sk < 256) sk = 256;
-  p.split_keys = sk;
-  p.n_splits = (max_keys + sk - 1) / sk;
+  int split_keys = 0;
+  // tuning override "rt,nw,split_keys" (values <= 0 keep the heuristic's choice)
+  if (const char *ov = getenv("VSTEP_ATTN_PLAN")) {
+    int rt = 0, nw = 0, sk = 0;
+    if (sscanf(ov, "%d,%d,%d", &rt, &nw, &sk) == 3) {
+      if ((rt == 1 || rt == 2) && nw >= 2 && nw <= (rt == 1 ? 8 : 4)) {
+        p.rt = rt;
+        p.nw = nw;
+      }
+      if (sk > 0) split_keys = ((sk + kKB - 1) / kKB) * kKB;
+    }
+  }
+  p.rows_per_block = p.rt * p.nw * 16;
+  p.n_rb = (tiles + p.rt * p.nw - 1) / (p.rt * p.nw);
+  if (split_keys == 0) {
+    const int groups = B * Hkv * p.n_rb;
+    int want = (256 + groups - 1) / groups;
+    if (want < 1) want = 1;
+    int sk = (max_keys + want - 1) / want;
+    sk = ((sk + kKB - 1) / kKB) * kKB;
+    if (sk < 256) sk = 256;
+    split_keys = sk;
+  }
+  p.split_keys = split_keys;
+  p.n_splits = (max_keys + split_keys - 1) / split_keys;
   if (p.n_splits < 1) p.n_splits = 1;
   return p;
 }

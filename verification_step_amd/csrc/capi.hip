@@ -6,10 +6,6 @@
 
 #include <math.h>
 
-namespace vs {
-hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
-}
-
 namespace {
 
 constexpr int kMaxRows = 1024;      // W*D per sequence
@@ -64,7 +60,7 @@ int check_sample(const vs_sample_desc *d) {
 float attn_scale(float scale, int hd) { return scale > 0.f ? scale : 1.0f / sqrtf((float)hd); }
 
 struct StepLayout {
-  size_t attn, head, total;
+  size_t attn, head, sample, total;
 };
 
 StepLayout step_layout(const vs_step_desc *d) {
@@ -74,7 +70,9 @@ StepLayout step_layout(const vs_step_desc *d) {
                                             d->max_pages, 16, d->dtype);
   L.head = align256(a);
   const size_t h = vs::head_workspace_bytes(d->B * d->W * d->D, d->d, d->V, 0, d->dtype);
-  L.total = align256(L.head + h);
+  L.sample = align256(L.head + h);
+  const size_t s = vs::sample_workspace_bytes(d->B, d->W, d->D, d->V);
+  L.total = align256(L.sample + s);
   return L;
 }
 
@@ -159,12 +157,13 @@ int vs_lm_head(const vs_head_desc *d, const void *h, const void *w_full, const v
   if (d->rank > 0 && (!w_down || !w_up || w_full)) return VS_ERR_INVALID_ARG;
   if (d->write_probs && !probs) return VS_ERR_INVALID_ARG;
   if (!workspace || ws_bytes < vs_head_workspace_bytes(d)) return VS_ERR_WORKSPACE;
+  const vs::HeadWs hw = vs::head_ws(workspace, d->M, d->V, d->rank);
   hipError_t e = vs::launch_head_gemm(d->M, d->d, d->V, d->rank, d->dtype, d->temperature, h,
-                                      w_full, w_down, w_up, logits, workspace, S(stream));
+                                      w_full, w_down, w_up, logits, hw, nullptr, 0, nullptr,
+                                      S(stream));
   if (e != hipSuccess) return VS_ERR_HIP;
-  return hip_status(vs::launch_head_finish(d->M, d->d, d->V, d->rank, d->dtype, d->temperature,
-                                           logits, row_lse, d->write_probs ? probs : nullptr,
-                                           workspace, S(stream)));
+  return hip_status(vs::launch_head_finish(d->M, d->V, d->temperature, logits, row_lse,
+                                           d->write_probs ? probs : nullptr, hw, S(stream)));
 }
 
 size_t vs_sample_workspace_bytes(const vs_sample_desc *d) {
@@ -184,11 +183,17 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
       !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
     return VS_ERR_INVALID_ARG;
   const size_t need = vs_sample_workspace_bytes(d);
-  if (need > 0 && (!workspace || ws_bytes < need)) return VS_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < need) return VS_ERR_WORKSPACE;
+  const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->V);
+  hipError_t e = vs::launch_root_stats(root_logits, d->B, d->V, d->temperature, sw.root_stats,
+                                       S(stream));
+  if (e != hipSuccess) return VS_ERR_HIP;
+  e = vs::launch_lse_from_stats(sw.root_stats, d->B, d->V, sw.root_lse, S(stream));
+  if (e != hipSuccess) return VS_ERR_HIP;
   return hip_status(vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, root_logits, logits,
-                                       row_lse, q, cand_tok, cand_len, u_acc, u_res, gate, n_acc,
-                                       best, out_tok, n_out, acc_per_cand, flags, 0, workspace,
-                                       S(stream)));
+                                       row_lse, sw.root_lse, q, cand_tok, cand_len, u_acc, u_res,
+                                       gate, n_acc, best, out_tok, n_out, acc_per_cand, flags, 0,
+                                       sw, S(stream)));
 }
 
 static int check_step(const vs_step_desc *d) {
@@ -258,18 +263,22 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
                            io->k_cand, io->v_cand, io->k_pool, io->v_pool, io->page_table,
                            io->prefix_len, io->attn_out, io->flags, ws + L.attn, s);
   if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
-  // 3. head: GEMM + tile statistics, then the row normaliser
+  // 3. head: GEMM + tile statistics (verify rows and root rows), then the normalisers
+  const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
+  const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->V);
   e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,
-                           nullptr, nullptr, io->logits, ws + L.head, s);
+                           nullptr, nullptr, io->logits, hw, io->root_logits, d->B,
+                           sw.root_stats, s);
   if (e != hipSuccess || !mark(3)) return VS_ERR_HIP;
-  e = vs::launch_head_finish(M, d->d, d->V, 0, d->dtype, d->temperature, io->logits, io->row_lse,
-                             nullptr, ws + L.head, s);
+  e = vs::launch_head_finish(M, d->V, d->temperature, io->logits, io->row_lse, nullptr, hw, s);
+  if (e != hipSuccess) return VS_ERR_HIP;
+  e = vs::launch_lse_from_stats(sw.root_stats, d->B, d->V, sw.root_lse, s);
   if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
   // 4. rejection sampling
   e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
-                         io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_acc,
-                         io->u_res, d->external_drafts ? nullptr : io->gate, io->n_acc, io->best,
-                         io->out_tok, io->n_out, io->acc_per_cand, io->flags, 1, nullptr, s);
+                         io->row_lse, sw.root_lse, io->q_draft, io->cand_tok, io->cand_len,
+                         io->u_acc, io->u_res, d->external_drafts ? nullptr : io->gate, io->n_acc,
+                         io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags, 1, sw, s);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
 }

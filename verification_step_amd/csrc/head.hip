@@ -1,50 +1,60 @@
 // Vocabulary projection of the verify step.
 //
-// Full head: z = W_full h for every verify row (the GEMM that batching the
-// candidates turns the decode GEMV into: rejection-sampling blog, blog.huny.dev,
+// Full head: z = W_full h for every verify row -- the GEMM that batching the
+// candidates turns the decode GEMV into (rejection-sampling blog, blog.huny.dev,
 // section 1).  Low-rank head: z = W_up (W_down h) ("SlimSpec: Low-Rank Draft
 // LM-Head ...", gist.science, "방법론 / 아키텍처"), the rank-r intermediate kept in fp32.
 //
-// bf16 GEMM out[M,N] = H[M,K] . W[N,K]^T, MFMA 16x16x32 bf16, fp32 accumulation:
-//   * a workgroup = 4 waves; each wave owns VT 16-row tiles of W (vocabulary) and
-//     all MT 16-row tiles of the workgroup's H block;
-//   * W is read exactly once, straight from HBM into registers in MFMA operand
-//     layout (16-byte loads; each row segment of 256 B is fully used), with the
-//     next K-chunk prefetched while the current one is multiplied;
-//   * the H block is shared through LDS one K-chunk at a time (padded rows: no bank
-//     conflicts on the 16-byte fragment reads);
-//   * H may be fp32 (the low-rank intermediate): it is then split on the fly into
-//     bf16 hi + lo parts and multiplied twice, keeping ~16 mantissa bits;
-//   * the epilogue writes fp32 logits and, per (row, workgroup vocabulary tile),
-//     the max and sum of exp(z/T - max): the sampler's normaliser needs no second
-//     pass over the logits.
+// bf16 GEMM out[M,N] = H[M,K] . W[N,K]^T on MFMA 16x16x32 bf16, fp32 accumulation.
+// For the verify head (M = W*D rows, N = V >= 1e5) the product is bound by reading
+// W once from HBM, so the kernel is built around keeping enough of W in flight:
+//   * a workgroup = 4 waves x 64 vocabulary rows; each wave streams its own rows of
+//     W and the H fragments straight into registers in MFMA operand layout,
+//     through a ring of register buffers issued several K-steps ahead (W and H at
+//     the same distance, so the in-order load counter never makes a wave wait for
+//     data it does not need yet);
+//   * no LDS and no barrier in the K loop: waves progress independently; H (a few
+//     hundred KB) stays in L2;
+//   * fp32 H (the low-rank intermediate) is split on the fly into bf16 hi + lo and
+//     multiplied twice (about 16 significant bits);
+//   * the epilogue writes fp32 logits and, per row and 256-row vocabulary tile,
+//     (max, sum exp(z/T - max)); the same tiles' statistics of the root logits
+//     can be folded in, so the sampler's normalisers need no pass over the logits.
+// Low-rank stage W_down (N = r = 512, K = d) splits K across workgroups and sums
+// the partials in a fixed order.
 
 #include "vs_internal.hpp"
+
+#include <type_traits>
 
 namespace vs {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKC = 128;            // K per chunk
-constexpr int kHStride = kKC + 8;   // staged H row (bf16 elements)
-constexpr int kVT = 2;              // vocabulary tiles per wave
-constexpr int kVocabPerWG = 4 * kVT * 16;
+constexpr int kVT = 4;             // 16-row vocabulary tiles per wave
+constexpr int kPD = 2;             // K-steps (of 32) loaded ahead of use
+constexpr int kRing = kPD + 1;
+static_assert(kHeadVocabTile == 4 * kVT * 16, "workgroup vocabulary span");
+
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 
 struct GemmArgs {
-  const void *h;      // [M, K] bf16, or fp32 when SPLIT
-  const bf16_t *w;    // [N, K]
-  float *out;         // [M, N]
-  float2 *stats;      // [n_vtiles, M] (max, sumexp) of out/T, or null
-  int M, N, K;
+  const void *h;        // [M, K] bf16, or fp32 when SPLIT
+  const bf16_t *w;      // [N, K]
+  float *out;           // [M, N] (or partial [ksplit][M][N])
+  float2 *stats;        // [M][n_vt] or null
+  const float *root;    // [B_root, N] or null
+  float2 *root_stats;   // [B_root][n_vt]
+  int M, N, K, B_root;
   int n_mblocks;
+  int kspan;            // K per split (multiple of 32)
   float inv_t;
 };
 
 template <int MT, bool SPLIT>
 __global__ void __launch_bounds__(kThreads)
-head_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Hs[(SPLIT ? 2 : 1) * MT * 16 * kHStride];
+head_stream_kernel(GemmArgs a) {
   __shared__ float2 red[4][MT * 16];
 
   const int tid = threadIdx.x;
@@ -52,76 +62,48 @@ head_gemm_kernel(GemmArgs a) {
   const int wv = tid >> 6;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  const int n_vtiles = (a.N + kVocabPerWG - 1) / kVocabPerWG;
-  const int nblocks = n_vtiles * a.n_mblocks;
+  const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
+  const int nblocks = n_vt * a.n_mblocks;
   const int bid = xcd_remap(blockIdx.x, nblocks);
-  const int mb = bid % a.n_mblocks;   // M blocks of one vocabulary tile are neighbours
+  const int mb = bid % a.n_mblocks;
   const int vt = bid / a.n_mblocks;
-  const int vbase = vt * kVocabPerWG;
+  const int ks = blockIdx.y;
+  const int vbase = vt * kHeadVocabTile + wv * (kVT * 16);
   const int mbase = mb * MT * 16;
-  const int nchunks = (a.K + kKC - 1) / kKC;
+  const int k0 = ks * a.kspan;
+  const int k1 = min(a.K, k0 + a.kspan);
+  const int nsteps = (k1 - k0) / 32;
 
-  // W operand pointers (rows clamped into range; masked in the epilogue)
-  const bf16_t *wrow[kVT];
+  const bf16_t *wp[kVT];
 #pragma unroll
   for (int v = 0; v < kVT; ++v) {
-    int n = vbase + (wv * kVT + v) * 16 + l16;
+    int n = vbase + v * 16 + l16;
     n = n < a.N ? n : a.N - 1;
-    wrow[v] = a.w + (int64_t)n * a.K + 8 * lg;
+    wp[v] = a.w + (int64_t)n * a.K + k0 + 8 * lg;
   }
-  auto load_w = [&](bf16x8 (&dst)[kVT][kKC / 32], int c) {
-    const int kc0 = c * kKC;
+  using HElem = typename std::conditional<SPLIT, f32x8, bf16x8>::type;
+  const HElem *hp[MT];
 #pragma unroll
-    for (int v = 0; v < kVT; ++v)
-#pragma unroll
-      for (int s = 0; s < kKC / 32; ++s)
-        dst[v][s] = (kc0 + 32 * s < a.K) ? *(const bf16x8 *)(wrow[v] + kc0 + 32 * s) : bf16x8{};
-  };
+  for (int mt = 0; mt < MT; ++mt) {
+    int m = mbase + mt * 16 + l16;
+    m = m < a.M ? m : a.M - 1;
+    if constexpr (SPLIT)
+      hp[mt] = (const HElem *)((const float *)a.h + (int64_t)m * a.K + k0 + 8 * lg);
+    else
+      hp[mt] = (const HElem *)((const bf16_t *)a.h + (int64_t)m * a.K + k0 + 8 * lg);
+  }
 
-  // H staging: MT*16 rows x kKC columns, 8 elements per thread per pass
-  constexpr int kHPass = (MT * 16 * (kKC / 8) + kThreads - 1) / kThreads;
-  typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
-  using HReg = typename std::conditional<SPLIT, f32x8, u32x4>::type;
-  HReg hreg[kHPass];
-  auto load_h = [&](int c) {
-    const int kc0 = c * kKC;
+  bf16x8 wr[kRing][kVT];
+  HElem hr[kRing][MT];
+  auto load = [&](int slot, int s) {
 #pragma unroll
-    for (int p = 0; p < kHPass; ++p) {
-      const int idx = tid + p * kThreads;
-      const int r = idx / (kKC / 8);
-      const int cc = (idx % (kKC / 8)) * 8;
-      const int m = mbase + r;
-      const bool ok = (r < MT * 16) && (m < a.M) && (kc0 + cc < a.K);
-      if constexpr (SPLIT) {
-        const float *src = (const float *)a.h + (int64_t)m * a.K + kc0 + cc;
-        hreg[p] = ok ? *(const f32x8 *)src : f32x8{};
-      } else {
-        const bf16_t *src = (const bf16_t *)a.h + (int64_t)m * a.K + kc0 + cc;
-        hreg[p] = ok ? *(const u32x4 *)src : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_h = [&]() {
+    for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 32 * s);
 #pragma unroll
-    for (int p = 0; p < kHPass; ++p) {
-      const int idx = tid + p * kThreads;
-      const int r = idx / (kKC / 8);
-      const int cc = (idx % (kKC / 8)) * 8;
-      if (r >= MT * 16) continue;
-      if constexpr (SPLIT) {
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = hreg[p][2 * e], x1 = hreg[p][2 * e + 1];
-          const bf16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
-          hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          lo[e] = pack_bf16x2(x0 - bf16_to_f32(h0), x1 - bf16_to_f32(h1));
-        }
-        *(u32x4 *)&Hs[r * kHStride + cc] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *(u32x4 *)&Hs[(MT * 16 + r) * kHStride + cc] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      } else {
-        *(u32x4 *)&Hs[r * kHStride + cc] = hreg[p];
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (SPLIT)
+        hr[slot][mt] = *(const HElem *)((const float *)hp[mt] + 32 * s);
+      else
+        hr[slot][mt] = *(const HElem *)((const bf16_t *)hp[mt] + 32 * s);
     }
   };
 
@@ -131,50 +113,54 @@ head_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[v][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wcur[kVT][kKC / 32], wnext[kVT][kKC / 32];
-  load_h(0);
-  load_w(wcur, 0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();
-    store_h();
-    __syncthreads();
-    if (c + 1 < nchunks) {
-      load_h(c + 1);
-      load_w(wnext, c + 1);
-    }
+  auto compute = [&](int slot) {
 #pragma unroll
-    for (int s = 0; s < kKC / 32; ++s) {
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (SPLIT) {
+        const f32x8 x = hr[slot][mt];
+        bf16x8 hi, lo;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 hf = *(const bf16x8 *)&Hs[(mt * 16 + l16) * kHStride + 32 * s + 8 * lg];
-#pragma unroll
-        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wcur[v][s], hf, acc[v][mt]);
-        if constexpr (SPLIT) {
-          const bf16x8 hl =
-              *(const bf16x8 *)&Hs[((MT + mt) * 16 + l16) * kHStride + 32 * s + 8 * lg];
-#pragma unroll
-          for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wcur[v][s], hl, acc[v][mt]);
+        for (int e = 0; e < 8; ++e) {
+          const bf16_t hb = f32_to_bf16(x[e]);
+          const bf16_t lb = f32_to_bf16(x[e] - bf16_to_f32(hb));
+          hi[e] = __builtin_bit_cast(__bf16, hb);
+          lo[e] = __builtin_bit_cast(__bf16, lb);
         }
+#pragma unroll
+        for (int v = 0; v < kVT; ++v) {
+          acc[v][mt] = mfma16x16x32(wr[slot][v], hi, acc[v][mt]);
+          acc[v][mt] = mfma16x16x32(wr[slot][v], lo, acc[v][mt]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wr[slot][v], hr[slot][mt], acc[v][mt]);
       }
     }
-    if (c + 1 < nchunks) {
+  };
+
 #pragma unroll
-      for (int v = 0; v < kVT; ++v)
+  for (int p = 0; p < kPD; ++p)
+    if (p < nsteps) load(p, p);
+  for (int s = 0; s < nsteps; s += kRing) {
 #pragma unroll
-        for (int s = 0; s < kKC / 32; ++s) wcur[v][s] = wnext[v][s];
+    for (int u = 0; u < kRing; ++u) {
+      const int ss = s + u;
+      if (ss + kPD < nsteps) load((u + kPD) % kRing, ss + kPD);
+      if (ss < nsteps) compute(u);
     }
   }
 
-  // ---- epilogue: logits and per-tile softmax statistics
+  float *out = a.out + (int64_t)ks * a.M * a.N;
+  // ---- epilogue: logits (+ tile statistics)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mbase + mt * 16 + l16;
     float vmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kVT; ++v) {
-      const int n0 = vbase + (wv * kVT + v) * 16 + 4 * lg;
+      const int n0 = vbase + v * 16 + 4 * lg;
       if (m < a.M) {
-        float *op = a.out + (int64_t)m * a.N + n0;
+        float *op = out + (int64_t)m * a.N + n0;
         if (n0 + 3 < a.N) {
           *(f32x4 *)op = acc[v][mt];
         } else {
@@ -192,7 +178,7 @@ head_gemm_kernel(GemmArgs a) {
     float vs = 0.f;
 #pragma unroll
     for (int v = 0; v < kVT; ++v) {
-      const int n0 = vbase + (wv * kVT + v) * 16 + 4 * lg;
+      const int n0 = vbase + v * 16 + 4 * lg;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (n0 + j < a.N) vs += expf(acc[v][mt][j] * a.inv_t - vmax);
@@ -202,6 +188,28 @@ head_gemm_kernel(GemmArgs a) {
     if (lg == 0) red[wv][mt * 16 + l16] = make_float2(vmax, vs);
   }
   if (a.stats == nullptr) return;
+
+  // root rows over this workgroup's vocabulary tile (one wave per row)
+  if (a.root != nullptr && mb == 0) {
+    for (int b = wv; b < a.B_root; b += 4) {
+      const float *row = a.root + (int64_t)b * a.N;
+      float x[kHeadVocabTile / 64];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kHeadVocabTile / 64; ++j) {
+        const int k = vt * kHeadVocabTile + j * 64 + lane;
+        x[j] = (k < a.N) ? row[k] * a.inv_t : -INFINITY;
+        mx = fmaxf(mx, x[j]);
+      }
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < kHeadVocabTile / 64; ++j)
+        if (x[j] != -INFINITY) sm += expf(x[j] - mx);
+      for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+      if (lane == 0) a.root_stats[(int64_t)b * n_vt + vt] = make_float2(mx, sm);
+    }
+  }
   __syncthreads();
   for (int r = tid; r < MT * 16; r += kThreads) {
     const int m = mbase + r;
@@ -211,12 +219,21 @@ head_gemm_kernel(GemmArgs a) {
     float sm = 0.f;
     for (int w2 = 0; w2 < 4; ++w2)
       if (red[w2][r].x != -INFINITY) sm += red[w2][r].y * expf(red[w2][r].x - mx);
-    a.stats[(int64_t)vt * a.M + m] = make_float2(mx, sm);
+    a.stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
   }
 }
 
-// fp32 GEMM on the vector ALU: out[m, n] = sum_k A[m,k] B[n,k]; optional tile stats
-// over the same vocabulary tiles as the MFMA kernel.
+// sum of K-split partials [ks][n] in split order
+__global__ void __launch_bounds__(kThreads)
+sum_splits_kernel(const float *part, int ksplit, int64_t n, float *out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < ksplit; ++k) s += part[(int64_t)k * n + i];
+  out[i] = s;
+}
+
+// fp32 GEMM on the vector ALU: out[m, n] = sum_k A[m,k] B[n,k]
 __global__ void __launch_bounds__(kThreads)
 gemm_f32_kernel(const float *A, const float *B, float *out, int M, int N, int K) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -230,55 +247,26 @@ gemm_f32_kernel(const float *A, const float *B, float *out, int M, int N, int K)
   out[gid] = s;
 }
 
-// Tile statistics from stored logits (used by the fp32 path).
+// Tile statistics [rows][n_vt] of stored logits (fp32 path).
 __global__ void __launch_bounds__(kThreads)
 tile_stats_kernel(const float *logits, float2 *stats, int M, int N, float inv_t) {
   const int vt = blockIdx.x;
   const int m = blockIdx.y;
-  __shared__ float2 red[kThreads];
-  const int n = vt * kVocabPerWG + threadIdx.x;
-  const bool ok = threadIdx.x < kVocabPerWG && n < N;
+  const int n_vt = gridDim.x;
+  __shared__ float red[kThreads];
+  const int n = vt * kHeadVocabTile + threadIdx.x;
+  const bool ok = n < N;
   const float x = ok ? logits[(int64_t)m * N + n] * inv_t : -INFINITY;
-  red[threadIdx.x] = make_float2(x, ok ? 1.f : 0.f);
+  red[threadIdx.x] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
     float mx = -INFINITY;
-    for (int i = 0; i < kVocabPerWG; ++i) mx = fmaxf(mx, red[i].x);
+    for (int i = 0; i < kThreads; ++i) mx = fmaxf(mx, red[i]);
     float sm = 0.f;
-    for (int i = 0; i < kVocabPerWG; ++i)
-      if (red[i].y > 0.f) sm += expf(red[i].x - mx);
-    stats[(int64_t)vt * M + m] = make_float2(mx, sm);
+    for (int i = 0; i < kThreads; ++i)
+      if (red[i] != -INFINITY) sm += expf(red[i] - mx);
+    stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
   }
-}
-
-// Row normaliser: lse[m] = max + log(sum_t s_t exp(m_t - max)) in fp64.
-__global__ void __launch_bounds__(kThreads)
-head_lse_kernel(const float2 *stats, double *row_lse, int M, int n_vtiles) {
-  const int m = blockIdx.x;
-  __shared__ double red[kThreads];
-  double mx = -INFINITY;
-  for (int t = threadIdx.x; t < n_vtiles; t += kThreads)
-    mx = fmax(mx, (double)stats[(int64_t)t * M + m].x);
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + off]);
-    __syncthreads();
-  }
-  const double M0 = red[0];
-  __syncthreads();
-  double s = 0.0;
-  for (int t = threadIdx.x; t < n_vtiles; t += kThreads) {
-    const float2 st = stats[(int64_t)t * M + m];
-    if (st.x != -INFINITY) s += (double)st.y * exp((double)st.x - M0);
-  }
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) row_lse[m] = M0 + log(red[0]);
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -309,26 +297,18 @@ int pick_mt(int M, int *n_mblocks) {
   return best;
 }
 
-hipError_t launch_gemm_bf16(const void *h, bool split, const bf16_t *w, float *out, float2 *stats,
-                            int M, int N, int K, float inv_t, hipStream_t st) {
-  GemmArgs a;
-  a.h = h;
-  a.w = w;
-  a.out = out;
-  a.stats = stats;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.inv_t = inv_t;
-  const int mt = pick_mt(M, &a.n_mblocks);
-  const int n_vtiles = (N + kVocabPerWG - 1) / kVocabPerWG;
-  const dim3 grid(n_vtiles * a.n_mblocks);
-#define VS_GEMM_CASE(MTV)                                                              \
-  case MTV:                                                                            \
-    if (split)                                                                         \
-      hipLaunchKernelGGL((head_gemm_kernel<MTV, true>), grid, dim3(kThreads), 0, st, a); \
-    else                                                                               \
-      hipLaunchKernelGGL((head_gemm_kernel<MTV, false>), grid, dim3(kThreads), 0, st, a); \
+constexpr int kLowrankSplit = 64;
+
+hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
+  const int mt = pick_mt(a.M, &a.n_mblocks);
+  const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
+  const dim3 grid(n_vt * a.n_mblocks, ksplit);
+#define VS_GEMM_CASE(MTV)                                                                   \
+  case MTV:                                                                                 \
+    if (split)                                                                              \
+      hipLaunchKernelGGL((head_stream_kernel<MTV, true>), grid, dim3(kThreads), 0, st, a);  \
+    else                                                                                    \
+      hipLaunchKernelGGL((head_stream_kernel<MTV, false>), grid, dim3(kThreads), 0, st, a); \
     break;
   switch (mt) {
     VS_GEMM_CASE(1)
@@ -346,46 +326,74 @@ hipError_t launch_gemm_bf16(const void *h, bool split, const bf16_t *w, float *o
   return hipGetLastError();
 }
 
-struct HeadWs {
-  float2 *stats;
-  float *t;  // low-rank intermediate [M, rank]
-};
+}  // namespace
 
-HeadWs head_ws(void *ws, int M, int V) {
+HeadWs head_ws(void *ws, int M, int V, int rank) {
   HeadWs w;
-  const int n_vtiles = (V + kVocabPerWG - 1) / kVocabPerWG;
-  w.stats = (float2 *)ws;
-  size_t off = (size_t)n_vtiles * M * sizeof(float2);
-  off = (off + 255) & ~(size_t)255;
-  w.t = (float *)((char *)ws + off);
+  const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
+  char *p = (char *)ws;
+  size_t off = 0;
+  w.stats = (float2 *)(p + off);
+  off += ((size_t)M * n_vt * sizeof(float2) + 255) & ~(size_t)255;
+  w.t = (float *)(p + off);
+  if (rank > 0) off += ((size_t)(kLowrankSplit + 1) * M * rank * sizeof(float) + 255) & ~(size_t)255;
+  w.bytes = off;
   return w;
 }
-
-}  // namespace
 
 size_t head_workspace_bytes(int M, int d, int V, int rank, int dtype) {
   (void)d;
   (void)dtype;
-  const int n_vtiles = (V + kVocabPerWG - 1) / kVocabPerWG;
-  size_t off = (size_t)n_vtiles * M * sizeof(float2);
-  off = (off + 255) & ~(size_t)255;
-  return off + (size_t)M * (rank > 0 ? rank : 0) * sizeof(float) + 256;
+  return head_ws(nullptr, M, V, rank).bytes;
 }
 
 hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temperature,
                             const void *h, const void *w_full, const void *w_down,
-                            const void *w_up, float *logits, void *ws, hipStream_t st) {
-  const HeadWs w = head_ws(ws, M, V);
+                            const void *w_up, float *logits, const HeadWs &ws,
+                            const float *root_logits, int B_root, float2 *root_stats,
+                            hipStream_t st) {
   const float inv_t = 1.0f / temperature;
   hipError_t e;
   if (dtype == 1) {
-    if (rank == 0)
-      return launch_gemm_bf16(h, false, (const bf16_t *)w_full, logits, w.stats, M, V, d, inv_t,
-                              st);
-    e = launch_gemm_bf16(h, false, (const bf16_t *)w_down, w.t, nullptr, M, rank, d, 1.f, st);
-    if (e != hipSuccess) return e;
-    return launch_gemm_bf16(w.t, true, (const bf16_t *)w_up, logits, w.stats, M, V, rank, inv_t,
-                            st);
+    GemmArgs a{};
+    a.inv_t = inv_t;
+    a.root = root_logits;
+    a.root_stats = root_stats;
+    a.B_root = B_root;
+    if (rank > 0) {
+      // t = H W_down^T, K split over workgroups, partials summed in split order
+      float *part = ws.t + (size_t)M * rank;
+      const int kspan = ((d / kLowrankSplit + 31) / 32) * 32;
+      const int ksplit = (d + kspan - 1) / kspan;
+      a.h = h;
+      a.w = (const bf16_t *)w_down;
+      a.out = part;
+      a.stats = nullptr;
+      a.root = nullptr;
+      a.M = M;
+      a.N = rank;
+      a.K = d;
+      a.kspan = kspan;
+      if ((e = launch_stream(a, false, ksplit, st)) != hipSuccess) return e;
+      const int64_t n = (int64_t)M * rank;
+      hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                         dim3(kThreads), 0, st, part, ksplit, n, ws.t);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      a.h = ws.t;
+      a.w = (const bf16_t *)w_up;
+      a.K = rank;
+      a.root = root_logits;
+    } else {
+      a.h = h;
+      a.w = (const bf16_t *)w_full;
+      a.K = d;
+    }
+    a.out = logits;
+    a.stats = ws.stats;
+    a.M = M;
+    a.N = V;
+    a.kspan = a.K;
+    return launch_stream(a, rank > 0, 1, st);
   }
   // fp32
   const float *A = (const float *)h;
@@ -393,9 +401,9 @@ hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temp
   if (rank > 0) {
     const int64_t n = (int64_t)M * rank;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, A, (const float *)w_down, w.t, M, rank, d);
+                       dim3(kThreads), 0, st, A, (const float *)w_down, ws.t, M, rank, d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    A = w.t;
+    A = ws.t;
     K = rank;
   }
   const float *Bm = (const float *)(rank > 0 ? w_up : w_full);
@@ -403,23 +411,18 @@ hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temp
   hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, st, A, Bm, logits, M, V, K);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int n_vtiles = (V + kVocabPerWG - 1) / kVocabPerWG;
-  hipLaunchKernelGGL(tile_stats_kernel, dim3(n_vtiles, M), dim3(kThreads), 0, st, logits,
-                     w.stats, M, V, inv_t);
-  return hipGetLastError();
+  const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
+  hipLaunchKernelGGL(tile_stats_kernel, dim3(n_vt, M), dim3(kThreads), 0, st, logits, ws.stats,
+                     M, V, inv_t);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (root_logits && root_stats) return launch_root_stats(root_logits, B_root, V, temperature,
+                                                          root_stats, st);
+  return hipSuccess;
 }
 
-hipError_t launch_head_finish(int M, int d, int V, int rank, int dtype, float temperature,
-                              const float *logits, double *row_lse, float *probs, void *ws,
-                              hipStream_t st) {
-  (void)d;
-  (void)rank;
-  (void)dtype;
-  const HeadWs w = head_ws(ws, M, V);
-  const int n_vtiles = (V + kVocabPerWG - 1) / kVocabPerWG;
-  hipLaunchKernelGGL(head_lse_kernel, dim3(M), dim3(kThreads), 0, st, w.stats, row_lse, M,
-                     n_vtiles);
-  hipError_t e = hipGetLastError();
+hipError_t launch_head_finish(int M, int V, float temperature, const float *logits,
+                              double *row_lse, float *probs, const HeadWs &ws, hipStream_t st) {
+  hipError_t e = launch_lse_from_stats(ws.stats, M, V, row_lse, st);
   if (e != hipSuccess || probs == nullptr) return e;
   const int64_t n = (int64_t)M * V;
   hipLaunchKernelGGL(head_probs_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),

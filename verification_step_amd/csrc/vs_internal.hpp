@@ -13,6 +13,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr int kWave = 64;
+// vocabulary span of one head workgroup; softmax tile statistics come at this grain
+constexpr int kHeadVocabTile = 256;
 
 // flag bits (same values as the public header)
 enum : int {
@@ -84,22 +86,47 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
                             const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
                             hipStream_t st);
 
+// Head workspace: per-tile (max, sumexp) statistics [rows][n_vt] and the low-rank
+// intermediate.
+struct HeadWs {
+  float2 *stats;   // [M][n_vt]
+  float *t;        // [M][rank]
+  size_t bytes;
+};
+HeadWs head_ws(void *ws, int M, int V, int rank);
 size_t head_workspace_bytes(int M, int d, int V, int rank, int dtype);
-// Two phases so that the step can time them separately: the GEMM (+ per-tile row
-// statistics), then the row normaliser (+ optional probabilities).
+// GEMM + tile statistics.  root_logits/root_stats (may be null): also compute the
+// tile statistics of B root rows over the same vocabulary tiles.
 hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temperature,
                             const void *h, const void *w_full, const void *w_down,
-                            const void *w_up, float *logits, void *ws, hipStream_t st);
-hipError_t launch_head_finish(int M, int d, int V, int rank, int dtype, float temperature,
-                              const float *logits, double *row_lse, float *probs, void *ws,
-                              hipStream_t st);
+                            const void *w_up, float *logits, const HeadWs &ws,
+                            const float *root_logits, int B_root, float2 *root_stats,
+                            hipStream_t st);
+// Row normalisers (and optional probabilities) from the tile statistics.
+hipError_t launch_head_finish(int M, int V, float temperature, const float *logits,
+                              double *row_lse, float *probs, const HeadWs &ws, hipStream_t st);
 
+struct SampleWs {
+  uint32_t *counters;   // [B], zero between calls
+  double2 *chunk_sums;  // [B][n_chunks]
+  float2 *root_stats;   // [B][n_vt]
+  double *root_lse;     // [B]
+  size_t bytes;
+};
+SampleWs sample_ws(void *ws, int B, int V);
 size_t sample_workspace_bytes(int B, int W, int D, int V);
+hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
+                             float2 *stats, hipStream_t st);
+hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *lse,
+                                 hipStream_t st);
 hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
-                          const float *logits, const double *row_lse, const float *q,
-                          const int32_t *cand_tok, const int32_t *cand_len, const double *u_acc,
-                          const double *u_res, const int32_t *gate, int32_t *n_acc, int32_t *best,
-                          int32_t *out_tok, int32_t *n_out, int32_t *acc_per_cand,
-                          int32_t *flags, int flags_accumulate, void *ws, hipStream_t st);
+                          const float *logits, const double *row_lse, const double *root_lse,
+                          const float *q, const int32_t *cand_tok, const int32_t *cand_len,
+                          const double *u_acc, const double *u_res, const int32_t *gate,
+                          int32_t *n_acc, int32_t *best, int32_t *out_tok, int32_t *n_out,
+                          int32_t *acc_per_cand, int32_t *flags, int flags_accumulate,
+                          const SampleWs &ws, hipStream_t st);
+
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 
 }  // namespace vs

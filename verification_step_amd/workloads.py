@@ -258,7 +258,8 @@ def make_case(shape: Shape, seed: int, variant: str = "measure",
       ctx int32 [sum P], ctx_off int32 [B+1]
       probe_h [B,d], probe_w f32 [d]
       q [B*M, Hq, hd], k_cand/v_cand [B*M, Hkv, hd]
-      k_pool/v_pool [n_pages, 16, Hkv, hd], page_table int32 [B, max_pages], prefix_len int32 [B]
+      k_pool [n_pages, Hkv, 16, hd], v_pool [n_pages, Hkv, hd, 16] (V transposed in a page),
+      page_table int32 [B, max_pages], prefix_len int32 [B]
       w_full [V, d]   (with_head)
       w_down [r, d], w_up [V, r], draft_h [gamma, d]  (rank > 0)
       q_draft f32 [B*M, V]  (q_mode == "dense" and with_q)
@@ -313,8 +314,9 @@ def make_case(shape: Shape, seed: int, variant: str = "measure",
     pages_per = [-(-p // PAGE) for p in sh.P]
     n_pages = int(sum(pages_per))
     max_pages = int(max(pages_per))
-    A["k_pool"] = _normal_model(R["kv_prefix"], (n_pages, PAGE, sh.Hkv, sh.hd), 1.0, sh.dtype)
-    A["v_pool"] = _normal_model(R["kv_prefix"], (n_pages, PAGE, sh.Hkv, sh.hd), 1.0, sh.dtype)
+    # paged cache, head-major pages: K [page, kv head, token, hd]; V [page, kv head, hd, token]
+    A["k_pool"] = _normal_model(R["kv_prefix"], (n_pages, sh.Hkv, PAGE, sh.hd), 1.0, sh.dtype)
+    A["v_pool"] = _normal_model(R["kv_prefix"], (n_pages, sh.Hkv, sh.hd, PAGE), 1.0, sh.dtype)
     if sh.paged_random:
         perm = R["page_perm"].permutation(n_pages).astype(np.int32)
     else:

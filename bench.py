@@ -150,10 +150,12 @@ def main():
     for _ in range(args.kv_buffers - 1):
         pools.append((torch.randn(I["k_pool"].shape, generator=g, device=dev).to(torch.bfloat16),
                       torch.randn(I["v_pool"].shape, generator=g, device=dev).to(torch.bfloat16)))
-    heads = [I["w_full"]]
+    heads = [step.w_packed]           # the head is prepacked once into MFMA tiles
     for _ in range(args.head_copies - 1):
-        heads.append((torch.randn(I["w_full"].shape, generator=g, device=dev)
-                      * (1.0 / np.sqrt(sh.d))).to(torch.bfloat16))
+        w = (torch.randn(I["w_full"].shape, generator=g, device=dev)
+             * (1.0 / np.sqrt(sh.d))).to(torch.bfloat16)
+        heads.append(api.pack_weight(w))
+        del w
     torch.cuda.synchronize()
 
     def bind(k):

@@ -129,10 +129,21 @@ int vs_verify_attention(const vs_attn_desc *desc, const void *q, const void *k_c
                         int32_t *flags, void *workspace, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Weight prepacking for the bf16 vocabulary projection (data movement only).
+ * A row-major bf16 matrix src [N, K] (K % 32 == 0) is rearranged into MFMA operand
+ * tiles: tile (t, s) covers rows 16t..16t+15 and columns 32s..32s+31 and holds 64
+ * lane slots of 8 values; slot l = row 16t + (l % 16), columns 32s + 8*(l / 16) .. +7.
+ * Tiles are ordered t-major ([ceil(N/16)][K/32][64][8]); rows past N are zero.
+ * dst must hold vs_packed_weight_bytes(N, K) bytes.  Done once per weight. */
+size_t vs_packed_weight_bytes(int N, int K);
+int vs_pack_weight(const void *src, void *dst, int N, int K, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Vocabulary projection [SL "방법론 / 아키텍처"].
- *   rank == 0: z = W_full h            (w_full [V, d] dtype)
+ *   rank == 0: z = W_full h            (w_full [V, d])
  *   rank  > 0: z = W_up (W_down h)     (w_down [rank, d], w_up [V, rank]; the rank-r
  *              intermediate is kept in fp32, not rounded to dtype)
+ * VS_BF16 weights are passed PACKED (vs_pack_weight); VS_F32 weights row-major.
  * for every row h of `h` [M, d] (dtype).  Outputs:
  *   logits  fp32 [M, V] (required)
  *   row_lse fp64 [M]    (required): log sum_v exp(z[r,v] / temperature), from the fp32 logits
@@ -213,7 +224,7 @@ typedef struct {
     const void *q, *k_cand, *v_cand, *k_pool, *v_pool;
     const int32_t *page_table, *prefix_len;
     /* head */
-    const void *w_full;         /* [V, d] */
+    const void *w_full;         /* [V, d]: packed (vs_pack_weight) for bf16, row-major fp32 */
     /* sampler */
     const float *root_logits;   /* [B, V] */
     const float *q_draft;       /* [B*W*D, V] or NULL (copy drafts: point mass) */

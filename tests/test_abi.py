@@ -138,6 +138,15 @@ def test_sample_validation(lib):
     assert lib.vs_reject_sample(C.byref(d), *bad, None, 0, None) == -1
 
 
+def test_pack_validation(lib):
+    fake = C.c_void_p(16)
+    assert lib.vs_packed_weight_bytes(1000, 96) == 1008 * 96 * 2      # rows padded to 16
+    assert lib.vs_packed_weight_bytes(1000, 100) == 0
+    assert lib.vs_pack_weight(fake, fake, 1000, 100, None) == -2      # K % 32 != 0
+    assert lib.vs_pack_weight(None, fake, 1000, 96, None) == -1
+    assert lib.vs_pack_weight(fake, fake, 0, 96, None) == -1
+
+
 def test_step_validation(lib):
     fake = C.c_void_p(16)
     base = dict(B=1, W=4, D=20, kappa=5, Hq=32, Hkv=8, head_dim=128, page_size=16, max_pages=256,

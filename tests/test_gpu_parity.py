@@ -225,6 +225,23 @@ def _head_case(M, d, V, dtype="bf16", rank=0, seed=0):
     return h, ws
 
 
+def test_pack_weight_layout():
+    """Packed tile (t, s), lane l holds row 16t + l%16, columns 32s + 8(l//16) .. +7
+    (rows past N zero) -- checked against numpy indexing of the row-major matrix."""
+    api = _api()
+    rng = np.random.default_rng(0)
+    for N, K in ((1000, 96), (64, 32), (17, 256)):
+        w = wl.f32_to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+        say("pack", N, K)
+        g = api.pack_weight(to_dev(w, True)).view(__import__("torch").int16).cpu().numpy()
+        g = g.view(np.uint16).reshape(-1, K // 32, 64, 8)
+        T = -(-N // 16)
+        wp = np.zeros((T * 16, K), dtype=np.uint16)
+        wp[:N] = w
+        exp = wp.reshape(T, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(T, K // 32, 64, 8)
+        assert np.array_equal(g, exp)
+
+
 @pytest.mark.parametrize("M,d,V,dtype,T", [
     (37, 256, 1000, "bf16", 1.0), (100, 512, 2000, "bf16", 0.7), (8, 64, 512, "f32", 1.0),
     (160, 1024, 777, "bf16", 1.0), (1024, 256, 300, "bf16", 1.0)])

@@ -27,7 +27,7 @@ EXPORTED = [
     "vs_abi_version", "vs_status_str", "vs_copy_match", "vs_probe_gate",
     "vs_attention_workspace_bytes", "vs_verify_attention", "vs_head_workspace_bytes",
     "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
-    "vs_step_workspace_bytes", "vs_verify_step",
+    "vs_step_workspace_bytes", "vs_verify_step", "vs_packed_weight_bytes", "vs_pack_weight",
 ]
 
 P = C.c_void_p
@@ -99,6 +99,9 @@ def load(path: str = LIB_PATH):
     lib.vs_step_workspace_bytes.restype = C.c_size_t
     lib.vs_step_workspace_bytes.argtypes = [C.POINTER(StepDesc)]
     lib.vs_verify_step.argtypes = [C.POINTER(StepDesc), C.POINTER(StepIO), P, C.c_size_t, P]
+    lib.vs_packed_weight_bytes.restype = C.c_size_t
+    lib.vs_packed_weight_bytes.argtypes = [C.c_int, C.c_int]
+    lib.vs_pack_weight.argtypes = [P, P, C.c_int, C.c_int, P]
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
             getattr(lib, fn).restype = C.c_int

@@ -144,16 +144,38 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, 
     return out, flags
 
 
+def pack_weight(w: torch.Tensor) -> torch.Tensor:
+    """Rearrange a row-major bf16 weight [N, K] into the packed MFMA-tile layout the
+    bf16 head expects (flat bf16 tensor).  Done once per weight."""
+    lib = L.load()
+    _check(w, torch.bfloat16, "w")
+    N, K = w.shape
+    nbytes = lib.vs_packed_weight_bytes(N, K)
+    if nbytes == 0:
+        raise VstepError(L.VS_ERR_UNSUPPORTED, "pack_weight (K must be a multiple of 32)")
+    out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.device)
+    _raise(lib.vs_pack_weight(_ptr(w), _ptr(out), N, K, _stream()), "pack_weight")
+    return out
+
+
 def lm_head(h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
-            write_probs: bool = False):
+            write_probs: bool = False, V: Optional[int] = None, rank: Optional[int] = None):
+    """bf16: pass weights as 2-D row-major tensors (packed here on the fly) or as flat
+    packed tensors (then give V and, for the low-rank head, rank)."""
     lib = L.load()
     dt = h.dtype
     _check(h, dt, "h")
     for name, t in (("w_full", w_full), ("w_down", w_down), ("w_up", w_up)):
         _check(t, dt, name)
     M, d = h.shape
-    rank = 0 if w_down is None else w_down.shape[0]
-    V = (w_full if rank == 0 else w_up).shape[0]
+    if rank is None:
+        rank = 0 if w_down is None else w_down.shape[0]
+    if V is None:
+        V = (w_full if rank == 0 else w_up).shape[0]
+    if dt == torch.bfloat16:
+        w_full = pack_weight(w_full) if (w_full is not None and w_full.dim() == 2) else w_full
+        w_down = pack_weight(w_down) if (w_down is not None and w_down.dim() == 2) else w_down
+        w_up = pack_weight(w_up) if (w_up is not None and w_up.dim() == 2) else w_up
     desc = L.HeadDesc(M, d, V, rank, _vs_dtype(h), float(temperature), int(write_probs))
     dev = h.device
     logits = torch.empty((M, V), dtype=torch.float32, device=dev)
@@ -204,13 +226,17 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
 
 class VerifyStep:
     """One verify step bound to fixed device buffers, so that repeated calls (timing,
-    a decode loop) enqueue the step without any host-side allocation."""
+    a decode loop) enqueue the step without any host-side allocation.  A 2-D bf16
+    inputs["w_full"] is packed once at construction (kept as self.w_packed)."""
 
     def __init__(self, inputs: dict, B: int, W: int, D: int, Hq: int, Hkv: int, hd: int,
                  V: int, tau: float = 0.4, temperature: float = 1.0, kappa: int = 5,
                  external_drafts: bool = False, scale: float = 0.0):
         self.lib = L.load()
-        I = inputs
+        I = dict(inputs)
+        if I["w_full"].dtype == torch.bfloat16 and I["w_full"].dim() == 2:
+            I["w_full"] = pack_weight(I["w_full"])
+        self.w_packed = I["w_full"]
         dt = I["q"].dtype
         dev = I["q"].device
         self.dtype = dt

@@ -33,8 +33,6 @@ namespace {
 
 constexpr int kHD = 128;
 constexpr int kKB = 32;            // keys per block
-constexpr int kKsStride = kHD + 8; // bf16 elements per staged K row (pad: no bank conflicts)
-constexpr int kVtStride = kKB + 8; // bf16 elements per staged V^T row
 constexpr int kPage = 16;
 
 struct AttnArgs {
@@ -57,30 +55,45 @@ __device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
   return P;
 }
 
-// One 32-key block of prefix keys (two 16-token pages) as 16-byte chunks: 512 chunks
-// of K (page, key, 8 head-dim values) and 512 chunks of V^T (page, head-dim row,
-// 8 keys).  Each thread owns chunks tid, tid + nthreads, ...
-constexpr int kChunksPerBlock = 1024;
-constexpr int kMaxChunksPerThread = 8;    // workgroups have >= 2 waves
+// LDS images of one 32-key block, both without padding and XOR-swizzled so that the
+// MFMA fragment reads are free of bank conflicts:
+//   K:   32 keys x 128 hd; the 16-byte chunk c of key k sits at position c ^ (k & 15)
+//   V^T: 128 hd rows x 32 keys; the 16-byte slot u (keys 8u..8u+7) of row r sits at
+//        position u ^ ((r >> 2) & 3)
+// Each is 8 KB = 8 wave-wide 16-byte-per-lane transfers, which global_load_lds
+// writes straight into LDS (lane l -> bytes 16l..16l+15 of the transfer).
+constexpr int kBlkElems = kKB * kHD;      // bf16 elements per K (or V^T) block image
+constexpr int kNBuf = 4;                  // blocks in flight per workgroup
+constexpr int kMaxSplitPages = 512;       // split_keys <= 8192
 
-struct BlockRegs {
-  u32x4 c[kMaxChunksPerThread];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int RT>
-__global__ void __launch_bounds__(RT == 1 ? 512 : 256)
+// 16 bytes per lane from global memory straight into LDS (lane l -> lds_dst + 16 l).
+// Issued as an opaque instruction: the compiler's automatic waits would otherwise
+// drain every in-flight transfer before any read of the ring; completion is tracked
+// explicitly with s_waitcnt vmcnt before the barrier that publishes a block.
+__device__ __forceinline__ void dma16(const void *g, bf16_t *lds_dst) {
+  // the destination is wave-uniform by construction; make that explicit for the SGPR
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int RT, int NW>
+__global__ void __launch_bounds__(64 * NW)
 attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kKB * kKsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][kHD * kVtStride];
-  __shared__ int kvalid[2][kKB];
+  __shared__ __attribute__((aligned(1024))) bf16_t Kb[kNBuf][kBlkElems];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vb[kNBuf][kBlkElems];
+  __shared__ int pages[kMaxSplitPages];
 
-  const int nthreads = blockDim.x;
+  constexpr int kIPW = 16 / NW;           // 1 KB transfers per wave per block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  const int nchunk = (kChunksPerBlock + nthreads - 1) / nthreads;
 
   const int n_sp = a.n_splits + 1;
   const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
@@ -102,6 +115,7 @@ attn_mfma_kernel(AttnArgs a) {
 
   const int k_begin = is_cand ? 0 : s * a.split_keys;
   const int k_end = is_cand ? a.M : min(P, (s + 1) * a.split_keys);
+  const int nblk = (k_end - k_begin + kKB - 1) / kKB;
 
   // ---- this lane's query rows and fragments
   int rr[RT], mrow[RT];
@@ -116,6 +130,9 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) qf[t][s4] = ok ? *(const bf16x8 *)(qp + 32 * s4 + 8 * lg) : bf16x8{};
   }
+  // all ordinary loads done before the ring starts: inside the loop the only vector
+  // memory operations are the explicitly counted LDS transfers
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x4 O[RT][8];
   float m_run[RT], l_part[RT];
@@ -127,66 +144,52 @@ attn_mfma_kernel(AttnArgs a) {
     for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages;
+  // ---- the split's page indices, once (bad pages -> -1, flagged)
+  if (!is_cand) {
+    const int32_t *ptab = a.page_table + (int64_t)b * a.max_pages + k_begin / kPage;
+    const int np = (k_end - k_begin + kPage - 1) / kPage;
+    bool bad = false;
+    for (int i = tid; i < np; i += 64 * NW) {
+      const int v = ptab[i];
+      const bool ok = v >= 0 && v < a.n_pool_pages;
+      pages[i] = ok ? v : -1;
+      bad |= !ok;
+    }
+    if (bad && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // ---- prefix blocks: global -> registers (next block) while this block is used
-  BlockRegs regs;
-  int pg_cur[2] = {-1, -1};
-  auto fetch_prefix = [&](int kb) {
-    int pg[2];
+  // issue this wave's share of block j (prefix) into ring slot `slot`
+  auto issue_prefix = [&](int j, int slot) {
+    const int kb = k_begin + j * kKB;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int pos = kb + 16 * p;
-      pg[p] = -1;
-      if (pos < k_end) {
-        const int v = ptab[pos / kPage];
-        if (v >= 0 && v < a.n_pool_pages) pg[p] = v;
-        else if (tid == 0 && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
+    for (int ii = 0; ii < kIPW; ++ii) {
+      const int i = wv + ii * NW;           // transfer index 0..15
+      if (i < 8) {
+        const int key = 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (key & 15);
+        const int pg = pages[(kb - k_begin) / kPage + (key >> 4)];
+        const bf16_t *src = a.k_pool;
+        if (pg >= 0 && kb + key < k_end)
+          src = a.k_pool + (((int64_t)pg * a.Hkv + kvh) * kPage + (key & 15)) * kHD + 8 * c;
+        dma16(src, &Kb[slot][i * 512]);
+      } else {
+        const int i2 = i - 8;
+        const int r = 16 * i2 + (lane >> 2);
+        const int u = (lane & 3) ^ ((r >> 2) & 3);
+        const int pl = (kb - k_begin) / kPage + (u >> 1);
+        const int pg = (kb + 16 * (u >> 1) < k_end) ? pages[pl] : -1;
+        const bf16_t *src = a.v_pool;
+        if (pg >= 0)
+          src = a.v_pool + (((int64_t)pg * a.Hkv + kvh) * kHD + r) * kPage + 8 * (u & 1);
+        dma16(src, &Vb[slot][i2 * 512]);
       }
-      pg_cur[p] = pg[p];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxChunksPerThread; ++j) {
-      if (j >= nchunk) break;
-      const int c = tid + j * nthreads;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < 512) {
-        const int p = c >> 8, key = (c & 255) >> 4, ch = c & 15;
-        if (pg[p] >= 0 && kb + 16 * p + key < k_end)
-          v = *(const u32x4 *)(a.k_pool + (((int64_t)pg[p] * a.Hkv + kvh) * kPage + key) * kHD +
-                               8 * ch);
-      } else if (c < 1024) {
-        const int c2 = c - 512;
-        const int p = c2 >> 8, hd = (c2 & 255) >> 1, half = c2 & 1;
-        if (pg[p] >= 0)
-          v = *(const u32x4 *)(a.v_pool + (((int64_t)pg[p] * a.Hkv + kvh) * kHD + hd) * kPage +
-                               8 * half);
-      }
-      regs.c[j] = v;
     }
   };
-  auto store_prefix = [&](int buf, int kb) {
-#pragma unroll
-    for (int j = 0; j < kMaxChunksPerThread; ++j) {
-      if (j >= nchunk) break;
-      const int c = tid + j * nthreads;
-      if (c < 512) {
-        const int p = c >> 8, key = (c & 255) >> 4, ch = c & 15;
-        *(u32x4 *)&Ks[buf][(16 * p + key) * kKsStride + 8 * ch] = regs.c[j];
-      } else if (c < 1024) {
-        const int c2 = c - 512;
-        const int p = c2 >> 8, hd = (c2 & 255) >> 1, half = c2 & 1;
-        *(u32x4 *)&Vt[buf][hd * kVtStride + 16 * p + 8 * half] = regs.c[j];
-      }
-    }
-    if (tid < kKB) {
-      const int p = tid >> 4;
-      kvalid[buf][tid] = (pg_cur[p] >= 0) && (kb + tid < k_end);
-    }
-  };
-  // candidate keys (row-major [B*M, Hkv, hd]): staged directly, V transposed on the way
-  auto stage_cand = [&](int buf, int kb) {
-    for (int c = tid; c < kKB * 16; c += nthreads) {
+  // candidate keys (row-major [B*M, Hkv, hd]): staged through registers, V transposed
+  auto stage_cand = [&](int slot, int kb) {
+    for (int c = tid; c < kKB * 16; c += 64 * NW) {
       const int key = c >> 4, ch = c & 15;
       const int pos = kb + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
@@ -195,34 +198,46 @@ attn_mfma_kernel(AttnArgs a) {
         kv = *(const u32x4 *)(a.k_cand + off);
         vv = *(const u32x4 *)(a.v_cand + off);
       }
-      *(u32x4 *)&Ks[buf][key * kKsStride + 8 * ch] = kv;
+      *(u32x4 *)&Kb[slot][key * kHD + 8 * (ch ^ (key & 15))] = kv;
       const bf16_t *ve = (const bf16_t *)&vv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[buf][(8 * ch + e) * kVtStride + key] = ve[e];
-      if (ch == 0) kvalid[buf][key] = pos < k_end;
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * ch + e;
+        const int u = (key >> 3) ^ ((r >> 2) & 3);
+        Vb[slot][r * kKB + 8 * u + (key & 7)] = ve[e];
+      }
     }
   };
 
-  auto compute = [&](int buf, int kb) {
+  auto compute = [&](int slot, int kb) {
     bf16x8 ka[4], kb2[4], vf[8];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      ka[s4] = *(const bf16x8 *)&Ks[buf][l16 * kKsStride + 32 * s4 + 8 * lg];
-      kb2[s4] = *(const bf16x8 *)&Ks[buf][(16 + l16) * kKsStride + 32 * s4 + 8 * lg];
+      const int pch = (4 * s4 + lg) ^ l16;
+      ka[s4] = *(const bf16x8 *)&Kb[slot][l16 * kHD + 8 * pch];
+      kb2[s4] = *(const bf16x8 *)&Kb[slot][(16 + l16) * kHD + 8 * pch];
     }
+    const int sw = (l16 >> 2) & 3;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const bf16_t *row = &Vt[buf][(16 * tt + l16) * kVtStride];
+      const bf16_t *row = &Vb[slot][(16 * tt + l16) * kKB];
       typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-      const bf16x4 lo = *(const bf16x4 *)(row + 4 * lg);
-      const bf16x4 hi = *(const bf16x4 *)(row + 16 + 4 * lg);
+      const bf16x4 lo = *(const bf16x4 *)(row + 8 * ((lg >> 1) ^ sw) + 4 * (lg & 1));
+      const bf16x4 hi = *(const bf16x4 *)(row + 8 * ((2 + (lg >> 1)) ^ sw) + 4 * (lg & 1));
       vf[tt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    // key validity: inside the range and (prefix) on a valid page
     bool vis_a[4], vis_b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vis_a[j] = kvalid[buf][4 * lg + j];
-      vis_b[j] = kvalid[buf][16 + 4 * lg + j];
+      const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
+      if (is_cand) {
+        vis_a[j] = ka_i < k_end;
+        vis_b[j] = kb_i < k_end;
+      } else {
+        vis_a[j] = ka_i < k_end && pages[(ka_i - k_begin) >> 4] >= 0;
+        vis_b[j] = kb_i < k_end && pages[(kb_i - k_begin) >> 4] >= 0;
+      }
     }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -284,22 +299,26 @@ attn_mfma_kernel(AttnArgs a) {
   };
 
   if (is_cand) {
-    int buf = 0;
-    for (int kb = k_begin; kb < k_end; kb += kKB) {
-      stage_cand(buf, kb);
+    for (int j = 0; j < nblk; ++j) {
+      const int slot = j & 1;
+      stage_cand(slot, k_begin + j * kKB);
       __syncthreads();
-      compute(buf, kb);
-      buf ^= 1;
+      compute(slot, k_begin + j * kKB);
     }
   } else {
-    if (k_begin < k_end) fetch_prefix(k_begin);
-    int buf = 0;
-    for (int kb = k_begin; kb < k_end; kb += kKB) {
-      store_prefix(buf, kb);
+    // ring: blocks j+1..j+kNBuf-2 stay in flight while block j is multiplied
+#pragma unroll
+    for (int j = 0; j < kNBuf - 1; ++j)
+      if (j < nblk) issue_prefix(j, j);
+    for (int j = 0; j < nblk; ++j) {
+      if (j + kNBuf - 2 < nblk)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (((kNBuf - 2) * kIPW) & 15) |
+                                   ((((kNBuf - 2) * kIPW) >> 4) << 14));
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // tail: everything issued is needed
       __syncthreads();
-      if (kb + kKB < k_end) fetch_prefix(kb + kKB);
-      compute(buf, kb);
-      buf ^= 1;
+      if (j + kNBuf - 1 < nblk) issue_prefix(j + kNBuf - 1, (j + kNBuf - 1) % kNBuf);
+      compute(j % kNBuf, k_begin + j * kKB);
     }
   }
 
@@ -455,7 +474,7 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   // row block: fewest padded rows, then the largest block (fewer re-reads of K/V)
   int best_waste = 1 << 30, best_rows = 0;
   for (int rt = 1; rt <= 2; ++rt) {
-    for (int nw = 2; nw <= (rt == 1 ? 8 : 4); ++nw) {
+    for (int nw = 2; nw <= (rt == 1 ? 8 : 4); nw *= 2) {
       const int tpb = rt * nw;
       const int nrb = (tiles + tpb - 1) / tpb;
       const int waste = nrb * tpb - tiles;
@@ -475,7 +494,7 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   if (const char *ov = getenv("VSTEP_ATTN_PLAN")) {
     int rt = 0, nw = 0, sk = 0;
     if (sscanf(ov, "%d,%d,%d", &rt, &nw, &sk) == 3) {
-      if ((rt == 1 || rt == 2) && nw >= 2 && nw <= (rt == 1 ? 8 : 4)) {
+      if ((rt == 1 && (nw == 2 || nw == 4 || nw == 8)) || (rt == 2 && (nw == 2 || nw == 4))) {
         p.rt = rt;
         p.nw = nw;
       }
@@ -493,6 +512,7 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
     if (sk < 256) sk = 256;
     split_keys = sk;
   }
+  if (split_keys > kMaxSplitPages * kPage) split_keys = kMaxSplitPages * kPage;
   p.split_keys = split_keys;
   p.n_splits = (max_keys + split_keys - 1) / split_keys;
   if (p.n_splits < 1) p.n_splits = 1;
@@ -558,10 +578,12 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   a.n_splits = p.n_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int nblocks = p.n_rb * (p.n_splits + 1) * B * Hkv;
-  if (p.rt == 1)
-    hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3(nblocks), dim3(64 * p.nw), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_mfma_kernel<2>, dim3(nblocks), dim3(64 * p.nw), 0, st, a);
+  const dim3 grid(nblocks), block(64 * p.nw);
+  if (p.rt == 1 && p.nw == 2) hipLaunchKernelGGL((attn_mfma_kernel<1, 2>), grid, block, 0, st, a);
+  else if (p.rt == 1 && p.nw == 4) hipLaunchKernelGGL((attn_mfma_kernel<1, 4>), grid, block, 0, st, a);
+  else if (p.rt == 1) hipLaunchKernelGGL((attn_mfma_kernel<1, 8>), grid, block, 0, st, a);
+  else if (p.nw == 2) hipLaunchKernelGGL((attn_mfma_kernel<2, 2>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_mfma_kernel<2, 4>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = (int64_t)B * Hkv * p.n_rb * p.rows_per_block * 32;

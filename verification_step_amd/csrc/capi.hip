@@ -142,6 +142,17 @@ int vs_verify_attention(const vs_attn_desc *d, const void *q, const void *k_cand
                                          workspace, S(stream)));
 }
 
+size_t vs_packed_weight_bytes(int N, int K) {
+  if (N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return vs::packed_weight_elems(N, K) * 2;
+}
+
+int vs_pack_weight(const void *src, void *dst, int N, int K, void *stream) {
+  if (!src || !dst || N <= 0 || K <= 0) return VS_ERR_INVALID_ARG;
+  if (K % 32 != 0) return VS_ERR_UNSUPPORTED;
+  return hip_status(vs::launch_pack_weight(src, dst, N, K, S(stream)));
+}
+
 size_t vs_head_workspace_bytes(const vs_head_desc *d) {
   if (check_head(d) != VS_OK) return 0;
   return vs::head_workspace_bytes(d->M, d->d, d->V, d->rank, d->dtype);

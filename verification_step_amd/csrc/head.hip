@@ -8,11 +8,14 @@
 // bf16 GEMM out[M,N] = H[M,K] . W[N,K]^T on MFMA 16x16x32 bf16, fp32 accumulation.
 // For the verify head (M = W*D rows, N = V >= 1e5) the product is bound by reading
 // W once from HBM, so the kernel is built around keeping enough of W in flight:
-//   * a workgroup = 4 waves x 64 vocabulary rows; each wave streams its own rows of
-//     W and the H fragments straight into registers in MFMA operand layout,
-//     through a ring of register buffers issued several K-steps ahead (W and H at
-//     the same distance, so the in-order load counter never makes a wave wait for
-//     data it does not need yet);
+//   * bf16 weights are prepacked once (vs_pack_weight) into MFMA operand tiles:
+//     16 rows x 32 columns = 1 KB, lane l's 16 bytes at offset 16*l, tiles of one
+//     16-row strip consecutive along K.  A wave's load of one tile is a single
+//     contiguous 1 KB access and each strip streams sequentially through memory;
+//   * a workgroup = 4 waves x 64 vocabulary rows; each wave streams its own strips
+//     of W and the H fragments straight into registers, through a ring of register
+//     buffers issued several K-steps ahead (W and H at the same distance, so the
+//     in-order load counter never makes a wave wait for data it does not need yet);
 //   * no LDS and no barrier in the K loop: waves progress independently; H (a few
 //     hundred KB) stays in L2;
 //   * fp32 H (the low-rank intermediate) is split on the fly into bf16 hi + lo and
@@ -41,7 +44,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 
 struct GemmArgs {
   const void *h;        // [M, K] bf16, or fp32 when SPLIT
-  const bf16_t *w;      // [N, K]
+  const bf16_t *w;      // packed [ceil(N/16)][K/32][64][8]
   float *out;           // [M, N] (or partial [ksplit][M][N])
   float2 *stats;        // [M][n_vt] or null
   const float *root;    // [B_root, N] or null
@@ -74,12 +77,15 @@ head_stream_kernel(GemmArgs a) {
   const int k1 = min(a.K, k0 + a.kspan);
   const int nsteps = (k1 - k0) / 32;
 
+  // packed W: strip (16 rows) t, K-step s at element ((t * ksteps + s) * 64 + lane) * 8
+  const int ksteps_all = a.K / 32;
+  const int n_strips = (a.N + 15) / 16;
   const bf16_t *wp[kVT];
 #pragma unroll
   for (int v = 0; v < kVT; ++v) {
-    int n = vbase + v * 16 + l16;
-    n = n < a.N ? n : a.N - 1;
-    wp[v] = a.w + (int64_t)n * a.K + k0 + 8 * lg;
+    int t = vbase / 16 + v;
+    t = t < n_strips ? t : n_strips - 1;
+    wp[v] = a.w + (((int64_t)t * ksteps_all + k0 / 32) * 64 + lane) * 8;
   }
   using HElem = typename std::conditional<SPLIT, f32x8, bf16x8>::type;
   const HElem *hp[MT];
@@ -97,7 +103,7 @@ head_stream_kernel(GemmArgs a) {
   HElem hr[kRing][MT];
   auto load = [&](int slot, int s) {
 #pragma unroll
-    for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 32 * s);
+    for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 512 * s);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if constexpr (SPLIT)
@@ -223,6 +229,25 @@ head_stream_kernel(GemmArgs a) {
   }
 }
 
+// Row-major [N, K] bf16 -> MFMA operand tiles [ceil(N/16)][K/32][64 lanes][8]; rows
+// past N are zero.  Pure data movement: one thread per 16-byte lane slot.
+__global__ void __launch_bounds__(kThreads)
+pack_weight_kernel(const bf16_t *src, bf16_t *dst, int N, int K) {
+  const int64_t slot = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t ks = K / 32;
+  const int64_t n_slots = (int64_t)((N + 15) / 16) * ks * 64;
+  if (slot >= n_slots) return;
+  const int lane = (int)(slot % 64);
+  const int64_t tile = slot / 64;
+  const int64_t s = tile % ks;
+  const int64_t t = tile / ks;
+  const int64_t n = t * 16 + (lane & 15);
+  const int64_t k = s * 32 + 8 * (lane >> 4);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < N) v = *(const u32x4 *)(src + n * K + k);
+  *(u32x4 *)(dst + slot * 8) = v;
+}
+
 // sum of K-split partials [ks][n] in split order
 __global__ void __launch_bounds__(kThreads)
 sum_splits_kernel(const float *part, int ksplit, int64_t n, float *out) {
@@ -327,6 +352,15 @@ hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t packed_weight_elems(int N, int K) { return (size_t)((N + 15) / 16) * 16 * K; }
+
+hipError_t launch_pack_weight(const void *src, void *dst, int N, int K, hipStream_t st) {
+  const int64_t n_slots = (int64_t)((N + 15) / 16) * (K / 32) * 64;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((n_slots + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, (const bf16_t *)src, (bf16_t *)dst, N, K);
+  return hipGetLastError();
+}
 
 HeadWs head_ws(void *ws, int M, int V, int rank) {
   HeadWs w;

@@ -94,6 +94,9 @@ struct HeadWs {
   size_t bytes;
 };
 HeadWs head_ws(void *ws, int M, int V, int rank);
+// bf16 weights [N, K] -> MFMA operand tiles (see head.hip); K % 32 == 0
+size_t packed_weight_elems(int N, int K);
+hipError_t launch_pack_weight(const void *src, void *dst, int N, int K, hipStream_t st);
 size_t head_workspace_bytes(int M, int d, int V, int rank, int dtype);
 // GEMM + tile statistics.  root_logits/root_stats (may be null): also compute the
 // tile statistics of B root rows over the same vocabulary tiles.

@@ -55,13 +55,15 @@ __device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
   return P;
 }
 
-// LDS images of one 32-key block, both without padding and XOR-swizzled so that the
-// MFMA fragment reads are free of bank conflicts:
+// LDS images of one 32-key block (two pages), both without padding and XOR-swizzled
+// so that the MFMA fragment reads are free of bank conflicts:
 //   K:   32 keys x 128 hd; the 16-byte chunk c of key k sits at position c ^ (k & 15)
-//   V^T: 128 hd rows x 32 keys; the 16-byte slot u (keys 8u..8u+7) of row r sits at
-//        position u ^ ((r >> 2) & 3)
+//   V^T: per page, 128 hd rows x 16 keys (32 bytes a row); the 16-byte half h (keys
+//        8h..8h+7) of row r sits at position h ^ ((r >> 3) & 1)
 // Each is 8 KB = 8 wave-wide 16-byte-per-lane transfers, which global_load_lds
-// writes straight into LDS (lane l -> bytes 16l..16l+15 of the transfer).
+// writes straight into LDS (lane l -> bytes 16l..16l+15 of the transfer); every
+// transfer reads one contiguous 1 KB run of the paged cache (4 key rows of K, or 32
+// head-dim rows of one V^T page).
 constexpr int kBlkElems = kKB * kHD;      // bf16 elements per K (or V^T) block image
 constexpr int kNBuf = 4;                  // blocks in flight per workgroup
 constexpr int kMaxSplitPages = 512;       // split_keys <= 8192
@@ -176,13 +178,13 @@ attn_mfma_kernel(AttnArgs a) {
         dma16(src, &Kb[slot][i * 512]);
       } else {
         const int i2 = i - 8;
-        const int r = 16 * i2 + (lane >> 2);
-        const int u = (lane & 3) ^ ((r >> 2) & 3);
-        const int pl = (kb - k_begin) / kPage + (u >> 1);
-        const int pg = (kb + 16 * (u >> 1) < k_end) ? pages[pl] : -1;
+        const int pp = i2 >> 2;                        // page within the block
+        const int r = 32 * (i2 & 3) + (lane >> 1);     // head-dim row
+        const int h = (lane & 1) ^ ((r >> 3) & 1);     // key half stored at this slot
+        const int pg = (kb + 16 * pp < k_end) ? pages[(kb - k_begin) / kPage + pp] : -1;
         const bf16_t *src = a.v_pool;
         if (pg >= 0)
-          src = a.v_pool + (((int64_t)pg * a.Hkv + kvh) * kHD + r) * kPage + 8 * (u & 1);
+          src = a.v_pool + (((int64_t)pg * a.Hkv + kvh) * kHD + r) * kPage + 8 * h;
         dma16(src, &Vb[slot][i2 * 512]);
       }
     }
@@ -200,11 +202,12 @@ attn_mfma_kernel(AttnArgs a) {
       }
       *(u32x4 *)&Kb[slot][key * kHD + 8 * (ch ^ (key & 15))] = kv;
       const bf16_t *ve = (const bf16_t *)&vv;
+      const int pp = key >> 4, kk = key & 15;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ch + e;
-        const int u = (key >> 3) ^ ((r >> 2) & 3);
-        Vb[slot][r * kKB + 8 * u + (key & 7)] = ve[e];
+        const int h = (kk >> 3) ^ ((r >> 3) & 1);
+        Vb[slot][pp * 2048 + r * 16 + 8 * h + (kk & 7)] = ve[e];
       }
     }
   };
@@ -217,28 +220,25 @@ attn_mfma_kernel(AttnArgs a) {
       ka[s4] = *(const bf16x8 *)&Kb[slot][l16 * kHD + 8 * pch];
       kb2[s4] = *(const bf16x8 *)&Kb[slot][(16 + l16) * kHD + 8 * pch];
     }
-    const int sw = (l16 >> 2) & 3;
+    // keys 4lg..4lg+3 of page 0 and of page 1 (block keys 16+4lg..): half lg>>1
+    const int hsw = ((lg >> 1) ^ ((l16 >> 3) & 1)) * 8 + 4 * (lg & 1);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const bf16_t *row = &Vb[slot][(16 * tt + l16) * kKB];
+      const int r = 16 * tt + l16;
       typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-      const bf16x4 lo = *(const bf16x4 *)(row + 8 * ((lg >> 1) ^ sw) + 4 * (lg & 1));
-      const bf16x4 hi = *(const bf16x4 *)(row + 8 * ((2 + (lg >> 1)) ^ sw) + 4 * (lg & 1));
+      const bf16x4 lo = *(const bf16x4 *)&Vb[slot][r * 16 + hsw];
+      const bf16x4 hi = *(const bf16x4 *)&Vb[slot][2048 + r * 16 + hsw];
       vf[tt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    // key validity: inside the range and (prefix) on a valid page
-    bool vis_a[4], vis_b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
-      if (is_cand) {
-        vis_a[j] = ka_i < k_end;
-        vis_b[j] = kb_i < k_end;
-      } else {
-        vis_a[j] = ka_i < k_end && pages[(ka_i - k_begin) >> 4] >= 0;
-        vis_b[j] = kb_i < k_end && pages[(kb_i - k_begin) >> 4] >= 0;
-      }
+    // block validity, uniform over the workgroup: two page lookups per block; a block
+    // of 32 in-range keys on two valid pages needs no per-key mask
+    int pv0 = 1, pv1 = 1;
+    if (!is_cand) {
+      const int pl = (kb - k_begin) >> 4;
+      pv0 = pages[pl] >= 0;
+      pv1 = (kb + 16 < k_end) ? (pages[pl + 1] >= 0) : 0;
     }
+    const bool full = !is_cand && pv0 && pv1 && (kb + kKB <= k_end);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -248,25 +248,44 @@ attn_mfma_kernel(AttnArgs a) {
         sb = mfma16x16x32(kb2[s4], qf[t][s4], sb);
       }
       float xa[4], xb[4];
-      float bmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bool va = vis_a[j], vb = vis_b[j];
-        if (is_cand) {
-          const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
-          const int m = mrow[t];
-          va = va && m < a.M && ka_i / a.D == m / a.D && ka_i <= m;
-          vb = vb && m < a.M && kb_i / a.D == m / a.D && kb_i <= m;
+        for (int j = 0; j < 4; ++j) {
+          xa[j] = sa[j] * a.scale_log2;
+          xb[j] = sb[j] * a.scale_log2;
         }
-        xa[j] = va ? sa[j] * a.scale_log2 : -INFINITY;
-        xb[j] = vb ? sb[j] * a.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, fmaxf(xa[j], xb[j]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
+          bool va, vb;
+          if (is_cand) {
+            const int m = mrow[t];
+            va = ka_i < k_end && m < a.M && ka_i / a.D == m / a.D && ka_i <= m;
+            vb = kb_i < k_end && m < a.M && kb_i / a.D == m / a.D && kb_i <= m;
+          } else {
+            va = pv0 && ka_i < k_end;
+            vb = pv1 && kb_i < k_end;
+          }
+          xa[j] = va ? sa[j] * a.scale_log2 : -INFINITY;
+          xb[j] = vb ? sb[j] * a.scale_log2 : -INFINITY;
+        }
       }
+      float bmax = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
+                         fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      // rescale the running sums only when some row's maximum grew
       const float mnew = fmaxf(m_run[t], bmax);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float corr = exp2f(m_run[t] - mref);
+      const bool grow = mnew > m_run[t];
+      if (__ballot(grow) != 0) {
+        const float corr = grow ? exp2f(m_run[t] - mnew) : 1.f;
+        l_part[t] *= corr;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) O[t][tt] *= corr;
+        m_run[t] = mnew;
+      }
+      const float mref = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
       float pa[4], pb[4], psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -274,24 +293,17 @@ attn_mfma_kernel(AttnArgs a) {
         pb[j] = exp2f(xb[j] - mref);
         psum += pa[j] + pb[j];
       }
-      l_part[t] = l_part[t] * corr + psum;
-      m_run[t] = mnew;
+      l_part[t] += psum;
       // P = hi + lo, both bf16: the PV product keeps ~16 significant bits of P
       uint32_t hk[4], lk[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16_t h0 = f32_to_bf16(pa[2 * j]), h1 = f32_to_bf16(pa[2 * j + 1]);
-        const bf16_t g0 = f32_to_bf16(pb[2 * j]), g1 = f32_to_bf16(pb[2 * j + 1]);
-        hk[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        hk[2 + j] = (uint32_t)g0 | ((uint32_t)g1 << 16);
-        lk[j] = pack_bf16x2(pa[2 * j] - bf16_to_f32(h0), pa[2 * j + 1] - bf16_to_f32(h1));
-        lk[2 + j] = pack_bf16x2(pb[2 * j] - bf16_to_f32(g0), pb[2 * j + 1] - bf16_to_f32(g1));
-      }
+      split_bf16x2(pa[0], pa[1], hk[0], lk[0]);
+      split_bf16x2(pa[2], pa[3], hk[1], lk[1]);
+      split_bf16x2(pb[0], pb[1], hk[2], lk[2]);
+      split_bf16x2(pb[2], pb[3], hk[3], lk[3]);
       const bf16x8 phi = *(const bf16x8 *)hk;
       const bf16x8 plo = *(const bf16x8 *)lk;
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        O[t][tt] *= corr;
         O[t][tt] = mfma16x16x32(vf[tt], phi, O[t][tt]);
         O[t][tt] = mfma16x16x32(vf[tt], plo, O[t][tt]);
       }

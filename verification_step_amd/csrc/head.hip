@@ -28,6 +28,7 @@
 
 #include "vs_internal.hpp"
 
+#include <stdlib.h>
 #include <type_traits>
 
 namespace vs {
@@ -124,14 +125,11 @@ head_stream_kernel(GemmArgs a) {
     for (int mt = 0; mt < MT; ++mt) {
       if constexpr (SPLIT) {
         const f32x8 x = hr[slot][mt];
-        bf16x8 hi, lo;
+        uint32_t hk[4], lk[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bf16_t hb = f32_to_bf16(x[e]);
-          const bf16_t lb = f32_to_bf16(x[e] - bf16_to_f32(hb));
-          hi[e] = __builtin_bit_cast(__bf16, hb);
-          lo[e] = __builtin_bit_cast(__bf16, lb);
-        }
+        for (int e = 0; e < 4; ++e) split_bf16x2(x[2 * e], x[2 * e + 1], hk[e], lk[e]);
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, *(const u32x4 *)hk);
+        const bf16x8 lo = __builtin_bit_cast(bf16x8, *(const u32x4 *)lk);
 #pragma unroll
         for (int v = 0; v < kVT; ++v) {
           acc[v][mt] = mfma16x16x32(wr[slot][v], hi, acc[v][mt]);
@@ -196,6 +194,180 @@ head_stream_kernel(GemmArgs a) {
   if (a.stats == nullptr) return;
 
   // root rows over this workgroup's vocabulary tile (one wave per row)
+  if (a.root != nullptr && mb == 0) {
+    for (int b = wv; b < a.B_root; b += 4) {
+      const float *row = a.root + (int64_t)b * a.N;
+      float x[kHeadVocabTile / 64];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kHeadVocabTile / 64; ++j) {
+        const int k = vt * kHeadVocabTile + j * 64 + lane;
+        x[j] = (k < a.N) ? row[k] * a.inv_t : -INFINITY;
+        mx = fmaxf(mx, x[j]);
+      }
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < kHeadVocabTile / 64; ++j)
+        if (x[j] != -INFINITY) sm += expf(x[j] - mx);
+      for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+      if (lane == 0) a.root_stats[(int64_t)b * n_vt + vt] = make_float2(mx, sm);
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < MT * 16; r += kThreads) {
+    const int m = mbase + r;
+    if (m >= a.M) continue;
+    float mx = -INFINITY;
+    for (int w2 = 0; w2 < 4; ++w2) mx = fmaxf(mx, red[w2][r].x);
+    float sm = 0.f;
+    for (int w2 = 0; w2 < 4; ++w2)
+      if (red[w2][r].x != -INFINITY) sm += red[w2][r].y * expf(red[w2][r].x - mx);
+    a.stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
+  }
+}
+
+// Head GEMM with H shared through LDS (bf16 H, K % 128 == 0): the workgroup stages
+// H in chunks of 128 columns with direct global->LDS transfers (double-buffered,
+// 16-byte chunk c of row r at position c ^ (r & 15): conflict-free fragment reads),
+// while each wave keeps streaming its packed W strips through its register ring.
+constexpr int kHC = 128;                 // H columns per LDS chunk (4 K-steps)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16_h(const void *g, bf16_t *lds_dst) {
+  // opaque to the compiler's wait insertion (which would drain every transfer before
+  // any LDS read); completion is waited for explicitly before the publishing barrier
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int MT>
+__global__ void __launch_bounds__(kThreads, 2)
+head_lds_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_t Hs[2][MT * 16 * kHC];
+  __shared__ float2 red[4][MT * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
+  const int nblocks = n_vt * a.n_mblocks;
+  const int bid = xcd_remap(blockIdx.x, nblocks);
+  const int mb = bid % a.n_mblocks;
+  const int vt = bid / a.n_mblocks;
+  const int vbase = vt * kHeadVocabTile + wv * (kVT * 16);
+  const int mbase = mb * MT * 16;
+  const int nsteps = a.K / 32;
+  const int nchunks = a.K / kHC;
+
+  const int n_strips = (a.N + 15) / 16;
+  const bf16_t *wp[kVT];
+#pragma unroll
+  for (int v = 0; v < kVT; ++v) {
+    int t = vbase / 16 + v;
+    t = t < n_strips ? t : n_strips - 1;
+    wp[v] = a.w + ((int64_t)t * nsteps * 64 + lane) * 8;
+  }
+  constexpr int kPDL = 3, kRingL = kPDL + 1;   // W steps in flight; one ring turn per chunk
+  bf16x8 wr[kRingL][kVT];
+  auto load_w = [&](int slot, int s) {
+#pragma unroll
+    for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 512 * s);
+  };
+  // H chunk c: MT*16 rows x 128 columns = MT*4 transfers of 1 KB (4 rows each); wave
+  // wv issues transfers wv, wv+4, ...
+  const bf16_t *hbase = (const bf16_t *)a.h;
+  auto issue_h = [&](int c, int buf) {
+#pragma unroll
+    for (int ii = 0; ii < MT; ++ii) {
+      const int i = wv + 4 * ii;
+      const int row = 4 * i + (lane >> 4);
+      const int ch = (lane & 15) ^ (row & 15);
+      int m = mbase + row;
+      m = m < a.M ? m : a.M - 1;
+      dma16_h(hbase + (int64_t)m * a.K + c * kHC + 8 * ch, &Hs[buf][i * 512]);
+    }
+  };
+
+  f32x4 acc[kVT][MT];
+#pragma unroll
+  for (int v = 0; v < kVT; ++v)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[v][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue_h(0, 0);
+#pragma unroll
+  for (int p = 0; p < kPDL; ++p) load_w(p, p);
+  __builtin_amdgcn_s_waitcnt(0);      // H chunk 0 (and the first W steps) have landed
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) issue_h(c + 1, buf ^ 1);
+#pragma unroll
+    for (int u = 0; u < kHC / 32; ++u) {
+      const int ss = c * (kHC / 32) + u;
+      // ring slot of step ss is ss % kRingL; kHC/32 == kRingL keeps it static
+      if (ss + kPDL < nsteps) load_w((u + kPDL) % kRingL, ss + kPDL);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + l16;
+        const int pch = (4 * u + lg) ^ (row & 15);
+        const bf16x8 hf = *(const bf16x8 *)&Hs[buf][row * kHC + 8 * pch];
+#pragma unroll
+        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wr[u][v], hf, acc[v][mt]);
+      }
+    }
+    if (c + 1 < nchunks) {
+      // everything up to this chunk's H transfers: only the W loads issued after them
+      // (kHC/32 steps x kVT) may still be in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((kHC / 32) * kVT & 15) | ((((kHC / 32) * kVT) >> 4) << 14));
+      __syncthreads();
+    }
+  }
+  static_assert(kHC / 32 == kRingL, "one ring turn per H chunk");
+
+  // ---- epilogue: logits + tile statistics (as the streaming kernel)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mbase + mt * 16 + l16;
+    float vmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kVT; ++v) {
+      const int n0 = vbase + v * 16 + 4 * lg;
+      if (m < a.M) {
+        float *op = a.out + (int64_t)m * a.N + n0;
+        if (n0 + 3 < a.N) {
+          *(f32x4 *)op = acc[v][mt];
+        } else {
+          for (int j = 0; j < 4; ++j)
+            if (n0 + j < a.N) op[j] = acc[v][mt][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.N) vmax = fmaxf(vmax, acc[v][mt][j] * a.inv_t);
+    }
+    if (a.stats == nullptr) continue;
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    float vs = 0.f;
+#pragma unroll
+    for (int v = 0; v < kVT; ++v) {
+      const int n0 = vbase + v * 16 + 4 * lg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + j < a.N) vs += expf(acc[v][mt][j] * a.inv_t - vmax);
+    }
+    vs += __shfl_xor(vs, 16);
+    vs += __shfl_xor(vs, 32);
+    if (lg == 0) red[wv][mt * 16 + l16] = make_float2(vmax, vs);
+  }
+  if (a.stats == nullptr) return;
   if (a.root != nullptr && mb == 0) {
     for (int b = wv; b < a.B_root; b += 4) {
       const float *row = a.root + (int64_t)b * a.N;
@@ -328,6 +500,26 @@ hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
   const int mt = pick_mt(a.M, &a.n_mblocks);
   const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
   const dim3 grid(n_vt * a.n_mblocks, ksplit);
+  if (!split && ksplit == 1 && a.K % kHC == 0 && getenv("VSTEP_HEAD_STREAM") == nullptr) {
+#define VS_LDS_CASE(MTV)                                                                  \
+  case MTV:                                                                               \
+    hipLaunchKernelGGL((head_lds_kernel<MTV>), grid, dim3(kThreads), 0, st, a);           \
+    break;
+    switch (mt) {
+      VS_LDS_CASE(1)
+      VS_LDS_CASE(2)
+      VS_LDS_CASE(3)
+      VS_LDS_CASE(4)
+      VS_LDS_CASE(5)
+      VS_LDS_CASE(6)
+      VS_LDS_CASE(7)
+      VS_LDS_CASE(8)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef VS_LDS_CASE
+    return hipGetLastError();
+  }
 #define VS_GEMM_CASE(MTV)                                                                   \
   case MTV:                                                                                 \
     if (split)                                                                              \

@@ -109,13 +109,17 @@ int vs_probe_gate(const void *h, int h_dtype, const float *w, int B, int d, floa
  * are invisible.  softmax(scale * q.k) over the visible keys, weighted sum of values.
  *   q             [B*W*D, Hq, hd]   dtype
  *   k_cand/v_cand [B*W*D, Hkv, hd]  dtype (the candidates' own keys/values)
- *   k_pool/v_pool [n_pool_pages, page_size, Hkv, hd] dtype (paged prefix cache)
+ *   k_pool        [n_pool_pages, Hkv, page_size, hd] dtype (paged prefix keys)
+ *   v_pool        [n_pool_pages, Hkv, hd, page_size] dtype (paged prefix values,
+ *                 transposed within each page: the page_size tokens of one head-dim
+ *                 coordinate are contiguous)
  *   page_table    int32 [B, max_pages]: page of prefix positions 16p..16p+15
  *   prefix_len    int32 [B]
  *   out           [B*W*D, Hq, hd] dtype (bf16 rounded to nearest even, or fp32)
  *   flags         int32 [B] out or NULL (VS_FLAG_BAD_PAGE: keys of a bad page are skipped)
  * Supported: VS_BF16 with head_dim 128 (MFMA path); VS_F32 with head_dim 16, 32 or 64.
- * page_size must be 16.  scale <= 0 selects 1/sqrt(head_dim).  Accumulation in fp32. */
+ * page_size must be 16; max_pages > 0 requires n_pool_pages >= 1.  scale <= 0 selects
+ * 1/sqrt(head_dim).  Accumulation in fp32. */
 typedef struct {
     int32_t B, W, D, Hq, Hkv, head_dim, page_size, max_pages, n_pool_pages;
     int32_t dtype;          /* vs_dtype */

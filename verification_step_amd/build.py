@@ -22,6 +22,9 @@ LIB = os.path.join(HERE, "libvstep.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["gate.hip", "attention.hip", "head.hip", "sampler.hip", "capi.hip"]
+# per-source flags: the attention scores are never NaN (masked keys are -inf), so its
+# max trees need no NaN canonicalisation (plain v_max3 instead of quieting each input)
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -39,7 +42,7 @@ def common_flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -5,19 +5,23 @@
 //
 // bf16 path (head_dim 128), per workgroup = (sequence b, KV head, row block, key split):
 //   * the g*M query rows that share a KV head (GQA) are ordered r = m*g + h_local
-//     and cut into blocks of NW waves x RT tiles x 16 rows;
+//     and cut into tiles of 32 rows, one per wave; NW waves form a row block and
+//     share one stream of K/V blocks through LDS;
 //   * prefix keys are split in ranges of `split_keys` (paged KV, 16-token pages);
 //     the candidates' own keys form one extra split;
 //   * the paged cache is head-major per page: K [page][kv head][16 tokens][hd] and
 //     V transposed within a page, [page][kv head][hd][16 tokens], so a 32-key block
-//     of either is a few contiguous 4 KB runs; the next block is loaded into
-//     registers while the current one (double-buffered in LDS) is multiplied;
-//   * K sits in LDS row-major and V key-contiguous, the A operand of the PV product;
-//   * S^T = K Q^T with MFMA 16x16x32 bf16: a lane holds 4 keys x 1 query row, so
-//     the row max needs two cross-lane exchanges and the probabilities P^T feed the
-//     next MFMA (O^T += V^T P^T) straight from registers;
-//   * online softmax in fp32 (exp2 domain); P enters the PV product as bf16 hi + lo
-//     (two MFMAs), which keeps the output error at the bf16 rounding of O itself;
+//     of either is a few contiguous 4 KB runs, moved by direct global->LDS transfers
+//     into a ring of kNBuf blocks that runs ahead of the multiplication;
+//   * S^T = K Q^T with MFMA 32x32x16 bf16: a lane holds 16 keys x 1 query row, the
+//     other 16 keys of that row sit in lane l^32, so the row max is one cross-lane
+//     swap; the probabilities P^T feed the PV product (O^T += V^T P^T) straight
+//     from registers;
+//   * online softmax in fp32 in the exp2 domain, with a lazy reference maximum: the
+//     accumulators are rescaled only when a row's block maximum exceeds the
+//     reference by more than kLazy (P stays below 2^kLazy, exact either way);
+//   * P enters the PV product as bf16 hi + lo (two MFMAs), which keeps the output
+//     error at the bf16 rounding of O itself;
 //   * partial (max, sum, O) per split go to the workspace and a combine kernel
 //     merges them in a fixed order.
 // fp32 path (head_dim 16/32/64): one thread per (query row, head), plain loops.
@@ -34,6 +38,26 @@ namespace {
 constexpr int kHD = 128;
 constexpr int kKB = 32;            // keys per block
 constexpr int kPage = 16;
+constexpr int kTileRows = 32;      // query rows per wave
+constexpr float kLazy = 8.0f;      // log2 headroom of the lazy reference maximum
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max of x over lanes l and l^32
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct AttnArgs {
   const bf16_t *q, *k_cand, *v_cand, *k_pool, *v_pool;
@@ -70,32 +94,60 @@ constexpr int kMaxSplitPages = 512;       // split_keys <= 8192
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16 bytes per lane from global memory straight into LDS (lane l -> lds_dst + 16 l).
-// Issued as an opaque instruction: the compiler's automatic waits would otherwise
-// drain every in-flight transfer before any read of the ring; completion is tracked
-// explicitly with s_waitcnt vmcnt before the barrier that publishes a block.
-__device__ __forceinline__ void dma16(const void *g, bf16_t *lds_dst) {
-  // the destination is wave-uniform by construction; make that explicit for the SGPR
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// 16 bytes per lane from global memory straight into LDS: lane l reads sbase + voff_l
+// and writes LDS bytes lds + 16 l .. lds + 16 l + 15.  sbase and lds are wave-uniform
+// (SGPRs).  Issued as an opaque instruction: the compiler's automatic waits would
+// otherwise drain every in-flight transfer before any read of the ring; completion is
+// tracked explicitly with s_waitcnt vmcnt before the barrier that publishes a block.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+  // both operands are uniform by construction; readfirstlane makes that visible
+  // (readfirstlane returns int: each half goes through uint32_t so that the low word
+  // is not sign-extended into the high one)
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32));
+  const uint64_t sbu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(lds)
+               : "v"(voff), "s"((const void *)(uintptr_t)sbu),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
-template <int RT, int NW>
-__global__ void __launch_bounds__(64 * NW)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)p);
+}
+
+// Key order of the QK product inside a 16-key page: MFMA row i holds key perm16(i),
+// bits 2 and 3 swapped, so that lane half h of the 32x32 result holds keys 8h..8h+7
+// of each page -- eight consecutive keys, one 16-byte V^T read for the PV product.
+__device__ __forceinline__ int perm16(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 2)
 attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t Kb[kNBuf][kBlkElems];
   __shared__ __attribute__((aligned(1024))) bf16_t Vb[kNBuf][kBlkElems];
   __shared__ int pages[kMaxSplitPages];
 
-  constexpr int kIPW = 16 / NW;           // 1 KB transfers per wave per block
+  // a block is 16 transfers of 1 KB (8 of K, 8 of V^T); wave wv issues wv, wv+NW, ...
+  constexpr int kT = 16;
+  constexpr int kIPW = (kT + NW - 1) / NW;
+  constexpr bool kEven = (kT % NW) == 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const bool full_share = kEven || wv < kT % NW;   // this wave issues kIPW transfers
 
   const int n_sp = a.n_splits + 1;
   const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
@@ -119,31 +171,16 @@ attn_mfma_kernel(AttnArgs a) {
   const int k_end = is_cand ? a.M : min(P, (s + 1) * a.split_keys);
   const int nblk = (k_end - k_begin + kKB - 1) / kKB;
 
-  // ---- this lane's query rows and fragments
-  int rr[RT], mrow[RT];
-  bf16x8 qf[RT][4];
+  // ---- this lane's query row (one of the wave's 32) and its Q^T fragments
+  const int rr = rb * a.rows_per_block + wv * kTileRows + l32;
+  const bool rok = rr < a.rows_per_kv;
+  const int mrow = rok ? rr / a.g : a.M;   // a.M marks a padding row
+  const int hq = kvh * a.g + (rok ? rr % a.g : 0);
+  bf16x8 qf[8];
+  {
+    const bf16_t *qp = a.q + (((int64_t)b * a.M + (rok ? mrow : 0)) * a.Hq + hq) * kHD + 8 * h;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    rr[t] = rb * a.rows_per_block + (wv * RT + t) * 16 + l16;
-    const bool ok = rr[t] < a.rows_per_kv;
-    mrow[t] = ok ? rr[t] / a.g : a.M;   // a.M marks a padding row
-    const int hq = kvh * a.g + (ok ? rr[t] % a.g : 0);
-    const bf16_t *qp = a.q + (((int64_t)b * a.M + (ok ? mrow[t] : 0)) * a.Hq + hq) * kHD;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) qf[t][s4] = ok ? *(const bf16x8 *)(qp + 32 * s4 + 8 * lg) : bf16x8{};
-  }
-  // all ordinary loads done before the ring starts: inside the loop the only vector
-  // memory operations are the explicitly counted LDS transfers
-  __builtin_amdgcn_s_waitcnt(0);
-
-  f32x4 O[RT][8];
-  float m_run[RT], l_part[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    m_run[t] = -INFINITY;
-    l_part[t] = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) O[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s8 = 0; s8 < 8; ++s8) qf[s8] = rok ? *(const bf16x8 *)(qp + 16 * s8) : bf16x8{};
   }
 
   // ---- the split's page indices, once (bad pages -> -1, flagged)
@@ -159,40 +196,66 @@ attn_mfma_kernel(AttnArgs a) {
     }
     if (bad && a.flags) atomicOr(&a.flags[b], FLAG_BAD_PAGE);
   }
+  // all ordinary loads done before the ring starts: inside the loop the only vector
+  // memory operations are the explicitly counted LDS transfers
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  f32x16 O[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) O[t][j] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+  const float c = a.scale_log2;
+
+  // this wave's transfers of a block: byte offset of each lane's 16 bytes inside the
+  // (page, KV head) run of the pool, and the transfer's place in the LDS block image
+  //   K transfer i < 8: keys 4i..4i+3 (page i/4); chunk c of key k lands at c ^ (k & 15)
+  //   V^T transfer i >= 8: page (i-8)/4, head-dim rows 32((i-8)%4) + l/2, key half
+  //   hh = (l & 1) ^ ((r >> 3) & 1) lands at position l & 1 of row r
+  uint32_t voff[kIPW];
+#pragma unroll
+  for (int ii = 0; ii < kIPW; ++ii) {
+    const int i = min(wv + ii * NW, kT - 1);
+    if (i < 8) {
+      const int key = 4 * i + (lane >> 4);
+      const int ch = (lane & 15) ^ (key & 15);
+      voff[ii] = (uint32_t)(((key & 15) * kHD + 8 * ch) * 2);
+    } else {
+      const int r = 32 * ((i - 8) & 3) + (lane >> 1);
+      const int hh = (lane & 1) ^ ((r >> 3) & 1);
+      voff[ii] = (uint32_t)((r * kPage + 8 * hh) * 2);
+    }
+  }
+  const uint32_t kb_lds = lds_addr(&Kb[0][0]);
+  const uint32_t vb_lds = lds_addr(&Vb[0][0]);
+  constexpr uint32_t kSlotBytes = kBlkElems * 2;
 
   // issue this wave's share of block j (prefix) into ring slot `slot`
   auto issue_prefix = [&](int j, int slot) {
     const int kb = k_begin + j * kKB;
+    const int pl = 2 * j;
+    const int pg0 = __builtin_amdgcn_readfirstlane(pages[pl]);
+    const int pg1 = __builtin_amdgcn_readfirstlane((kb + kPage < k_end) ? pages[pl + 1] : -1);
+    // a missing or bad page reads the pool's first run instead; its keys are masked
+    const int64_t run0 = pg0 >= 0 ? ((int64_t)pg0 * a.Hkv + kvh) * (kPage * kHD) : 0;
+    const int64_t run1 = pg1 >= 0 ? ((int64_t)pg1 * a.Hkv + kvh) * (kPage * kHD) : 0;
 #pragma unroll
     for (int ii = 0; ii < kIPW; ++ii) {
       const int i = wv + ii * NW;           // transfer index 0..15
-      if (i < 8) {
-        const int key = 4 * i + (lane >> 4);
-        const int c = (lane & 15) ^ (key & 15);
-        const int pg = pages[(kb - k_begin) / kPage + (key >> 4)];
-        const bf16_t *src = a.k_pool;
-        if (pg >= 0 && kb + key < k_end)
-          src = a.k_pool + (((int64_t)pg * a.Hkv + kvh) * kPage + (key & 15)) * kHD + 8 * c;
-        dma16(src, &Kb[slot][i * 512]);
-      } else {
-        const int i2 = i - 8;
-        const int pp = i2 >> 2;                        // page within the block
-        const int r = 32 * (i2 & 3) + (lane >> 1);     // head-dim row
-        const int h = (lane & 1) ^ ((r >> 3) & 1);     // key half stored at this slot
-        const int pg = (kb + 16 * pp < k_end) ? pages[(kb - k_begin) / kPage + pp] : -1;
-        const bf16_t *src = a.v_pool;
-        if (pg >= 0)
-          src = a.v_pool + (((int64_t)pg * a.Hkv + kvh) * kHD + r) * kPage + 8 * h;
-        dma16(src, &Vb[slot][i2 * 512]);
-      }
+      if (i >= kT) break;
+      const int64_t run = ((i & 7) >> 2) ? run1 : run0;
+      if (i < 8)
+        dma16(a.k_pool + run, voff[ii], kb_lds + slot * kSlotBytes + i * 1024);
+      else
+        dma16(a.v_pool + run, voff[ii], vb_lds + slot * kSlotBytes + (i - 8) * 1024);
     }
   };
   // candidate keys (row-major [B*M, Hkv, hd]): staged through registers, V transposed
   auto stage_cand = [&](int slot, int kb) {
-    for (int c = tid; c < kKB * 16; c += 64 * NW) {
-      const int key = c >> 4, ch = c & 15;
+    for (int cc = tid; cc < kKB * 16; cc += 64 * NW) {
+      const int key = cc >> 4, ch = cc & 15;
       const int pos = kb + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (pos < k_end) {
@@ -206,32 +269,46 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ch + e;
-        const int h = (kk >> 3) ^ ((r >> 3) & 1);
-        Vb[slot][pp * 2048 + r * 16 + 8 * h + (kk & 7)] = ve[e];
+        const int hh = (kk >> 3) ^ ((r >> 3) & 1);
+        Vb[slot][pp * 2048 + r * 16 + 8 * hh + (kk & 7)] = ve[e];
       }
     }
   };
 
-  auto compute = [&](int slot, int kb) {
-    bf16x8 ka[4], kb2[4], vf[8];
+  // MFMA row l32 of the QK product is key krow of the block; lane l, register j of
+  // S^T then holds key 16*(j/8) + 8h + j%8, row l32
+  const int krow = (l32 & 16) | perm16(l32 & 15);
+  auto load_k = [&](int slot, bf16x8 *kf) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int pch = (4 * s4 + lg) ^ l16;
-      ka[s4] = *(const bf16x8 *)&Kb[slot][l16 * kHD + 8 * pch];
-      kb2[s4] = *(const bf16x8 *)&Kb[slot][(16 + l16) * kHD + 8 * pch];
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int pc = (2 * s8 + h) ^ (krow & 15);
+      kf[s8] = *(const bf16x8 *)&Kb[slot][krow * kHD + 8 * pc];
     }
-    // keys 4lg..4lg+3 of page 0 and of page 1 (block keys 16+4lg..): half lg>>1
-    const int hsw = ((lg >> 1) ^ ((l16 >> 3) & 1)) * 8 + 4 * (lg & 1);
+  };
+  // V^T fragment (t, ks): head-dim row 32t + l32, keys 8h..8h+7 of page ks
+  auto load_v = [&](int slot, bf16x8 *vf) {
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const int r = 16 * tt + l16;
-      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-      const bf16x4 lo = *(const bf16x4 *)&Vb[slot][r * 16 + hsw];
-      const bf16x4 hi = *(const bf16x4 *)&Vb[slot][2048 + r * 16 + hsw];
-      vf[tt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int t = 0; t < 4; ++t) {
+      const int r = 32 * t + l32;
+      const int sw = (r >> 3) & 1;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        vf[2 * t + ks] = *(const bf16x8 *)&Vb[slot][ks * 2048 + r * 16 + 8 * (h ^ sw)];
     }
-    // block validity, uniform over the workgroup: two page lookups per block; a block
-    // of 32 in-range keys on two valid pages needs no per-key mask
+  };
+  auto qk_mma = [&](const bf16x8 *kf) -> f32x16 {
+    f32x16 S;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S[j] = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) S = mfma32x32x16(kf[s8], qf[s8], S);
+    return S;
+  };
+
+  // masking and the running maximum of one block's scores (may rescale O and l)
+  auto softmax_max = [&](f32x16 &S, int kb) {
+    // block validity, uniform over the workgroup: a block of 32 in-range keys on two
+    // valid pages needs no per-key mask
     int pv0 = 1, pv1 = 1;
     if (!is_cand) {
       const int pl = (kb - k_begin) >> 4;
@@ -239,136 +316,168 @@ attn_mfma_kernel(AttnArgs a) {
       pv1 = (kb + 16 < k_end) ? (pages[pl + 1] >= 0) : 0;
     }
     const bool full = !is_cand && pv0 && pv1 && (kb + kKB <= k_end);
+    if (!full) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        sa = mfma16x16x32(ka[s4], qf[t][s4], sa);
-        sb = mfma16x16x32(kb2[s4], qf[t][s4], sb);
+      for (int j = 0; j < 16; ++j) {
+        const int kpos = kb + 16 * (j >> 3) + 8 * h + (j & 7);
+        bool v;
+        if (is_cand)
+          v = kpos < k_end && mrow < a.M && kpos / a.D == mrow / a.D && kpos <= mrow;
+        else
+          v = (j < 8 ? pv0 : pv1) && kpos < k_end;
+        S[j] = v ? S[j] : -INFINITY;
       }
-      float xa[4], xb[4];
-      if (full) {
+    }
+    float bm = fmaxf(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])),
+                     fmaxf(fmaxf(S[4], S[5]), fmaxf(S[6], S[7])));
+    bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(S[8], S[9]), fmaxf(S[10], S[11])),
+                         fmaxf(fmaxf(S[12], S[13]), fmaxf(S[14], S[15]))));
+    const float bms = max_xor32(bm) * c;
+    // lazy reference maximum: rescale only when a row outgrows it by more than kLazy
+    const bool grow = bms > m_run + kLazy;
+    if (__ballot(grow) != 0) {
+      const float mn = grow ? bms : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mn) : 1.f;
+      l_part *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xa[j] = sa[j] * a.scale_log2;
-          xb[j] = sb[j] * a.scale_log2;
-        }
-      } else {
+      for (int t = 0; t < 4; ++t) O[t] *= alpha;
+      m_run = mn;
+    }
+  };
+
+  // probabilities of one block (P = hi + lo, both bf16: the PV product keeps ~16
+  // significant bits of P) and its PV product
+  auto softmax_pv = [&](const f32x16 &S, const bf16x8 *vf) {
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    float p[16];
+    float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ka_i = kb + 4 * lg + j, kb_i = kb + 16 + 4 * lg + j;
-          bool va, vb;
-          if (is_cand) {
-            const int m = mrow[t];
-            va = ka_i < k_end && m < a.M && ka_i / a.D == m / a.D && ka_i <= m;
-            vb = kb_i < k_end && m < a.M && kb_i / a.D == m / a.D && kb_i <= m;
-          } else {
-            va = pv0 && ka_i < k_end;
-            vb = pv1 && kb_i < k_end;
-          }
-          xa[j] = va ? sa[j] * a.scale_log2 : -INFINITY;
-          xb[j] = vb ? sb[j] * a.scale_log2 : -INFINITY;
-        }
-      }
-      float bmax = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
-                         fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      // rescale the running sums only when some row's maximum grew
-      const float mnew = fmaxf(m_run[t], bmax);
-      const bool grow = mnew > m_run[t];
-      if (__ballot(grow) != 0) {
-        const float corr = grow ? exp2f(m_run[t] - mnew) : 1.f;
-        l_part[t] *= corr;
+    for (int j = 0; j < 16; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(fmaf(S[j], c, -mref));
+      psum += p[j];
+    }
+    l_part += psum;
+    uint32_t hk[8], lk[8];
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) O[t][tt] *= corr;
-        m_run[t] = mnew;
-      }
-      const float mref = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
-      float pa[4], pb[4], psum = 0.f;
+    for (int e = 0; e < 8; ++e) split_bf16x2(p[2 * e], p[2 * e + 1], hk[e], lk[e]);
+    const bf16x8 ph0 = __builtin_bit_cast(bf16x8, u32x4{hk[0], hk[1], hk[2], hk[3]});
+    const bf16x8 ph1 = __builtin_bit_cast(bf16x8, u32x4{hk[4], hk[5], hk[6], hk[7]});
+    const bf16x8 pl0 = __builtin_bit_cast(bf16x8, u32x4{lk[0], lk[1], lk[2], lk[3]});
+    const bf16x8 pl1 = __builtin_bit_cast(bf16x8, u32x4{lk[4], lk[5], lk[6], lk[7]});
+    // the four head-dim tiles are independent accumulation chains: interleave them
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pa[j] = exp2f(xa[j] - mref);
-        pb[j] = exp2f(xb[j] - mref);
-        psum += pa[j] + pb[j];
-      }
-      l_part[t] += psum;
-      // P = hi + lo, both bf16: the PV product keeps ~16 significant bits of P
-      uint32_t hk[4], lk[4];
-      split_bf16x2(pa[0], pa[1], hk[0], lk[0]);
-      split_bf16x2(pa[2], pa[3], hk[1], lk[1]);
-      split_bf16x2(pb[0], pb[1], hk[2], lk[2]);
-      split_bf16x2(pb[2], pb[3], hk[3], lk[3]);
-      const bf16x8 phi = *(const bf16x8 *)hk;
-      const bf16x8 plo = *(const bf16x8 *)lk;
+    for (int t = 0; t < 4; ++t) O[t] = mfma32x32x16(vf[2 * t], ph0, O[t]);
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        O[t][tt] = mfma16x16x32(vf[tt], phi, O[t][tt]);
-        O[t][tt] = mfma16x16x32(vf[tt], plo, O[t][tt]);
-      }
+    for (int t = 0; t < 4; ++t) O[t] = mfma32x32x16(vf[2 * t], pl0, O[t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = mfma32x32x16(vf[2 * t + 1], ph1, O[t]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = mfma32x32x16(vf[2 * t + 1], pl1, O[t]);
+  };
+
+  // ring waits: all of this wave's transfers except those of the last n blocks issued
+  auto wait_blocks = [&](int n) {
+    if (n >= 2) {
+      if (full_share) wait_vmcnt<2 * kIPW>();
+      else wait_vmcnt<2 * (kIPW - 1)>();
+    } else if (n == 1) {
+      if (full_share) wait_vmcnt<kIPW>();
+      else wait_vmcnt<kIPW - 1>();
+    } else {
+      wait_vmcnt<0>();
     }
   };
 
   if (is_cand) {
     for (int j = 0; j < nblk; ++j) {
       const int slot = j & 1;
-      stage_cand(slot, k_begin + j * kKB);
+      const int kb = k_begin + j * kKB;
+      stage_cand(slot, kb);
       __syncthreads();
-      compute(slot, k_begin + j * kKB);
+      bf16x8 kf[8], vf[8];
+      load_k(slot, kf);
+      load_v(slot, vf);
+      f32x16 S = qk_mma(kf);
+      softmax_max(S, kb);
+      softmax_pv(S, vf);
     }
-  } else {
-    // ring: blocks j+1..j+kNBuf-2 stay in flight while block j is multiplied
+  } else if (nblk > 0) {
+    // software pipeline over the ring: in iteration j block j+1's QK product is
+    // interleaved with block j's softmax and PV product, and block j+3 is in flight
+    static_assert(kNBuf == 4, "ring of four blocks");
 #pragma unroll
-    for (int j = 0; j < kNBuf - 1; ++j)
+    for (int j = 0; j < 3; ++j)
       if (j < nblk) issue_prefix(j, j);
+    wait_blocks(min(nblk - 1, 2));   // block 0
+    __syncthreads();
+    f32x16 S_cur;
+    {
+      bf16x8 kf[8];
+      load_k(0, kf);
+      S_cur = qk_mma(kf);
+    }
     for (int j = 0; j < nblk; ++j) {
-      if (j + kNBuf - 2 < nblk)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (((kNBuf - 2) * kIPW) & 15) |
-                                   ((((kNBuf - 2) * kIPW) >> 4) << 14));
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // tail: everything issued is needed
+      const int kb = k_begin + j * kKB;
+      // block j+1 must have landed; the blocks issued after it may still be in flight
+      wait_blocks(min(nblk - 1, j + 2) - (j + 1));
       __syncthreads();
-      if (j + kNBuf - 1 < nblk) issue_prefix(j + kNBuf - 1, (j + kNBuf - 1) % kNBuf);
-      compute(j % kNBuf, k_begin + j * kKB);
+      if (j + 3 < nblk) issue_prefix(j + 3, (j + 3) & 3);
+      const bool more = j + 1 < nblk;
+      bf16x8 kf[8], vf[8];
+      load_k(more ? (j + 1) & 3 : j & 3, kf);
+      load_v(j & 3, vf);
+      softmax_max(S_cur, kb);
+      f32x16 S_next = qk_mma(kf);     // harmless recomputation on the last block
+      softmax_pv(S_cur, vf);
+      // issue order: QK products between the exponentials, PV products as P is ready
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+      }
+#pragma unroll
+      for (int g16 = 0; g16 < 16; ++g16) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      S_cur = S_next;
     }
   }
 
-  // ---- finish: row sums over the 4 lane groups, then final output or partials
+  // ---- finish: the row's sum over both lane halves, then final output or partials
+  const float l = sum_xor32(l_part);
+  if (!rok) return;
+  // O^T register j of tile t: head dim 32t + 8*(j/4) + 4h + j%4
+  if (n_active == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16_t *op = a.out + (((int64_t)b * a.M + mrow) * a.Hq + hq) * kHD + 4 * h;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    float l = l_part[t];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const bool ok = rr[t] < a.rows_per_kv;
-    if (!ok) continue;
-    const int row_in_block = (wv * RT + t) * 16 + l16;
-    if (n_active == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int hq = kvh * a.g + rr[t] % a.g;
-      bf16_t *op = a.out + (((int64_t)b * a.M + mrow[t]) * a.Hq + hq) * kHD;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        uint32_t w0 = pack_bf16x2(O[t][tt][0] * inv, O[t][tt][1] * inv);
-        uint32_t w1 = pack_bf16x2(O[t][tt][2] * inv, O[t][tt][3] * inv);
-        *(uint2 *)(op + 16 * tt + 4 * lg) = make_uint2(w0, w1);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t w0 = pack_bf16x2(O[t][4 * q4] * inv, O[t][4 * q4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(O[t][4 * q4 + 2] * inv, O[t][4 * q4 + 3] * inv);
+        *(uint2 *)(op + 32 * t + 8 * q4) = make_uint2(w0, w1);
       }
-    } else {
-      const int64_t slot =
-          (((int64_t)z * a.n_rb + rb) * n_sp + s) * a.rows_per_block + row_in_block;
-      float *po = a.part_o + slot * kHD;
+  } else {
+    const int row_in_block = wv * kTileRows + l32;
+    const int64_t slot =
+        (((int64_t)z * a.n_rb + rb) * n_sp + s) * a.rows_per_block + row_in_block;
+    float *po = a.part_o + slot * kHD + 4 * h;
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) *(f32x4 *)(po + 16 * tt + 4 * lg) = O[t][tt];
-      if (lg == 0) {
-        a.part_ml[slot * 2 + 0] = m_run[t];
-        a.part_ml[slot * 2 + 1] = l;
-      }
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4 *)(po + 32 * t + 8 * q4) =
+            f32x4{O[t][4 * q4], O[t][4 * q4 + 1], O[t][4 * q4 + 2], O[t][4 * q4 + 3]};
+    if (h == 0) *(float2 *)(a.part_ml + slot * 2) = make_float2(m_run, l);
   }
 }
 
 // Merge the split partials of every row in a fixed order (prefix splits ascending,
-// then the candidate split).  One thread per (row, 4 head-dim values).
+// then the candidate split): one pass over groups of eight splits, whose loads are
+// independent, with the running maximum rescaled between groups.  One thread per
+// (row, 4 head-dim values).
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a) {
   const int n_sp = a.n_splits + 1;
@@ -387,22 +496,40 @@ attn_combine_kernel(AttnArgs a) {
   const int P = clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
   const int n_pref = (P + a.split_keys - 1) / a.split_keys;
   if (n_pref == 0) return;  // the candidate split alone wrote the output
+  const int n = n_pref + 1;
   const int64_t base = ((int64_t)z * a.n_rb + rb) * n_sp;
-  float mx = -INFINITY;
-  for (int k = 0; k <= n_pref; ++k) {
-    const int sp = (k == n_pref) ? a.n_splits : k;
-    mx = fmaxf(mx, a.part_ml[((base + sp) * a.rows_per_block + row_in_block) * 2]);
-  }
-  const float mref = (mx == -INFINITY) ? 0.f : mx;
-  float l = 0.f;
+  float mx = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k <= n_pref; ++k) {
-    const int sp = (k == n_pref) ? a.n_splits : k;
-    const int64_t slot = (base + sp) * a.rows_per_block + row_in_block;
-    const float w = exp2f(a.part_ml[slot * 2] - mref);
-    l += w * a.part_ml[slot * 2 + 1];
-    const f32x4 o = *(const f32x4 *)(a.part_o + slot * kHD + c4);
-    acc += w * o;
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    float2 ml[8];
+    f32x4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      ml[u] = make_float2(-INFINITY, 0.f);
+      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < n) {
+        const int sp = (k == n_pref) ? a.n_splits : k;
+        const int64_t slot = (base + sp) * a.rows_per_block + row_in_block;
+        ml[u] = *(const float2 *)(a.part_ml + slot * 2);
+        o[u] = *(const f32x4 *)(a.part_o + slot * kHD + c4);
+      }
+    }
+    float gm = ml[0].x;
+#pragma unroll
+    for (int u = 1; u < 8; ++u) gm = fmaxf(gm, ml[u].x);
+    const float mnew = fmaxf(mx, gm);
+    if (mnew == -INFINITY) continue;     // no visible key so far
+    const float sc = exp2f(mx - mnew);   // 0 while mx is still -inf
+    acc *= sc;
+    l *= sc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = exp2f(ml[u].x - mnew);
+      acc += w * o[u];
+      l += w * ml[u].y;
+    }
+    mx = mnew;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int m = rr / a.g;
@@ -482,47 +609,32 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   const int M = W * D;
   const int g = Hq / Hkv;
   p.rows_per_kv = g * M;
-  const int tiles = (p.rows_per_kv + 15) / 16;
-  // row block: fewest padded rows, then the largest block (fewer re-reads of K/V)
-  int best_waste = 1 << 30, best_rows = 0;
-  for (int rt = 1; rt <= 2; ++rt) {
-    for (int nw = 2; nw <= (rt == 1 ? 8 : 4); nw *= 2) {
-      const int tpb = rt * nw;
-      const int nrb = (tiles + tpb - 1) / tpb;
-      const int waste = nrb * tpb - tiles;
-      const int rows = tpb * 16;
-      if (waste < best_waste || (waste == best_waste && rows > best_rows)) {
-        best_waste = waste;
-        best_rows = rows;
-        p.rt = rt;
-        p.nw = nw;
-      }
-    }
-  }
-  // key splits: about 256 workgroups of prefix work for the longest sequence's share
+  p.rt = 1;
+  const int tiles = (p.rows_per_kv + kTileRows - 1) / kTileRows;
+  // row block: four waves (measured best at the Llama-8B/70B and batched shapes), fewer
+  // when the KV head has fewer row tiles
+  static const int kNW[] = {1, 2, 4, 5, 8};
+  p.nw = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+  // key splits: about 512 workgroups, 256..1024 keys per split
   const int max_keys = max_pages * page;
   int split_keys = 0;
-  // tuning override "rt,nw,split_keys" (values <= 0 keep the heuristic's choice)
+  // tuning override "nw,split_keys" (values <= 0 keep the heuristic's choice)
   if (const char *ov = getenv("VSTEP_ATTN_PLAN")) {
-    int rt = 0, nw = 0, sk = 0;
-    if (sscanf(ov, "%d,%d,%d", &rt, &nw, &sk) == 3) {
-      if ((rt == 1 && (nw == 2 || nw == 4 || nw == 8)) || (rt == 2 && (nw == 2 || nw == 4))) {
-        p.rt = rt;
-        p.nw = nw;
-      }
+    int nw = 0, sk = 0;
+    if (sscanf(ov, "%d,%d", &nw, &sk) == 2) {
+      for (int v : kNW)
+        if (nw == v) p.nw = nw;
       if (sk > 0) split_keys = ((sk + kKB - 1) / kKB) * kKB;
     }
   }
-  p.rows_per_block = p.rt * p.nw * 16;
-  p.n_rb = (tiles + p.rt * p.nw - 1) / (p.rt * p.nw);
+  p.rows_per_block = p.nw * kTileRows;
+  p.n_rb = (tiles + p.nw - 1) / p.nw;
   if (split_keys == 0) {
     const int groups = B * Hkv * p.n_rb;
-    int want = (256 + groups - 1) / groups;
-    if (want < 1) want = 1;
+    const int want = (512 + groups - 1) / groups;
     int sk = (max_keys + want - 1) / want;
     sk = ((sk + kKB - 1) / kKB) * kKB;
-    if (sk < 256) sk = 256;
-    split_keys = sk;
+    split_keys = sk < 256 ? 256 : (sk > 1024 ? 1024 : sk);
   }
   if (split_keys > kMaxSplitPages * kPage) split_keys = kMaxSplitPages * kPage;
   p.split_keys = split_keys;
@@ -591,11 +703,14 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   a.scale_log2 = scale * 1.4426950408889634f;
   const int nblocks = p.n_rb * (p.n_splits + 1) * B * Hkv;
   const dim3 grid(nblocks), block(64 * p.nw);
-  if (p.rt == 1 && p.nw == 2) hipLaunchKernelGGL((attn_mfma_kernel<1, 2>), grid, block, 0, st, a);
-  else if (p.rt == 1 && p.nw == 4) hipLaunchKernelGGL((attn_mfma_kernel<1, 4>), grid, block, 0, st, a);
-  else if (p.rt == 1) hipLaunchKernelGGL((attn_mfma_kernel<1, 8>), grid, block, 0, st, a);
-  else if (p.nw == 2) hipLaunchKernelGGL((attn_mfma_kernel<2, 2>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attn_mfma_kernel<2, 4>), grid, block, 0, st, a);
+  switch (p.nw) {
+    case 1: hipLaunchKernelGGL((attn_mfma_kernel<1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_mfma_kernel<2>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_mfma_kernel<4>), grid, block, 0, st, a); break;
+    case 5: hipLaunchKernelGGL((attn_mfma_kernel<5>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_mfma_kernel<8>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = (int64_t)B * Hkv * p.n_rb * p.rows_per_block * 32;

@@ -24,6 +24,8 @@ int check_attn(const vs_attn_desc *d) {
     return VS_ERR_INVALID_ARG;
   if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
   if (d->Hq % d->Hkv != 0) return VS_ERR_INVALID_ARG;
+  // a paged prefix needs a non-empty pool: masked keys of bad pages are read from it
+  if (d->max_pages > 0 && d->n_pool_pages < 1) return VS_ERR_INVALID_ARG;
   if (d->page_size != 16) return VS_ERR_UNSUPPORTED;
   if (d->dtype == VS_BF16) {
     if (d->head_dim != 128) return VS_ERR_UNSUPPORTED;
@@ -195,16 +197,18 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
     return VS_ERR_INVALID_ARG;
   const size_t need = vs_sample_workspace_bytes(d);
   if (!workspace || ws_bytes < need) return VS_ERR_WORKSPACE;
-  const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->V);
+  const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->W, d->D, d->V);
   hipError_t e = vs::launch_root_stats(root_logits, d->B, d->V, d->temperature, sw.root_stats,
                                        S(stream));
   if (e != hipSuccess) return VS_ERR_HIP;
-  e = vs::launch_lse_from_stats(sw.root_stats, d->B, d->V, sw.root_lse, S(stream));
+  // row_lse is an input here: only the root normalisers and the tests are computed
+  e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, nullptr,
+                           const_cast<double *>(row_lse), root_logits, logits, q, cand_tok,
+                           cand_len, gate, u_acc, sw, S(stream));
   if (e != hipSuccess) return VS_ERR_HIP;
   return hip_status(vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, root_logits, logits,
-                                       row_lse, sw.root_lse, q, cand_tok, cand_len, u_acc, u_res,
-                                       gate, n_acc, best, out_tok, n_out, acc_per_cand, flags, 0,
-                                       sw, S(stream)));
+                                       row_lse, q, cand_tok, cand_len, u_res, gate, n_acc, best,
+                                       out_tok, n_out, acc_per_cand, flags, 0, sw, S(stream)));
 }
 
 static int check_step(const vs_step_desc *d) {
@@ -276,20 +280,22 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
   // 3. head: GEMM + tile statistics (verify rows and root rows), then the normalisers
   const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
-  const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->V);
+  const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
   e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,
                            nullptr, nullptr, io->logits, hw, io->root_logits, d->B,
                            sw.root_stats, s);
   if (e != hipSuccess || !mark(3)) return VS_ERR_HIP;
-  e = vs::launch_head_finish(M, d->V, d->temperature, io->logits, io->row_lse, nullptr, hw, s);
-  if (e != hipSuccess) return VS_ERR_HIP;
-  e = vs::launch_lse_from_stats(sw.root_stats, d->B, d->V, sw.root_lse, s);
+  // 4. normalisers of every row and the acceptance test of every draft token
+  const int32_t *gate = d->external_drafts ? nullptr : io->gate;
+  e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, hw.stats, io->row_lse,
+                           io->root_logits, io->logits, io->q_draft, io->cand_tok, io->cand_len,
+                           gate, io->u_acc, sw, s);
   if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
-  // 4. rejection sampling
+  // 5. longest accepted run and the extra token
   e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
-                         io->row_lse, sw.root_lse, io->q_draft, io->cand_tok, io->cand_len,
-                         io->u_acc, io->u_res, d->external_drafts ? nullptr : io->gate, io->n_acc,
-                         io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags, 1, sw, s);
+                         io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_res, gate,
+                         io->n_acc, io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags,
+                         1, sw, s);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
 }

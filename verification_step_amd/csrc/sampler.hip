@@ -32,25 +32,157 @@ constexpr int kPer = 8;               // vocabulary entries per thread per chunk
 constexpr int kChunk = kST * kPer;    // 2048
 constexpr int kMaxRows = 1024;
 
-struct SampShared {
-  int a_len[kMaxRows];
-  int lens[kMaxRows];
-  unsigned char tie[kMaxRows];
-  double red[kST / 64];
-  double red2[kST / 64];
-  double scan[kST];
-  int flags;
-  int best, ab, mode, xpt, is_last, owner, y;
-  int64_t prow, qrow;
-  double lse, u, S, excl, lo, hi;
-};
-
-enum { MODE_ROOT = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_TARGET = 3 };
+// Acceptance codes per draft position, written by the normaliser kernel and read by
+// the sampler.
+enum : uint8_t { CODE_ACCEPT = 1, CODE_TIE = 2, CODE_BAD = 4 };
 
 __device__ __forceinline__ double warp_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
+
+__device__ __forceinline__ double warp_max(double v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// Normalisers and acceptance tests.  One workgroup per distribution row: rows
+// [0, B*M) are the verify rows (row (b, i, o) is the target distribution after draft
+// token o of candidate i), rows [B*M, B*M + B) are the root distributions.  The
+// workgroup forms lse = max + log(sum_t s_t exp(m_t - max)) in fp64 from the head's
+// per-tile (max, sumexp) statistics, then tests the draft tokens this row scores:
+// token o+1 of candidate i for a verify row, token 0 of every candidate for a root
+// row.  A token x is kept iff u * q(x) < p(x) with p(x) = exp(z_x/T - lse).
+struct TestArgs {
+  int B, W, D, V, n_vt;
+  double inv_t;
+  const float2 *row_stats;    // [B*M][n_vt], or null: row_lse is an input
+  const float2 *root_stats;   // [B][n_vt]
+  double *row_lse;            // [B*M]
+  double *root_lse;           // [B]
+  const float *root_logits, *logits, *q;
+  const int32_t *cand_tok, *cand_len, *gate;
+  const double *u_acc;
+  uint8_t *code;              // [B*W*D], or null: normalisers only
+};
+
+__device__ double lse_of_stats(const float2 *st, int n_vt, double *red) {
+  const int tid = threadIdx.x;
+  double mx = -INFINITY;
+  for (int t = tid; t < n_vt; t += 256) mx = fmax(mx, (double)st[t].x);
+  mx = warp_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  __syncthreads();
+  double sm = 0.0;
+  for (int t = tid; t < n_vt; t += 256) {
+    const float2 v = st[t];
+    if (v.x != -INFINITY) sm += (double)v.y * exp((double)v.x - mx);
+  }
+  sm = warp_sum(sm);
+  if ((tid & 63) == 0) red[tid >> 6] = sm;
+  __syncthreads();
+  return mx + log((red[0] + red[1]) + (red[2] + red[3]));
+}
+
+struct PosIn {
+  int x, len;
+  double u, Q;
+  float z;
+};
+
+// inputs of the test at draft position (b, i, oo) scored by row r (r < 0: root row)
+__device__ __forceinline__ PosIn load_pos(const TestArgs &a, int b, int r, int i, int oo) {
+  PosIn in{-1, 0, 0.0, 1.0, 0.f};
+  const bool open = (a.gate == nullptr) || a.gate[b] != 0;
+  const int ln = open ? a.cand_len[(int64_t)b * a.W + i] : 0;
+  in.len = ln < 0 ? 0 : (ln > a.D ? a.D : ln);
+  const int64_t pos = ((int64_t)b * a.W + i) * a.D + oo;
+  if (oo < in.len) {
+    in.x = a.cand_tok[pos];
+    in.u = a.u_acc[pos];
+    if (in.x >= 0 && in.x < a.V) {
+      in.z = (r < 0) ? a.root_logits[(int64_t)b * a.V + in.x] : a.logits[(int64_t)r * a.V + in.x];
+      if (a.q) in.Q = (double)a.q[pos * a.V + in.x];
+    }
+  }
+  return in;
+}
+
+__device__ __forceinline__ void store_test(const TestArgs &a, const PosIn &in, int b, int i,
+                                           int oo, double lse) {
+  uint8_t c = 0;
+  if (oo < in.len) {
+    if (in.x >= 0 && in.x < a.V) {
+      const double p = exp((double)in.z * a.inv_t - lse);
+      const double lhs = in.u * in.Q;
+      if (lhs < p) c |= CODE_ACCEPT;
+      if (fabs(lhs - p) < 1e-4 * fmax(p, lhs)) c |= CODE_TIE;
+    } else {
+      c = CODE_BAD;
+    }
+  }
+  a.code[((int64_t)b * a.W + i) * a.D + oo] = c;
+}
+
+__global__ void __launch_bounds__(256)
+lse_tests_kernel(TestArgs a) {
+  __shared__ double red[4];
+  const int tid = threadIdx.x;
+  const int M = a.W * a.D;
+  const int r = blockIdx.x;
+  const bool root = r >= a.B * M;
+  const int b = root ? r - a.B * M : r / M;
+
+  // positions scored by this row (their loads are issued before the reduction)
+  int i0 = 0, oo = 0, npos = 0;
+  if (a.code != nullptr) {
+    if (root) {
+      npos = a.W;
+    } else {
+      const int rr = r % M;
+      i0 = rr / a.D;
+      oo = rr % a.D + 1;
+      npos = (oo < a.D) ? 1 : 0;
+    }
+  }
+  const int rrow = root ? -1 : r;
+  PosIn first{-1, 0, 0.0, 1.0, 0.f};
+  if (tid < npos) first = load_pos(a, b, rrow, root ? tid : i0, oo);
+
+  double lse;
+  if (root) {
+    lse = lse_of_stats(a.root_stats + (int64_t)b * a.n_vt, a.n_vt, red);
+    if (tid == 0) a.root_lse[b] = lse;
+  } else if (a.row_stats != nullptr) {
+    lse = lse_of_stats(a.row_stats + (int64_t)r * a.n_vt, a.n_vt, red);
+    if (tid == 0) a.row_lse[r] = lse;
+  } else {
+    lse = a.row_lse[r];
+  }
+
+  if (tid < npos) store_test(a, first, b, root ? tid : i0, oo, lse);
+  for (int t = tid + 256; t < npos; t += 256) store_test(a, load_pos(a, b, rrow, t, oo), b, t, oo, lse);
+}
+
+// ---------------------------------------------------------------------------------
+struct SampShared {
+  int a_len[kMaxRows];
+  int lens[kMaxRows];
+  int tok[kMaxRows];
+  uint8_t code[kMaxRows];
+  double scan[kST];
+  double red[kST / 64];
+  double red2[kST / 64];
+  int flags;
+  int best, ab, mode, xpt, is_last, owner, y, last_pos;
+  int64_t prow, qrow;
+  double lse, u, S, excl, lo, hi;
+};
+
+enum { MODE_ROOT = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_TARGET = 3 };
 
 // fixed-order block sum of two values (every thread receives the totals)
 __device__ void block_sum2(SampShared &sh, double &a, double &b) {
@@ -62,14 +194,25 @@ __device__ void block_sum2(SampShared &sh, double &a, double &b) {
     sh.red2[tid >> 6] = b;
   }
   __syncthreads();
-  double ra = 0.0, rb = 0.0;
-  for (int w = 0; w < kST / 64; ++w) {
-    ra += sh.red[w];
-    rb += sh.red2[w];
-  }
+  a = (sh.red[0] + sh.red[1]) + (sh.red[2] + sh.red[3]);
+  b = (sh.red2[0] + sh.red2[1]) + (sh.red2[2] + sh.red2[3]);
   __syncthreads();
-  a = ra;
-  b = rb;
+}
+
+// inclusive prefix sum over the block in thread order (Hillis-Steele, fixed order)
+__device__ double block_incl_scan(SampShared &sh, double v) {
+  const int tid = threadIdx.x;
+  sh.scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kST; off <<= 1) {
+    const double add = (tid >= off) ? sh.scan[tid - off] : 0.0;
+    __syncthreads();
+    sh.scan[tid] += add;
+    __syncthreads();
+  }
+  const double r = sh.scan[tid];
+  __syncthreads();
+  return r;
 }
 
 struct SampArgs {
@@ -79,8 +222,9 @@ struct SampArgs {
   const double *row_lse, *root_lse;
   const float *q;
   const int32_t *cand_tok, *cand_len;
-  const double *u_acc, *u_res;
+  const double *u_res;
   const int32_t *gate;
+  const uint8_t *code;
   int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
   int flags_accumulate;
   double2 *chunk_sums;   // [B][nch]: (residual-or-bonus weight sum, target p sum)
@@ -95,9 +239,8 @@ sampler_kernel(SampArgs a) {
   const int tid = threadIdx.x;
   const int W = a.W, D = a.D, V = a.V, M = W * D;
   const float *root = a.root_logits + (int64_t)b * V;
-  const double lse_root = a.root_lse[b];
 
-  // ---- acceptance tests (repeated by every chunk workgroup of the sequence)
+  // ---- one round of independent loads: lengths, acceptance codes, draft tokens
   const bool open = (a.gate == nullptr) || a.gate[b] != 0;
   if (tid == 0) sh.flags = 0;
   for (int i = tid; i < W; i += kST) {
@@ -106,38 +249,26 @@ sampler_kernel(SampArgs a) {
     sh.lens[i] = ln;
     sh.a_len[i] = ln;
   }
+  for (int idx = tid; idx < M; idx += kST) {
+    sh.code[idx] = a.code[(int64_t)b * M + idx];
+    sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
+  }
   __syncthreads();
+  // accepted run of each candidate: up to its first rejected position
   for (int idx = tid; idx < M; idx += kST) {
     const int i = idx / D, o = idx % D;
-    sh.tie[idx] = 0;
+    if (o < sh.lens[i] && !(sh.code[idx] & CODE_ACCEPT)) atomicMin(&sh.a_len[i], o);
+  }
+  __syncthreads();
+  int fl = 0;
+  for (int idx = tid; idx < M; idx += kST) {
+    const int i = idx / D, o = idx % D;
     if (o >= sh.lens[i]) continue;
-    const int x = a.cand_tok[((int64_t)b * W + i) * D + o];
-    double p = 0.0, Q = 1.0;
-    if (x >= 0 && x < V) {
-      double z, l;
-      if (o == 0) {
-        z = (double)root[x];
-        l = lse_root;
-      } else {
-        const int64_t r = (int64_t)b * M + i * D + o - 1;
-        z = (double)a.logits[r * V + x];
-        l = a.row_lse[r];
-      }
-      p = exp(z * a.inv_t - l);
-      if (a.q) Q = (double)a.q[((int64_t)b * M + idx) * V + x];
-    } else {
-      atomicOr(&sh.flags, FLAG_BAD_TOKEN);
-    }
-    const double lhs = a.u_acc[((int64_t)b * W + i) * D + o] * Q;
-    if (fabs(lhs - p) < 1e-4 * fmax(p, lhs)) sh.tie[idx] = 1;
-    if (!(lhs < p)) atomicMin(&sh.a_len[i], o);
+    const uint8_t cd = sh.code[idx];
+    if (cd & CODE_BAD) fl |= FLAG_BAD_TOKEN;
+    if (o <= sh.a_len[i] && (cd & CODE_TIE)) fl |= FLAG_ACCEPT_TIE;
   }
-  __syncthreads();
-  for (int idx = tid; idx < M; idx += kST) {
-    const int i = idx / D, o = idx % D;
-    if (o < sh.lens[i] && o <= sh.a_len[i] && sh.tie[idx]) atomicOr(&sh.flags, FLAG_ACCEPT_TIE);
-  }
-  __syncthreads();
+  if (fl) atomicOr(&sh.flags, fl);
 
   // ---- the chosen candidate and the distribution of the extra token
   if (tid == 0) {
@@ -152,7 +283,7 @@ sampler_kernel(SampArgs a) {
       sh.mode = MODE_ROOT;
       sh.prow = -1;
       sh.u = a.u_res[(int64_t)b * W];
-      sh.flags |= FLAG_NO_CANDIDATE;
+      atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
     } else {
       const int ab = sh.a_len[best];
       sh.ab = ab;
@@ -161,12 +292,12 @@ sampler_kernel(SampArgs a) {
       if (ab < sh.lens[best]) {
         sh.mode = MODE_RESID;
         if (a.q) sh.qrow = (int64_t)b * M + best * D + ab;
-        else sh.xpt = a.cand_tok[((int64_t)b * W + best) * D + ab];
+        else sh.xpt = sh.tok[best * D + ab];
       } else {
         sh.mode = MODE_BONUS;
       }
     }
-    sh.lse = (sh.prow < 0) ? lse_root : a.row_lse[sh.prow];
+    sh.lse = (sh.prow < 0) ? a.root_lse[b] : a.row_lse[sh.prow];
   }
   __syncthreads();
   const float *zrow = (sh.prow < 0) ? root : a.logits + sh.prow * V;
@@ -210,52 +341,40 @@ sampler_kernel(SampArgs a) {
   __threadfence();
 
   // ---- last workgroup of the sequence: total, owner chunk, ordered scan, outputs
+  // chunk k's sums on thread k (nch <= kST)
+  double2 cs = make_double2(0.0, 0.0);
+  if (tid < a.nch) cs = a.chunk_sums[(int64_t)b * a.nch + tid];
+  double Sx = cs.x, Sy = cs.y;
+  block_sum2(sh, Sx, Sy);
+  const bool use_target = !(Sx > 0.0);
+  const double S = use_target ? Sy : Sx;
+  const double xs = sh.u * S;
+  const double v = use_target ? cs.y : cs.x;
+  const double incl = block_incl_scan(sh, v);
+  // the owner chunk: first with weight whose inclusive sum passes u*S; if rounding
+  // leaves u*S at or past the total, the last chunk with weight
   if (tid == 0) {
-    const double2 *cs = a.chunk_sums + (int64_t)b * a.nch;
-    double S = 0.0;
-    for (int k = 0; k < a.nch; ++k) S += cs[k].x;
-    bool use_target = false;
-    if (!(S > 0.0)) {
-      use_target = true;
-      sh.flags |= FLAG_DEGENERATE;
-      S = 0.0;
-      for (int k = 0; k < a.nch; ++k) S += cs[k].y;
-    }
-    const double xs = sh.u * S;
-    double run = 0.0;
-    int owner = -1;
-    double excl = 0.0;
-    for (int k = 0; k < a.nch; ++k) {
-      const double v = use_target ? cs[k].y : cs[k].x;
-      if (run + v > xs && v > 0.0) {
-        owner = k;
-        excl = run;
-        break;
-      }
-      run += v;
-    }
-    if (owner < 0) {
-      // u*S at or (by rounding) past the total: the last chunk with weight
-      owner = a.nch - 1;
-      for (int k = a.nch - 1; k >= 0; --k)
-        if ((use_target ? cs[k].y : cs[k].x) > 0.0) {
-          owner = k;
-          break;
-        }
-      excl = 0.0;
-      for (int k = 0; k < owner; ++k) excl += use_target ? cs[k].y : cs[k].x;
-    }
-    sh.owner = owner;
-    sh.excl = excl;
-    sh.S = S;
-    if (use_target) sh.mode = MODE_TARGET;
+    sh.owner = INT_MAX;
+    sh.last_pos = -1;
     sh.y = INT_MAX;
+    if (use_target) {
+      sh.mode = MODE_TARGET;
+      atomicOr(&sh.flags, FLAG_DEGENERATE);
+    }
     a.counters[b] = 0u;   // ready for the next call on this workspace
   }
   __syncthreads();
+  if (tid < a.nch && v > 0.0) {
+    if (incl > xs) atomicMin(&sh.owner, tid);
+    atomicMax(&sh.last_pos, tid);
+  }
+  __syncthreads();
+  if (sh.owner == INT_MAX && tid == 0) sh.owner = sh.last_pos >= 0 ? sh.last_pos : a.nch - 1;
+  __syncthreads();
+  if (tid == sh.owner) sh.excl = incl - v;
+  __syncthreads();
+
   const bool use_p = sh.mode == MODE_TARGET;
-  const double S = sh.S;
-  const double xs = sh.u * S;
   // ordered scan of the owner chunk: thread t owns entries t*kPer .. t*kPer+kPer-1
   double vals[kPer];
   double tsum = 0.0;
@@ -268,16 +387,7 @@ sampler_kernel(SampArgs a) {
     vals[j] = use_p ? pk : rk;
     tsum += vals[j];
   }
-  // inclusive prefix of thread sums in thread order (Hillis-Steele, fixed order)
-  sh.scan[tid] = tsum;
-  __syncthreads();
-  for (int off = 1; off < kST; off <<= 1) {
-    const double add = (tid >= off) ? sh.scan[tid - off] : 0.0;
-    __syncthreads();
-    sh.scan[tid] += add;
-    __syncthreads();
-  }
-  double run = sh.excl + (sh.scan[tid] - tsum);
+  double run = sh.excl + (block_incl_scan(sh, tsum) - tsum);
   int y = -1;
   double lo = 0.0, hi = 0.0;
   for (int j = 0; j < kPer; ++j) {
@@ -296,29 +406,29 @@ sampler_kernel(SampArgs a) {
     sh.hi = hi;
   }
   __syncthreads();
+  const int best = sh.best, ab = sh.ab;
+  int yy = sh.y;
   if (tid == 0) {
-    int yy = sh.y;
-    int fl = sh.flags;
+    int f = sh.flags;
     if (yy == INT_MAX) {
-      // rounding at the chunk edge left u*S past this chunk's scan: last weighted entry
+      // rounding at the chunk edge left u*S past this chunk's scan: last entry
       yy = min(V, (sh.owner + 1) * kChunk) - 1;
-      fl |= FLAG_CDF_TIE;
+      f |= FLAG_CDF_TIE;
     } else if (fabs(xs - sh.lo) < 1e-8 * S || fabs(sh.hi - xs) < 1e-8 * S) {
-      fl |= FLAG_CDF_TIE;
+      f |= FLAG_CDF_TIE;
     }
-    const int best = sh.best, ab = sh.ab;
-    int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
-    for (int o = 0; o < ab; ++o) ot[o] = a.cand_tok[((int64_t)b * W + best) * D + o];
-    ot[ab] = yy;
-    for (int o = ab + 1; o <= D; ++o) ot[o] = -1;
     a.n_acc[b] = ab;
     a.best[b] = best;
     a.n_out[b] = ab + 1;
     if (a.flags) {
-      if (a.flags_accumulate) atomicOr(&a.flags[b], fl);
-      else a.flags[b] = fl;
+      if (a.flags_accumulate) atomicOr(&a.flags[b], f);
+      else a.flags[b] = f;
     }
   }
+  if (yy == INT_MAX) yy = min(V, (sh.owner + 1) * kChunk) - 1;
+  int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
+  for (int o = tid; o <= D; o += kST)
+    ot[o] = (o < ab) ? sh.tok[best * D + o] : (o == ab ? yy : -1);
   for (int i = tid; i < W; i += kST)
     a.acc_per_cand[(int64_t)b * W + i] = (sh.lens[i] >= 1) ? sh.a_len[i] : 0;
 }
@@ -351,34 +461,9 @@ root_stats_kernel(const float *root_logits, int B, int V, float inv_t, float2 *s
   }
 }
 
-// Row normalisers lse = max + log(sum_t s_t exp(m_t - max)) in fp64 from tile
-// statistics [rows][n_vt].  One workgroup per row.
-__global__ void __launch_bounds__(256)
-lse_from_stats_kernel(const float2 *stats, int n_vt, double *lse) {
-  const int r = blockIdx.x;
-  __shared__ double red[4];
-  const float2 *st = stats + (int64_t)r * n_vt;
-  double mx = -INFINITY;
-  for (int t = threadIdx.x; t < n_vt; t += 256) mx = fmax(mx, (double)st[t].x);
-  for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-  __syncthreads();
-  double s = 0.0;
-  for (int t = threadIdx.x; t < n_vt; t += 256) {
-    const float2 v = st[t];
-    if (v.x != -INFINITY) s += (double)v.y * exp((double)v.x - mx);
-  }
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) lse[r] = mx + log(red[0] + red[1] + red[2] + red[3]);
-}
-
 }  // namespace
 
-SampleWs sample_ws(void *ws, int B, int V) {
+SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
   SampleWs w;
   const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
   const int nch = (V + kChunk - 1) / kChunk;
@@ -392,14 +477,14 @@ SampleWs sample_ws(void *ws, int B, int V) {
   off += ((size_t)B * n_vt * sizeof(float2) + 255) & ~(size_t)255;
   w.root_lse = (double *)(p + off);
   off += ((size_t)B * sizeof(double) + 255) & ~(size_t)255;
+  w.code = (uint8_t *)(p + off);
+  off += ((size_t)B * W * D + 255) & ~(size_t)255;
   w.bytes = off;
   return w;
 }
 
 size_t sample_workspace_bytes(int B, int W, int D, int V) {
-  (void)W;
-  (void)D;
-  return sample_ws(nullptr, B, V).bytes;
+  return sample_ws(nullptr, B, W, D, V).bytes;
 }
 
 hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
@@ -412,18 +497,52 @@ hipError_t launch_root_stats(const float *root_logits, int B, int V, float tempe
 
 hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *lse,
                                  hipStream_t st) {
-  const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
-  hipLaunchKernelGGL(lse_from_stats_kernel, dim3(rows), dim3(256), 0, st, stats, n_vt, lse);
+  TestArgs a{};
+  a.B = rows;
+  a.W = 1;
+  a.D = 1;
+  a.V = V;
+  a.n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
+  a.row_stats = stats;
+  a.row_lse = lse;
+  hipLaunchKernelGGL(lse_tests_kernel, dim3(rows), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
+                            const float2 *row_stats, double *row_lse, const float *root_logits,
+                            const float *logits, const float *q, const int32_t *cand_tok,
+                            const int32_t *cand_len, const int32_t *gate, const double *u_acc,
+                            const SampleWs &ws, hipStream_t st) {
+  TestArgs a{};
+  a.B = B;
+  a.W = W;
+  a.D = D;
+  a.V = V;
+  a.n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
+  a.inv_t = 1.0 / (double)temperature;
+  a.row_stats = row_stats;
+  a.root_stats = ws.root_stats;
+  a.row_lse = row_lse;
+  a.root_lse = ws.root_lse;
+  a.root_logits = root_logits;
+  a.logits = logits;
+  a.q = q;
+  a.cand_tok = cand_tok;
+  a.cand_len = cand_len;
+  a.gate = gate;
+  a.u_acc = u_acc;
+  a.code = ws.code;
+  hipLaunchKernelGGL(lse_tests_kernel, dim3(B * W * D + B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
-                          const float *logits, const double *row_lse, const double *root_lse,
-                          const float *q, const int32_t *cand_tok, const int32_t *cand_len,
-                          const double *u_acc, const double *u_res, const int32_t *gate,
-                          int32_t *n_acc, int32_t *best, int32_t *out_tok, int32_t *n_out,
-                          int32_t *acc_per_cand, int32_t *flags, int flags_accumulate,
-                          const SampleWs &ws, hipStream_t st) {
+                          const float *logits, const double *row_lse, const float *q,
+                          const int32_t *cand_tok, const int32_t *cand_len, const double *u_res,
+                          const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
+                          int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
+                          int flags_accumulate, const SampleWs &ws, hipStream_t st) {
   SampArgs a;
   a.B = B;
   a.W = W;
@@ -434,13 +553,13 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.root_logits = root_logits;
   a.logits = logits;
   a.row_lse = row_lse;
-  a.root_lse = root_lse;
+  a.root_lse = ws.root_lse;
   a.q = q;
   a.cand_tok = cand_tok;
   a.cand_len = cand_len;
-  a.u_acc = u_acc;
   a.u_res = u_res;
   a.gate = gate;
+  a.code = ws.code;
   a.n_acc = n_acc;
   a.best = best;
   a.out_tok = out_tok;

@@ -38,11 +38,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for a pair of values
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for a pair of values (x - hi
+// is exact in fp32).  hi is converted once, in an opaque instruction, and read back
+// from its packed bits (the compiler would otherwise convert each value again).
 __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
-  const bf16x2_t h = {(__bf16)x0, (__bf16)x1};
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = pack_bf16x2(x0 - (float)h[0], x1 - (float)h[1]);
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(hi) : "v"(x0), "v"(x1));
+  const float h0 = __uint_as_float(hi << 16);
+  const float h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = pack_bf16x2(x0 - h0, x1 - h1);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -122,21 +125,31 @@ struct SampleWs {
   double2 *chunk_sums;  // [B][n_chunks]
   float2 *root_stats;   // [B][n_vt]
   double *root_lse;     // [B]
+  uint8_t *code;        // [B][W][D] acceptance codes
   size_t bytes;
 };
-SampleWs sample_ws(void *ws, int B, int V);
+SampleWs sample_ws(void *ws, int B, int W, int D, int V);
 size_t sample_workspace_bytes(int B, int W, int D, int V);
 hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
                              float2 *stats, hipStream_t st);
+// fp64 row normalisers from tile statistics [rows][n_vt]
 hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *lse,
                                  hipStream_t st);
+// Normalisers of the verify rows (row_stats != null; else row_lse is an input) and of
+// the root rows (ws.root_stats -> ws.root_lse), and the acceptance test of every draft
+// position (-> ws.code).
+hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
+                            const float2 *row_stats, double *row_lse, const float *root_logits,
+                            const float *logits, const float *q, const int32_t *cand_tok,
+                            const int32_t *cand_len, const int32_t *gate, const double *u_acc,
+                            const SampleWs &ws, hipStream_t st);
+// Longest accepted run, residual / bonus draw, outputs (reads ws.code, ws.root_lse).
 hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
-                          const float *logits, const double *row_lse, const double *root_lse,
-                          const float *q, const int32_t *cand_tok, const int32_t *cand_len,
-                          const double *u_acc, const double *u_res, const int32_t *gate,
-                          int32_t *n_acc, int32_t *best, int32_t *out_tok, int32_t *n_out,
-                          int32_t *acc_per_cand, int32_t *flags, int flags_accumulate,
-                          const SampleWs &ws, hipStream_t st);
+                          const float *logits, const double *row_lse, const float *q,
+                          const int32_t *cand_tok, const int32_t *cand_len, const double *u_res,
+                          const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
+                          int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
+                          int flags_accumulate, const SampleWs &ws, hipStream_t st);
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 

@@ -22,6 +22,13 @@ where the pages are silent or garbled are listed next to the code that uses them
 Parity pins: every function here is pinned by tests that do not call it to
 produce the expected value (brute force, closed forms, library routines,
 hand-derived values); see tests/test_oracle_*.py.
+
+Parity unpinned: the law of the emitted token when W > 1 candidates are sampled
+(not greedy).  The pages state only "keep the longest verified run"; they give no
+distribution for it, and the literal rule is not lossless for W > 1 (a W = 2
+counterexample gives (3/4, 1/4) for p = (1/2, 1/2)).  reject_sample follows the
+literal rule; for W > 1 it is pinned only against the enumerated law of that same
+rule and against the greedy limit, where it reduces to plain greedy decoding.
 """
 from __future__ import annotations
 

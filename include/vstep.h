@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VS_ABI_VERSION 1
+#define VS_ABI_VERSION 2
 
 typedef enum {
     VS_OK = 0,
@@ -205,8 +205,15 @@ int vs_reject_sample(const vs_sample_desc *desc, const float *root_logits,
  *   -> verify_attention -> lm_head (full rank, head input = attention output viewed
  *   as [B*W*D, Hq*hd], so d must equal Hq*head_dim) -> reject_sample.
  * stage_events: NULL, or 6 hipEvent_t handles recorded on `stream` before stage 1
- * and after each of the 5 stages (retrieval+gate, attention, head GEMM, head
- * normaliser, sampler) -- for timing only. */
+ * and after each of the 5 stages (retrieval+gate, attention, head GEMM, normalisers
+ * and acceptance tests, sampler) -- for timing only.
+ * aux_stream, fork_event, join_event: NULL, or a second stream (default priority)
+ * and two events owned by the caller.  Then retrieval + gate, which nothing before
+ * the acceptance tests reads, run on aux_stream concurrently with attention and the
+ * head: fork_event is recorded on `stream` and waited for on aux_stream before the
+ * retrieval; join_event is recorded on aux_stream after it and waited for on
+ * `stream` before the tests.  Stage event 1 then follows event 0 directly (the
+ * retrieval is off the main stream). */
 typedef struct {
     int32_t B, W, D, kappa;
     int32_t Hq, Hkv, head_dim, page_size, max_pages, n_pool_pages;
@@ -244,6 +251,8 @@ typedef struct {
     int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand;
     int32_t *flags;                         /* [B]: OR of every stage's flags */
     void **stage_events;                    /* NULL or 6 hipEvent_t */
+    void *aux_stream;                       /* NULL or hipStream_t (see above) */
+    void *fork_event, *join_event;          /* hipEvent_t, required with aux_stream */
 } vs_step_io;
 
 size_t vs_step_workspace_bytes(const vs_step_desc *desc);

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vs_abi_version() == 1
+    assert lib.vs_abi_version() == 2
     assert lib.vs_status_str(0) == b"ok"
     assert b"workspace" in lib.vs_status_str(-3)
     assert lib.vs_status_str(99) == b"unknown status"
@@ -56,7 +56,7 @@ def test_struct_layouts_match_header():
     # int32 fields then int64 ctx_total at its natural alignment
     assert C.sizeof(L.StepDesc) == 80
     assert L.StepDesc.ctx_total.offset == 72
-    assert C.sizeof(L.StepIO) == 32 * 8
+    assert C.sizeof(L.StepIO) == 35 * 8
     assert C.sizeof(L.AttnDesc) == 44
     assert C.sizeof(L.HeadDesc) == 28
     assert C.sizeof(L.SampleDesc) == 20

@@ -430,3 +430,27 @@ def test_verify_step_equals_its_calls():
     assert np.array_equal(tensor_np(g["row_lse"]), tensor_np(lse))
     for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand"):
         assert np.array_equal(tensor_np(g[k]), tensor_np(rs[k])), k
+
+
+def test_verify_step_overlap_and_flag_reset():
+    """Retrieval on the auxiliary stream gives the same bits as the serial step; a bad
+    page raised inside attention reaches `flags` on every call (the workspace word it
+    goes through is reset by the sampler), and only for the sequence that has it."""
+    api = _api()
+    sh = small_shape(B=2, P=(64, 64), paged_random=False)
+    case = get_case(("step", "badpage"), lambda: wl.make_case(sh, 13))
+    case.arrays["page_table"][1, 2] = 10 ** 6
+    I = _step_inputs(case, 1.0)
+    say("verify_step overlap vs serial, bad page")
+    kw = dict(B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V)
+    serial = api.VerifyStep(I, overlap=False, **kw)
+    over = api.VerifyStep(I, overlap=True, **kw)
+    ref = None
+    for step in (serial, over, serial, over):
+        g = step()
+        got = {k: tensor_np(v).copy() for k, v in g.items()}
+        assert got["flags"][1] & oracle.FLAG_BAD_PAGE and not got["flags"][0] & oracle.FLAG_BAD_PAGE
+        if ref is None:
+            ref = got
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), k

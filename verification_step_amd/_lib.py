@@ -64,7 +64,8 @@ class StepIO(C.Structure):
         "w_full", "root_logits", "q_draft", "u_acc", "u_res",
         "cand_tok", "cand_len", "cand_pos", "n_found", "score", "gate",
         "attn_out", "logits", "row_lse",
-        "n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags", "stage_events")]
+        "n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags", "stage_events",
+        "aux_stream", "fork_event", "join_event")]
 
 
 _lib = None

@@ -227,11 +227,15 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
 class VerifyStep:
     """One verify step bound to fixed device buffers, so that repeated calls (timing,
     a decode loop) enqueue the step without any host-side allocation.  A 2-D bf16
-    inputs["w_full"] is packed once at construction (kept as self.w_packed)."""
+    inputs["w_full"] is packed once at construction (kept as self.w_packed).
+    overlap=True gives the step a second stream (default priority) and two events, so
+    that retrieval + gate run concurrently with attention and the head.  It is off by
+    default: on the measured MI355X stack the fork and join events cost the main stream
+    ~6 us each, more than the overlap saves once the retrieval takes a few us."""
 
     def __init__(self, inputs: dict, B: int, W: int, D: int, Hq: int, Hkv: int, hd: int,
                  V: int, tau: float = 0.4, temperature: float = 1.0, kappa: int = 5,
-                 external_drafts: bool = False, scale: float = 0.0):
+                 external_drafts: bool = False, scale: float = 0.0, overlap: bool = False):
         self.lib = L.load()
         I = dict(inputs)
         if I["w_full"].dtype == torch.bfloat16 and I["w_full"].dim() == 2:
@@ -270,6 +274,16 @@ class VerifyStep:
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.io = L.StepIO()
         self.bind(I)
+        if overlap and not external_drafts:
+            self.aux = torch.cuda.Stream(device=dev)
+            self.fork = torch.cuda.Event()
+            self.join = torch.cuda.Event()
+            for e in (self.fork, self.join):
+                e.record()                  # the handles exist once recorded
+            torch.cuda.synchronize()
+            self.io.aux_stream = self.aux.cuda_stream
+            self.io.fork_event = self.fork.cuda_event
+            self.io.join_event = self.join.cuda_event
 
     def bind(self, I: dict):
         """(Re)point the step at a set of input tensors of the same shapes."""

@@ -251,6 +251,7 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
         !io->cand_pos || !io->n_found || !io->score || !io->gate)
       return VS_ERR_INVALID_ARG;
   }
+  if (io->aux_stream && (!io->fork_event || !io->join_event)) return VS_ERR_INVALID_ARG;
   const StepLayout L = step_layout(d);
   if (!workspace || ws_bytes < L.total) return VS_ERR_WORKSPACE;
   hipStream_t s = S(stream);
@@ -260,42 +261,55 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   };
   const int M = d->B * d->W * d->D;
   char *ws = (char *)workspace;
+  const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
+  const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
   hipError_t e;
   if (!mark(0)) return VS_ERR_HIP;
-  // 1. copy retrieval + probe gate (one launch), or external drafts
+  // 1. copy retrieval + probe gate (one launch), on the auxiliary stream when given.
+  //    It is the first writer of io->flags; attention reports into the workspace
+  //    (sw.attn_flags), which the sampler folds in, so the two never race.
+  const bool fork = io->aux_stream != nullptr && !d->external_drafts;
+  hipStream_t gs = s;
+  if (fork) {
+    gs = S(io->aux_stream);
+    if (hipEventRecord((hipEvent_t)io->fork_event, s) != hipSuccess ||
+        hipStreamWaitEvent(gs, (hipEvent_t)io->fork_event, 0) != hipSuccess)
+      return VS_ERR_HIP;
+  }
   if (!d->external_drafts) {
     e = vs::launch_copy_match(io->ctx, d->ctx_total, io->ctx_off, d->B, d->kappa, d->W, d->D,
                               io->cand_tok, io->cand_len, io->cand_pos, io->n_found, io->flags,
                               io->probe_h, d->dtype == VS_BF16, io->probe_w, d->d, d->tau,
-                              io->score, io->gate, s);
-  } else {
-    e = vs::launch_zero_i32(io->flags, d->B, s);
+                              io->score, io->gate, gs);
+    if (e != hipSuccess) return VS_ERR_HIP;
+    if (fork && hipEventRecord((hipEvent_t)io->join_event, gs) != hipSuccess) return VS_ERR_HIP;
   }
-  if (e != hipSuccess || !mark(1)) return VS_ERR_HIP;
+  if (!mark(1)) return VS_ERR_HIP;
   // 2. verify attention
   e = vs::launch_attention(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->max_pages,
                            d->n_pool_pages, d->dtype, attn_scale(d->scale, d->head_dim), io->q,
                            io->k_cand, io->v_cand, io->k_pool, io->v_pool, io->page_table,
-                           io->prefix_len, io->attn_out, io->flags, ws + L.attn, s);
+                           io->prefix_len, io->attn_out, sw.attn_flags, ws + L.attn, s);
   if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
-  // 3. head: GEMM + tile statistics (verify rows and root rows), then the normalisers
-  const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
-  const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
+  // 3. head: GEMM + tile statistics (verify rows and root rows)
   e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,
                            nullptr, nullptr, io->logits, hw, io->root_logits, d->B,
                            sw.root_stats, s);
   if (e != hipSuccess || !mark(3)) return VS_ERR_HIP;
+  if (fork && hipStreamWaitEvent(s, (hipEvent_t)io->join_event, 0) != hipSuccess)
+    return VS_ERR_HIP;
   // 4. normalisers of every row and the acceptance test of every draft token
   const int32_t *gate = d->external_drafts ? nullptr : io->gate;
   e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, hw.stats, io->row_lse,
                            io->root_logits, io->logits, io->q_draft, io->cand_tok, io->cand_len,
                            gate, io->u_acc, sw, s);
   if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
-  // 5. longest accepted run and the extra token
+  // 5. longest accepted run and the extra token (flags: accumulate onto the gate's,
+  //    or written whole when there was no retrieval)
   e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
                          io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_res, gate,
                          io->n_acc, io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags,
-                         1, sw, s);
+                         d->external_drafts ? 0 : 1, sw, s, sw.attn_flags);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
 }

@@ -32,7 +32,9 @@ struct GateShared {
   float red[kGateThreads / kWave];
 };
 
-// Retrieval for sequence b; returns n_found (uniform over the workgroup).
+// Retrieval for sequence b; returns n_found (uniform over the workgroup).  The first
+// segment staged is the top of the context including the current token t, so the
+// key and (nearly always) the continuations are read from LDS, not global memory.
 __device__ int copy_match_wg(GateShared &sh, const int32_t *ctx, int64_t ctx_total,
                              const int32_t *ctx_off, int b, int kappa, int W, int D,
                              int32_t *cand_tok, int32_t *cand_len, int32_t *cand_pos,
@@ -47,34 +49,38 @@ __device__ int copy_match_wg(GateShared &sh, const int32_t *ctx, int64_t ctx_tot
   const int64_t t = L - 1;
   const int32_t *c = ctx + (bad ? 0 : lo);
   if (tid == 0) sh.found = 0;
-  __syncthreads();
 
   if (L >= kappa + 1) {
-    // key and its hash (every thread keeps them in registers)
+    // end positions j run from t-1 down to kappa-1, a segment of kSeg at a time; the
+    // segment [seg_lo, seg_hi] stages tokens base = seg_lo-kappa+1 .. top, where top
+    // is t for the first segment (key and continuations) and seg_hi afterwards
     int32_t key[kMaxKappa];
     uint32_t key_hash = 0;
-#pragma unroll
-    for (int m = 0; m < kMaxKappa; ++m) {
-      key[m] = (m < kappa) ? c[t - kappa + 1 + m] : 0;
-      if (m < kappa) key_hash = key_hash * kHashMul + (uint32_t)key[m];
-    }
-    // end positions j run from t-1 down to kappa-1
     int64_t seg_hi = t - 1;
+    bool first = true;
     while (seg_hi >= kappa - 1) {
       const int64_t seg_lo = max((int64_t)(kappa - 1), seg_hi - kSeg + 1);
       const int n = (int)(seg_hi - seg_lo + 1);
-      // stage tokens c[seg_lo-kappa+1 .. seg_hi]; token of end position j sits at
-      // tok[j - seg_lo + kappa - 1]
       const int64_t base = seg_lo - kappa + 1;
-      for (int k = tid; k < n + kappa - 1; k += kGateThreads) sh.tok[k] = c[base + k];
+      const int64_t top = first ? t : seg_hi;
+      const int ns = (int)(top - base + 1);
+      __syncthreads();          // the previous segment's readers are done
+      for (int k = tid; k < ns; k += kGateThreads) sh.tok[k] = c[base + k];
       __syncthreads();
+      if (first) {
+#pragma unroll
+        for (int m = 0; m < kMaxKappa; ++m) {
+          key[m] = (m < kappa) ? sh.tok[(int)(t - kappa + 1 + m - base)] : 0;
+          if (m < kappa) key_hash = key_hash * kHashMul + (uint32_t)key[m];
+        }
+      }
       // scan the segment from its top in steps of 1024 positions
       for (int s0 = 0; s0 < n; s0 += kGateThreads) {
         const int r = s0 + tid;                 // rank of the position inside the segment
         bool match = false;
         int64_t j = seg_hi - r;
         if (r < n) {
-          const int e = (int)(j - seg_lo) + kappa - 1;   // index of token j in tok[]
+          const int e = (int)(j - base);        // index of token j in tok[]
           uint32_t hsh = 0;
           for (int m = 0; m < kappa; ++m) hsh = hsh * kHashMul + (uint32_t)sh.tok[e - kappa + 1 + m];
           if (hsh == key_hash) {
@@ -93,7 +99,10 @@ __device__ int copy_match_wg(GateShared &sh, const int32_t *ctx, int64_t ctx_tot
           cand_pos[(int64_t)b * W + rank] = (int32_t)j;
           cand_len[(int64_t)b * W + rank] = ln;
           int32_t *dst = cand_tok + ((int64_t)b * W + rank) * D;
-          for (int o = 0; o < D; ++o) dst[o] = (o < ln) ? c[j + 1 + o] : -1;
+          for (int o = 0; o < D; ++o) {
+            const int64_t pos = j + 1 + o;
+            dst[o] = (o >= ln) ? -1 : (pos <= top ? sh.tok[(int)(pos - base)] : c[pos]);
+          }
         }
         __syncthreads();
         if (tid == 0) {
@@ -106,9 +115,10 @@ __device__ int copy_match_wg(GateShared &sh, const int32_t *ctx, int64_t ctx_tot
       }
       if (sh.found >= W) break;
       seg_hi = seg_lo - 1;
-      __syncthreads();
+      first = false;
     }
   }
+  __syncthreads();
   const int nf = sh.found;
   // missing candidates
   for (int k = tid; k < (W - nf) * D; k += kGateThreads) {
@@ -123,23 +133,58 @@ __device__ int copy_match_wg(GateShared &sh, const int32_t *ctx, int64_t ctx_tot
   return nf;
 }
 
-// score = sigmoid(w . h): fp32 products and accumulation in a fixed tree order.
-__device__ float probe_wg(GateShared &sh, const void *h, int h_bf16, const float *w, int b, int d) {
+// this thread's share of w . h.  The first kProbeRegs products' operands are loaded
+// into registers before the retrieval and multiplied after it, so that their latency
+// overlaps the retrieval; any remainder (d > kProbeRegs * threads) is read after.
+constexpr int kProbeRegs = 8;
+struct ProbeRegs {
+  float w[kProbeRegs];
+  uint32_t h[kProbeRegs];   // raw bits (bf16 in the low half, or fp32), decoded at use
+};
+__device__ __forceinline__ ProbeRegs probe_load(const void *h, int h_bf16, const float *w, int b,
+                                                int d) {
+  // branch-free: out-of-range slots read element d-1 and get weight 0, so every load
+  // is issued before the first use (no wait between them)
+  ProbeRegs r;
   const int tid = threadIdx.x;
-  float acc = 0.f;
+  int kk[kProbeRegs];
+#pragma unroll
+  for (int i = 0; i < kProbeRegs; ++i) kk[i] = min(tid + i * kGateThreads, d - 1);
   if (h_bf16) {
     const bf16_t *hb = (const bf16_t *)h + (int64_t)b * d;
-    for (int k = tid; k < d; k += kGateThreads) acc = fmaf(w[k], bf16_to_f32(hb[k]), acc);
+#pragma unroll
+    for (int i = 0; i < kProbeRegs; ++i) r.h[i] = hb[kk[i]];
   } else {
     const float *hf = (const float *)h + (int64_t)b * d;
-    for (int k = tid; k < d; k += kGateThreads) acc = fmaf(w[k], hf[k], acc);
+#pragma unroll
+    for (int i = 0; i < kProbeRegs; ++i) r.h[i] = __float_as_uint(hf[kk[i]]);
   }
+#pragma unroll
+  for (int i = 0; i < kProbeRegs; ++i) r.w[i] = (tid + i * kGateThreads < d) ? w[kk[i]] : 0.f;
+  return r;
+}
+__device__ float probe_partial(const ProbeRegs &r, const void *h, int h_bf16, const float *w,
+                               int b, int d) {
+  const int tid = threadIdx.x;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kProbeRegs; ++i)
+    acc = fmaf(r.w[i], h_bf16 ? __uint_as_float(r.h[i] << 16) : __uint_as_float(r.h[i]), acc);
+  for (int k = tid + kProbeRegs * kGateThreads; k < d; k += kGateThreads)
+    acc = fmaf(w[k], h_bf16 ? bf16_to_f32(((const bf16_t *)h)[(int64_t)b * d + k])
+                            : ((const float *)h)[(int64_t)b * d + k], acc);
+  return acc;
+}
+
+// workgroup sum of the partials in a fixed tree order (every thread gets the total)
+__device__ float probe_reduce(GateShared &sh, float acc) {
+  const int tid = threadIdx.x;
   for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  __syncthreads();
   if ((tid & (kWave - 1)) == 0) sh.red[tid / kWave] = acc;
   __syncthreads();
   float x = 0.f;
   for (int w2 = 0; w2 < kGateThreads / kWave; ++w2) x += sh.red[w2];
-  __syncthreads();
   return x;
 }
 
@@ -151,12 +196,14 @@ gate_kernel(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int k
   __shared__ GateShared sh;
   const int b = blockIdx.x;
   int fl = 0;
+  ProbeRegs pr{};
+  if (h != nullptr) pr = probe_load(h, h_bf16, w, b, d);
   const int nf = copy_match_wg(sh, ctx, ctx_total, ctx_off, b, kappa, W, D, cand_tok, cand_len,
                                cand_pos, &fl);
   float s = 0.f;
   int g = 0;
   if (h != nullptr) {
-    const float x = probe_wg(sh, h, h_bf16, w, b, d);
+    const float x = probe_reduce(sh, probe_partial(pr, h, h_bf16, w, b, d));
     const double sd = 1.0 / (1.0 + exp(-(double)x));
     s = (float)sd;
     g = (sd >= (double)tau) && (nf >= 1);
@@ -177,7 +224,7 @@ probe_kernel(const void *h, int h_bf16, const float *w, int d, float tau, const 
              float *score, int32_t *gate, int32_t *flags) {
   __shared__ GateShared sh;
   const int b = blockIdx.x;
-  const float x = probe_wg(sh, h, h_bf16, w, b, d);
+  const float x = probe_reduce(sh, probe_partial(probe_load(h, h_bf16, w, b, d), h, h_bf16, w, b, d));
   if (threadIdx.x == 0) {
     const double sd = 1.0 / (1.0 + exp(-(double)x));
     score[b] = (float)sd;

@@ -227,6 +227,7 @@ struct SampArgs {
   const uint8_t *code;
   int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
   int flags_accumulate;
+  int32_t *attn_flags;   // [B] or null: flags raised by attention, folded and reset here
   double2 *chunk_sums;   // [B][nch]: (residual-or-bonus weight sum, target p sum)
   uint32_t *counters;    // [B]
 };
@@ -420,6 +421,10 @@ sampler_kernel(SampArgs a) {
     a.n_acc[b] = ab;
     a.best[b] = best;
     a.n_out[b] = ab + 1;
+    if (a.attn_flags) {
+      f |= a.attn_flags[b];
+      a.attn_flags[b] = 0;      // ready for the next call on this workspace
+    }
     if (a.flags) {
       if (a.flags_accumulate) atomicOr(&a.flags[b], f);
       else a.flags[b] = f;
@@ -479,6 +484,8 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
   off += ((size_t)B * sizeof(double) + 255) & ~(size_t)255;
   w.code = (uint8_t *)(p + off);
   off += ((size_t)B * W * D + 255) & ~(size_t)255;
+  w.attn_flags = (int32_t *)(p + off);
+  off += ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
   w.bytes = off;
   return w;
 }
@@ -542,7 +549,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const int32_t *cand_tok, const int32_t *cand_len, const double *u_res,
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
-                          int flags_accumulate, const SampleWs &ws, hipStream_t st) {
+                          int flags_accumulate, const SampleWs &ws, hipStream_t st,
+                          int32_t *attn_flags) {
   SampArgs a;
   a.B = B;
   a.W = W;
@@ -567,6 +575,7 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.acc_per_cand = acc_per_cand;
   a.flags = flags;
   a.flags_accumulate = flags_accumulate;
+  a.attn_flags = attn_flags;
   a.chunk_sums = ws.chunk_sums;
   a.counters = ws.counters;
   hipLaunchKernelGGL(sampler_kernel, dim3(a.nch, B), dim3(kST), 0, st, a);

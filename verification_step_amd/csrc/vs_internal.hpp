@@ -126,6 +126,7 @@ struct SampleWs {
   float2 *root_stats;   // [B][n_vt]
   double *root_lse;     // [B]
   uint8_t *code;        // [B][W][D] acceptance codes
+  int32_t *attn_flags;  // [B] flags raised by attention inside the step, zero between calls
   size_t bytes;
 };
 SampleWs sample_ws(void *ws, int B, int W, int D, int V);
@@ -149,7 +150,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const int32_t *cand_tok, const int32_t *cand_len, const double *u_res,
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
-                          int flags_accumulate, const SampleWs &ws, hipStream_t st);
+                          int flags_accumulate, const SampleWs &ws, hipStream_t st,
+                          int32_t *attn_flags = nullptr);
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 

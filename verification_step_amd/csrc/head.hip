@@ -244,23 +244,27 @@ __device__ __forceinline__ void dma16_h(const void *g, bf16_t *lds_dst) {
                : "memory", "m0");
 }
 
-template <int MT>
-__global__ void __launch_bounds__(kThreads, 2)
+// NG vocabulary tiles (of 4 waves each) share one workgroup and one staging of H.
+template <int MT, int NG>
+__global__ void __launch_bounds__(kThreads * NG, 2)
 head_lds_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t Hs[2][MT * 16 * kHC];
-  __shared__ float2 red[4][MT * 16];
+  __shared__ float2 red[4 * NG][MT * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
+  const int grp = wv >> 2;          // vocabulary tile of this wave within the workgroup
+  const int wq = wv & 3;            // wave within the tile
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
-  const int nblocks = n_vt * a.n_mblocks;
+  const int nblocks = ((n_vt + NG - 1) / NG) * a.n_mblocks;
   const int bid = xcd_remap(blockIdx.x, nblocks);
   const int mb = bid % a.n_mblocks;
-  const int vt = bid / a.n_mblocks;
-  const int vbase = vt * kHeadVocabTile + wv * (kVT * 16);
+  const int vt = (bid / a.n_mblocks) * NG + grp;
+  const bool tile_ok = vt < n_vt;
+  const int vbase = vt * kHeadVocabTile + wq * (kVT * 16);
   const int mbase = mb * MT * 16;
   const int nsteps = a.K / 32;
   const int nchunks = a.K / kHC;
@@ -280,12 +284,13 @@ head_lds_kernel(GemmArgs a) {
     for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 512 * s);
   };
   // H chunk c: MT*16 rows x 128 columns = MT*4 transfers of 1 KB (4 rows each); wave
-  // wv issues transfers wv, wv+4, ...
+  // wv issues transfers wv, wv+4*NG, ...
   const bf16_t *hbase = (const bf16_t *)a.h;
   auto issue_h = [&](int c, int buf) {
 #pragma unroll
-    for (int ii = 0; ii < MT; ++ii) {
-      const int i = wv + 4 * ii;
+    for (int ii = 0; ii < (MT + NG - 1) / NG; ++ii) {
+      const int i = wv + 4 * NG * ii;
+      if (i >= MT * 4) break;
       const int row = 4 * i + (lane >> 4);
       const int ch = (lane & 15) ^ (row & 15);
       int m = mbase + row;
@@ -368,8 +373,8 @@ head_lds_kernel(GemmArgs a) {
     if (lg == 0) red[wv][mt * 16 + l16] = make_float2(vmax, vs);
   }
   if (a.stats == nullptr) return;
-  if (a.root != nullptr && mb == 0) {
-    for (int b = wv; b < a.B_root; b += 4) {
+  if (a.root != nullptr && mb == 0 && tile_ok) {
+    for (int b = wq; b < a.B_root; b += 4) {
       const float *row = a.root + (int64_t)b * a.N;
       float x[kHeadVocabTile / 64];
       float mx = -INFINITY;
@@ -389,14 +394,16 @@ head_lds_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  for (int r = tid; r < MT * 16; r += kThreads) {
+  if (!tile_ok) return;
+  for (int r = tid & (kThreads - 1); r < MT * 16; r += kThreads) {
     const int m = mbase + r;
     if (m >= a.M) continue;
     float mx = -INFINITY;
-    for (int w2 = 0; w2 < 4; ++w2) mx = fmaxf(mx, red[w2][r].x);
+    for (int w2 = 0; w2 < 4; ++w2) mx = fmaxf(mx, red[4 * grp + w2][r].x);
     float sm = 0.f;
     for (int w2 = 0; w2 < 4; ++w2)
-      if (red[w2][r].x != -INFINITY) sm += red[w2][r].y * expf(red[w2][r].x - mx);
+      if (red[4 * grp + w2][r].x != -INFINITY)
+        sm += red[4 * grp + w2][r].y * expf(red[4 * grp + w2][r].x - mx);
     a.stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
   }
 }
@@ -501,9 +508,17 @@ hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
   const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
   const dim3 grid(n_vt * a.n_mblocks, ksplit);
   if (!split && ksplit == 1 && a.K % kHC == 0 && getenv("VSTEP_HEAD_STREAM") == nullptr) {
+    // two vocabulary tiles per workgroup (one workgroup per CU): H is staged once per
+    // CU instead of twice, which measured faster at every M tried (7, 32, 80)
+    const char *ngv = getenv("VSTEP_HEAD_NG");
+    const int ng = ngv ? atoi(ngv) : 2;
 #define VS_LDS_CASE(MTV)                                                                  \
   case MTV:                                                                               \
-    hipLaunchKernelGGL((head_lds_kernel<MTV>), grid, dim3(kThreads), 0, st, a);           \
+    if (ng == 2)                                                                          \
+      hipLaunchKernelGGL((head_lds_kernel<MTV, 2>), dim3(((n_vt + 1) / 2) * a.n_mblocks),    \
+                         dim3(2 * kThreads), 0, st, a);                                   \
+    else                                                                                  \
+      hipLaunchKernelGGL((head_lds_kernel<MTV, 1>), grid, dim3(kThreads), 0, st, a);      \
     break;
     switch (mt) {
       VS_LDS_CASE(1)

@@ -172,14 +172,15 @@ struct SampShared {
   int a_len[kMaxRows];
   int lens[kMaxRows];
   int tok[kMaxRows];
+  double rlse[kMaxRows];
+  double ures[kMaxRows];
   uint8_t code[kMaxRows];
-  double scan[kST];
   double red[kST / 64];
   double red2[kST / 64];
   int flags;
-  int best, ab, mode, xpt, is_last, owner, y, last_pos;
+  int best, ab, mode, xpt, is_last, owner, last_pos, tstar;
   int64_t prow, qrow;
-  double lse, u, S, excl, lo, hi;
+  double lse, u, excl;
 };
 
 enum { MODE_ROOT = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_TARGET = 3 };
@@ -199,20 +200,22 @@ __device__ void block_sum2(SampShared &sh, double &a, double &b) {
   __syncthreads();
 }
 
-// inclusive prefix sum over the block in thread order (Hillis-Steele, fixed order)
+// inclusive prefix sum over the block in thread order, in a fixed order: a shuffle
+// scan inside each wave, then the totals of the earlier waves
 __device__ double block_incl_scan(SampShared &sh, double v) {
   const int tid = threadIdx.x;
-  sh.scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kST; off <<= 1) {
-    const double add = (tid >= off) ? sh.scan[tid - off] : 0.0;
-    __syncthreads();
-    sh.scan[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(v, off);
+    if (lane >= off) v += y;
   }
-  const double r = sh.scan[tid];
+  if (lane == 63) sh.red[wv] = v;
   __syncthreads();
-  return r;
+  double base = 0.0;
+  for (int w2 = 0; w2 < wv; ++w2) base += sh.red[w2];
+  __syncthreads();
+  return base + v;
 }
 
 struct SampArgs {
@@ -229,6 +232,7 @@ struct SampArgs {
   int flags_accumulate;
   int32_t *attn_flags;   // [B] or null: flags raised by attention, folded and reset here
   double2 *chunk_sums;   // [B][nch]: (residual-or-bonus weight sum, target p sum)
+  double2 *thread_sums;  // [B][nch][kST]: the same over each thread's kPer ids
   uint32_t *counters;    // [B]
 };
 
@@ -241,7 +245,8 @@ sampler_kernel(SampArgs a) {
   const int W = a.W, D = a.D, V = a.V, M = W * D;
   const float *root = a.root_logits + (int64_t)b * V;
 
-  // ---- one round of independent loads: lengths, acceptance codes, draft tokens
+  // ---- one round of independent loads: lengths, acceptance codes, draft tokens, the
+  //      residual uniforms and the normalisers of every row
   const bool open = (a.gate == nullptr) || a.gate[b] != 0;
   if (tid == 0) sh.flags = 0;
   for (int i = tid; i < W; i += kST) {
@@ -249,11 +254,14 @@ sampler_kernel(SampArgs a) {
     ln = ln < 0 ? 0 : (ln > D ? D : ln);
     sh.lens[i] = ln;
     sh.a_len[i] = ln;
+    sh.ures[i] = a.u_res[(int64_t)b * W + i];
   }
   for (int idx = tid; idx < M; idx += kST) {
     sh.code[idx] = a.code[(int64_t)b * M + idx];
     sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
+    sh.rlse[idx] = a.row_lse[(int64_t)b * M + idx];
   }
+  const double lse_root = a.root_lse[b];
   __syncthreads();
   // accepted run of each candidate: up to its first rejected position
   for (int idx = tid; idx < M; idx += kST) {
@@ -279,17 +287,17 @@ sampler_kernel(SampArgs a) {
     sh.best = best;
     sh.qrow = -1;
     sh.xpt = -1;
+    int prow_local = -1;
     if (best < 0) {
       sh.ab = 0;
       sh.mode = MODE_ROOT;
-      sh.prow = -1;
-      sh.u = a.u_res[(int64_t)b * W];
+      sh.u = sh.ures[0];
       atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
     } else {
       const int ab = sh.a_len[best];
       sh.ab = ab;
-      sh.u = a.u_res[(int64_t)b * W + best];
-      sh.prow = (ab == 0) ? -1 : (int64_t)b * M + best * D + ab - 1;
+      sh.u = sh.ures[best];
+      prow_local = (ab == 0) ? -1 : best * D + ab - 1;
       if (ab < sh.lens[best]) {
         sh.mode = MODE_RESID;
         if (a.q) sh.qrow = (int64_t)b * M + best * D + ab;
@@ -298,7 +306,8 @@ sampler_kernel(SampArgs a) {
         sh.mode = MODE_BONUS;
       }
     }
-    sh.lse = (sh.prow < 0) ? a.root_lse[b] : a.row_lse[sh.prow];
+    sh.prow = (prow_local < 0) ? -1 : (int64_t)b * M + prow_local;
+    sh.lse = (prow_local < 0) ? lse_root : sh.rlse[prow_local];
   }
   __syncthreads();
   const float *zrow = (sh.prow < 0) ? root : a.logits + sh.prow * V;
@@ -307,29 +316,66 @@ sampler_kernel(SampArgs a) {
   const int xpt = sh.xpt;
   const bool resid = sh.mode == MODE_RESID;
 
-  // target probability and residual weight of token k
-  auto weights = [&](int k, double &pk, double &rk) {
-    pk = exp((double)zrow[k] * a.inv_t - lse);
-    if (resid) {
-      const double qk = qrow ? (double)qrow[k] : (k == xpt ? 1.0 : 0.0);
-      rk = fmax(0.0, pk - qk);
+  // target probability and residual weight of the kPer ids k0 .. k0+kPer-1 (ids at or
+  // past V weigh nothing)
+  auto weights = [&](int k0, double *pk, double *rk) {
+    float z[kPer], qv[kPer];
+    if (k0 + kPer <= V) {
+      const f32x4 z0 = *(const f32x4 *)(zrow + k0), z1 = *(const f32x4 *)(zrow + k0 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        z[j] = z0[j];
+        z[4 + j] = z1[j];
+      }
+      if (qrow) {
+        const f32x4 q0 = *(const f32x4 *)(qrow + k0), q1 = *(const f32x4 *)(qrow + k0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qv[j] = q0[j];
+          qv[4 + j] = q1[j];
+        }
+      }
     } else {
-      rk = pk;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        z[j] = (k0 + j < V) ? zrow[k0 + j] : 0.f;
+        qv[j] = (qrow && k0 + j < V) ? qrow[k0 + j] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = k0 + j;
+      if (k >= V) {
+        pk[j] = 0.0;
+        rk[j] = 0.0;
+        continue;
+      }
+      pk[j] = exp((double)z[j] * a.inv_t - lse);
+      if (resid) {
+        const double qk = qrow ? (double)qv[j] : (k == xpt ? 1.0 : 0.0);
+        rk[j] = fmax(0.0, pk[j] - qk);
+      } else {
+        rk[j] = pk[j];
+      }
     }
   };
 
-  // ---- this chunk's sums (coalesced: entry c*kChunk + j*kST + tid)
+  // ---- this chunk's sums: thread t owns the kPer consecutive ids c*kChunk + t*kPer ..
+  //      (vector loads; 8 KB contiguous per chunk); its sums are kept for the draw
   double sr = 0.0, sp = 0.0;
+  {
+    double pk[kPer], rk[kPer];
+    weights(c * kChunk + tid * kPer, pk, rk);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int k = c * kChunk + j * kST + tid;
-    if (k < V) {
-      double pk, rk;
-      weights(k, pk, rk);
-      sr += rk;
-      sp += pk;
+    for (int j = 0; j < kPer; ++j) {
+      sr += rk[j];
+      sp += pk[j];
     }
   }
+  double2 *ts = a.thread_sums + ((int64_t)b * a.nch + c) * kST;
+  // every thread's sums reach memory before the barriers of block_sum2; thread 0's
+  // device-scope release below then publishes them with the chunk sum
+  ts[tid] = make_double2(sr, sp);
   block_sum2(sh, sr, sp);
   if (tid == 0) {
     a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
@@ -341,7 +387,7 @@ sampler_kernel(SampArgs a) {
   if (!sh.is_last) return;
   __threadfence();
 
-  // ---- last workgroup of the sequence: total, owner chunk, ordered scan, outputs
+  // ---- last workgroup of the sequence: total, owner chunk, owner thread, draw
   // chunk k's sums on thread k (nch <= kST)
   double2 cs = make_double2(0.0, 0.0);
   if (tid < a.nch) cs = a.chunk_sums[(int64_t)b * a.nch + tid];
@@ -357,7 +403,7 @@ sampler_kernel(SampArgs a) {
   if (tid == 0) {
     sh.owner = INT_MAX;
     sh.last_pos = -1;
-    sh.y = INT_MAX;
+    sh.tstar = INT_MAX;
     if (use_target) {
       sh.mode = MODE_TARGET;
       atomicOr(&sh.flags, FLAG_DEGENERATE);
@@ -374,50 +420,52 @@ sampler_kernel(SampArgs a) {
   __syncthreads();
   if (tid == sh.owner) sh.excl = incl - v;
   __syncthreads();
-
+  const int owner = sh.owner;
   const bool use_p = sh.mode == MODE_TARGET;
-  // ordered scan of the owner chunk: thread t owns entries t*kPer .. t*kPer+kPer-1
-  double vals[kPer];
-  double tsum = 0.0;
-  const int base = sh.owner * kChunk + tid * kPer;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int k = base + j;
-    double pk = 0.0, rk = 0.0;
-    if (k < V) weights(k, pk, rk);
-    vals[j] = use_p ? pk : rk;
-    tsum += vals[j];
-  }
-  double run = sh.excl + (block_incl_scan(sh, tsum) - tsum);
-  int y = -1;
-  double lo = 0.0, hi = 0.0;
-  for (int j = 0; j < kPer; ++j) {
-    const double prev = run;
-    run += vals[j];
-    if (y < 0 && vals[j] > 0.0 && run > xs) {
-      y = base + j;
-      lo = prev;
-      hi = run;
-    }
-  }
-  if (y >= 0) atomicMin(&sh.y, y);
-  __syncthreads();
-  if (y >= 0 && y == sh.y) {
-    sh.lo = lo;
-    sh.hi = hi;
-  }
+  // the owner chunk's thread sums (kept by its workgroup) in id order: the thread
+  // whose range holds u*S
+  const double2 tsum2 = a.thread_sums[((int64_t)b * a.nch + owner) * kST + tid];
+  const double tv = use_p ? tsum2.y : tsum2.x;
+  const double tincl = block_incl_scan(sh, tv);
+  const double texcl = sh.excl + (tincl - tv);
+  if (tv > 0.0 && sh.excl + tincl > xs) atomicMin(&sh.tstar, tid);
   __syncthreads();
   const int best = sh.best, ab = sh.ab;
-  int yy = sh.y;
-  if (tid == 0) {
+  __shared__ int y_sh;
+  if (tid == sh.tstar || (sh.tstar == INT_MAX && tid == 0)) {
     int f = sh.flags;
-    if (yy == INT_MAX) {
-      // rounding at the chunk edge left u*S past this chunk's scan: last entry
-      yy = min(V, (sh.owner + 1) * kChunk) - 1;
-      f |= FLAG_CDF_TIE;
-    } else if (fabs(xs - sh.lo) < 1e-8 * S || fabs(sh.hi - xs) < 1e-8 * S) {
+    int yy = -1;
+    if (sh.tstar != INT_MAX) {
+      // the owning thread recomputes its kPer weights (same arithmetic, same order)
+      double pk[kPer], rk[kPer];
+      weights(owner * kChunk + tid * kPer, pk, rk);
+      double run = texcl;
+      double lo = 0.0, hi = 0.0;
+      int last_w = -1;
+      for (int j = 0; j < kPer; ++j) {
+        const double w = use_p ? pk[j] : rk[j];
+        const double prev = run;
+        run += w;
+        if (w > 0.0) last_w = owner * kChunk + tid * kPer + j;
+        if (yy < 0 && w > 0.0 && run > xs) {
+          yy = owner * kChunk + tid * kPer + j;
+          lo = prev;
+          hi = run;
+        }
+      }
+      if (yy >= 0 && (fabs(xs - lo) < 1e-8 * S || fabs(hi - xs) < 1e-8 * S)) f |= FLAG_CDF_TIE;
+      if (yy < 0) {
+        // the sequential re-sum fell a rounding step short of the scan: last weighted id
+        yy = last_w;
+        f |= FLAG_CDF_TIE;
+      }
+    }
+    if (yy < 0) {
+      // rounding at a chunk or thread edge left u*S past the scan: last id of the chunk
+      yy = min(V, (owner + 1) * kChunk) - 1;
       f |= FLAG_CDF_TIE;
     }
+    y_sh = yy;
     a.n_acc[b] = ab;
     a.best[b] = best;
     a.n_out[b] = ab + 1;
@@ -430,7 +478,8 @@ sampler_kernel(SampArgs a) {
       else a.flags[b] = f;
     }
   }
-  if (yy == INT_MAX) yy = min(V, (sh.owner + 1) * kChunk) - 1;
+  __syncthreads();
+  const int yy = y_sh;
   int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
   for (int o = tid; o <= D; o += kST)
     ot[o] = (o < ab) ? sh.tok[best * D + o] : (o == ab ? yy : -1);
@@ -486,6 +535,8 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
   off += ((size_t)B * W * D + 255) & ~(size_t)255;
   w.attn_flags = (int32_t *)(p + off);
   off += ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
+  w.thread_sums = (double2 *)(p + off);
+  off += ((size_t)B * nch * kST * sizeof(double2) + 255) & ~(size_t)255;
   w.bytes = off;
   return w;
 }
@@ -577,6 +628,7 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.flags_accumulate = flags_accumulate;
   a.attn_flags = attn_flags;
   a.chunk_sums = ws.chunk_sums;
+  a.thread_sums = ws.thread_sums;
   a.counters = ws.counters;
   hipLaunchKernelGGL(sampler_kernel, dim3(a.nch, B), dim3(kST), 0, st, a);
   return hipGetLastError();

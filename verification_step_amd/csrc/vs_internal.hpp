@@ -127,6 +127,7 @@ struct SampleWs {
   double *root_lse;     // [B]
   uint8_t *code;        // [B][W][D] acceptance codes
   int32_t *attn_flags;  // [B] flags raised by attention inside the step, zero between calls
+  double2 *thread_sums; // [B][n_chunks][256] per-thread weight sums of the sampler
   size_t bytes;
 };
 SampleWs sample_ws(void *ws, int B, int W, int D, int V);

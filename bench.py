@@ -1,15 +1,21 @@
 #!/usr/bin/env python3
 """Verify-step throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one pass of the whole verify path (copy retrieval + probe gate, block-
 triangular verify attention, full LM head, rejection sampling) over one batch of
-seeded synthetic inputs shaped like Llama-3.1-8B (d=4096, 32/8 heads, hd=128,
-prefix 4096, W=4 candidates x D=20 tokens, V=128256, bf16).  Inputs are resident
-in HBM before timing starts.  Each timed step reads a different one of 32 KV
-buffers (a Llama-8B has 32 layers) and alternates between 2 copies of the head,
-so that no step is served from the 256 MB Infinity Cache left warm by the last.
+seeded synthetic inputs.  The default workload (the headline line) is shaped like
+Llama-3.1-8B (d=4096, 32/8 heads, hd=128, prefix 4096, W=4 candidates x D=20 tokens,
+V=128256, bf16).  Inputs are resident in HBM before timing starts.  Each timed step
+reads a different one of 32 KV buffers (a Llama-8B has 32 layers) and alternates
+between 2 copies of the head, so that no step is served from the 256 MB Infinity
+Cache left warm by the last.
+
+Other workloads (--workload): tiny (fp32, V=512), slimspec (the low-rank draft head
+r=512 writing q for 7 drafts, then a W=1, D=7 verify step of those drafts), llama70b
+(d=8192, 64/8 heads, prefix 16384, W=8, D=20) and ragged (32 sequences, prefixes
+U[512, 8192], randomly ordered pages, W=4, D=8, point-mass drafts).
 
 Prints ONE JSON line.  Two timed passes of K steps each, both bracketed by
 synchronisation and HIP events on the step's stream:
@@ -37,13 +43,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_llama8b_traffic.json")
 HEAD_SRC = os.path.join(ROOT, "verification_step_amd", "csrc", "head.hip")
 
 
-def head_bytes(M, d, V):
-    """Algorithmic bytes of one full-head launch: W (bf16) + H (bf16) + fp32 logits."""
-    return V * d * 2 + M * d * 2 + M * V * 4
+def head_bytes(M, d, V, esz=2):
+    """Algorithmic bytes of one full-head launch: W + H (esz bytes each) + fp32 logits."""
+    return V * d * esz + M * d * esz + M * V * 4
 
 
-def attn_bytes(B, M, Hq, Hkv, hd, sum_p):
-    return 2 * sum_p * Hkv * hd * 2 + B * M * Hq * hd * 2 * 2 + 2 * B * M * Hkv * hd * 2
+def attn_bytes(B, M, Hq, Hkv, hd, sum_p, esz=2):
+    """Prefix K and V once, Q in and O out, the candidates' own K and V."""
+    return (2 * sum_p * Hkv * hd + B * M * Hq * hd * 2 + 2 * B * M * Hkv * hd) * esz
 
 
 def attn_flops(B, W, D, Hq, hd, sum_p):
@@ -66,9 +73,11 @@ def upload(case):
     return out
 
 
-def cpu_baseline(case, shape, min_seconds=10.0):
+def cpu_baseline(case, shape, drafts=None, min_seconds=10.0):
     """The CPU oracle, as it stands, on full steps of the same inputs, repeated until at
-    least `min_seconds` of CPU work have been timed."""
+    least `min_seconds` of CPU work have been timed.  With external drafts a step is the
+    oracle's low-rank draft head followed by its verify step over the given drafts."""
+    import numpy as np
     import oracle
     threads = None
     try:
@@ -79,18 +88,30 @@ def cpu_baseline(case, shape, min_seconds=10.0):
         pass
     if not threads:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    A = case.arrays
+    sh = shape
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.verify_step(case.arrays, shape)
+        if sh.external_drafts:
+            z, l, _ = oracle.lm_head_lowrank(oracle.as_f64(A["draft_h"], "bf16"), A["w_down"],
+                                             A["w_up"])
+            A2 = dict(A)
+            A2["q_draft"] = oracle.head_softmax(z, l).astype(np.float32)
+            oracle.verify_step(A2, sh, drafts=drafts)
+        else:
+            oracle.verify_step(A, sh)
         n += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    what = ("low-rank draft head (r=%d) + " % sh.rank) if sh.external_drafts else \
+        "retrieval, probe, "
     return {"value": n / dt, "unit": "verify steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d full Llama-8B-shaped verify steps (retrieval, probe, attention over "
-                      "4096 prefix keys, 128256x4096 head, sampler) on the same inputs, fp64 "
-                      "NumPy/BLAS; %.1f s" % (n, dt),
+            "sample": "%d full %s verify steps (%sattention over %d prefix keys in all, "
+                      "%dx%d head over %d rows, sampler) on the same inputs, fp64 "
+                      "NumPy/BLAS; %.1f s" % (n, sh.name, what, int(sum(sh.P)), sh.V, sh.d,
+                                              sh.B * sh.M, dt),
             "seconds_per_step": dt / n,
             "host_cpus": len(os.sched_getaffinity(0))}
 
@@ -110,13 +131,53 @@ def traffic_entry():
         return None
 
 
+# workload name -> (config index, KV buffers, head copies).  KV buffers and head copies
+# are sized so that consecutive steps do not find their inputs in the 256 MB MALL.
+WORKLOADS = {
+    "llama8b": (2, 32, 2),      # the headline line
+    "tiny": (1, 1, 1),
+    "slimspec": (3, 32, 2),
+    "llama70b": (4, 8, 2),
+    "ragged": (5, 2, 2),
+}
+WORKLOAD_NAMES = {"llama8b": "llama8b_verify_step", "tiny": "tiny_verify_step",
+                  "slimspec": "slimspec_draft_head_and_verify_step",
+                  "llama70b": "llama70b_verify_step", "ragged": "ragged_batch32_verify_step"}
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense bf16 MFMA; fp32 vector (the f32 head)
+
+
+def slimspec_drafts(api, sh, case, I, dev):
+    """The SlimSpec side of the workload: the low-rank draft head, bound so that it
+    writes its probabilities straight into the verify step's q input, and the draft
+    tokens sampled once from them by inverse CDF (the drafter's job, not timed)."""
+    import numpy as np
+    import torch
+    A = case.arrays
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    qbuf = torch.empty((sh.M, sh.V), dtype=torch.float32, device=dev)
+    draft = api.LmHead(bf(A["draft_h"]), w_down=bf(A["w_down"]), w_up=bf(A["w_up"]),
+                       write_probs=True, probs=qbuf)
+    draft()
+    q = qbuf.double().cpu().numpy()
+    tok = np.zeros((1, 1, sh.D), dtype=np.int32)
+    for o in range(sh.D):
+        c = np.cumsum(q[o])
+        tok[0, 0, o] = min(int(np.searchsorted(c, A["u_draft"][0, 0, o] * c[-1], "right")),
+                           sh.V - 1)
+    I["q_draft"] = qbuf
+    I["cand_tok"] = torch.from_numpy(tok).to(dev)
+    I["cand_len"] = torch.full((1, 1), sh.D, dtype=torch.int32, device=dev)
+    return draft, (tok, np.array([[sh.D]], dtype=np.int32))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--kv-buffers", type=int, default=32)
-    ap.add_argument("--head-copies", type=int, default=2)
+    ap.add_argument("--workload", choices=list(WORKLOADS), default="llama8b")
+    ap.add_argument("--kv-buffers", type=int, default=0, help="0: the workload's default")
+    ap.add_argument("--head-copies", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
@@ -146,25 +207,32 @@ def main():
         print(json.dumps({"copy_calib_bytes": 1 << 30, "copies": args.copy_calib}))
         return
 
-    sh = wl.config(2)
-    case = wl.make_case(sh, wl.CONFIG_SEED[2], "measure")
+    cfg, n_kv, n_head = WORKLOADS[args.workload]
+    n_kv = args.kv_buffers or n_kv
+    n_head = args.head_copies or n_head
+    sh = wl.config(cfg)
+    case = wl.make_case(sh, wl.CONFIG_SEED[cfg], "measure")
     I = upload(case)
     B, W, D, M = sh.B, sh.W, sh.D, sh.M
+    draft, drafts = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else (None, None)
     step = api.VerifyStep(I, B=B, W=W, D=D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V, tau=sh.tau,
-                          temperature=sh.temperature, kappa=sh.kappa)
+                          temperature=sh.temperature, kappa=sh.kappa,
+                          external_drafts=sh.external_drafts)
+    mdt = I["q"].dtype
+    esz = I["q"].element_size()
 
     # distinct KV buffers (layers) and head copies; buffer 0 / copy 0 are the seeded inputs
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     pools = [(I["k_pool"], I["v_pool"])]
-    for _ in range(args.kv_buffers - 1):
-        pools.append((torch.randn(I["k_pool"].shape, generator=g, device=dev).to(torch.bfloat16),
-                      torch.randn(I["v_pool"].shape, generator=g, device=dev).to(torch.bfloat16)))
-    heads = [step.w_packed]           # the head is prepacked once into MFMA tiles
-    for _ in range(args.head_copies - 1):
+    for _ in range(n_kv - 1):
+        pools.append((torch.randn(I["k_pool"].shape, generator=g, device=dev).to(mdt),
+                      torch.randn(I["v_pool"].shape, generator=g, device=dev).to(mdt)))
+    heads = [step.w_packed]           # a bf16 head is prepacked once into MFMA tiles
+    for _ in range(n_head - 1):
         w = (torch.randn(I["w_full"].shape, generator=g, device=dev)
-             * (1.0 / np.sqrt(sh.d))).to(torch.bfloat16)
-        heads.append(api.pack_weight(w))
+             * (1.0 / np.sqrt(sh.d))).to(mdt)
+        heads.append(api.pack_weight(w) if mdt == torch.bfloat16 else w)
         del w
     torch.cuda.synchronize()
 
@@ -174,10 +242,15 @@ def main():
         step.io.v_pool = vp.data_ptr()
         step.io.w_full = heads[k % len(heads)].data_ptr()
 
+    def run(k):
+        bind(k)
+        if draft is not None:
+            draft()
+        step()
+
     K, Wm = args.steps, args.warmup
     for k in range(Wm):
-        bind(k)
-        step()
+        run(k)
     torch.cuda.synchronize()
 
     # events on the step's stream (torch's current stream is the one VerifyStep uses)
@@ -188,20 +261,24 @@ def main():
     torch.cuda.synchronize()
     t0.record()
     for k in range(K):
-        bind(Wm + k)
-        step()
+        run(Wm + k)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / K
 
-    # pass 2: the same K steps with stage events (6 per step, made beforehand)
+    # pass 2: the same K steps with stage events (6 per step, made beforehand; one more
+    # before the draft head where there is one)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev_ptrs = [step.event_array(e) for e in ev]
     torch.cuda.synchronize()
     t0.record()
     for k in range(K):
         bind(Wm + k)
         step.use_events(ev_ptrs[k])
+        if draft is not None:
+            ev_d[k].record()
+            draft()
         step()
     t1.record()
     torch.cuda.synchronize()
@@ -209,18 +286,49 @@ def main():
     ms_staged = t0.elapsed_time(t1) / K
 
     names = ["retrieval_gate", "attention", "head_gemm", "lse_tests", "sampler"]
-    stage_ms = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)]))
-                for i, n in enumerate(names)}
+    stage_ms = {}
+    if draft is not None:
+        stage_ms["draft_head_lowrank"] = float(np.mean([ev_d[k].elapsed_time(ev[k][0])
+                                                        for k in range(K)]))
+    for i, n in enumerate(names):
+        stage_ms[n] = float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)]))
 
     steps_per_s = 1000.0 / ms
-    hb = head_bytes(M, sh.d, sh.V)
+    dt_name = "bf16" if mdt == torch.bfloat16 else "f32"
+    # the dominant kernel is the full LM head: HBM- or matrix-bound, whichever takes longer
+    MR = B * M                        # head rows over the whole batch
+    hb = head_bytes(MR, sh.d, sh.V, esz)
+    hf = 2.0 * MR * sh.V * sh.d
     head_s = stage_ms["head_gemm"] * 1e-3
-    achieved = hb / head_s / 1e9
+    t_hbm, t_mm = hb / (HBM_PEAK_GBS * 1e9), hf / MFMA_PEAK[dt_name]
+    if t_hbm >= t_mm:
+        roof = {"bound": "hbm", "achieved": hb / head_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if dt_name == "bf16" else "alu",
+                "achieved": hf / head_s / 1e12, "peak": MFMA_PEAK[dt_name] / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_entry() if args.workload == "llama8b" else None
+    kname = "vs::head_lds_kernel" if dt_name == "bf16" else "vs::gemm_f32_kernel"
+    roof.update({"kernel": kname + " (full LM head GEMM + tile statistics), M=%d" % MR,
+                 "algorithmic_bytes": hb, "algorithmic_flops": hf,
+                 "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mm * 1e6})
     sum_p = int(sum(sh.P))
-    ab = attn_bytes(B, M, sh.Hq, sh.Hkv, sh.hd, sum_p)
+    ab = attn_bytes(B, M, sh.Hq, sh.Hkv, sh.hd, sum_p, esz)
     af = attn_flops(B, W, D, sh.Hq, sh.hd, sum_p)
     att_s = stage_ms["attention"] * 1e-3
     out = step.out
+    config = {"workload": WORKLOAD_NAMES[args.workload], "B": B, "W": W, "D": D,
+              "prefix": sh.P[0] if B == 1 else {"sum": sum_p, "min": min(sh.P),
+                                                "max": max(sh.P)},
+              "d": sh.d, "Hq": sh.Hq, "Hkv": sh.Hkv, "head_dim": sh.hd, "V": sh.V,
+              "kv_buffers": len(pools), "head_copies": len(heads),
+              "timing": "hip events on the step stream, no graph; value from a pass "
+                        "without stage events, stages from a second pass with them"}
+    if draft is not None:
+        config.update({"draft_head": "low-rank r=%d, gamma=%d, probabilities into q"
+                                     % (sh.rank, sh.gamma), "drafts": "external"})
     rec = {
         "metric": METRIC,
         "value": steps_per_s,
@@ -232,31 +340,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dt_name,
         "data": "synthetic",
-        "config": {"workload": "llama8b_verify_step", "B": B, "W": W, "D": D,
-                   "prefix": sh.P[0], "d": sh.d, "Hq": sh.Hq, "Hkv": sh.Hkv, "head_dim": sh.hd,
-                   "V": sh.V, "kv_buffers": len(pools), "head_copies": len(heads),
-                   "timing": "hip events on the step stream, no graph; value from a pass "
-                             "without stage events, stages from a second pass with them"},
+        "config": config,
         "candidate_tokens_per_s": steps_per_s * B * W * D,
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
         "ms_per_step_with_stage_events": ms_staged,
-        "roofline": {"kernel": "vs::head_lds_kernel<5> (full LM head GEMM + tile statistics)",
-                     "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_entry(),
-                     "algorithmic_bytes": hb},
+        "roofline": roof,
         "attention_roofline": {"achieved_GBs": ab / att_s / 1e9,
                                "achieved_TFLOPs": af / att_s / 1e12,
                                "t_hbm_us": ab / HBM_PEAK_GBS / 1e3,
-                               "t_mfma_us": af / 2.5e15 * 1e6,
+                               "t_mfma_us": af / MFMA_PEAK[dt_name] * 1e6,
                                "frac_of_max_bound": max(ab / (HBM_PEAK_GBS * 1e9),
-                                                        af / 2.5e15) / att_s},
-        "accepted": int(out["n_acc"][0].item()),
+                                                        af / MFMA_PEAK[dt_name]) / att_s},
+        "accepted": [int(x) for x in out["n_acc"].cpu().tolist()][:4],
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(case, sh)
+        rec["cpu_baseline"] = cpu_baseline(case, sh, drafts)
     print(json.dumps(rec), flush=True)
 
 

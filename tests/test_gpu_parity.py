@@ -328,6 +328,46 @@ def test_reject_sample_synthetic(qmode, T):
     assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
 
 
+@pytest.mark.parametrize("qmode", ["dense", "point"])
+def test_reject_sample_fused_and_two_launch_agree(qmode, monkeypatch):
+    """The sampler's two ways to reach the draw (last workgroup of a fused launch, or a
+    second launch) give the same bits, on a batch where the vocabulary spans several
+    chunks and the sequences' chunks outnumber the CUs; both match the oracle."""
+    api = _api()
+    rng = np.random.default_rng(21)
+    B, W, D, V = 40, 2, 4, 9000
+    M = W * D
+    root = (rng.standard_normal((B, V)) * 1.5).astype(np.float32)
+    logits = (rng.standard_normal((B * M, V)) * 1.5).astype(np.float32)
+    lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+    q = wl.draft_probs_from_logits(rng, (B * M, V), 1.5) if qmode == "dense" else None
+    cand = rng.integers(0, 30, size=(B, W, D)).astype(np.int32)
+    clen = rng.integers(0, D + 1, size=(B, W)).astype(np.int32)
+    for b in range(B):
+        for i in range(W):
+            cand[b, i, clen[b, i]:] = -1
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    args = (to_dev(root), to_dev(logits), to_dev(lse), to_dev(q) if q is not None else None,
+            to_dev(cand), to_dev(clen), to_dev(ua), to_dev(ur), 1.0)
+    got = {}
+    for mode in ("0", "1", "0", "1"):
+        monkeypatch.setenv("VSTEP_SAMPLER_TWO_PASS", mode)
+        say("reject_sample two-launch", qmode, mode)
+        g = api.reject_sample(*args)
+        g = {k: tensor_np(v).copy() for k, v in g.items()}
+        if mode in got:
+            for k in g:
+                assert np.array_equal(g[k], got[mode][k]), (mode, k)
+        got[mode] = g
+    for k in got["0"]:
+        assert np.array_equal(got["0"][k], got["1"][k]), k
+    o = oracle.reject_sample(root, logits, q, cand, clen, ua, ur, 1.0, None)
+    import torch
+    n_cmp, n_exc = compare_sampler({k: torch.from_numpy(v) for k, v in got["1"].items()}, o, B)
+    assert n_exc <= 1 and n_cmp >= B - 1
+
+
 # =============================================================================== whole step
 
 def _step_inputs(case, T, external=None):

@@ -158,35 +158,58 @@ def pack_weight(w: torch.Tensor) -> torch.Tensor:
     return out
 
 
+class LmHead:
+    """The LM head bound to fixed buffers: h, the weights, logits [M,V], row_lse [M] and,
+    with write_probs, probs [M,V] (pass `probs` to have them land in a buffer of the
+    caller's, e.g. the q input of a verify step).  Repeated calls enqueue the head with
+    no host-side allocation.  bf16: weights as 2-D row-major tensors (packed once here)
+    or as flat packed tensors (then give V and, for the low-rank head, rank)."""
+
+    def __init__(self, h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
+                 write_probs: bool = False, V: Optional[int] = None,
+                 rank: Optional[int] = None, probs: Optional[torch.Tensor] = None):
+        self.lib = L.load()
+        dt = h.dtype
+        _check(h, dt, "h")
+        for name, t in (("w_full", w_full), ("w_down", w_down), ("w_up", w_up)):
+            _check(t, dt, name)
+        M, d = h.shape
+        if rank is None:
+            rank = 0 if w_down is None else w_down.shape[0]
+        if V is None:
+            V = (w_full if rank == 0 else w_up).shape[0]
+        if dt == torch.bfloat16:
+            w_full = pack_weight(w_full) if (w_full is not None and w_full.dim() == 2) else w_full
+            w_down = pack_weight(w_down) if (w_down is not None and w_down.dim() == 2) else w_down
+            w_up = pack_weight(w_up) if (w_up is not None and w_up.dim() == 2) else w_up
+        self.h, self.w_full, self.w_down, self.w_up = h, w_full, w_down, w_up
+        self.desc = L.HeadDesc(M, d, V, rank, _vs_dtype(h), float(temperature), int(write_probs))
+        dev = h.device
+        self.logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+        self.row_lse = torch.empty(M, dtype=torch.float64, device=dev)
+        if write_probs and probs is None:
+            probs = torch.empty((M, V), dtype=torch.float32, device=dev)
+        if probs is not None:
+            _check(probs, torch.float32, "probs")
+            if probs.numel() != M * V:
+                raise VstepError(L.VS_ERR_INVALID_ARG, "lm_head (probs must hold M*V floats)")
+        self.probs = probs if write_probs else None
+        nbytes = self.lib.vs_head_workspace_bytes(C.byref(self.desc))
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self):
+        st = self.lib.vs_lm_head(C.byref(self.desc), _ptr(self.h), _ptr(self.w_full),
+                                 _ptr(self.w_down), _ptr(self.w_up), _ptr(self.logits),
+                                 _ptr(self.row_lse), _ptr(self.probs), _ptr(self.ws),
+                                 self.ws.numel(), _stream())
+        _raise(st, "lm_head")
+        return self.logits, self.row_lse, self.probs
+
+
 def lm_head(h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
             write_probs: bool = False, V: Optional[int] = None, rank: Optional[int] = None):
-    """bf16: pass weights as 2-D row-major tensors (packed here on the fly) or as flat
-    packed tensors (then give V and, for the low-rank head, rank)."""
-    lib = L.load()
-    dt = h.dtype
-    _check(h, dt, "h")
-    for name, t in (("w_full", w_full), ("w_down", w_down), ("w_up", w_up)):
-        _check(t, dt, name)
-    M, d = h.shape
-    if rank is None:
-        rank = 0 if w_down is None else w_down.shape[0]
-    if V is None:
-        V = (w_full if rank == 0 else w_up).shape[0]
-    if dt == torch.bfloat16:
-        w_full = pack_weight(w_full) if (w_full is not None and w_full.dim() == 2) else w_full
-        w_down = pack_weight(w_down) if (w_down is not None and w_down.dim() == 2) else w_down
-        w_up = pack_weight(w_up) if (w_up is not None and w_up.dim() == 2) else w_up
-    desc = L.HeadDesc(M, d, V, rank, _vs_dtype(h), float(temperature), int(write_probs))
-    dev = h.device
-    logits = torch.empty((M, V), dtype=torch.float32, device=dev)
-    row_lse = torch.empty(M, dtype=torch.float64, device=dev)
-    probs = torch.empty((M, V), dtype=torch.float32, device=dev) if write_probs else None
-    nbytes = lib.vs_head_workspace_bytes(C.byref(desc))
-    ws = workspace(nbytes, dev, "head")
-    st = lib.vs_lm_head(C.byref(desc), _ptr(h), _ptr(w_full), _ptr(w_down), _ptr(w_up),
-                        _ptr(logits), _ptr(row_lse), _ptr(probs), _ptr(ws), ws.numel(), _stream())
-    _raise(st, "lm_head")
-    return logits, row_lse, probs
+    """One-shot LM head (allocates its outputs and workspace); see LmHead."""
+    return LmHead(h, w_full, w_down, w_up, temperature, write_probs, V, rank)()
 
 
 def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_res,

@@ -540,24 +540,43 @@ attn_combine_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------- fp32 path
+// One wave per (sequence, row, query head).  Lane l takes keys l, l+64, ... with its own
+// running max, sum and output accumulator; the 64 partial softmaxes are then merged
+// across the wave.  Keys are independent across lanes, so the dependent chain of one
+// lane is ceil(keys/64) long instead of keys long.
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <int HD>
 __global__ void __launch_bounds__(256)
 attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const float *k_pool,
                 const float *v_pool, const int32_t *page_table, const int32_t *prefix_len,
                 float *out, int32_t *flags, int B, int W, int D, int Hq, int Hkv, int max_pages,
                 int n_pool_pages, float scale) {
+  static_assert(HD <= 64, "one output element per lane");
   const int M = W * D;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)B * M * Hq) return;
-  const int hq = (int)(gid % Hq);
-  const int r = (int)((gid / Hq) % M);
-  const int b = (int)(gid / ((int64_t)Hq * M));
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= (int64_t)B * M * Hq) return;     // uniform per wave
+  const int hq = (int)(task % Hq);
+  const int r = (int)((task / Hq) % M);
+  const int b = (int)(task / ((int64_t)Hq * M));
   const int kvh = hq / (Hq / Hkv);
   bool badP = false;
   const int P = clamp_prefix(prefix_len[b], max_pages * kPage, &badP);
-  if (badP && flags && r == 0 && hq == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
+  if (badP && flags && r == 0 && hq == 0 && lane == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
   float qv[HD], acc[HD];
   const float *qp = q + (((int64_t)b * M + r) * Hq + hq) * HD;
+#pragma unroll
   for (int e = 0; e < HD; ++e) {
     qv[e] = qp[e];
     acc[e] = 0.f;
@@ -565,7 +584,7 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
   float mx = -INFINITY, l = 0.f;
   const int i = r / D, o = r % D;
   const int nkeys = P + o + 1;
-  for (int k = 0; k < nkeys; ++k) {
+  for (int k = lane; k < nkeys; k += 64) {
     const float *kp, *vp;
     int vstride = 1;
     if (k < P) {
@@ -583,18 +602,28 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
       vp = v_cand + off;
     }
     float sdot = 0.f;
+#pragma unroll
     for (int e = 0; e < HD; ++e) sdot = fmaf(qv[e], kp[e], sdot);
     sdot *= scale;
     const float mnew = fmaxf(mx, sdot);
     const float corr = expf(mx - mnew);
     const float p = expf(sdot - mnew);
     l = l * corr + p;
+#pragma unroll
     for (int e = 0; e < HD; ++e) acc[e] = acc[e] * corr + p * vp[e * vstride];
     mx = mnew;
   }
-  float *op = out + (((int64_t)b * M + r) * Hq + hq) * HD;
+  // merge the lanes' partial softmaxes (a lane without keys carries weight 0)
+  const float gmax = wave_max_f32(mx);
+  const float c = (mx == -INFINITY) ? 0.f : expf(mx - gmax);
+  l = wave_sum_f32(l * c);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int e = 0; e < HD; ++e) op[e] = acc[e] * inv;
+  float *op = out + (((int64_t)b * M + r) * Hq + hq) * HD;
+#pragma unroll
+  for (int e = 0; e < HD; ++e) {
+    const float v = wave_sum_f32(acc[e] * c);
+    if (lane == e) op[e] = v * inv;
+  }
 }
 
 __global__ void zero_i32_kernel(int32_t *p, int n) {
@@ -659,8 +688,8 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
                             hipStream_t st) {
   const int M = W * D;
   if (dtype == 0) {
-    const int64_t n = (int64_t)B * M * Hq;
-    const int blocks = (int)((n + 255) / 256);
+    const int64_t n = (int64_t)B * M * Hq;    // one wave each, four per workgroup
+    const int blocks = (int)((n + 3) / 4);
 #define VS_F32_ATTN(HDV)                                                                       \
   hipLaunchKernelGGL(attn_f32_kernel<HDV>, dim3(blocks), dim3(256), 0, st, (const float *)q,   \
                      (const float *)k_cand, (const float *)v_cand, (const float *)k_pool,      \

@@ -427,13 +427,22 @@ pack_weight_kernel(const bf16_t *src, bf16_t *dst, int N, int K) {
   *(u32x4 *)(dst + slot * 8) = v;
 }
 
-// sum of K-split partials [ks][n] in split order
+// sum of K-split partials [ks][n] in split order; the loads of 16 splits are issued
+// together so that one thread does not wait out ksplit memory latencies in a row
 __global__ void __launch_bounds__(kThreads)
 sum_splits_kernel(const float *part, int ksplit, int64_t n, float *out) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
-  for (int k = 0; k < ksplit; ++k) s += part[(int64_t)k * n + i];
+  int k = 0;
+  for (; k + 16 <= ksplit; k += 16) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = part[(int64_t)(k + j) * n + i];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += x[j];
+  }
+  for (; k < ksplit; ++k) s += part[(int64_t)k * n + i];
   out[i] = s;
 }
 
@@ -451,26 +460,31 @@ gemm_f32_kernel(const float *A, const float *B, float *out, int M, int N, int K)
   out[gid] = s;
 }
 
-// Tile statistics [rows][n_vt] of stored logits (fp32 path).
+// Tile statistics [rows][n_vt] of stored logits (fp32 path): max and sum of
+// exp(x - max) over one 256-wide vocabulary tile, by wave shuffles and 4 LDS slots.
 __global__ void __launch_bounds__(kThreads)
 tile_stats_kernel(const float *logits, float2 *stats, int M, int N, float inv_t) {
+  static_assert(kThreads == 256 && kHeadVocabTile == 256, "one logit per thread");
   const int vt = blockIdx.x;
   const int m = blockIdx.y;
   const int n_vt = gridDim.x;
-  __shared__ float red[kThreads];
+  const int wv = threadIdx.x >> 6;
+  __shared__ float wred[2][4];
   const int n = vt * kHeadVocabTile + threadIdx.x;
   const bool ok = n < N;
   const float x = ok ? logits[(int64_t)m * N + n] * inv_t : -INFINITY;
-  red[threadIdx.x] = x;
+  float v = x;
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) wred[0][wv] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mx = -INFINITY;
-    for (int i = 0; i < kThreads; ++i) mx = fmaxf(mx, red[i]);
-    float sm = 0.f;
-    for (int i = 0; i < kThreads; ++i)
-      if (red[i] != -INFINITY) sm += expf(red[i] - mx);
-    stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
-  }
+  const float mx = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  float e = ok ? expf(x - mx) : 0.f;
+  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+  if ((threadIdx.x & 63) == 0) wred[1][wv] = e;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    stats[(int64_t)m * n_vt + vt] =
+        make_float2(mx, (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]));
 }
 
 __global__ void __launch_bounds__(kThreads)

@@ -15,13 +15,21 @@
 // Layout of the work: grid (vocabulary chunks, sequences).  Every workgroup of a
 // sequence repeats the (cheap) acceptance tests and the choice of candidate, then
 // sums the residual weights of its own vocabulary chunk with coalesced loads.  The
-// last workgroup of the sequence to finish (atomic counter in the workspace) adds
-// the chunk sums in chunk order, finds the chunk holding u*S, rescans that chunk
-// with an ordered block scan and writes the outputs; it then resets the counter.
+// draw then adds the chunk sums in chunk order, finds the chunk holding u*S, finds
+// the thread range holding it with an ordered block scan of that chunk's per-thread
+// sums and writes the outputs.  Two ways to reach the draw:
+//   * fused: the last workgroup of the sequence to finish (atomic counter in the
+//     workspace, reset afterwards) does it.  Each workgroup then publishes its sums
+//     with a device-scope release, which writes back its XCD's L2; with a few dozen
+//     workgroups that is cheap;
+//   * two launches: the chunk sums kernel ends, and a second kernel of one workgroup
+//     per sequence draws.  With thousands of workgroups (large batches) the releases
+//     of the fused form queue up behind each other and this is faster.
 
 #include "vs_internal.hpp"
 
 #include <limits.h>
+#include <stdlib.h>
 
 namespace vs {
 
@@ -236,6 +244,9 @@ struct SampArgs {
   uint32_t *counters;    // [B]
 };
 
+enum { SAMP_FUSED = 0, SAMP_SUMS = 1, SAMP_DRAW = 2 };
+
+template <int PHASE>
 __global__ void __launch_bounds__(kST)
 sampler_kernel(SampArgs a) {
   __shared__ SampShared sh;
@@ -362,30 +373,37 @@ sampler_kernel(SampArgs a) {
 
   // ---- this chunk's sums: thread t owns the kPer consecutive ids c*kChunk + t*kPer ..
   //      (vector loads; 8 KB contiguous per chunk); its sums are kept for the draw
-  double sr = 0.0, sp = 0.0;
-  {
-    double pk[kPer], rk[kPer];
-    weights(c * kChunk + tid * kPer, pk, rk);
+  if constexpr (PHASE != SAMP_DRAW) {
+    double sr = 0.0, sp = 0.0;
+    {
+      double pk[kPer], rk[kPer];
+      weights(c * kChunk + tid * kPer, pk, rk);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      sr += rk[j];
-      sp += pk[j];
+      for (int j = 0; j < kPer; ++j) {
+        sr += rk[j];
+        sp += pk[j];
+      }
+    }
+    double2 *ts = a.thread_sums + ((int64_t)b * a.nch + c) * kST;
+    // every thread's sums reach memory before the barriers of block_sum2; thread 0's
+    // device-scope release below (or the end of the kernel) publishes them
+    ts[tid] = make_double2(sr, sp);
+    block_sum2(sh, sr, sp);
+    if constexpr (PHASE == SAMP_SUMS) {
+      if (tid == 0) a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
+      return;
+    } else {
+      if (tid == 0) {
+        a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
+        __threadfence();
+        const uint32_t old = atomicAdd(&a.counters[b], 1u);
+        sh.is_last = (old == (uint32_t)(a.nch - 1));
+      }
+      __syncthreads();
+      if (!sh.is_last) return;
+      __threadfence();
     }
   }
-  double2 *ts = a.thread_sums + ((int64_t)b * a.nch + c) * kST;
-  // every thread's sums reach memory before the barriers of block_sum2; thread 0's
-  // device-scope release below then publishes them with the chunk sum
-  ts[tid] = make_double2(sr, sp);
-  block_sum2(sh, sr, sp);
-  if (tid == 0) {
-    a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
-    __threadfence();
-    const uint32_t old = atomicAdd(&a.counters[b], 1u);
-    sh.is_last = (old == (uint32_t)(a.nch - 1));
-  }
-  __syncthreads();
-  if (!sh.is_last) return;
-  __threadfence();
 
   // ---- last workgroup of the sequence: total, owner chunk, owner thread, draw
   // chunk k's sums on thread k (nch <= kST)
@@ -408,7 +426,7 @@ sampler_kernel(SampArgs a) {
       sh.mode = MODE_TARGET;
       atomicOr(&sh.flags, FLAG_DEGENERATE);
     }
-    a.counters[b] = 0u;   // ready for the next call on this workspace
+    if (PHASE == SAMP_FUSED) a.counters[b] = 0u;   // ready for the next call on this workspace
   }
   __syncthreads();
   if (tid < a.nch && v > 0.0) {
@@ -630,7 +648,17 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.chunk_sums = ws.chunk_sums;
   a.thread_sums = ws.thread_sums;
   a.counters = ws.counters;
-  hipLaunchKernelGGL(sampler_kernel, dim3(a.nch, B), dim3(kST), 0, st, a);
+  // fused while the workgroups number about one per CU or fewer (measured: B = 1 at
+  // V = 128256 is faster fused, B = 32 far faster in two launches)
+  bool two = (int64_t)a.nch * B > 256;
+  if (const char *ov = getenv("VSTEP_SAMPLER_TWO_PASS")) two = atoi(ov) != 0;
+  if (!two) {
+    hipLaunchKernelGGL(sampler_kernel<SAMP_FUSED>, dim3(a.nch, B), dim3(kST), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(sampler_kernel<SAMP_SUMS>, dim3(a.nch, B), dim3(kST), 0, st, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(sampler_kernel<SAMP_DRAW>, dim3(1, B), dim3(kST), 0, st, a);
   return hipGetLastError();
 }
 

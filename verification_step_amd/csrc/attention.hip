@@ -26,6 +26,7 @@
 //     merges them in a fixed order.
 // fp32 path (head_dim 16/32/64): one thread per (query row, head), plain loops.
 
+#include "gate_wg.hpp"
 #include "vs_internal.hpp"
 
 #include <stdio.h>
@@ -69,6 +70,8 @@ struct AttnArgs {
   int B, W, D, M, Hq, Hkv, g, max_pages, n_pool_pages;
   int rows_per_kv, n_rb, rows_per_block, split_keys, n_splits;
   float scale_log2;
+  int n_gate;        // leading workgroups that run the copy path's gate (0: none)
+  GateArgs gate;
 };
 
 __device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
@@ -149,9 +152,18 @@ attn_mfma_kernel(AttnArgs a) {
   const int h = lane >> 5;
   const bool full_share = kEven || wv < kT % NW;   // this wave issues kIPW transfers
 
+  // the first n_gate workgroups retrieve and gate one sequence each, in the LDS of the
+  // K ring, while the attention workgroups after them start
+  if constexpr (NW >= 4) {
+    static_assert(sizeof(GateShared<64 * NW>) <= sizeof(Kb), "gate state fits the K ring");
+    if ((int)blockIdx.x < a.n_gate) {
+      gate_wg<64 * NW>(a.gate, blockIdx.x, *reinterpret_cast<GateShared<64 * NW> *>(&Kb[0][0]));
+      return;
+    }
+  }
   const int n_sp = a.n_splits + 1;
   const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
-  const int bid = xcd_remap(blockIdx.x, nblocks);
+  const int bid = xcd_remap((int)blockIdx.x - a.n_gate, nblocks);
   const int rb = bid % a.n_rb;
   const int s = (bid / a.n_rb) % n_sp;
   const int z = bid / (a.n_rb * n_sp);
@@ -633,6 +645,10 @@ __global__ void zero_i32_kernel(int32_t *p, int n) {
 
 }  // namespace
 
+bool attn_fuses_gate(int B, int W, int D, int Hq, int Hkv, int max_pages, int dtype) {
+  return dtype == 1 && attn_plan(B, W, D, Hq, Hkv, max_pages, kPage).nw >= 4;
+}
+
 AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page) {
   AttnPlan p{};
   const int M = W * D;
@@ -685,7 +701,7 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
                             const void *k_cand, const void *v_cand, const void *k_pool,
                             const void *v_pool, const int32_t *page_table,
                             const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
-                            hipStream_t st) {
+                            hipStream_t st, const GateArgs *gate) {
   const int M = W * D;
   if (dtype == 0) {
     const int64_t n = (int64_t)B * M * Hq;    // one wave each, four per workgroup
@@ -730,8 +746,14 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   a.split_keys = p.split_keys;
   a.n_splits = p.n_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_gate = 0;
+  if (gate != nullptr) {
+    if (p.nw < 4) return hipErrorInvalidValue;
+    a.n_gate = B;
+    a.gate = *gate;
+  }
   const int nblocks = p.n_rb * (p.n_splits + 1) * B * Hkv;
-  const dim3 grid(nblocks), block(64 * p.nw);
+  const dim3 grid(nblocks + a.n_gate), block(64 * p.nw);
   switch (p.nw) {
     case 1: hipLaunchKernelGGL((attn_mfma_kernel<1>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_mfma_kernel<2>), grid, block, 0, st, a); break;

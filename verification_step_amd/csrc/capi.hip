@@ -265,10 +265,20 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
   hipError_t e;
   if (!mark(0)) return VS_ERR_HIP;
-  // 1. copy retrieval + probe gate (one launch), on the auxiliary stream when given.
-  //    It is the first writer of io->flags; attention reports into the workspace
-  //    (sw.attn_flags), which the sampler folds in, so the two never race.
-  const bool fork = io->aux_stream != nullptr && !d->external_drafts;
+  // 1. copy retrieval + probe gate.  When the attention row blocks have four or more
+  //    waves, its B workgroups ride in the attention launch (step 2) and run beside
+  //    the attention workgroups; otherwise one launch of its own, on the auxiliary
+  //    stream when given.  It is the first writer of io->flags; attention reports
+  //    into the workspace (sw.attn_flags), which the sampler folds in, so the two never
+  //    race.
+  const bool copy_path = !d->external_drafts;
+  const bool fuse = copy_path && vs::attn_fuses_gate(d->B, d->W, d->D, d->Hq, d->Hkv,
+                                                     d->max_pages, d->dtype);
+  const vs::GateArgs ga = vs::gate_args(io->ctx, d->ctx_total, io->ctx_off, d->kappa, d->W, d->D,
+                                        io->cand_tok, io->cand_len, io->cand_pos, io->n_found,
+                                        io->flags, io->probe_h, d->dtype == VS_BF16, io->probe_w,
+                                        d->d, d->tau, io->score, io->gate);
+  const bool fork = io->aux_stream != nullptr && copy_path && !fuse;
   hipStream_t gs = s;
   if (fork) {
     gs = S(io->aux_stream);
@@ -276,7 +286,7 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
         hipStreamWaitEvent(gs, (hipEvent_t)io->fork_event, 0) != hipSuccess)
       return VS_ERR_HIP;
   }
-  if (!d->external_drafts) {
+  if (copy_path && !fuse) {
     e = vs::launch_copy_match(io->ctx, d->ctx_total, io->ctx_off, d->B, d->kappa, d->W, d->D,
                               io->cand_tok, io->cand_len, io->cand_pos, io->n_found, io->flags,
                               io->probe_h, d->dtype == VS_BF16, io->probe_w, d->d, d->tau,
@@ -285,11 +295,12 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
     if (fork && hipEventRecord((hipEvent_t)io->join_event, gs) != hipSuccess) return VS_ERR_HIP;
   }
   if (!mark(1)) return VS_ERR_HIP;
-  // 2. verify attention
+  // 2. verify attention (with the gate's workgroups in front when fused)
   e = vs::launch_attention(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->max_pages,
                            d->n_pool_pages, d->dtype, attn_scale(d->scale, d->head_dim), io->q,
                            io->k_cand, io->v_cand, io->k_pool, io->v_pool, io->page_table,
-                           io->prefix_len, io->attn_out, sw.attn_flags, ws + L.attn, s);
+                           io->prefix_len, io->attn_out, sw.attn_flags, ws + L.attn, s,
+                           fuse ? &ga : nullptr);
   if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
   // 3. head: GEMM + tile statistics (verify rows and root rows)
   e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,

@@ -79,6 +79,26 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
 size_t attn_workspace_bytes(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages, int page,
                             int dtype);
 
+// Retrieval + probe of the copy path, one sequence per workgroup (gate_wg.hpp).
+struct GateArgs {
+  const int32_t *ctx;
+  int64_t ctx_total;
+  const int32_t *ctx_off;
+  int kappa, W, D;
+  int32_t *cand_tok, *cand_len, *cand_pos, *n_found, *flags;
+  const void *h;            // probe input [B, d] or null (retrieval only)
+  int h_bf16;
+  const float *w;
+  int d;
+  float tau;
+  float *score;
+  int32_t *gate;
+};
+GateArgs gate_args(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int kappa, int W,
+                   int D, int32_t *cand_tok, int32_t *cand_len, int32_t *cand_pos,
+                   int32_t *n_found, int32_t *flags, const void *h, int h_bf16, const float *w,
+                   int d, float tau, float *score, int32_t *gate);
+
 hipError_t launch_copy_match(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B,
                              int kappa, int W, int D, int32_t *cand_tok, int32_t *cand_len,
                              int32_t *cand_pos, int32_t *n_found, int32_t *flags,
@@ -90,12 +110,17 @@ hipError_t launch_probe_gate(const void *h, int h_bf16, const float *w, int B, i
                              const int32_t *n_found, float *score, int32_t *gate, int32_t *flags,
                              hipStream_t st);
 
+// Whether the attention launch of these shapes can carry the copy path's gate as extra
+// workgroups (bf16 row blocks of at least four waves).
+bool attn_fuses_gate(int B, int W, int D, int Hq, int Hkv, int max_pages, int dtype);
+// gate != null: the B gate workgroups run first in the same launch (attn_fuses_gate
+// must hold).
 hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages,
                             int n_pool_pages, int dtype, float scale, const void *q,
                             const void *k_cand, const void *v_cand, const void *k_pool,
                             const void *v_pool, const int32_t *page_table,
                             const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
-                            hipStream_t st);
+                            hipStream_t st, const GateArgs *gate = nullptr);
 
 // Head workspace: per-tile (max, sumexp) statistics [rows][n_vt] and the low-rank
 // intermediate.

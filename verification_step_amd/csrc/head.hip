@@ -347,7 +347,7 @@ head_lds_kernel(GemmArgs a) {
       if (m < a.M) {
         float *op = a.out + (int64_t)m * a.N + n0;
         if (n0 + 3 < a.N) {
-          __builtin_nontemporal_store(acc[v][mt], (f32x4 *)op);
+          *(f32x4 *)op = acc[v][mt];
         } else {
           for (int j = 0; j < 4; ++j)
             if (n0 + j < a.N) op[j] = acc[v][mt][j];

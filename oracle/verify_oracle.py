@@ -409,13 +409,136 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
     return out
 
 
+def reject_sample_multi(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
+                        temperature: float = 1.0, gate=None):
+    """Lossless acceptance over W candidates: recursive residual across the sibling
+    candidates at each depth (the survey's next item N1; built from section 3's
+    single-draft rule and its residual).
+
+    Depth a starts from the target distribution P of the reference row: the root for
+    a = 0, else row (ref, a-1), ref being the smallest surviving candidate.  The
+    siblings at depth a are the surviving candidates i with len_i > a, in index
+    order; candidate i proposes x_i = cand[i, a] with draft distribution Q_i =
+    q[(i, a)] (a point mass on x_i when q is None).  With the current residual p'
+    (initially P), sibling i is accepted iff u_acc[i, a] * Q_i(x_i) < p'(x_i) -- the
+    min(1, p'/q) rule -- and otherwise p' <- max(0, p' - Q_i), renormalised (if that
+    leaves no mass, p' is kept and DEGENERATE flagged).  An accepted x is emitted and
+    the survivors become the siblings whose token at depth a is x.  If every sibling
+    is rejected, one token is drawn from p' with u_res[i_last] (the last sibling
+    tested); if no survivor has a token at depth a, a bonus token is drawn from P
+    with u_res[ref].  Each rejection removes exactly the mass the draft claimed, so
+    the emitted token follows P at every depth whenever the drafts are independent
+    draws from their Q (for copy drafts Q is the point mass they are).
+
+    best = the final reference candidate; acc_per_cand[i] = the length of the
+    common prefix of candidate i with the accepted tokens.  Same outputs and flags
+    as reject_sample."""
+    root_logits = np.asarray(root_logits, dtype=np.float32)
+    logits = np.asarray(logits, dtype=np.float32)
+    B, W, D = cand_tok.shape
+    V = root_logits.shape[1]
+    M = W * D
+    T = float(temperature)
+    z_root = root_logits.astype(np.float64) / T
+    lse_root = _logsumexp_rows(z_root)
+    out = dict(
+        n_acc=np.zeros(B, dtype=np.int32), best=np.full(B, -1, dtype=np.int32),
+        out_tok=np.full((B, D + 1), -1, dtype=np.int32), n_out=np.zeros(B, dtype=np.int32),
+        acc_per_cand=np.zeros((B, W), dtype=np.int32), flags=np.zeros(B, dtype=np.int32),
+        accept_margin=np.full(B, np.inf), cdf_margin=np.full(B, np.inf),
+    )
+
+    def row_p(b, prow):
+        if prow < 0:
+            return np.exp(z_root[b] - lse_root[b])
+        zz = logits[b * M + prow].astype(np.float64) / T
+        m = zz.max()
+        return np.exp(zz - (m + np.log(np.exp(zz - m).sum())))
+
+    for b in range(B):
+        flags = 0
+        lens = np.clip(np.asarray(cand_len[b]).copy(), 0, D)
+        if gate is not None and not gate[b]:
+            lens[:] = 0
+        surv = [i for i in range(W) if lens[i] >= 1]
+        if not surv:
+            y, tie, out["cdf_margin"][b] = _draw(row_p(b, -1), u_res[b, 0])
+            out["out_tok"][b, 0] = y
+            out["n_out"][b] = 1
+            out["flags"][b] = FLAG_NO_CANDIDATE | (FLAG_CDF_TIE if tie else 0)
+            continue
+        a = 0
+        acc = []
+        y = None
+        while True:
+            ref = surv[0]
+            P = row_p(b, -1 if a == 0 else ref * D + a - 1)
+            sib = [i for i in surv if lens[i] > a]
+            if not sib:
+                y, tie, out["cdf_margin"][b] = _draw(P, u_res[b, ref])
+                break
+            r = P.copy()
+            accepted = None
+            last = sib[0]
+            for i in sib:
+                last = i
+                x = int(cand_tok[b, i, a])
+                if q is None:
+                    Qi = np.zeros(V)
+                    if 0 <= x < V:
+                        Qi[x] = 1.0
+                else:
+                    Qi = q[b * M + i * D + a].astype(np.float64)
+                if 0 <= x < V:
+                    pp = r[x] / r.sum()
+                    Qx = Qi[x] if q is not None else 1.0
+                else:
+                    flags |= FLAG_BAD_TOKEN
+                    pp, Qx = 0.0, 1.0
+                lhs = u_acc[b, i, a] * Qx
+                if max(pp, lhs) > 0:
+                    out["accept_margin"][b] = min(out["accept_margin"][b],
+                                                  abs(lhs - pp) / max(pp, lhs))
+                if abs(lhs - pp) < ACCEPT_TIE_REL * max(pp, lhs):
+                    flags |= FLAG_ACCEPT_TIE
+                if lhs < pp:
+                    accepted = x
+                    break
+                rn = np.maximum(0.0, r / r.sum() - Qi)
+                if rn.sum() > 0.0:
+                    r = rn
+                else:
+                    flags |= FLAG_DEGENERATE
+            if accepted is None:
+                y, tie, out["cdf_margin"][b] = _draw(r, u_res[b, last])
+                break
+            acc.append(accepted)
+            surv = [i for i in sib if int(cand_tok[b, i, a]) == accepted]
+            a += 1
+        if tie:
+            flags |= FLAG_CDF_TIE
+        out["best"][b] = surv[0]
+        out["n_acc"][b] = a
+        out["out_tok"][b, :a] = acc
+        out["out_tok"][b, a] = y
+        out["n_out"][b] = a + 1
+        for i in range(W):
+            k = 0
+            while k < min(lens[i], a) and int(cand_tok[b, i, k]) == acc[k]:
+                k += 1
+            out["acc_per_cand"][b, i] = k
+        out["flags"][b] = flags
+    return out
+
+
 # ----------------------------------------------------------------------------------
 # a7: the whole verify step
 
-def verify_step(case_arrays: dict, shape, drafts=None, q_override=None):
+def verify_step(case_arrays: dict, shape, drafts=None, q_override=None, accept: str = "longest"):
     """copy_match -> probe_gate -> verify_attention -> lm_head -> reject_sample on one
     batch.  `drafts` = (cand_tok, cand_len) for the neural-draft path (copy retrieval
-    skipped, gate open).  Returns every stage's outputs."""
+    skipped, gate open).  accept = "longest" (the pages' longest verified run) or
+    "multi" (reject_sample_multi).  Returns every stage's outputs."""
     A = case_arrays
     sh = shape
     res = {}
@@ -434,8 +557,9 @@ def verify_step(case_arrays: dict, shape, drafts=None, q_override=None):
     H = O_r.reshape(O_r.shape[0], -1)
     logits, lse = lm_head_full(H, A["w_full"], sh.temperature, sh.dtype)
     q = q_override if q_override is not None else A.get("q_draft")
-    rs = reject_sample(A["root_logits"], logits, q, cand_tok, cand_len, A["u_acc"],
-                       A["u_res"], sh.temperature, gate)
+    rule = reject_sample_multi if accept == "multi" else reject_sample
+    rs = rule(A["root_logits"], logits, q, cand_tok, cand_len, A["u_acc"], A["u_res"],
+              sh.temperature, gate)
     res.update(attn=O_r, attn_exact=O, attn_flags=aflags, logits=logits, lse=lse, sample=rs,
                cand_tok=cand_tok, cand_len=cand_len, gate=gate)
     return res

@@ -274,3 +274,171 @@ def test_ties_choose_smallest_candidate_and_bad_token_rejects():
     assert r["acc_per_cand"][0].tolist() == [1, 1] and r["best"][0] == 0
     r = run(p, [p], None, [7], [1], [0.0], [0.3], 1, 1)
     assert r["n_acc"][0] == 0 and r["flags"][0] & oracle.FLAG_BAD_TOKEN
+
+
+# ----------------------------------------------------------------- lossless multi-candidate
+# (the survey's next item N1: recursive residual across sibling candidates)
+
+def run_multi(root_p, rows_p, q, toks, lens, u_acc, u_res, W, D):
+    V = len(root_p)
+    root = _logits_of(root_p)[None, :]
+    logits = np.stack([_logits_of(r) for r in rows_p]) if rows_p else np.zeros((W * D, V), np.float32)
+    return oracle.reject_sample_multi(root, logits, q, np.asarray(toks, np.int32).reshape(1, W, D),
+                                      np.asarray(lens, np.int32).reshape(1, W),
+                                      np.asarray(u_acc, np.float64).reshape(1, W, D),
+                                      np.asarray(u_res, np.float64).reshape(1, W))
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_multi_equals_literal_for_one_candidate(dense):
+    """With W = 1 there are no siblings: the rule is section 3's chain exactly."""
+    rng = np.random.default_rng(3)
+    B, D, V = 40, 5, 12
+    root = rng.standard_normal((B, V)).astype(np.float32)
+    lg = (rng.standard_normal((B * D, V)) * 2).astype(np.float32)
+    tok = rng.integers(0, 4, (B, 1, D)).astype(np.int32)
+    ln = rng.integers(0, D + 1, (B, 1)).astype(np.int32)
+    ua, ur = rng.random((B, 1, D)), rng.random((B, 1))
+    q = None
+    if dense:
+        q = rng.dirichlet(np.ones(V), size=B * D).astype(np.float32)
+    a = oracle.reject_sample_multi(root, lg, q, tok, ln, ua, ur)
+    b = oracle.reject_sample(root, lg, q, tok, ln, ua, ur)
+    for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def multi_first_law(root_p, qrows, W, V):
+    """Law of the first emitted token of the multi rule with sibling drafts x_i ~
+    q_i drawn independently (D = 1), from thresholds located by bisection on the
+    oracle's uniforms only."""
+    q = np.asarray(qrows, dtype=np.float32)
+    rows_p = [root_p] * W                      # D = 1: rows are never used
+    hi = np.nextafter(1.0, 0)
+    law = np.zeros(V)
+    for xs in itertools.product(range(V), repeat=W):
+        w = float(np.prod([float(q[i, xs[i]]) for i in range(W)]))
+        if w == 0.0:
+            continue
+        reach = 1.0
+        for i in range(W):
+            # sibling i's acceptance threshold: earlier siblings pushed to rejection
+            # (u just below 1), later ones given an out-of-range token (always rejected)
+            def acc(u, i=i):
+                ua = [hi] * W
+                ua[i] = u
+                xs_i = list(xs[:i + 1]) + [V] * (W - i - 1)
+                return run_multi(root_p, rows_p, q, xs_i, [1] * W, ua, [0.5] * W, W, 1)["n_acc"][0] == 1
+            th = _threshold(acc)
+            law[xs[i]] += w * reach * th
+            reach *= 1.0 - th
+        if reach == 0.0:
+            continue
+
+        def tok_le(k, u):
+            r = run_multi(root_p, rows_p, q, list(xs), [1] * W, [hi] * W, [u] * W, W, 1)
+            assert r["n_acc"][0] == 0
+            return r["out_tok"][0, 0] <= k
+        F = [_threshold(lambda u, k=k: tok_le(k, u)) for k in range(V)]
+        law += w * reach * np.diff(np.concatenate([[0.0], F]))
+    return law
+
+
+@pytest.mark.parametrize("seed,W,V", [(0, 2, 3), (1, 2, 4), (2, 3, 3)])
+def test_multi_first_token_law_is_target(seed, W, V):
+    """Dense sibling drafts drawn independently from their own q: the emitted token
+    follows the target exactly (the literal longest-run rule does not, see the
+    counterexample above)."""
+    rng = np.random.default_rng(seed)
+    root_p = rng.dirichlet(np.ones(V))
+    qrows = [_dyadic(rng.dirichlet(np.ones(V) * 0.7)) for _ in range(W)]
+    law = multi_first_law(root_p, qrows, W, V)
+    assert np.abs(law - _stored_p(root_p)).max() < 1e-9
+
+
+def test_multi_counterexample_is_lossless():
+    """The W = 2 counterexample of the literal rule (law (3/4, 1/4) for p = (1/2, 1/2))
+    gives p under the multi rule."""
+    g = json.load(open(os.path.join(GOLD, "sampler_cases.json")))["multi_candidate_counterexample"]
+    law = multi_first_law(np.array(g["p"]), [g["q"], g["q"]], 2, 2)
+    assert np.abs(law - _stored_p(g["p"])).max() < 1e-12
+
+
+def test_multi_point_mass_siblings_law_is_target():
+    """Copy drafts (point masses) at one depth, with a repeated token: trying x1, x2,
+    x3 in turn and removing each rejected token's mass, then drawing from what is
+    left, emits exactly the target law."""
+    V = 5
+    p = np.array([0.05, 0.3, 0.15, 0.4, 0.1])
+    ps = _stored_p(p)
+    hi = np.nextafter(1.0, 0)
+    for xs in ([1, 3, 0], [3, 3, 2], [4, 4, 4]):
+        W = len(xs)
+        law = np.zeros(V)
+        reach = 1.0
+        for i in range(W):
+            def acc(u, i=i):
+                ua = [hi] * W
+                ua[i] = u
+                return run_multi(p, [p] * W, None, xs, [1] * W, ua, [0.5] * W, W, 1)["n_acc"][0] == 1
+            th = _threshold(acc)
+            law[xs[i]] += reach * th
+            reach *= 1.0 - th
+
+        def tok_le(k, u):
+            return run_multi(p, [p] * W, None, xs, [1] * W, [hi] * W, [u] * W, W, 1)["out_tok"][0, 0] <= k
+        F = [_threshold(lambda u, k=k: tok_le(k, u)) for k in range(V)]
+        law += reach * np.diff(np.concatenate([[0.0], F]))
+        assert np.abs(law - ps).max() < 1e-9, xs
+
+
+def test_multi_second_depth_follows_reference_row():
+    """Two copy candidates sharing their first token a: after a is accepted both
+    survive, the second depth is judged by the reference candidate's row (0, 0) and
+    the second emitted token follows that row exactly; candidate 1's own row is not
+    used."""
+    V = 4
+    root_p = np.array([0.4, 0.3, 0.2, 0.1])
+    row00 = np.array([0.1, 0.2, 0.3, 0.4])       # judges depth 1 for candidate 0
+    row10 = np.array([0.7, 0.1, 0.1, 0.1])       # candidate 1's own row: never used
+    rows_p = [row00, root_p, row10, root_p]       # rows (0,0), (0,1), (1,0), (1,1)
+    toks = [0, 2, 0, 3]                           # cand 0 = (0, 2), cand 1 = (0, 3)
+    hi = np.nextafter(1.0, 0)
+    W, D = 2, 2
+    law = np.zeros(V)
+    reach = 1.0
+    for i, x in ((0, 2), (1, 3)):
+        def acc(u, i=i):
+            ua = [0.0, hi, 0.0, hi]               # depth 0 accepted by candidate 0
+            ua[i * D + 1] = u
+            return run_multi(root_p, rows_p, None, toks, [2, 2], ua, [0.5, 0.5], W, D)["n_acc"][0] == 2
+        th = _threshold(acc)
+        law[x] += reach * th
+        reach *= 1.0 - th
+
+    def tok_le(k, u):
+        r = run_multi(root_p, rows_p, None, toks, [2, 2], [0.0, hi, 0.0, hi], [u, u], W, D)
+        assert r["n_acc"][0] == 1 and r["out_tok"][0, 0] == 0 and r["best"][0] == 0
+        return r["out_tok"][0, 1] <= k
+    F = [_threshold(lambda u, k=k: tok_le(k, u)) for k in range(V)]
+    law += reach * np.diff(np.concatenate([[0.0], F]))
+    assert np.abs(law - _stored_p(row00)).max() < 1e-9
+    # both candidates survive depth 0: their common prefix with the accepted tokens
+    r = run_multi(root_p, rows_p, None, toks, [2, 2], [0.0, hi, 0.0, hi], [0.5, 0.5], W, D)
+    assert r["acc_per_cand"][0].tolist() == [1, 1]
+
+
+def test_multi_greedy_limit():
+    """One-hot targets: the multi rule emits the argmax chain as long as some
+    candidate proposes it, then the argmax."""
+    V, W, D = 6, 3, 3
+    hot = lambda k: [1 - 1e-30 * (V - 1) if j == k else 1e-30 for j in range(V)]
+    greedy = [4, 1, 5, 2]
+    toks = [[4, 0, 0], [4, 1, 0], [3, 1, 5]]
+    rows = [hot(greedy[1]), hot(greedy[2]), hot(greedy[3])] * W
+    r = run_multi(hot(greedy[0]), rows, None, toks, [D] * W, [0.3] * (W * D), [0.7] * W, W, D)
+    # depth 0: candidates 0, 1 propose 4 (accepted); depth 1: candidate 1 proposes 1
+    # (accepted, judged by row (0, 0)); depth 2: candidate 1 proposes 0 -> residual
+    assert r["n_acc"][0] == 2 and r["best"][0] == 1
+    assert r["out_tok"][0].tolist() == [4, 1, 5, -1]
+    assert r["acc_per_cand"][0].tolist() == [1, 2, 0]

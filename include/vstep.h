@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VS_ABI_VERSION 2
+#define VS_ABI_VERSION 3
 
 typedef enum {
     VS_OK = 0,
@@ -55,12 +55,20 @@ typedef enum {
 
 typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
 
+/* How the sampler chooses among W candidates (vs_sample_desc / vs_step_desc). */
+typedef enum {
+    VS_ACCEPT_LONGEST = 0,   /* each candidate judged alone; the longest accepted run wins */
+    VS_ACCEPT_MULTI = 1      /* lossless multi-candidate acceptance (see vs_reject_sample) */
+} vs_accept_mode;
+
 /* Per-sequence device flags (bitwise OR). */
 enum {
     VS_FLAG_PROBE_TIE = 1,            /* |score - tau| < 1e-5: probe decision is a near tie */
     VS_FLAG_ACCEPT_TIE = 2,           /* a decisive acceptance test has |u*Q - p| < 1e-4*max(p, u*Q) */
     VS_FLAG_CDF_TIE = 4,              /* the final draw lies within 1e-8*S of a CDF step */
-    VS_FLAG_DEGENERATE_RESIDUAL = 8,  /* residual mass <= 0: drew from the target p instead */
+    VS_FLAG_DEGENERATE_RESIDUAL = 8,  /* residual mass <= 0: drew from the target p instead
+                                         (multi: also a removal that would leave no mass,
+                                         which is then skipped) */
     VS_FLAG_NO_CANDIDATE = 16,        /* gate closed or no candidate: one token from the root p */
     VS_FLAG_BAD_PAGE = 32,            /* page index outside the pool, or prefix_len out of range */
     VS_FLAG_BAD_CTX = 64,             /* context offsets outside [0, ctx_total] or decreasing */
@@ -184,10 +192,28 @@ int vs_lm_head(const vs_head_desc *desc, const void *h, const void *w_full,
  *   u_acc fp64 [B,W,D]; u_res fp64 [B,W]  (uniforms in [0,1), indexed by position)
  *   gate int32 [B] or NULL (NULL = open)
  * Outputs: n_acc [B], best [B] (-1 if none), out_tok [B, D+1] (-1 padded),
- *   n_out [B] (= n_acc + 1), acc_per_cand [B, W], flags [B] (may be NULL). */
+ *   n_out [B] (= n_acc + 1), acc_per_cand [B, W], flags [B] (may be NULL).
+ *
+ * accept_mode VS_ACCEPT_MULTI: lossless acceptance over the W candidates, built from
+ * the single-draft rule and its residual [SD section 3] applied across sibling
+ * drafts.  Depth a (from 0) starts from the target p of the reference row -- the
+ * root for a = 0, else row (b, ref, a-1), ref = the smallest surviving candidate
+ * (all candidates with cand_len >= 1 survive at a = 0).  The survivors with
+ * cand_len > a are tried in index order: with p' the current residual (initially p),
+ * candidate i's token x is accepted iff u_acc[b,i,a] < p'(x); a rejection sets
+ * p' <- normalise(max(0, p' - point mass on x)).  An accepted x is emitted and the
+ * survivors become the tried candidates whose token at depth a is x.  If all are
+ * rejected, one token is drawn from p' with u_res[b, last candidate tried]; if no
+ * survivor has a token at depth a, a bonus token is drawn from p with
+ * u_res[b, ref].  Outputs as above with best = the final reference candidate and
+ * acc_per_cand[b,i] = the length of candidate i's common prefix with the accepted
+ * tokens.  Copy drafts only (q == NULL) when W > 1 (else VS_ERR_UNSUPPORTED), at
+ * most 64 candidates and (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); with
+ * W == 1 the rule is the single-chain rule above, which is what runs. */
 typedef struct {
     int32_t B, W, D, V;
     float temperature;
+    int32_t accept_mode;      /* vs_accept_mode */
 } vs_sample_desc;
 
 size_t vs_sample_workspace_bytes(const vs_sample_desc *desc);
@@ -224,6 +250,7 @@ typedef struct {
     float temperature;
     int32_t external_drafts;
     int64_t ctx_total;
+    int32_t accept_mode;      /* vs_accept_mode of the sampler (same limits as vs_reject_sample) */
 } vs_step_desc;
 
 typedef struct {

@@ -46,20 +46,21 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vs_abi_version() == 2
+    assert lib.vs_abi_version() == 3
     assert lib.vs_status_str(0) == b"ok"
     assert b"workspace" in lib.vs_status_str(-3)
     assert lib.vs_status_str(99) == b"unknown status"
 
 
 def test_struct_layouts_match_header():
-    # int32 fields then int64 ctx_total at its natural alignment
-    assert C.sizeof(L.StepDesc) == 80
+    # int32 fields, int64 ctx_total at its natural alignment, int32 accept_mode, padding
+    assert C.sizeof(L.StepDesc) == 88
     assert L.StepDesc.ctx_total.offset == 72
+    assert L.StepDesc.accept_mode.offset == 80
     assert C.sizeof(L.StepIO) == 35 * 8
     assert C.sizeof(L.AttnDesc) == 44
     assert C.sizeof(L.HeadDesc) == 28
-    assert C.sizeof(L.SampleDesc) == 20
+    assert C.sizeof(L.SampleDesc) == 24
 
 
 def test_copy_match_validation(lib):
@@ -136,6 +137,22 @@ def test_sample_validation(lib):
     bad = list(args)
     bad[0] = None
     assert lib.vs_reject_sample(C.byref(d), *bad, None, 0, None) == -1
+    # accept modes: unknown -> invalid; multi with dense drafts (q given) and W > 1, more
+    # than 64 candidates, or too many p values for LDS -> unsupported; multi with W == 1
+    # takes dense drafts (single-chain rule) and gets as far as the workspace check
+    def samp(W, D, mode, q=fake):
+        a = list(args)
+        a[3] = q
+        return lib.vs_reject_sample(C.byref(L.SampleDesc(2, W, D, 1000, 1.0, mode)), *a, None,
+                                    0, None)
+    assert samp(4, 20, 2) == -1
+    assert samp(4, 20, L.VS_ACCEPT_MULTI) == -2
+    assert samp(4, 20, L.VS_ACCEPT_MULTI, q=None) == -3
+    assert samp(65, 1, L.VS_ACCEPT_MULTI, q=None) == -2
+    assert samp(16, 40, L.VS_ACCEPT_MULTI, q=None) == -2     # (640+1)*16 + 640 > 4096
+    assert samp(8, 20, L.VS_ACCEPT_MULTI, q=None) == -3      # (160+1)*8 + 160 fits
+    assert samp(1, 20, L.VS_ACCEPT_MULTI) == -3
+    assert lib.vs_sample_workspace_bytes(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 2))) == 0
 
 
 def test_pack_validation(lib):
@@ -164,3 +181,11 @@ def test_step_validation(lib):
     assert lib.vs_verify_step(C.byref(d2), C.byref(io), fake, 1 << 40, None) == -1
     d3 = L.StepDesc(**{**base, "kappa": 20})
     assert lib.vs_verify_step(C.byref(d3), C.byref(io), fake, 1 << 40, None) == -2
+    # multi-candidate acceptance takes copy drafts only: q_draft must be null
+    d4 = L.StepDesc(**{**base, "accept_mode": L.VS_ACCEPT_MULTI})
+    assert lib.vs_step_workspace_bytes(C.byref(d4)) > 0
+    assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 1 << 40, None) == -2
+    io.q_draft = None
+    assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 16, None) == -3
+    d5 = L.StepDesc(**{**base, "accept_mode": 7})
+    assert lib.vs_step_workspace_bytes(C.byref(d5)) == 0

@@ -388,6 +388,121 @@ def test_reject_sample_fused_and_two_launch_agree(qmode, monkeypatch):
     assert n_exc <= 1 and n_cmp >= B - 1
 
 
+def _multi_case(rng, B, W, D, V, boost=8.0, n_hot=2):
+    """Logits with n_hot tokens boosted in every row (so acceptances are frequent) and
+    copy candidates over those tokens that share prefixes: candidate i copies a prefix
+    of an earlier candidate and then goes its own way, as copy candidates of one
+    context do.  Some tokens are out of range, some lengths are zero."""
+    M = W * D
+    hot = np.arange(1, 1 + n_hot)
+    root = rng.standard_normal((B, V)).astype(np.float32)
+    logits = rng.standard_normal((B * M, V)).astype(np.float32)
+    root[:, hot] += boost
+    logits[:, hot] += boost
+    cand = rng.choice(hot, size=(B, W, D)).astype(np.int32)
+    for b in range(B):
+        for i in range(1, W):
+            j = rng.integers(0, i)
+            k = rng.integers(0, D + 1)
+            cand[b, i, :k] = cand[b, j, :k]
+    rare = rng.random((B, W, D)) < 0.03
+    cand[rare] = rng.integers(0, V, size=rare.sum())
+    cand[rng.random((B, W, D)) < 0.01] = V + 3               # out of range: rejected
+    clen = rng.integers(0, D + 1, size=(B, W)).astype(np.int32)
+    clen[rng.random((B, W)) < 0.5] = D
+    for b in range(B):
+        for i in range(W):
+            cand[b, i, clen[b, i]:] = -1
+    return root, logits, cand, clen
+
+
+@pytest.mark.parametrize("B,W,D,V,T", [(96, 4, 6, 1000, 1.0), (64, 8, 20, 3000, 0.8),
+                                       (48, 3, 2, 2100, 1.0)])
+def test_reject_sample_multi(B, W, D, V, T):
+    """Lossless multi-candidate acceptance against the oracle's rule on candidates that
+    branch from shared prefixes (siblings with equal, distinct and invalid tokens)."""
+    api = _api()
+    rng = np.random.default_rng(31 + W)
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    clen[0] = 0
+    lse = scipy.special.logsumexp(logits.astype(np.float64) / T, axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    gate = np.ones(B, dtype=np.int32)
+    gate[1] = 0
+    say("reject_sample multi", B, W, D, V, T)
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), to_dev(ua), to_dev(ur), T, to_dev(gate), accept="multi")
+    o = oracle.reject_sample_multi(root, logits, None, cand, clen, ua, ur, T, gate)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    assert n_exc <= 2 and n_cmp >= B - 2
+    # the chains did branch: sequences whose final reference is not candidate 0
+    assert (o["best"] > 0).sum() >= 3 and (o["n_acc"] >= 2).sum() >= 3
+    assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
+
+
+@pytest.mark.parametrize("mode", ["0", "1"])
+def test_reject_sample_multi_launch_modes(mode, monkeypatch):
+    """Multi-candidate acceptance through both ways to reach the draw, with more
+    sequence chunks than CUs, against the oracle."""
+    api = _api()
+    rng = np.random.default_rng(77)
+    B, W, D, V = 40, 4, 8, 9000
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    monkeypatch.setenv("VSTEP_SAMPLER_TWO_PASS", mode)
+    say("reject_sample multi launch mode", mode)
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), to_dev(ua), to_dev(ur), 1.0, accept="multi")
+    o = oracle.reject_sample_multi(root, logits, None, cand, clen, ua, ur, 1.0, None)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    assert n_exc <= 1 and n_cmp >= B - 1
+
+
+def test_reject_sample_multi_single_candidate_is_literal():
+    """With one candidate the multi rule is the single-chain rule: same bits, dense or
+    point-mass drafts."""
+    api = _api()
+    rng = np.random.default_rng(8)
+    B, W, D, V = 32, 1, 7, 5000
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+    q = wl.draft_probs_from_logits(rng, (B * W * D, V), 1.5)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    for qq in (q, None):
+        args = (to_dev(root), to_dev(logits), to_dev(lse), None if qq is None else to_dev(qq),
+                to_dev(cand), to_dev(clen), to_dev(ua), to_dev(ur), 1.0)
+        say("reject_sample multi W=1", qq is None)
+        a = api.reject_sample(*args, accept="multi")
+        b = api.reject_sample(*args, accept="longest")
+        for k in a:
+            assert np.array_equal(tensor_np(a[k]), tensor_np(b[k])), k
+
+
+def test_reject_sample_workspace_reused_across_shapes(monkeypatch):
+    """The binding's cached workspace is zeroed when the shape changes: a two-launch
+    call on a small batch leaves chunk sums where a larger batch keeps its counters,
+    and the larger batch still completes every sequence."""
+    api = _api()
+    rng = np.random.default_rng(4)
+    for B, V, two in ((40, 9000, "1"), (96, 1000, "0")):
+        W, D = 4, 6
+        root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+        lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+        ua = rng.random((B, W, D))
+        ur = rng.random((B, W))
+        monkeypatch.setenv("VSTEP_SAMPLER_TWO_PASS", two)
+        say("reject_sample workspace reuse", B, V)
+        g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                              to_dev(clen), to_dev(ua), to_dev(ur), 1.0)
+        o = oracle.reject_sample(root, logits, None, cand, clen, ua, ur, 1.0, None)
+        n_cmp, n_exc = compare_sampler(g, o, B)
+        assert n_exc <= 1 and n_cmp >= B - 1
+
+
 # =============================================================================== whole step
 
 def _step_inputs(case, T, external=None):
@@ -435,6 +550,31 @@ def test_verify_step_end_to_end(name):
                           tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa)
     g = step()
     o = oracle.verify_step(case.arrays, sh)
+    n_cmp, n_exc = _check_step(case, g, o)
+    assert n_exc <= max(1, sh.B // 16), (n_cmp, n_exc)
+
+
+@pytest.mark.parametrize("name", ["small", "llama8b", "ragged"])
+def test_verify_step_multi(name):
+    """The whole step with multi-candidate acceptance of the copy candidates (point-mass
+    drafts: the case's dense q is not passed) against the oracle's step."""
+    api = _api()
+    if name == "small":
+        sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
+    elif name == "llama8b":
+        sh, seed = wl.config(2), 2000
+    else:
+        sh, seed = wl.config(5), 5000
+    case = get_case(("step", name), lambda: wl.make_case(sh, seed))
+    I = _step_inputs(case, sh.temperature)
+    I["q_draft"] = None
+    say("verify_step multi", name)
+    step = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa,
+                          accept="multi")
+    g = step()
+    A = {k: v for k, v in case.arrays.items() if k != "q_draft"}
+    o = oracle.verify_step(A, sh, accept="multi")
     n_cmp, n_exc = _check_step(case, g, o)
     assert n_exc <= max(1, sh.B // 16), (n_cmp, n_exc)
 

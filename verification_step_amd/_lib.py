@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libvstep.so")
 
 VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = 0, -1, -2, -3, -4
 VS_F32, VS_BF16 = 0, 1
+VS_ACCEPT_LONGEST, VS_ACCEPT_MULTI = 0, 1
 
 FLAG_PROBE_TIE = 1
 FLAG_ACCEPT_TIE = 2
@@ -46,7 +47,8 @@ class HeadDesc(C.Structure):
 
 
 class SampleDesc(C.Structure):
-    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("V", I32), ("temperature", C.c_float)]
+    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("V", I32), ("temperature", C.c_float),
+                ("accept_mode", I32)]
 
 
 class StepDesc(C.Structure):
@@ -54,7 +56,7 @@ class StepDesc(C.Structure):
                 ("head_dim", I32), ("page_size", I32), ("max_pages", I32),
                 ("n_pool_pages", I32), ("d", I32), ("V", I32), ("dtype", I32),
                 ("scale", C.c_float), ("tau", C.c_float), ("temperature", C.c_float),
-                ("external_drafts", I32), ("ctx_total", C.c_int64)]
+                ("external_drafts", I32), ("ctx_total", C.c_int64), ("accept_mode", I32)]
 
 
 class StepIO(C.Structure):

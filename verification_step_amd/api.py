@@ -61,14 +61,19 @@ def _raise(st, where):
 _ws_cache = {}
 
 
-def workspace(nbytes: int, device=None, key: str = "default") -> torch.Tensor:
-    """A zero-initialised device workspace of at least nbytes, cached per device/key."""
+def workspace(nbytes: int, device=None, key: str = "default", layout=None) -> torch.Tensor:
+    """A device workspace of at least nbytes, cached per device/key.  The library needs
+    a workspace that is zero before its first use with a given layout (its calls leave
+    their counters at zero, but another shape places them elsewhere), so the cached
+    buffer is zeroed again whenever `layout` (the shape it is used for) changes."""
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     k = (dev.index, key)
-    ws = _ws_cache.get(k)
+    ws, last = _ws_cache.get(k, (None, None))
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _ws_cache[k] = ws
+    elif last != layout:
+        ws.zero_()
+    _ws_cache[k] = (ws, layout)
     return ws
 
 
@@ -136,7 +141,8 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, 
         out = torch.empty_like(q)
     flags = torch.empty(B, dtype=torch.int32, device=q.device)
     nbytes = lib.vs_attention_workspace_bytes(C.byref(desc))
-    ws = workspace(nbytes, q.device)
+    ws = workspace(nbytes, q.device, "attention",
+                   (B, W, D, Hq, Hkv, hd, page_table.shape[1], k_pool.shape[0], _vs_dtype(q)))
     st = lib.vs_verify_attention(C.byref(desc), _ptr(q), _ptr(k_cand), _ptr(v_cand), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(page_table), _ptr(prefix_len), _ptr(out),
                                  _ptr(flags), _ptr(ws), ws.numel(), _stream())
@@ -212,8 +218,19 @@ def lm_head(h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
     return LmHead(h, w_full, w_down, w_up, temperature, write_probs, V, rank)()
 
 
+_ACCEPT = {"longest": L.VS_ACCEPT_LONGEST, "multi": L.VS_ACCEPT_MULTI}
+
+
+def _accept_mode(accept: str) -> int:
+    if accept not in _ACCEPT:
+        raise ValueError(f"accept must be one of {sorted(_ACCEPT)}, got {accept!r}")
+    return _ACCEPT[accept]
+
+
 def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_res,
-                  temperature: float = 1.0, gate=None):
+                  temperature: float = 1.0, gate=None, accept: str = "longest"):
+    """accept = "longest" (each candidate judged alone, longest run kept) or "multi"
+    (lossless multi-candidate acceptance; copy drafts, q None, when W > 1)."""
     lib = L.load()
     _check(root_logits, torch.float32, "root_logits")
     _check(logits, torch.float32, "logits")
@@ -227,7 +244,7 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
     B, W, D = cand_tok.shape
     V = root_logits.shape[1]
     dev = root_logits.device
-    desc = L.SampleDesc(B, W, D, V, float(temperature))
+    desc = L.SampleDesc(B, W, D, V, float(temperature), _accept_mode(accept))
     out = dict(n_acc=torch.empty(B, dtype=torch.int32, device=dev),
                best=torch.empty(B, dtype=torch.int32, device=dev),
                out_tok=torch.empty((B, D + 1), dtype=torch.int32, device=dev),
@@ -235,7 +252,7 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
                acc_per_cand=torch.empty((B, W), dtype=torch.int32, device=dev),
                flags=torch.empty(B, dtype=torch.int32, device=dev))
     nbytes = lib.vs_sample_workspace_bytes(C.byref(desc))
-    ws = workspace(nbytes, dev, "sample")
+    ws = workspace(nbytes, dev, "sample", (B, W, D, V))
     st = lib.vs_reject_sample(C.byref(desc), _ptr(root_logits), _ptr(logits), _ptr(row_lse),
                               _ptr(q), _ptr(cand_tok), _ptr(cand_len), _ptr(u_acc), _ptr(u_res),
                               _ptr(gate), _ptr(out["n_acc"]), _ptr(out["best"]),
@@ -258,7 +275,8 @@ class VerifyStep:
 
     def __init__(self, inputs: dict, B: int, W: int, D: int, Hq: int, Hkv: int, hd: int,
                  V: int, tau: float = 0.4, temperature: float = 1.0, kappa: int = 5,
-                 external_drafts: bool = False, scale: float = 0.0, overlap: bool = False):
+                 external_drafts: bool = False, scale: float = 0.0, overlap: bool = False,
+                 accept: str = "longest"):
         self.lib = L.load()
         I = dict(inputs)
         if I["w_full"].dtype == torch.bfloat16 and I["w_full"].dim() == 2:
@@ -273,7 +291,8 @@ class VerifyStep:
         self.desc = L.StepDesc(B, W, D, kappa, Hq, Hkv, hd, 16, I["page_table"].shape[1],
                                I["k_pool"].shape[0], d, V, _vs_dtype(I["q"]), float(scale),
                                float(tau), float(temperature), int(external_drafts),
-                               I["ctx"].numel() if not external_drafts else 0)
+                               I["ctx"].numel() if not external_drafts else 0,
+                               _accept_mode(accept))
         self.out = dict(
             cand_tok=I["cand_tok"] if external_drafts else torch.empty((B, W, D), dtype=torch.int32, device=dev),
             cand_len=I["cand_len"] if external_drafts else torch.empty((B, W), dtype=torch.int32, device=dev),

@@ -56,8 +56,16 @@ int check_sample(const vs_sample_desc *d) {
   if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
   if (!(d->temperature > 0.f) || !isfinite(d->temperature)) return VS_ERR_INVALID_ARG;
   if (d->V > kMaxVocabSampler) return VS_ERR_UNSUPPORTED;
+  if (d->accept_mode != VS_ACCEPT_LONGEST && d->accept_mode != VS_ACCEPT_MULTI)
+    return VS_ERR_INVALID_ARG;
+  if (d->accept_mode == VS_ACCEPT_MULTI && d->W > 1 && !vs::sampler_multi_fits(d->W, d->D))
+    return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
+
+// the multi-candidate kernels run when there is more than one candidate (with one, the
+// rule is the single-chain rule); they take copy drafts only
+static bool sample_multi(int accept_mode, int W) { return accept_mode == VS_ACCEPT_MULTI && W > 1; }
 
 float attn_scale(float scale, int hd) { return scale > 0.f ? scale : 1.0f / sqrtf((float)hd); }
 
@@ -195,6 +203,8 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
   if (!root_logits || !logits || !row_lse || !cand_tok || !cand_len || !u_acc || !u_res ||
       !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
     return VS_ERR_INVALID_ARG;
+  const bool multi = sample_multi(d->accept_mode, d->W);
+  if (multi && q) return VS_ERR_UNSUPPORTED;
   const size_t need = vs_sample_workspace_bytes(d);
   if (!workspace || ws_bytes < need) return VS_ERR_WORKSPACE;
   const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->W, d->D, d->V);
@@ -204,11 +214,12 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
   // row_lse is an input here: only the root normalisers and the tests are computed
   e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, nullptr,
                            const_cast<double *>(row_lse), root_logits, logits, q, cand_tok,
-                           cand_len, gate, u_acc, sw, S(stream));
+                           cand_len, gate, u_acc, sw, S(stream), multi);
   if (e != hipSuccess) return VS_ERR_HIP;
   return hip_status(vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, root_logits, logits,
                                        row_lse, q, cand_tok, cand_len, u_res, gate, n_acc, best,
-                                       out_tok, n_out, acc_per_cand, flags, 0, sw, S(stream)));
+                                       out_tok, n_out, acc_per_cand, flags, 0, sw, S(stream),
+                                       nullptr, multi, u_acc));
 }
 
 static int check_step(const vs_step_desc *d) {
@@ -219,7 +230,7 @@ static int check_step(const vs_step_desc *d) {
   if (st != VS_OK) return st;
   vs_head_desc hd = {d->B * d->W * d->D, d->d, d->V, 0, d->dtype, d->temperature, 0};
   if ((st = check_head(&hd)) != VS_OK) return st;
-  vs_sample_desc sd = {d->B, d->W, d->D, d->V, d->temperature};
+  vs_sample_desc sd = {d->B, d->W, d->D, d->V, d->temperature, d->accept_mode};
   if ((st = check_sample(&sd)) != VS_OK) return st;
   if (d->d != d->Hq * d->head_dim) return VS_ERR_INVALID_ARG;
   if (!d->external_drafts) {
@@ -252,6 +263,8 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
       return VS_ERR_INVALID_ARG;
   }
   if (io->aux_stream && (!io->fork_event || !io->join_event)) return VS_ERR_INVALID_ARG;
+  const bool multi = sample_multi(d->accept_mode, d->W);
+  if (multi && io->q_draft) return VS_ERR_UNSUPPORTED;
   const StepLayout L = step_layout(d);
   if (!workspace || ws_bytes < L.total) return VS_ERR_WORKSPACE;
   hipStream_t s = S(stream);
@@ -313,14 +326,14 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   const int32_t *gate = d->external_drafts ? nullptr : io->gate;
   e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, hw.stats, io->row_lse,
                            io->root_logits, io->logits, io->q_draft, io->cand_tok, io->cand_len,
-                           gate, io->u_acc, sw, s);
+                           gate, io->u_acc, sw, s, multi);
   if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
-  // 5. longest accepted run and the extra token (flags: accumulate onto the gate's,
+  // 5. longest accepted run (or the multi-candidate chain) and the extra token (flags: accumulate onto the gate's,
   //    or written whole when there was no retrieval)
   e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
                          io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_res, gate,
                          io->n_acc, io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags,
-                         d->external_drafts ? 0 : 1, sw, s, sw.attn_flags);
+                         d->external_drafts ? 0 : 1, sw, s, sw.attn_flags, multi, io->u_acc);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
 }

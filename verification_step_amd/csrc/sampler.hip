@@ -12,6 +12,13 @@
 // normalisers, the acceptance comparison, and the inverse-CDF draw over ascending
 // token ids.
 //
+// Lossless multi-candidate acceptance (accept mode MULTI, copy drafts): at each depth
+// the surviving candidates' tokens are tried in index order against one target
+// distribution (the reference candidate's row) with the single-draft rule, each
+// rejection removing the rejected token's mass; the normaliser kernel computes p of
+// every candidate's token under every row, the chain itself is a short serial walk in
+// LDS, and the draw excludes the rejected tokens.
+//
 // Layout of the work: grid (vocabulary chunks, sequences).  Every workgroup of a
 // sequence repeats the (cheap) acceptance tests and the choice of candidate, then
 // sums the residual weights of its own vocabulary chunk with coalesced loads.  The
@@ -73,6 +80,7 @@ struct TestArgs {
   const int32_t *cand_tok, *cand_len, *gate;
   const double *u_acc;
   uint8_t *code;              // [B*W*D], or null: normalisers only
+  double *pv;                 // MULTI: [B][M+1 rows][W] p of every candidate's token
 };
 
 __device__ double lse_of_stats(const float2 *st, int n_vt, double *red) {
@@ -171,6 +179,31 @@ lse_tests_kernel(TestArgs a) {
     lse = a.row_lse[r];
   }
 
+  if (a.pv != nullptr) {
+    // MULTI: p under this row of every candidate's token at the depth the row judges
+    // (0 for the root row, o+1 for verify row (i, o)); -1 marks an out-of-range token,
+    // 0 a candidate without a token there
+    const int M = a.W * a.D;
+    const int depth = root ? 0 : (r % M) % a.D + 1;
+    const int rowidx = root ? M : r % M;
+    for (int j = tid; j < a.W; j += 256) {
+      double v = 0.0;
+      const bool open = (a.gate == nullptr) || a.gate[b] != 0;
+      int ln = open ? a.cand_len[(int64_t)b * a.W + j] : 0;
+      ln = ln < 0 ? 0 : (ln > a.D ? a.D : ln);
+      if (depth < ln) {
+        const int x = a.cand_tok[((int64_t)b * a.W + j) * a.D + depth];
+        if (x >= 0 && x < a.V) {
+          const float z = root ? a.root_logits[(int64_t)b * a.V + x] : a.logits[(int64_t)r * a.V + x];
+          v = exp((double)z * a.inv_t - lse);
+        } else {
+          v = -1.0;
+        }
+      }
+      a.pv[((int64_t)b * (M + 1) + rowidx) * a.W + j] = v;
+    }
+    return;
+  }
   if (tid < npos) store_test(a, first, b, root ? tid : i0, oo, lse);
   for (int t = tid + 256; t < npos; t += 256) store_test(a, load_pos(a, b, rrow, t, oo), b, t, oo, lse);
 }
@@ -192,6 +225,21 @@ struct SampShared {
 };
 
 enum { MODE_ROOT = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_TARGET = 3 };
+
+// MULTI: at most kMaxWMulti candidates; the p values [M+1][W] and the acceptance
+// uniforms [M] sit in dynamic LDS, at most kMaxMultiLds doubles
+constexpr int kMaxWMulti = 64;
+constexpr int kMaxMultiLds = 4096;
+
+__host__ __device__ constexpr int multi_lds_doubles(int W, int D) { return (W * D + 1) * W + W * D; }
+
+template <bool MULTI> struct SampSharedT : SampShared {};
+template <> struct SampSharedT<true> : SampShared {
+  int excl_tok[kMaxWMulti];           // tokens rejected at the final depth (mass removed)
+  int surv[kMaxWMulti];               // surviving candidates, ascending
+  int sib[kMaxWMulti];
+  int n_excl;
+};
 
 // fixed-order block sum of two values (every thread receives the totals)
 __device__ void block_sum2(SampShared &sh, double &a, double &b) {
@@ -236,6 +284,8 @@ struct SampArgs {
   const double *u_res;
   const int32_t *gate;
   const uint8_t *code;
+  const double *pv;      // MULTI: [B][M+1][W] (see TestArgs)
+  const double *u_acc;   // MULTI: [B, W, D]
   int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
   int flags_accumulate;
   int32_t *attn_flags;   // [B] or null: flags raised by attention, folded and reset here
@@ -246,79 +296,176 @@ struct SampArgs {
 
 enum { SAMP_FUSED = 0, SAMP_SUMS = 1, SAMP_DRAW = 2 };
 
-template <int PHASE>
+template <int PHASE, bool MULTI>
 __global__ void __launch_bounds__(kST)
 sampler_kernel(SampArgs a) {
-  __shared__ SampShared sh;
+  __shared__ SampSharedT<MULTI> sh;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int W = a.W, D = a.D, V = a.V, M = W * D;
   const float *root = a.root_logits + (int64_t)b * V;
 
-  // ---- one round of independent loads: lengths, acceptance codes, draft tokens, the
-  //      residual uniforms and the normalisers of every row
-  const bool open = (a.gate == nullptr) || a.gate[b] != 0;
-  if (tid == 0) sh.flags = 0;
-  for (int i = tid; i < W; i += kST) {
-    int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
-    ln = ln < 0 ? 0 : (ln > D ? D : ln);
-    sh.lens[i] = ln;
-    sh.a_len[i] = ln;
-    sh.ures[i] = a.u_res[(int64_t)b * W + i];
-  }
-  for (int idx = tid; idx < M; idx += kST) {
-    sh.code[idx] = a.code[(int64_t)b * M + idx];
-    sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
-    sh.rlse[idx] = a.row_lse[(int64_t)b * M + idx];
-  }
-  const double lse_root = a.root_lse[b];
-  __syncthreads();
-  // accepted run of each candidate: up to its first rejected position
-  for (int idx = tid; idx < M; idx += kST) {
-    const int i = idx / D, o = idx % D;
-    if (o < sh.lens[i] && !(sh.code[idx] & CODE_ACCEPT)) atomicMin(&sh.a_len[i], o);
-  }
-  __syncthreads();
-  int fl = 0;
-  for (int idx = tid; idx < M; idx += kST) {
-    const int i = idx / D, o = idx % D;
-    if (o >= sh.lens[i]) continue;
-    const uint8_t cd = sh.code[idx];
-    if (cd & CODE_BAD) fl |= FLAG_BAD_TOKEN;
-    if (o <= sh.a_len[i] && (cd & CODE_TIE)) fl |= FLAG_ACCEPT_TIE;
-  }
-  if (fl) atomicOr(&sh.flags, fl);
-
-  // ---- the chosen candidate and the distribution of the extra token
-  if (tid == 0) {
-    int best = -1;
-    for (int i = 0; i < W; ++i)
-      if (sh.lens[i] >= 1 && (best < 0 || sh.a_len[i] > sh.a_len[best])) best = i;
-    sh.best = best;
-    sh.qrow = -1;
-    sh.xpt = -1;
-    int prow_local = -1;
-    if (best < 0) {
-      sh.ab = 0;
-      sh.mode = MODE_ROOT;
-      sh.u = sh.ures[0];
-      atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
-    } else {
-      const int ab = sh.a_len[best];
-      sh.ab = ab;
-      sh.u = sh.ures[best];
-      prow_local = (ab == 0) ? -1 : best * D + ab - 1;
-      if (ab < sh.lens[best]) {
-        sh.mode = MODE_RESID;
-        if (a.q) sh.qrow = (int64_t)b * M + best * D + ab;
-        else sh.xpt = sh.tok[best * D + ab];
-      } else {
-        sh.mode = MODE_BONUS;
-      }
+  if constexpr (MULTI) {
+    extern __shared__ double multi_lds[];
+    double *pv = multi_lds;                      // [M+1][W]
+    double *uacc = multi_lds + (M + 1) * W;      // [M]
+    // ---- one round of loads: lengths, tokens, uniforms, normalisers, p values
+    const bool open = (a.gate == nullptr) || a.gate[b] != 0;
+    if (tid == 0) sh.flags = 0;
+    for (int i = tid; i < W; i += kST) {
+      int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
+      ln = ln < 0 ? 0 : (ln > D ? D : ln);
+      sh.lens[i] = ln;
+      sh.ures[i] = a.u_res[(int64_t)b * W + i];
     }
-    sh.prow = (prow_local < 0) ? -1 : (int64_t)b * M + prow_local;
-    sh.lse = (prow_local < 0) ? lse_root : sh.rlse[prow_local];
+    for (int idx = tid; idx < M; idx += kST) {
+      sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
+      sh.rlse[idx] = a.row_lse[(int64_t)b * M + idx];
+      uacc[idx] = a.u_acc[(int64_t)b * M + idx];
+    }
+    for (int k = tid; k < (M + 1) * W; k += kST) pv[k] = a.pv[(int64_t)b * (M + 1) * W + k];
+    const double lse_root = a.root_lse[b];
+    __syncthreads();
+    // ---- the chain (one thread): depth by depth, siblings in index order against the
+    //      reference row; each rejection removes its token's mass
+    if (tid == 0) {
+      int fl = 0;
+      int ns = 0;
+      for (int i = 0; i < W; ++i)
+        if (sh.lens[i] >= 1) sh.surv[ns++] = i;
+      sh.qrow = -1;
+      sh.xpt = -1;
+      sh.n_excl = 0;
+      int depth = 0, row = M;      // row M: the root distribution
+      if (ns == 0) {
+        sh.best = -1;
+        sh.mode = MODE_ROOT;
+        sh.u = sh.ures[0];
+        fl |= FLAG_NO_CANDIDATE;
+      } else {
+        while (true) {
+          const int ref = sh.surv[0];
+          row = (depth == 0) ? M : ref * D + depth - 1;
+          int nsib = 0;
+          for (int k = 0; k < ns; ++k)
+            if (sh.lens[sh.surv[k]] > depth) sh.sib[nsib++] = sh.surv[k];
+          if (nsib == 0) {
+            sh.mode = MODE_BONUS;
+            sh.u = sh.ures[ref];
+            break;
+          }
+          double removed = 0.0;
+          int n_excl = 0, last = sh.sib[0], acc = -1;
+          for (int k = 0; k < nsib; ++k) {
+            const int i = sh.sib[k];
+            last = i;
+            const int x = sh.tok[i * D + depth];
+            const double pvv = pv[row * W + i];
+            const bool valid = pvv >= 0.0;
+            bool dup = false;
+            for (int e = 0; e < n_excl; ++e) dup |= (sh.excl_tok[e] == x);
+            if (!valid) fl |= FLAG_BAD_TOKEN;
+            const double pp = (valid && !dup) ? pvv / (1.0 - removed) : 0.0;
+            const double lhs = uacc[i * D + depth];
+            if (fabs(lhs - pp) < 1e-4 * fmax(pp, lhs)) fl |= FLAG_ACCEPT_TIE;
+            if (lhs < pp) {
+              acc = x;
+              break;
+            }
+            if (valid && !dup) {
+              if (1.0 - (removed + pvv) > 0.0) {
+                removed += pvv;
+                sh.excl_tok[n_excl++] = x;
+              } else {
+                fl |= FLAG_DEGENERATE;
+              }
+            }
+          }
+          if (acc < 0) {
+            sh.mode = MODE_RESID;
+            sh.u = sh.ures[last];
+            sh.n_excl = n_excl;
+            break;
+          }
+          ns = 0;
+          for (int k = 0; k < nsib; ++k)
+            if (sh.tok[sh.sib[k] * D + depth] == acc) sh.surv[ns++] = sh.sib[k];
+          ++depth;
+        }
+        sh.best = sh.surv[0];
+      }
+      sh.ab = depth;
+      sh.prow = (row == M) ? -1 : (int64_t)b * M + row;
+      sh.lse = (row == M) ? lse_root : sh.rlse[row];
+      if (fl) atomicOr(&sh.flags, fl);
+    }
+  } else {
+    // ---- one round of independent loads: lengths, acceptance codes, draft tokens, the
+    //      residual uniforms and the normalisers of every row
+    const bool open = (a.gate == nullptr) || a.gate[b] != 0;
+    if (tid == 0) sh.flags = 0;
+    for (int i = tid; i < W; i += kST) {
+      int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
+      ln = ln < 0 ? 0 : (ln > D ? D : ln);
+      sh.lens[i] = ln;
+      sh.a_len[i] = ln;
+      sh.ures[i] = a.u_res[(int64_t)b * W + i];
+    }
+    for (int idx = tid; idx < M; idx += kST) {
+      sh.code[idx] = a.code[(int64_t)b * M + idx];
+      sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
+      sh.rlse[idx] = a.row_lse[(int64_t)b * M + idx];
+    }
+    const double lse_root = a.root_lse[b];
+    __syncthreads();
+    // accepted run of each candidate: up to its first rejected position
+    for (int idx = tid; idx < M; idx += kST) {
+      const int i = idx / D, o = idx % D;
+      if (o < sh.lens[i] && !(sh.code[idx] & CODE_ACCEPT)) atomicMin(&sh.a_len[i], o);
+    }
+    __syncthreads();
+    int fl = 0;
+    for (int idx = tid; idx < M; idx += kST) {
+      const int i = idx / D, o = idx % D;
+      if (o >= sh.lens[i]) continue;
+      const uint8_t cd = sh.code[idx];
+      if (cd & CODE_BAD) fl |= FLAG_BAD_TOKEN;
+      if (o <= sh.a_len[i] && (cd & CODE_TIE)) fl |= FLAG_ACCEPT_TIE;
+    }
+    if (fl) atomicOr(&sh.flags, fl);
+
+    // ---- the chosen candidate and the distribution of the extra token
+    if (tid == 0) {
+      int best = -1;
+      for (int i = 0; i < W; ++i)
+        if (sh.lens[i] >= 1 && (best < 0 || sh.a_len[i] > sh.a_len[best])) best = i;
+      sh.best = best;
+      sh.qrow = -1;
+      sh.xpt = -1;
+      int prow_local = -1;
+      if (best < 0) {
+        sh.ab = 0;
+        sh.mode = MODE_ROOT;
+        sh.u = sh.ures[0];
+        atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
+      } else {
+        const int ab = sh.a_len[best];
+        sh.ab = ab;
+        sh.u = sh.ures[best];
+        prow_local = (ab == 0) ? -1 : best * D + ab - 1;
+        if (ab < sh.lens[best]) {
+          sh.mode = MODE_RESID;
+          if (a.q) sh.qrow = (int64_t)b * M + best * D + ab;
+          else sh.xpt = sh.tok[best * D + ab];
+        } else {
+          sh.mode = MODE_BONUS;
+        }
+      }
+      sh.prow = (prow_local < 0) ? -1 : (int64_t)b * M + prow_local;
+      sh.lse = (prow_local < 0) ? lse_root : sh.rlse[prow_local];
+    }
+
   }
   __syncthreads();
   const float *zrow = (sh.prow < 0) ? root : a.logits + sh.prow * V;
@@ -326,6 +473,8 @@ sampler_kernel(SampArgs a) {
   const float *qrow = (sh.qrow < 0) ? nullptr : a.q + sh.qrow * V;
   const int xpt = sh.xpt;
   const bool resid = sh.mode == MODE_RESID;
+  int n_excl = 0;
+  if constexpr (MULTI) n_excl = sh.n_excl;
 
   // target probability and residual weight of the kPer ids k0 .. k0+kPer-1 (ids at or
   // past V weigh nothing)
@@ -363,7 +512,15 @@ sampler_kernel(SampArgs a) {
       }
       pk[j] = exp((double)z[j] * a.inv_t - lse);
       if (resid) {
-        const double qk = qrow ? (double)qv[j] : (k == xpt ? 1.0 : 0.0);
+        double qk;
+        if constexpr (MULTI) {
+          // the rejected tokens' point masses, each removed in turn
+          bool ex = false;
+          for (int e = 0; e < n_excl; ++e) ex |= (sh.excl_tok[e] == k);
+          qk = ex ? 1.0 : 0.0;
+        } else {
+          qk = qrow ? (double)qv[j] : (k == xpt ? 1.0 : 0.0);
+        }
         rk[j] = fmax(0.0, pk[j] - qk);
       } else {
         rk[j] = pk[j];
@@ -501,8 +658,17 @@ sampler_kernel(SampArgs a) {
   int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
   for (int o = tid; o <= D; o += kST)
     ot[o] = (o < ab) ? sh.tok[best * D + o] : (o == ab ? yy : -1);
-  for (int i = tid; i < W; i += kST)
-    a.acc_per_cand[(int64_t)b * W + i] = (sh.lens[i] >= 1) ? sh.a_len[i] : 0;
+  for (int i = tid; i < W; i += kST) {
+    int k = 0;
+    if constexpr (MULTI) {
+      // common prefix with the emitted accepted tokens (those of the final reference)
+      const int lim = min(sh.lens[i], ab);
+      while (k < lim && sh.tok[i * D + k] == sh.tok[best * D + k]) ++k;
+    } else {
+      k = (sh.lens[i] >= 1) ? sh.a_len[i] : 0;
+    }
+    a.acc_per_cand[(int64_t)b * W + i] = k;
+  }
 }
 
 // (max, sum exp(x - max)) of x = logits/T over one vocabulary tile, for B rows;
@@ -555,8 +721,14 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
   off += ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
   w.thread_sums = (double2 *)(p + off);
   off += ((size_t)B * nch * kST * sizeof(double2) + 255) & ~(size_t)255;
+  w.pv = (double *)(p + off);
+  off += ((size_t)B * (W * D + 1) * W * sizeof(double) + 255) & ~(size_t)255;
   w.bytes = off;
   return w;
+}
+
+bool sampler_multi_fits(int W, int D) {
+  return W <= kMaxWMulti && multi_lds_doubles(W, D) <= kMaxMultiLds;
 }
 
 size_t sample_workspace_bytes(int B, int W, int D, int V) {
@@ -589,7 +761,7 @@ hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
                             const float2 *row_stats, double *row_lse, const float *root_logits,
                             const float *logits, const float *q, const int32_t *cand_tok,
                             const int32_t *cand_len, const int32_t *gate, const double *u_acc,
-                            const SampleWs &ws, hipStream_t st) {
+                            const SampleWs &ws, hipStream_t st, bool multi) {
   TestArgs a{};
   a.B = B;
   a.W = W;
@@ -608,7 +780,8 @@ hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
   a.cand_len = cand_len;
   a.gate = gate;
   a.u_acc = u_acc;
-  a.code = ws.code;
+  a.code = multi ? nullptr : ws.code;
+  a.pv = multi ? ws.pv : nullptr;
   hipLaunchKernelGGL(lse_tests_kernel, dim3(B * W * D + B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -619,7 +792,7 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
                           int flags_accumulate, const SampleWs &ws, hipStream_t st,
-                          int32_t *attn_flags) {
+                          int32_t *attn_flags, bool multi, const double *u_acc) {
   SampArgs a;
   a.B = B;
   a.W = W;
@@ -637,6 +810,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.u_res = u_res;
   a.gate = gate;
   a.code = ws.code;
+  a.pv = ws.pv;
+  a.u_acc = u_acc;
   a.n_acc = n_acc;
   a.best = best;
   a.out_tok = out_tok;
@@ -652,13 +827,24 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   // V = 128256 is faster fused, B = 32 far faster in two launches)
   bool two = (int64_t)a.nch * B > 256;
   if (const char *ov = getenv("VSTEP_SAMPLER_TWO_PASS")) two = atoi(ov) != 0;
-  if (!two) {
-    hipLaunchKernelGGL(sampler_kernel<SAMP_FUSED>, dim3(a.nch, B), dim3(kST), 0, st, a);
+  if (multi) {
+    const size_t lds = (size_t)multi_lds_doubles(W, D) * sizeof(double);
+    if (!two) {
+      hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, true>), dim3(a.nch, B), dim3(kST), lds, st, a);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, true>), dim3(a.nch, B), dim3(kST), lds, st, a);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, true>), dim3(1, B), dim3(kST), lds, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(sampler_kernel<SAMP_SUMS>, dim3(a.nch, B), dim3(kST), 0, st, a);
+  if (!two) {
+    hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, false>), dim3(a.nch, B), dim3(kST), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, false>), dim3(a.nch, B), dim3(kST), 0, st, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL(sampler_kernel<SAMP_DRAW>, dim3(1, B), dim3(kST), 0, st, a);
+  hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, false>), dim3(1, B), dim3(kST), 0, st, a);
   return hipGetLastError();
 }
 

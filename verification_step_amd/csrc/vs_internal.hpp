@@ -153,10 +153,13 @@ struct SampleWs {
   uint8_t *code;        // [B][W][D] acceptance codes
   int32_t *attn_flags;  // [B] flags raised by attention inside the step, zero between calls
   double2 *thread_sums; // [B][n_chunks][256] per-thread weight sums of the sampler
+  double *pv;           // [B][W*D+1][W] multi-candidate acceptance: p of each candidate token
   size_t bytes;
 };
 SampleWs sample_ws(void *ws, int B, int W, int D, int V);
 size_t sample_workspace_bytes(int B, int W, int D, int V);
+// whether the multi-candidate acceptance handles W candidates of D tokens
+bool sampler_multi_fits(int W, int D);
 hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
                              float2 *stats, hipStream_t st);
 // fp64 row normalisers from tile statistics [rows][n_vt]
@@ -164,20 +167,23 @@ hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *l
                                  hipStream_t st);
 // Normalisers of the verify rows (row_stats != null; else row_lse is an input) and of
 // the root rows (ws.root_stats -> ws.root_lse), and the acceptance test of every draft
-// position (-> ws.code).
+// position (-> ws.code), or with multi the p of every candidate token under every row
+// (-> ws.pv).
 hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
                             const float2 *row_stats, double *row_lse, const float *root_logits,
                             const float *logits, const float *q, const int32_t *cand_tok,
                             const int32_t *cand_len, const int32_t *gate, const double *u_acc,
-                            const SampleWs &ws, hipStream_t st);
-// Longest accepted run, residual / bonus draw, outputs (reads ws.code, ws.root_lse).
+                            const SampleWs &ws, hipStream_t st, bool multi = false);
+// Longest accepted run (or with multi the multi-candidate chain over ws.pv and u_acc),
+// residual / bonus draw, outputs (reads ws.code, ws.root_lse).
 hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
                           const float *logits, const double *row_lse, const float *q,
                           const int32_t *cand_tok, const int32_t *cand_len, const double *u_res,
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
                           int flags_accumulate, const SampleWs &ws, hipStream_t st,
-                          int32_t *attn_flags = nullptr);
+                          int32_t *attn_flags = nullptr, bool multi = false,
+                          const double *u_acc = nullptr);
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 

@@ -73,7 +73,7 @@ def upload(case):
     return out
 
 
-def cpu_baseline(case, shape, drafts=None, min_seconds=10.0):
+def cpu_baseline(case, shape, drafts=None, min_seconds=10.0, accept="longest"):
     """The CPU oracle, as it stands, on full steps of the same inputs, repeated until at
     least `min_seconds` of CPU work have been timed.  With external drafts a step is the
     oracle's low-rank draft head followed by its verify step over the given drafts."""
@@ -89,6 +89,8 @@ def cpu_baseline(case, shape, drafts=None, min_seconds=10.0):
     if not threads:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     A = case.arrays
+    if accept == "multi" and not shape.external_drafts:
+        A = {k: v for k, v in A.items() if k != "q_draft"}     # copy drafts: point masses
     sh = shape
     n = 0
     t0 = time.perf_counter()
@@ -98,9 +100,9 @@ def cpu_baseline(case, shape, drafts=None, min_seconds=10.0):
                                              A["w_up"])
             A2 = dict(A)
             A2["q_draft"] = oracle.head_softmax(z, l).astype(np.float32)
-            oracle.verify_step(A2, sh, drafts=drafts)
+            oracle.verify_step(A2, sh, drafts=drafts, accept=accept)
         else:
-            oracle.verify_step(A, sh)
+            oracle.verify_step(A, sh, accept=accept)
         n += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -179,6 +181,9 @@ def main():
     ap.add_argument("--kv-buffers", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--head-copies", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--accept", choices=["longest", "multi"], default="longest",
+                    help="longest verified run (default) or lossless multi-candidate "
+                         "acceptance (copy candidates as point-mass drafts)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -215,9 +220,11 @@ def main():
     I = upload(case)
     B, W, D, M = sh.B, sh.W, sh.D, sh.M
     draft, drafts = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else (None, None)
+    if args.accept == "multi" and not sh.external_drafts:
+        I["q_draft"] = None                      # copy candidates judged as point masses
     step = api.VerifyStep(I, B=B, W=W, D=D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V, tau=sh.tau,
                           temperature=sh.temperature, kappa=sh.kappa,
-                          external_drafts=sh.external_drafts)
+                          external_drafts=sh.external_drafts, accept=args.accept)
     mdt = I["q"].dtype
     esz = I["q"].element_size()
 
@@ -326,6 +333,8 @@ def main():
               "kv_buffers": len(pools), "head_copies": len(heads),
               "timing": "hip events on the step stream, no graph; value from a pass "
                         "without stage events, stages from a second pass with them"}
+    if args.accept != "longest":
+        config["accept"] = args.accept
     if draft is not None:
         config.update({"draft_head": "low-rank r=%d, gamma=%d, probabilities into q"
                                      % (sh.rank, sh.gamma), "drafts": "external"})
@@ -356,7 +365,7 @@ def main():
         "accepted": [int(x) for x in out["n_acc"].cpu().tolist()][:4],
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(case, sh, drafts)
+        rec["cpu_baseline"] = cpu_baseline(case, sh, drafts, accept=args.accept)
     print(json.dumps(rec), flush=True)
 
 

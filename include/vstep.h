@@ -72,7 +72,7 @@ enum {
     VS_FLAG_NO_CANDIDATE = 16,        /* gate closed or no candidate: one token from the root p */
     VS_FLAG_BAD_PAGE = 32,            /* page index outside the pool, or prefix_len out of range */
     VS_FLAG_BAD_CTX = 64,             /* context offsets outside [0, ctx_total] or decreasing */
-    VS_FLAG_BAD_TOKEN = 128           /* candidate token id outside [0, V): treated as rejected */
+    VS_FLAG_BAD_TOKEN = 128           /* a tested candidate token id is outside [0, V): rejected */
 };
 
 int         vs_abi_version(void);

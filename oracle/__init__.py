@@ -9,5 +9,5 @@ from .verify_oracle import (  # noqa: F401
     FLAG_BAD_PAGE, FLAG_BAD_CTX, FLAG_BAD_TOKEN,
     bf16_bits_to_f64, round_f64_to_bf16, as_f64,
     copy_match, probe_gate, verify_attention, lm_head_full, lm_head_lowrank,
-    head_softmax, reject_sample, reject_sample_multi, verify_step,
+    head_softmax, reject_sample, reject_sample_multi, reject_sample_greedy, verify_step,
 )

@@ -47,6 +47,7 @@ FLAG_BAD_TOKEN = 128        # candidate token id outside [0, V)
 PROBE_TIE_EPS = 1e-5
 ACCEPT_TIE_REL = 1e-4
 CDF_TIE_EPS = 1e-8
+GREEDY_TIE_REL = 1e-3       # greedy: top two logits of a row closer than this (x max(1, |top|))
 
 
 # ----------------------------------------------------------------------------------
@@ -531,14 +532,100 @@ def reject_sample_multi(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res
     return out
 
 
+def _row_argmax(z: np.ndarray):
+    """First index of the largest value, and whether the two largest values are within
+    GREEDY_TIE_REL * max(1, |largest|) of each other (a near tie)."""
+    z = np.asarray(z, dtype=np.float64)
+    k = int(np.argmax(z))
+    if z.size < 2:
+        return k, False
+    top2 = np.partition(z, z.size - 2)[-2:]
+    gap = float(top2[1] - top2[0])
+    return k, gap < GREEDY_TIE_REL * max(1.0, abs(float(top2[1])))
+
+
+def reject_sample_greedy(root_logits, logits, cand_tok, cand_len, gate=None):
+    """Greedy verification (temperature 0).
+
+    The limit T -> 0 of section 3's rule [SD], where every target p becomes the point
+    mass on its row's argmax: a draft token is accepted iff it is the argmax of the
+    preceding row (root for offset 0, row (i, o-1) otherwise), a candidate's run
+    stops at its first other token ([EX] step 2: cut at the first mismatch), and the
+    extra token is the argmax of the row after the run (the residual of a point mass
+    p against any rejected draft is that same point mass, and so is the bonus p).
+    The draft distribution and the uniforms play no part.  Over W candidates the
+    longest run is kept (ties: smallest index), and since every p is a point mass
+    this emits exactly what plain greedy decoding emits, for any W.
+
+    argmax is taken over the fp32 logits as given, first index among equal maxima.
+    A tested position whose row has a near tie (_row_argmax) flags ACCEPT_TIE; a near
+    tie in the row of the extra token flags CDF_TIE.  Same outputs as reject_sample."""
+    root_logits = np.asarray(root_logits, dtype=np.float32)
+    logits = np.asarray(logits, dtype=np.float32)
+    B, W, D = cand_tok.shape
+    V = root_logits.shape[1]
+    M = W * D
+    out = dict(
+        n_acc=np.zeros(B, dtype=np.int32), best=np.full(B, -1, dtype=np.int32),
+        out_tok=np.full((B, D + 1), -1, dtype=np.int32), n_out=np.zeros(B, dtype=np.int32),
+        acc_per_cand=np.zeros((B, W), dtype=np.int32), flags=np.zeros(B, dtype=np.int32),
+    )
+
+    def row(b, prow):
+        return root_logits[b] if prow < 0 else logits[b * M + prow]
+
+    for b in range(B):
+        flags = 0
+        lens = np.clip(np.asarray(cand_len[b]).copy(), 0, D)
+        if gate is not None and not gate[b]:
+            lens[:] = 0
+        a = np.zeros(W, dtype=np.int64)
+        for i in range(W):
+            a[i] = lens[i]
+            for o in range(lens[i]):
+                x = int(cand_tok[b, i, o])
+                g, tie = _row_argmax(row(b, -1 if o == 0 else i * D + o - 1))
+                if tie:
+                    flags |= FLAG_ACCEPT_TIE
+                if not (0 <= x < V):
+                    flags |= FLAG_BAD_TOKEN
+                if x != g:
+                    a[i] = o
+                    break
+        out["acc_per_cand"][b] = a
+        have = [i for i in range(W) if lens[i] >= 1]
+        if not have:
+            y, tie = _row_argmax(row(b, -1))
+            out["out_tok"][b, 0] = y
+            out["n_out"][b] = 1
+            out["flags"][b] = FLAG_NO_CANDIDATE | (FLAG_CDF_TIE if tie else 0)
+            continue
+        best = have[0]
+        for i in have:
+            if a[i] > a[best]:
+                best = i
+        ab = int(a[best])
+        y, tie = _row_argmax(row(b, -1 if ab == 0 else best * D + ab - 1))
+        if tie:
+            flags |= FLAG_CDF_TIE
+        out["best"][b] = best
+        out["n_acc"][b] = ab
+        out["out_tok"][b, :ab] = cand_tok[b, best, :ab]
+        out["out_tok"][b, ab] = y
+        out["n_out"][b] = ab + 1
+        out["flags"][b] = flags
+    return out
+
+
 # ----------------------------------------------------------------------------------
 # a7: the whole verify step
 
 def verify_step(case_arrays: dict, shape, drafts=None, q_override=None, accept: str = "longest"):
     """copy_match -> probe_gate -> verify_attention -> lm_head -> reject_sample on one
     batch.  `drafts` = (cand_tok, cand_len) for the neural-draft path (copy retrieval
-    skipped, gate open).  accept = "longest" (the pages' longest verified run) or
-    "multi" (reject_sample_multi).  Returns every stage's outputs."""
+    skipped, gate open).  accept = "longest" (the pages' longest verified run),
+    "multi" (reject_sample_multi) or "greedy" (reject_sample_greedy).  Returns every
+    stage's outputs."""
     A = case_arrays
     sh = shape
     res = {}
@@ -557,9 +644,12 @@ def verify_step(case_arrays: dict, shape, drafts=None, q_override=None, accept: 
     H = O_r.reshape(O_r.shape[0], -1)
     logits, lse = lm_head_full(H, A["w_full"], sh.temperature, sh.dtype)
     q = q_override if q_override is not None else A.get("q_draft")
-    rule = reject_sample_multi if accept == "multi" else reject_sample
-    rs = rule(A["root_logits"], logits, q, cand_tok, cand_len, A["u_acc"], A["u_res"],
-              sh.temperature, gate)
+    if accept == "greedy":
+        rs = reject_sample_greedy(A["root_logits"], logits, cand_tok, cand_len, gate)
+    else:
+        rule = reject_sample_multi if accept == "multi" else reject_sample
+        rs = rule(A["root_logits"], logits, q, cand_tok, cand_len, A["u_acc"], A["u_res"],
+                  sh.temperature, gate)
     res.update(attn=O_r, attn_exact=O, attn_flags=aflags, logits=logits, lse=lse, sample=rs,
                cand_tok=cand_tok, cand_len=cand_len, gate=gate)
     return res

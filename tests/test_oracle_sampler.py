@@ -442,3 +442,133 @@ def test_multi_greedy_limit():
     assert r["n_acc"][0] == 2 and r["best"][0] == 1
     assert r["out_tok"][0].tolist() == [4, 1, 5, -1]
     assert r["acc_per_cand"][0].tolist() == [1, 2, 0]
+
+
+# ----------------------------------------------------------------- greedy (T = 0)
+
+def _spread_rows(rng, n, V, gap=0.05):
+    """Random logits whose largest value leads the next by at least `gap`."""
+    z = rng.standard_normal((n, V))
+    k = z.argmax(axis=1)
+    second = np.partition(z, V - 2, axis=1)[:, -2]
+    z[np.arange(n), k] = np.maximum(z[np.arange(n), k], second + gap)
+    return z.astype(np.float32)
+
+
+@pytest.mark.parametrize("qmode", ["point", "dense"])
+def test_greedy_is_the_zero_temperature_limit(qmode):
+    """reject_sample at T = 1e-3 on rows whose top two logits are >= 0.05 apart gives
+    every p(non-argmax) < exp(-50): whatever the uniforms and the draft distribution,
+    it must emit what the greedy rule emits."""
+    rng = np.random.default_rng(40)
+    B, W, D, V = 60, 3, 4, 50
+    M = W * D
+    root = _spread_rows(rng, B, V)
+    logits = _spread_rows(rng, B * M, V)
+    cand = rng.integers(0, V, size=(B, W, D)).astype(np.int32)
+    # make many tokens the argmax of their preceding row, so that runs are long
+    for b in range(B):
+        for i in range(W):
+            for o in range(D):
+                if rng.random() < 0.7:
+                    r = root[b] if o == 0 else logits[b * M + i * D + o - 1]
+                    cand[b, i, o] = int(np.argmax(r))
+    clen = rng.integers(0, D + 1, size=(B, W)).astype(np.int32)
+    q = None
+    if qmode == "dense":
+        q = rng.dirichlet(np.ones(V), size=B * M).astype(np.float32)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    s = oracle.reject_sample(root, logits, q, cand, clen, ua, ur, 1e-3)
+    g = oracle.reject_sample_greedy(root, logits, cand, clen)
+    for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand"):
+        assert np.array_equal(s[k], g[k]), k
+    assert (g["n_acc"] >= 2).sum() > B // 4
+    assert not (g["flags"] & (oracle.FLAG_ACCEPT_TIE | oracle.FLAG_CDF_TIE)).any()
+
+
+def _tree_model(V, seed):
+    """A toy deterministic model: the logits after a context depend only on the
+    context's tokens."""
+    def f(prefix):
+        h = (seed * 1000003 + len(prefix)) & 0xFFFFFFFF
+        for t in prefix:
+            h = (h * 2654435761 + int(t) + 1) & 0xFFFFFFFF
+        return np.random.default_rng(h).standard_normal(V).astype(np.float32)
+    return f
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_greedy_equals_plain_greedy_decoding(seed):
+    """Under a model whose logits depend only on the context, greedy verification of W
+    candidates emits a prefix of plain greedy decoding, as long as the longest
+    candidate agreement plus one; the multi-candidate rule at T -> 0 emits the same."""
+    V, W, D = 12, 4, 6
+    f = _tree_model(V, seed)
+    gd = []
+    for _ in range(D + 1):
+        gd.append(int(np.argmax(f(gd))))
+    rng = np.random.default_rng(seed)
+    cand = np.zeros((1, W, D), dtype=np.int32)
+    for i in range(W):
+        k = int(rng.integers(0, D + 1))              # agree with greedy for k tokens
+        cand[0, i, :k] = gd[:k]
+        for o in range(k, D):
+            cand[0, i, o] = int(rng.integers(0, V))
+    clen = rng.integers(1, D + 1, size=(1, W)).astype(np.int32)
+    root = f([])[None, :]
+    logits = np.stack([f(cand[0, i, :o + 1]) for i in range(W) for o in range(D)])
+    g = oracle.reject_sample_greedy(root, logits, cand, clen)
+    agree = []
+    for i in range(W):
+        k = 0
+        while k < clen[0, i] and cand[0, i, k] == gd[k]:
+            k += 1
+        agree.append(k)
+    n = g["n_out"][0]
+    assert g["n_acc"][0] == max(agree) and n == max(agree) + 1
+    assert g["out_tok"][0, :n].tolist() == gd[:n]
+    assert g["acc_per_cand"][0].tolist() == agree
+    m = oracle.reject_sample_multi(root, logits, None, cand, clen, np.full((1, W, D), 0.5),
+                                   np.full((1, W), 0.5), 1e-3)
+    assert m["n_acc"][0] == g["n_acc"][0]
+    assert m["out_tok"][0].tolist() == g["out_tok"][0].tolist()
+
+
+def test_greedy_ties_take_first_index_and_flag():
+    V, W, D = 8, 2, 2
+    z = np.zeros(V, np.float32)
+    z[[2, 5]] = 3.0                                   # exact tie: argmax is 2
+    zc = np.zeros(V, np.float32)
+    zc[6] = 1.0
+    zc[1] = 1.0 - 5e-4                                # near tie (within 1e-3)
+    root = z[None, :]
+    logits = np.stack([zc, zc, zc, zc])
+    # candidate 0 proposes 5 (rejected against the tie), candidate 1 proposes 2 then 6
+    cand = np.array([[[5, 0], [2, 6]]], np.int32)
+    g = oracle.reject_sample_greedy(root, logits, cand, np.array([[2, 2]], np.int32))
+    assert g["acc_per_cand"][0].tolist() == [0, 2]
+    assert g["best"][0] == 1 and g["out_tok"][0].tolist() == [2, 6, 6]
+    assert g["flags"][0] & oracle.FLAG_ACCEPT_TIE and g["flags"][0] & oracle.FLAG_CDF_TIE
+    # no tie anywhere: no flags
+    g2 = oracle.reject_sample_greedy(np.eye(V, dtype=np.float32)[3][None, :] * 4,
+                                     np.tile(np.eye(V, dtype=np.float32)[7] * 4, (4, 1)),
+                                     np.array([[[3, 7], [3, 1]]], np.int32),
+                                     np.array([[2, 2]], np.int32))
+    assert g2["flags"][0] == 0 and g2["out_tok"][0].tolist() == [3, 7, 7]
+    assert g2["acc_per_cand"][0].tolist() == [2, 1]
+
+
+def test_greedy_no_candidate_and_bad_token():
+    V, W, D = 6, 2, 3
+    root = np.array([[0, 1, 0, 4, 0, 0]], np.float32)
+    logits = np.tile(np.array([5, 0, 0, 0, 0, 0], np.float32), (W * D, 1))
+    cand = np.array([[[3, 0, 0], [3, 99, 0]]], np.int32)
+    clen = np.array([[3, 3]], np.int32)
+    g = oracle.reject_sample_greedy(root, logits, cand, clen, gate=np.array([0]))
+    assert g["n_acc"][0] == 0 and g["best"][0] == -1 and g["out_tok"][0, 0] == 3
+    assert g["flags"][0] == oracle.FLAG_NO_CANDIDATE
+    g = oracle.reject_sample_greedy(root, logits, cand, clen)
+    assert g["acc_per_cand"][0].tolist() == [3, 1]
+    assert g["flags"][0] == oracle.FLAG_BAD_TOKEN
+    assert g["out_tok"][0].tolist() == [3, 0, 0, 0]

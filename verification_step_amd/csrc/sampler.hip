@@ -429,9 +429,11 @@ sampler_kernel(SampArgs a) {
     for (int idx = tid; idx < M; idx += kST) {
       const int i = idx / D, o = idx % D;
       if (o >= sh.lens[i]) continue;
+      // only the tested positions (up to the first rejection) raise flags
+      if (o > sh.a_len[i]) continue;
       const uint8_t cd = sh.code[idx];
       if (cd & CODE_BAD) fl |= FLAG_BAD_TOKEN;
-      if (o <= sh.a_len[i] && (cd & CODE_TIE)) fl |= FLAG_ACCEPT_TIE;
+      if (cd & CODE_TIE) fl |= FLAG_ACCEPT_TIE;
     }
     if (fl) atomicOr(&sh.flags, fl);
 

@@ -181,9 +181,9 @@ def main():
     ap.add_argument("--kv-buffers", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--head-copies", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--accept", choices=["longest", "multi"], default="longest",
-                    help="longest verified run (default) or lossless multi-candidate "
-                         "acceptance (copy candidates as point-mass drafts)")
+    ap.add_argument("--accept", choices=["longest", "multi", "greedy"], default="longest",
+                    help="longest verified run (default), lossless multi-candidate "
+                         "acceptance (copy candidates as point-mass drafts) or greedy")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -222,6 +222,9 @@ def main():
     draft, drafts = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else (None, None)
     if args.accept == "multi" and not sh.external_drafts:
         I["q_draft"] = None                      # copy candidates judged as point masses
+    if args.accept == "greedy":
+        for k in ("q_draft", "u_acc", "u_res"):  # argmax tests: nothing random is read
+            I[k] = None
     step = api.VerifyStep(I, B=B, W=W, D=D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V, tau=sh.tau,
                           temperature=sh.temperature, kappa=sh.kappa,
                           external_drafts=sh.external_drafts, accept=args.accept)

@@ -58,7 +58,8 @@ typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
 /* How the sampler chooses among W candidates (vs_sample_desc / vs_step_desc). */
 typedef enum {
     VS_ACCEPT_LONGEST = 0,   /* each candidate judged alone; the longest accepted run wins */
-    VS_ACCEPT_MULTI = 1      /* lossless multi-candidate acceptance (see vs_reject_sample) */
+    VS_ACCEPT_MULTI = 1,     /* lossless multi-candidate acceptance (see vs_reject_sample) */
+    VS_ACCEPT_GREEDY = 2     /* greedy verification, temperature 0 (see vs_reject_sample) */
 } vs_accept_mode;
 
 /* Per-sequence device flags (bitwise OR). */
@@ -209,7 +210,17 @@ int vs_lm_head(const vs_head_desc *desc, const void *h, const void *w_full,
  * acc_per_cand[b,i] = the length of candidate i's common prefix with the accepted
  * tokens.  Copy drafts only (q == NULL) when W > 1 (else VS_ERR_UNSUPPORTED), at
  * most 64 candidates and (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); with
- * W == 1 the rule is the single-chain rule above, which is what runs. */
+ * W == 1 the rule is the single-chain rule above, which is what runs.
+ *
+ * accept_mode VS_ACCEPT_GREEDY: greedy verification, the temperature -> 0 limit of
+ * the rule above [SD section 3] (every p becomes the point mass on its row's argmax):
+ * draft x at offset o is accepted iff x is the argmax of the preceding row, a
+ * candidate's run stops at its first other token, the longest run wins (ties:
+ * smallest i) and the extra token is the argmax of the row after the run (root for
+ * a = 0).  argmax = first index of the largest fp32 logit.  q, u_acc and u_res are
+ * not read (may be NULL); temperature (> 0) only scales the normalisers computed on
+ * the way.  A tested row, or the extra token's row, whose two largest logits are
+ * within 1e-3 * max(1, |largest|) raises VS_FLAG_ACCEPT_TIE, resp. VS_FLAG_CDF_TIE. */
 typedef struct {
     int32_t B, W, D, V;
     float temperature;
@@ -250,7 +261,8 @@ typedef struct {
     float temperature;
     int32_t external_drafts;
     int64_t ctx_total;
-    int32_t accept_mode;      /* vs_accept_mode of the sampler (same limits as vs_reject_sample) */
+    int32_t accept_mode;      /* vs_accept_mode of the sampler (same limits as vs_reject_sample;
+                                 greedy: u_acc, u_res and q_draft are not read) */
 } vs_step_desc;
 
 typedef struct {

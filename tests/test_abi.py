@@ -137,7 +137,7 @@ def test_sample_validation(lib):
     bad = list(args)
     bad[0] = None
     assert lib.vs_reject_sample(C.byref(d), *bad, None, 0, None) == -1
-    # accept modes: unknown -> invalid; multi with dense drafts (q given) and W > 1, more
+    # accept modes: unknown (3) -> invalid; multi with dense drafts (q given) and W > 1, more
     # than 64 candidates, or too many p values for LDS -> unsupported; multi with W == 1
     # takes dense drafts (single-chain rule) and gets as far as the workspace check
     def samp(W, D, mode, q=fake):
@@ -145,14 +145,26 @@ def test_sample_validation(lib):
         a[3] = q
         return lib.vs_reject_sample(C.byref(L.SampleDesc(2, W, D, 1000, 1.0, mode)), *a, None,
                                     0, None)
-    assert samp(4, 20, 2) == -1
+    assert samp(4, 20, 3) == -1
     assert samp(4, 20, L.VS_ACCEPT_MULTI) == -2
     assert samp(4, 20, L.VS_ACCEPT_MULTI, q=None) == -3
     assert samp(65, 1, L.VS_ACCEPT_MULTI, q=None) == -2
     assert samp(16, 40, L.VS_ACCEPT_MULTI, q=None) == -2     # (640+1)*16 + 640 > 4096
     assert samp(8, 20, L.VS_ACCEPT_MULTI, q=None) == -3      # (160+1)*8 + 160 fits
     assert samp(1, 20, L.VS_ACCEPT_MULTI) == -3
-    assert lib.vs_sample_workspace_bytes(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 2))) == 0
+    assert lib.vs_sample_workspace_bytes(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 3))) == 0
+    # greedy: the uniforms and q are not read (NULL passes validation); its workspace
+    # also holds the tile statistics of the given logits
+    g = list(args)
+    g[3] = g[6] = g[7] = None
+    gd = L.SampleDesc(2, 4, 20, 1000, 1.0, L.VS_ACCEPT_GREEDY)
+    assert lib.vs_reject_sample(C.byref(gd), *g, None, 0, None) == -3
+    g[6] = None
+    assert lib.vs_reject_sample(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 0)), *g, None, 0,
+                                None) == -1
+    assert (lib.vs_sample_workspace_bytes(C.byref(gd))
+            >= lib.vs_sample_workspace_bytes(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 0)))
+            + 2 * 80 * 4 * 8)
 
 
 def test_pack_validation(lib):

@@ -503,6 +503,57 @@ def test_reject_sample_workspace_reused_across_shapes(monkeypatch):
         assert n_exc <= 1 and n_cmp >= B - 1
 
 
+def _greedy_case(rng, B, W, D, V):
+    """Random logits; draft tokens that are mostly the argmax of their preceding row
+    (so runs are long); rows with exact ties (inside a tile and across tiles), a row
+    of equal logits (every tile holds the maximum), out-of-range tokens, a closed
+    gate and a sequence without candidates."""
+    M = W * D
+    root = rng.standard_normal((B, V)).astype(np.float32)
+    logits = rng.standard_normal((B * M, V)).astype(np.float32)
+    for r in rng.choice(B * M, size=B * M // 6, replace=False):
+        k = int(np.argmax(logits[r]))
+        j = int(rng.integers(0, V))
+        logits[r, j] = logits[r, k]                 # exact tie, possibly in another tile
+    logits[5] = 0.25                                 # all equal: argmax is token 0
+    root[3, :] = root[3, int(np.argmax(root[3]))]
+    cand = rng.integers(0, V, size=(B, W, D)).astype(np.int32)
+    for b in range(B):
+        for i in range(W):
+            for o in range(D):
+                if rng.random() < 0.8:
+                    row = root[b] if o == 0 else logits[b * M + i * D + o - 1]
+                    cand[b, i, o] = int(np.argmax(row))
+    cand[rng.random((B, W, D)) < 0.01] = V + 7
+    clen = rng.integers(0, D + 1, size=(B, W)).astype(np.int32)
+    clen[rng.random((B, W)) < 0.5] = D
+    clen[0] = 0
+    gate = np.ones(B, dtype=np.int32)
+    gate[1] = 0
+    return root, logits, cand, clen, gate
+
+
+@pytest.mark.parametrize("B,W,D,V,T", [(64, 4, 6, 3000, 1.0), (40, 3, 5, 1000, 0.7),
+                                       (16, 8, 20, 128256, 1.0)])
+def test_reject_sample_greedy(B, W, D, V, T):
+    """Greedy verification against the oracle on the same fp32 logits: every output and
+    every flag equal, near and exact ties included (both sides decide on the same
+    values; exact ties take the first index)."""
+    api = _api()
+    rng = np.random.default_rng(60 + W)
+    root, logits, cand, clen, gate = _greedy_case(rng, B, W, D, V)
+    lse = scipy.special.logsumexp(logits.astype(np.float64) / T, axis=1)
+    say("reject_sample greedy", B, W, D, V, T)
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), None, None, T, to_dev(gate), accept="greedy")
+    o = oracle.reject_sample_greedy(root, logits, cand, clen, gate)
+    for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), (k, np.nonzero(
+            (tensor_np(g[k]) != o[k]).reshape(B, -1).any(axis=1))[0][:5])
+    assert (o["n_acc"] >= 3).sum() > B // 4
+    assert (o["flags"] & oracle.FLAG_CDF_TIE).any() or (o["flags"] & oracle.FLAG_ACCEPT_TIE).any()
+
+
 # =============================================================================== whole step
 
 def _step_inputs(case, T, external=None):
@@ -575,6 +626,31 @@ def test_verify_step_multi(name):
     g = step()
     A = {k: v for k, v in case.arrays.items() if k != "q_draft"}
     o = oracle.verify_step(A, sh, accept="multi")
+    n_cmp, n_exc = _check_step(case, g, o)
+    assert n_exc <= max(1, sh.B // 16), (n_cmp, n_exc)
+
+
+@pytest.mark.parametrize("name", ["small", "llama8b", "ragged"])
+def test_verify_step_greedy(name):
+    """The whole step with greedy verification (no uniforms, no draft distribution)
+    against the oracle's step; sequences whose decisions are near ties are left out."""
+    api = _api()
+    if name == "small":
+        sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
+    elif name == "llama8b":
+        sh, seed = wl.config(2), 2000
+    else:
+        sh, seed = wl.config(5), 5000
+    case = get_case(("step", name), lambda: wl.make_case(sh, seed))
+    I = _step_inputs(case, sh.temperature)
+    for k in ("q_draft", "u_acc", "u_res"):
+        I[k] = None
+    say("verify_step greedy", name)
+    step = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa,
+                          accept="greedy")
+    g = step()
+    o = oracle.verify_step(case.arrays, sh, accept="greedy")
     n_cmp, n_exc = _check_step(case, g, o)
     assert n_exc <= max(1, sh.B // 16), (n_cmp, n_exc)
 

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libvstep.so")
 
 VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = 0, -1, -2, -3, -4
 VS_F32, VS_BF16 = 0, 1
-VS_ACCEPT_LONGEST, VS_ACCEPT_MULTI = 0, 1
+VS_ACCEPT_LONGEST, VS_ACCEPT_MULTI, VS_ACCEPT_GREEDY = 0, 1, 2
 
 FLAG_PROBE_TIE = 1
 FLAG_ACCEPT_TIE = 2

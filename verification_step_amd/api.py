@@ -218,7 +218,8 @@ def lm_head(h, w_full=None, w_down=None, w_up=None, temperature: float = 1.0,
     return LmHead(h, w_full, w_down, w_up, temperature, write_probs, V, rank)()
 
 
-_ACCEPT = {"longest": L.VS_ACCEPT_LONGEST, "multi": L.VS_ACCEPT_MULTI}
+_ACCEPT = {"longest": L.VS_ACCEPT_LONGEST, "multi": L.VS_ACCEPT_MULTI,
+           "greedy": L.VS_ACCEPT_GREEDY}
 
 
 def _accept_mode(accept: str) -> int:
@@ -229,8 +230,9 @@ def _accept_mode(accept: str) -> int:
 
 def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_res,
                   temperature: float = 1.0, gate=None, accept: str = "longest"):
-    """accept = "longest" (each candidate judged alone, longest run kept) or "multi"
-    (lossless multi-candidate acceptance; copy drafts, q None, when W > 1)."""
+    """accept = "longest" (each candidate judged alone, longest run kept), "multi"
+    (lossless multi-candidate acceptance; copy drafts, q None, when W > 1) or
+    "greedy" (temperature 0: argmax tests; q, u_acc and u_res may be None)."""
     lib = L.load()
     _check(root_logits, torch.float32, "root_logits")
     _check(logits, torch.float32, "logits")
@@ -252,7 +254,7 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
                acc_per_cand=torch.empty((B, W), dtype=torch.int32, device=dev),
                flags=torch.empty(B, dtype=torch.int32, device=dev))
     nbytes = lib.vs_sample_workspace_bytes(C.byref(desc))
-    ws = workspace(nbytes, dev, "sample", (B, W, D, V))
+    ws = workspace(nbytes, dev, "sample", (B, W, D, V, accept))
     st = lib.vs_reject_sample(C.byref(desc), _ptr(root_logits), _ptr(logits), _ptr(row_lse),
                               _ptr(q), _ptr(cand_tok), _ptr(cand_len), _ptr(u_acc), _ptr(u_res),
                               _ptr(gate), _ptr(out["n_acc"]), _ptr(out["best"]),

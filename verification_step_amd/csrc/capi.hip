@@ -56,7 +56,8 @@ int check_sample(const vs_sample_desc *d) {
   if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
   if (!(d->temperature > 0.f) || !isfinite(d->temperature)) return VS_ERR_INVALID_ARG;
   if (d->V > kMaxVocabSampler) return VS_ERR_UNSUPPORTED;
-  if (d->accept_mode != VS_ACCEPT_LONGEST && d->accept_mode != VS_ACCEPT_MULTI)
+  if (d->accept_mode != VS_ACCEPT_LONGEST && d->accept_mode != VS_ACCEPT_MULTI &&
+      d->accept_mode != VS_ACCEPT_GREEDY)
     return VS_ERR_INVALID_ARG;
   if (d->accept_mode == VS_ACCEPT_MULTI && d->W > 1 && !vs::sampler_multi_fits(d->W, d->D))
     return VS_ERR_UNSUPPORTED;
@@ -66,6 +67,11 @@ int check_sample(const vs_sample_desc *d) {
 // the multi-candidate kernels run when there is more than one candidate (with one, the
 // rule is the single-chain rule); they take copy drafts only
 static bool sample_multi(int accept_mode, int W) { return accept_mode == VS_ACCEPT_MULTI && W > 1; }
+
+// sampler rule: 0 longest run (also multi with one candidate), 1 multi, 2 greedy
+static int sample_rule(int accept_mode, int W) {
+  return accept_mode == VS_ACCEPT_GREEDY ? 2 : (sample_multi(accept_mode, W) ? 1 : 0);
+}
 
 float attn_scale(float scale, int hd) { return scale > 0.f ? scale : 1.0f / sqrtf((float)hd); }
 
@@ -189,7 +195,8 @@ int vs_lm_head(const vs_head_desc *d, const void *h, const void *w_full, const v
 
 size_t vs_sample_workspace_bytes(const vs_sample_desc *d) {
   if (check_sample(d) != VS_OK) return 0;
-  return vs::sample_workspace_bytes(d->B, d->W, d->D, d->V);
+  // greedy without a head before it: the tile statistics of the given logits
+  return vs::sample_workspace_bytes(d->B, d->W, d->D, d->V, d->accept_mode == VS_ACCEPT_GREEDY);
 }
 
 int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const float *logits,
@@ -200,26 +207,32 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
                      size_t ws_bytes, void *stream) {
   int st = check_sample(d);
   if (st != VS_OK) return st;
-  if (!root_logits || !logits || !row_lse || !cand_tok || !cand_len || !u_acc || !u_res ||
-      !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
+  const int rule = sample_rule(d->accept_mode, d->W);
+  const bool greedy = rule == 2;
+  if (!root_logits || !logits || !row_lse || !cand_tok || !cand_len ||
+      (!greedy && (!u_acc || !u_res)) || !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
     return VS_ERR_INVALID_ARG;
-  const bool multi = sample_multi(d->accept_mode, d->W);
-  if (multi && q) return VS_ERR_UNSUPPORTED;
+  if (rule == 1 && q) return VS_ERR_UNSUPPORTED;
   const size_t need = vs_sample_workspace_bytes(d);
   if (!workspace || ws_bytes < need) return VS_ERR_WORKSPACE;
-  const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->W, d->D, d->V);
+  const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->W, d->D, d->V, greedy);
   hipError_t e = vs::launch_root_stats(root_logits, d->B, d->V, d->temperature, sw.root_stats,
                                        S(stream));
   if (e != hipSuccess) return VS_ERR_HIP;
+  if (greedy) {
+    e = vs::launch_row_stats(logits, d->B * d->W * d->D, d->V, d->temperature, sw.row_stats,
+                             S(stream));
+    if (e != hipSuccess) return VS_ERR_HIP;
+  }
   // row_lse is an input here: only the root normalisers and the tests are computed
   e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, nullptr,
                            const_cast<double *>(row_lse), root_logits, logits, q, cand_tok,
-                           cand_len, gate, u_acc, sw, S(stream), multi);
+                           cand_len, gate, u_acc, sw, S(stream), rule, sw.row_stats);
   if (e != hipSuccess) return VS_ERR_HIP;
   return hip_status(vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, root_logits, logits,
                                        row_lse, q, cand_tok, cand_len, u_res, gate, n_acc, best,
                                        out_tok, n_out, acc_per_cand, flags, 0, sw, S(stream),
-                                       nullptr, multi, u_acc));
+                                       nullptr, rule, u_acc));
 }
 
 static int check_step(const vs_step_desc *d) {
@@ -250,8 +263,10 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   int st = check_step(d);
   if (st != VS_OK) return st;
   if (!io) return VS_ERR_INVALID_ARG;
+  const int rule = sample_rule(d->accept_mode, d->W);
   if (!io->q || !io->k_cand || !io->v_cand || !io->prefix_len || !io->w_full ||
-      !io->root_logits || !io->u_acc || !io->u_res || !io->cand_tok || !io->cand_len ||
+      !io->root_logits || (rule != 2 && (!io->u_acc || !io->u_res)) || !io->cand_tok ||
+      !io->cand_len ||
       !io->attn_out || !io->logits || !io->row_lse || !io->n_acc || !io->best || !io->out_tok ||
       !io->n_out || !io->acc_per_cand || !io->flags)
     return VS_ERR_INVALID_ARG;
@@ -263,8 +278,7 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
       return VS_ERR_INVALID_ARG;
   }
   if (io->aux_stream && (!io->fork_event || !io->join_event)) return VS_ERR_INVALID_ARG;
-  const bool multi = sample_multi(d->accept_mode, d->W);
-  if (multi && io->q_draft) return VS_ERR_UNSUPPORTED;
+  if (rule == 1 && io->q_draft) return VS_ERR_UNSUPPORTED;
   const StepLayout L = step_layout(d);
   if (!workspace || ws_bytes < L.total) return VS_ERR_WORKSPACE;
   hipStream_t s = S(stream);
@@ -326,14 +340,14 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   const int32_t *gate = d->external_drafts ? nullptr : io->gate;
   e = vs::launch_lse_tests(d->B, d->W, d->D, d->V, d->temperature, hw.stats, io->row_lse,
                            io->root_logits, io->logits, io->q_draft, io->cand_tok, io->cand_len,
-                           gate, io->u_acc, sw, s, multi);
+                           gate, io->u_acc, sw, s, rule, hw.stats);
   if (e != hipSuccess || !mark(4)) return VS_ERR_HIP;
   // 5. longest accepted run (or the multi-candidate chain) and the extra token (flags: accumulate onto the gate's,
   //    or written whole when there was no retrieval)
   e = vs::launch_sampler(d->B, d->W, d->D, d->V, d->temperature, io->root_logits, io->logits,
                          io->row_lse, io->q_draft, io->cand_tok, io->cand_len, io->u_res, gate,
                          io->n_acc, io->best, io->out_tok, io->n_out, io->acc_per_cand, io->flags,
-                         d->external_drafts ? 0 : 1, sw, s, sw.attn_flags, multi, io->u_acc);
+                         d->external_drafts ? 0 : 1, sw, s, sw.attn_flags, rule, io->u_acc);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
 }

@@ -19,6 +19,12 @@
 // every candidate's token under every row, the chain itself is a short serial walk in
 // LDS, and the draw excludes the rejected tokens.
 //
+// Greedy verification (accept mode GREEDY, temperature 0): a draft token is kept iff
+// it is the argmax of the preceding row and the extra token is the argmax of the row
+// after the run.  The normaliser kernel finds each row's argmax from the per-tile
+// maxima (only the tiles holding the row maximum are read again) and writes the tests;
+// one workgroup per sequence then picks the longest run.
+//
 // Layout of the work: grid (vocabulary chunks, sequences).  Every workgroup of a
 // sequence repeats the (cheap) acceptance tests and the choice of candidate, then
 // sums the residual weights of its own vocabulary chunk with coalesced loads.  The
@@ -81,6 +87,10 @@ struct TestArgs {
   const double *u_acc;
   uint8_t *code;              // [B*W*D], or null: normalisers only
   double *pv;                 // MULTI: [B][M+1 rows][W] p of every candidate's token
+  int greedy;                 // GREEDY: argmax tests instead of the probability tests
+  const float2 *am_stats;     // GREEDY: tile maxima of the verify rows [B*M][n_vt]
+  int32_t *amax;              // GREEDY: [B*M + B] argmax of every row (root rows last)
+  uint8_t *amax_tie;          // GREEDY: [B*M + B] near tie between the two largest logits
 };
 
 __device__ double lse_of_stats(const float2 *st, int n_vt, double *red) {
@@ -118,7 +128,7 @@ __device__ __forceinline__ PosIn load_pos(const TestArgs &a, int b, int r, int i
   const int64_t pos = ((int64_t)b * a.W + i) * a.D + oo;
   if (oo < in.len) {
     in.x = a.cand_tok[pos];
-    in.u = a.u_acc[pos];
+    if (a.u_acc) in.u = a.u_acc[pos];
     if (in.x >= 0 && in.x < a.V) {
       in.z = (r < 0) ? a.root_logits[(int64_t)b * a.V + in.x] : a.logits[(int64_t)r * a.V + in.x];
       if (a.q) in.Q = (double)a.q[pos * a.V + in.x];
@@ -139,6 +149,104 @@ __device__ __forceinline__ void store_test(const TestArgs &a, const PosIn &in, i
     } else {
       c = CODE_BAD;
     }
+  }
+  a.code[((int64_t)b * a.W + i) * a.D + oo] = c;
+}
+
+// ---- greedy: the argmax of a row from its tile maxima
+constexpr int kTieTiles = 16;
+constexpr double kGreedyTieRel = 1e-3;   // near tie: top two within this x max(1, |top|)
+
+struct ArgmaxShared {
+  float v1[4], v2[4];
+  int i1[4];
+  int n_list;
+  int list[kTieTiles];
+};
+
+// (largest value, its first index, second largest value) of a multiset, merged with
+// another such summary
+__device__ __forceinline__ void am_merge(float &v1, int &i1, float &v2, float ov1, int oi1,
+                                         float ov2) {
+  if (ov1 > v1 || (ov1 == v1 && oi1 < i1)) {
+    v2 = fmaxf(v1, ov2);
+    v1 = ov1;
+    i1 = oi1;
+  } else {
+    v2 = fmaxf(v2, ov1);
+  }
+}
+
+// First index of the largest logit of row z[0, V) and whether the two largest are a
+// near tie.  st[t].x is the maximum of fl(z * inv_t) over tile t; fl is monotone, so
+// the argmax lies in a tile whose maximum equals the row's, and only those tiles
+// (usually one; all of them if more than kTieTiles) are read.  The second largest
+// logit outside them is estimated from their maxima (for the tie test only).
+__device__ void row_argmax(const float2 *st, int n_vt, const float *z, int V, float inv_t,
+                           ArgmaxShared &s, int &am, bool &tie) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float g = -INFINITY;
+  for (int t = tid; t < n_vt; t += 256) g = fmaxf(g, st[t].x);
+  for (int off = 32; off > 0; off >>= 1) g = fmaxf(g, __shfl_xor(g, off));
+  if (lane == 0) s.v1[wv] = g;
+  if (tid == 0) s.n_list = 0;
+  __syncthreads();
+  g = fmaxf(fmaxf(s.v1[0], s.v1[1]), fmaxf(s.v1[2], s.v1[3]));
+  float s2 = -INFINITY;
+  for (int t = tid; t < n_vt; t += 256) {
+    const float x = st[t].x;
+    if (x == g) {
+      const int k = atomicAdd(&s.n_list, 1);
+      if (k < kTieTiles) s.list[k] = t;
+    } else {
+      s2 = fmaxf(s2, x);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) s2 = fmaxf(s2, __shfl_xor(s2, off));
+  if (lane == 0) s.v2[wv] = s2;
+  __syncthreads();
+  s2 = fmaxf(fmaxf(s.v2[0], s.v2[1]), fmaxf(s.v2[2], s.v2[3]));
+  const int nl = s.n_list;
+  const bool all = nl > kTieTiles;
+  const int nscan = all ? n_vt : nl;
+  float v1 = -INFINITY, v2 = -INFINITY;
+  int i1 = INT_MAX;
+  for (int l = 0; l < nscan; ++l) {
+    const int k = (all ? l : s.list[l]) * kHeadVocabTile + tid;
+    if (k < V) am_merge(v1, i1, v2, z[k], k, -INFINITY);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov1 = __shfl_xor(v1, off), ov2 = __shfl_xor(v2, off);
+    const int oi1 = __shfl_xor(i1, off);
+    am_merge(v1, i1, v2, ov1, oi1, ov2);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    s.v1[wv] = v1;
+    s.i1[wv] = i1;
+    s.v2[wv] = v2;
+  }
+  __syncthreads();
+  v1 = s.v1[0];
+  i1 = s.i1[0];
+  v2 = s.v2[0];
+  for (int w2 = 1; w2 < 4; ++w2) am_merge(v1, i1, v2, s.v1[w2], s.i1[w2], s.v2[w2]);
+  am = i1;
+  const double zm = v1;
+  const double z2 = fmax((double)v2, (double)s2 / (double)inv_t);
+  tie = (zm - z2) < kGreedyTieRel * fmax(1.0, fabs(zm));
+}
+
+__device__ __forceinline__ void store_test_greedy(const TestArgs &a, const PosIn &in, int b,
+                                                  int i, int oo, int am, bool tie) {
+  uint8_t c = 0;
+  if (oo < in.len) {
+    if (in.x >= 0 && in.x < a.V) {
+      if (in.x == am) c |= CODE_ACCEPT;
+    } else {
+      c = CODE_BAD;
+    }
+    if (tie) c |= CODE_TIE;
   }
   a.code[((int64_t)b * a.W + i) * a.D + oo] = c;
 }
@@ -179,6 +287,23 @@ lse_tests_kernel(TestArgs a) {
     lse = a.row_lse[r];
   }
 
+  if (a.greedy) {
+    __shared__ ArgmaxShared ash;
+    const float *zr = root ? a.root_logits + (int64_t)b * a.V : a.logits + (int64_t)r * a.V;
+    const float2 *st = root ? a.root_stats + (int64_t)b * a.n_vt : a.am_stats + (int64_t)r * a.n_vt;
+    int am;
+    bool tie;
+    row_argmax(st, a.n_vt, zr, a.V, (float)a.inv_t, ash, am, tie);
+    const int64_t gr = root ? (int64_t)a.B * M + b : r;
+    if (tid == 0) {
+      a.amax[gr] = am;
+      a.amax_tie[gr] = tie ? 1 : 0;
+    }
+    if (tid < npos) store_test_greedy(a, first, b, root ? tid : i0, oo, am, tie);
+    for (int t = tid + 256; t < npos; t += 256)
+      store_test_greedy(a, load_pos(a, b, rrow, t, oo), b, t, oo, am, tie);
+    return;
+  }
   if (a.pv != nullptr) {
     // MULTI: p under this row of every candidate's token at the depth the row judges
     // (0 for the root row, o+1 for verify row (i, o)); -1 marks an out-of-range token,
@@ -286,6 +411,8 @@ struct SampArgs {
   const uint8_t *code;
   const double *pv;      // MULTI: [B][M+1][W] (see TestArgs)
   const double *u_acc;   // MULTI: [B, W, D]
+  const int32_t *amax;   // GREEDY: [B*M + B] (see TestArgs)
+  const uint8_t *amax_tie;
   int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
   int flags_accumulate;
   int32_t *attn_flags;   // [B] or null: flags raised by attention, folded and reset here
@@ -295,10 +422,27 @@ struct SampArgs {
 };
 
 enum { SAMP_FUSED = 0, SAMP_SUMS = 1, SAMP_DRAW = 2 };
+enum { RULE_LONGEST = 0, RULE_MULTI = 1, RULE_GREEDY = 2 };
 
-template <int PHASE, bool MULTI>
+// the per-sequence scalar outputs and the flags (with attention's, which are reset)
+__device__ void store_scalars(const SampArgs &a, int b, int ab, int best, int f) {
+  a.n_acc[b] = ab;
+  a.best[b] = best;
+  a.n_out[b] = ab + 1;
+  if (a.attn_flags) {
+    f |= a.attn_flags[b];
+    a.attn_flags[b] = 0;      // ready for the next call on this workspace
+  }
+  if (a.flags) {
+    if (a.flags_accumulate) atomicOr(&a.flags[b], f);
+    else a.flags[b] = f;
+  }
+}
+
+template <int PHASE, int RULE>
 __global__ void __launch_bounds__(kST)
 sampler_kernel(SampArgs a) {
+  constexpr bool MULTI = RULE == RULE_MULTI;
   __shared__ SampSharedT<MULTI> sh;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
@@ -317,7 +461,7 @@ sampler_kernel(SampArgs a) {
       int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
       ln = ln < 0 ? 0 : (ln > D ? D : ln);
       sh.lens[i] = ln;
-      sh.ures[i] = a.u_res[(int64_t)b * W + i];
+      sh.ures[i] = a.u_res ? a.u_res[(int64_t)b * W + i] : 0.0;   // greedy: not given
     }
     for (int idx = tid; idx < M; idx += kST) {
       sh.tok[idx] = a.cand_tok[(int64_t)b * M + idx];
@@ -410,7 +554,7 @@ sampler_kernel(SampArgs a) {
       ln = ln < 0 ? 0 : (ln > D ? D : ln);
       sh.lens[i] = ln;
       sh.a_len[i] = ln;
-      sh.ures[i] = a.u_res[(int64_t)b * W + i];
+      sh.ures[i] = a.u_res ? a.u_res[(int64_t)b * W + i] : 0.0;   // greedy: not given
     }
     for (int idx = tid; idx < M; idx += kST) {
       sh.code[idx] = a.code[(int64_t)b * M + idx];
@@ -470,6 +614,19 @@ sampler_kernel(SampArgs a) {
 
   }
   __syncthreads();
+  if constexpr (RULE == RULE_GREEDY) {
+    // the extra token: the argmax of the row after the run, found with the tests
+    const int64_t frow = (sh.prow < 0) ? (int64_t)a.B * M + b : sh.prow;
+    const int best = sh.best, ab = sh.ab;
+    if (tid == 0) store_scalars(a, b, ab, best, sh.flags | (a.amax_tie[frow] ? FLAG_CDF_TIE : 0));
+    const int yy = a.amax[frow];
+    int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
+    for (int o = tid; o <= D; o += kST)
+      ot[o] = (o < ab) ? sh.tok[best * D + o] : (o == ab ? yy : -1);
+    for (int i = tid; i < W; i += kST)
+      a.acc_per_cand[(int64_t)b * W + i] = (sh.lens[i] >= 1) ? sh.a_len[i] : 0;
+    return;
+  }
   const float *zrow = (sh.prow < 0) ? root : a.logits + sh.prow * V;
   const double lse = sh.lse;
   const float *qrow = (sh.qrow < 0) ? nullptr : a.q + sh.qrow * V;
@@ -482,6 +639,14 @@ sampler_kernel(SampArgs a) {
   // past V weigh nothing)
   auto weights = [&](int k0, double *pk, double *rk) {
     float z[kPer], qv[kPer];
+    // MULTI: the rejected tokens among k0 .. k0+kPer-1 (their point masses are removed)
+    unsigned exm = 0;
+    if constexpr (MULTI) {
+      for (int e = 0; e < n_excl; ++e) {
+        const unsigned j = (unsigned)(sh.excl_tok[e] - k0);
+        if (j < (unsigned)kPer) exm |= 1u << j;
+      }
+    }
     if (k0 + kPer <= V) {
       const f32x4 z0 = *(const f32x4 *)(zrow + k0), z1 = *(const f32x4 *)(zrow + k0 + 4);
 #pragma unroll
@@ -516,10 +681,7 @@ sampler_kernel(SampArgs a) {
       if (resid) {
         double qk;
         if constexpr (MULTI) {
-          // the rejected tokens' point masses, each removed in turn
-          bool ex = false;
-          for (int e = 0; e < n_excl; ++e) ex |= (sh.excl_tok[e] == k);
-          qk = ex ? 1.0 : 0.0;
+          qk = ((exm >> j) & 1u) ? 1.0 : 0.0;
         } else {
           qk = qrow ? (double)qv[j] : (k == xpt ? 1.0 : 0.0);
         }
@@ -643,17 +805,7 @@ sampler_kernel(SampArgs a) {
       f |= FLAG_CDF_TIE;
     }
     y_sh = yy;
-    a.n_acc[b] = ab;
-    a.best[b] = best;
-    a.n_out[b] = ab + 1;
-    if (a.attn_flags) {
-      f |= a.attn_flags[b];
-      a.attn_flags[b] = 0;      // ready for the next call on this workspace
-    }
-    if (a.flags) {
-      if (a.flags_accumulate) atomicOr(&a.flags[b], f);
-      else a.flags[b] = f;
-    }
+    store_scalars(a, b, ab, best, f);
   }
   __syncthreads();
   const int yy = y_sh;
@@ -681,7 +833,7 @@ root_stats_kernel(const float *root_logits, int B, int V, float inv_t, float2 *s
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
-  for (int b = wv; b < B; b += 4) {
+  for (int b = blockIdx.y * 4 + wv; b < B; b += 4 * gridDim.y) {
     const float *row = root_logits + (int64_t)b * V;
     float x[kHeadVocabTile / 64];
     float mx = -INFINITY;
@@ -703,7 +855,7 @@ root_stats_kernel(const float *root_logits, int B, int V, float inv_t, float2 *s
 
 }  // namespace
 
-SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
+SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats) {
   SampleWs w;
   const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
   const int nch = (V + kChunk - 1) / kChunk;
@@ -725,6 +877,15 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V) {
   off += ((size_t)B * nch * kST * sizeof(double2) + 255) & ~(size_t)255;
   w.pv = (double *)(p + off);
   off += ((size_t)B * (W * D + 1) * W * sizeof(double) + 255) & ~(size_t)255;
+  w.amax = (int32_t *)(p + off);
+  off += ((size_t)B * (W * D + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  w.amax_tie = (uint8_t *)(p + off);
+  off += ((size_t)B * (W * D + 1) + 255) & ~(size_t)255;
+  w.row_stats = nullptr;
+  if (row_stats) {
+    w.row_stats = (float2 *)(p + off);
+    off += ((size_t)B * W * D * n_vt * sizeof(float2) + 255) & ~(size_t)255;
+  }
   w.bytes = off;
   return w;
 }
@@ -733,14 +894,23 @@ bool sampler_multi_fits(int W, int D) {
   return W <= kMaxWMulti && multi_lds_doubles(W, D) <= kMaxMultiLds;
 }
 
-size_t sample_workspace_bytes(int B, int W, int D, int V) {
-  return sample_ws(nullptr, B, W, D, V).bytes;
+size_t sample_workspace_bytes(int B, int W, int D, int V, bool row_stats) {
+  return sample_ws(nullptr, B, W, D, V, row_stats).bytes;
 }
 
 hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
                              float2 *stats, hipStream_t st) {
   const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
   hipLaunchKernelGGL(root_stats_kernel, dim3(n_vt), dim3(256), 0, st, root_logits, B, V,
+                     1.0f / temperature, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(const float *logits, int rows, int V, float temperature,
+                            float2 *stats, hipStream_t st) {
+  const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
+  const int gy = min((rows + 3) / 4, 256);
+  hipLaunchKernelGGL(root_stats_kernel, dim3(n_vt, gy), dim3(256), 0, st, logits, rows, V,
                      1.0f / temperature, stats);
   return hipGetLastError();
 }
@@ -763,7 +933,9 @@ hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
                             const float2 *row_stats, double *row_lse, const float *root_logits,
                             const float *logits, const float *q, const int32_t *cand_tok,
                             const int32_t *cand_len, const int32_t *gate, const double *u_acc,
-                            const SampleWs &ws, hipStream_t st, bool multi) {
+                            const SampleWs &ws, hipStream_t st, int rule,
+                            const float2 *am_stats) {
+  const bool multi = rule == 1, greedy = rule == 2;
   TestArgs a{};
   a.B = B;
   a.W = W;
@@ -784,6 +956,13 @@ hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
   a.u_acc = u_acc;
   a.code = multi ? nullptr : ws.code;
   a.pv = multi ? ws.pv : nullptr;
+  if (greedy) {
+    a.q = nullptr;                 // draft probabilities play no part
+    a.greedy = 1;
+    a.am_stats = am_stats;
+    a.amax = ws.amax;
+    a.amax_tie = ws.amax_tie;
+  }
   hipLaunchKernelGGL(lse_tests_kernel, dim3(B * W * D + B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -794,7 +973,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
                           int flags_accumulate, const SampleWs &ws, hipStream_t st,
-                          int32_t *attn_flags, bool multi, const double *u_acc) {
+                          int32_t *attn_flags, int rule, const double *u_acc) {
+  const bool multi = rule == 1;
   SampArgs a;
   a.B = B;
   a.W = W;
@@ -814,6 +994,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.code = ws.code;
   a.pv = ws.pv;
   a.u_acc = u_acc;
+  a.amax = ws.amax;
+  a.amax_tie = ws.amax_tie;
   a.n_acc = n_acc;
   a.best = best;
   a.out_tok = out_tok;
@@ -829,24 +1011,29 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   // V = 128256 is faster fused, B = 32 far faster in two launches)
   bool two = (int64_t)a.nch * B > 256;
   if (const char *ov = getenv("VSTEP_SAMPLER_TWO_PASS")) two = atoi(ov) != 0;
+  if (rule == 2) {
+    // greedy: no vocabulary sweep, one workgroup per sequence
+    hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, RULE_GREEDY>), dim3(1, B), dim3(kST), 0, st, a);
+    return hipGetLastError();
+  }
   if (multi) {
     const size_t lds = (size_t)multi_lds_doubles(W, D) * sizeof(double);
     if (!two) {
-      hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, true>), dim3(a.nch, B), dim3(kST), lds, st, a);
+      hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, RULE_MULTI>), dim3(a.nch, B), dim3(kST), lds, st, a);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, true>), dim3(a.nch, B), dim3(kST), lds, st, a);
+    hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, RULE_MULTI>), dim3(a.nch, B), dim3(kST), lds, st, a);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, true>), dim3(1, B), dim3(kST), lds, st, a);
+    hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, RULE_MULTI>), dim3(1, B), dim3(kST), lds, st, a);
     return hipGetLastError();
   }
   if (!two) {
-    hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, false>), dim3(a.nch, B), dim3(kST), 0, st, a);
+    hipLaunchKernelGGL((sampler_kernel<SAMP_FUSED, RULE_LONGEST>), dim3(a.nch, B), dim3(kST), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, false>), dim3(a.nch, B), dim3(kST), 0, st, a);
+  hipLaunchKernelGGL((sampler_kernel<SAMP_SUMS, RULE_LONGEST>), dim3(a.nch, B), dim3(kST), 0, st, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, false>), dim3(1, B), dim3(kST), 0, st, a);
+  hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, RULE_LONGEST>), dim3(1, B), dim3(kST), 0, st, a);
   return hipGetLastError();
 }
 

@@ -154,26 +154,34 @@ struct SampleWs {
   int32_t *attn_flags;  // [B] flags raised by attention inside the step, zero between calls
   double2 *thread_sums; // [B][n_chunks][256] per-thread weight sums of the sampler
   double *pv;           // [B][W*D+1][W] multi-candidate acceptance: p of each candidate token
+  int32_t *amax;        // [B*W*D + B] greedy: argmax of every verify row, then the root rows
+  uint8_t *amax_tie;    // [B*W*D + B] greedy: near tie between the two largest logits
+  float2 *row_stats;    // [B*W*D][n_vt] tile statistics of given logits (greedy, standalone)
   size_t bytes;
 };
-SampleWs sample_ws(void *ws, int B, int W, int D, int V);
-size_t sample_workspace_bytes(int B, int W, int D, int V);
+SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats = false);
+size_t sample_workspace_bytes(int B, int W, int D, int V, bool row_stats = false);
 // whether the multi-candidate acceptance handles W candidates of D tokens
 bool sampler_multi_fits(int W, int D);
 hipError_t launch_root_stats(const float *root_logits, int B, int V, float temperature,
                              float2 *stats, hipStream_t st);
+// tile statistics (max, sum exp) [rows][n_vt] of any fp32 rows
+hipError_t launch_row_stats(const float *logits, int rows, int V, float temperature,
+                            float2 *stats, hipStream_t st);
 // fp64 row normalisers from tile statistics [rows][n_vt]
 hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *lse,
                                  hipStream_t st);
 // Normalisers of the verify rows (row_stats != null; else row_lse is an input) and of
 // the root rows (ws.root_stats -> ws.root_lse), and the acceptance test of every draft
-// position (-> ws.code), or with multi the p of every candidate token under every row
-// (-> ws.pv).
+// position (-> ws.code), or with multi (rule 1) the p of every candidate token under
+// every row (-> ws.pv), or with greedy (rule 2) the argmax of every row (-> ws.amax,
+// from am_stats and ws.root_stats) and the argmax tests (-> ws.code).
 hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
                             const float2 *row_stats, double *row_lse, const float *root_logits,
                             const float *logits, const float *q, const int32_t *cand_tok,
                             const int32_t *cand_len, const int32_t *gate, const double *u_acc,
-                            const SampleWs &ws, hipStream_t st, bool multi = false);
+                            const SampleWs &ws, hipStream_t st, int rule = 0,
+                            const float2 *am_stats = nullptr);
 // Longest accepted run (or with multi the multi-candidate chain over ws.pv and u_acc),
 // residual / bonus draw, outputs (reads ws.code, ws.root_lse).
 hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const float *root_logits,
@@ -182,7 +190,7 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const int32_t *gate, int32_t *n_acc, int32_t *best, int32_t *out_tok,
                           int32_t *n_out, int32_t *acc_per_cand, int32_t *flags,
                           int flags_accumulate, const SampleWs &ws, hipStream_t st,
-                          int32_t *attn_flags = nullptr, bool multi = false,
+                          int32_t *attn_flags = nullptr, int rule = 0,
                           const double *u_acc = nullptr);
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);

@@ -16,6 +16,9 @@ Sources (web pages; cited by title and section):
         step 2 (batch verify, cut at the first mismatch).
   [SL]  "SlimSpec: Low-Rank Draft LM-Head for Accelerated Speculative Decoding"
         (gist.science/ko/paper/2605.10453): "방법론 / 아키텍처", z = W_up W_down h.
+  [SD6] the same blog's section 6 (production checklist): KV-cache rollback with a
+        paged memory pool -- the KV blocks of rejected tokens go back to the pool
+        at once, and no block may leak.
 
 Every function below is the plain definition of its step; the readings taken
 where the pages are silent or garbled are listed next to the code that uses them.
@@ -43,6 +46,7 @@ FLAG_NO_CANDIDATE = 16      # no candidate (gate closed or nothing found): root 
 FLAG_BAD_PAGE = 32          # page-table entry or prefix length out of range
 FLAG_BAD_CTX = 64           # context offsets out of range
 FLAG_BAD_TOKEN = 128        # candidate token id outside [0, V)
+FLAG_POOL_EMPTY = 256       # KV commit: not enough free pages for the accepted rows
 
 PROBE_TIE_EPS = 1e-5
 ACCEPT_TIE_REL = 1e-4
@@ -615,6 +619,108 @@ def reject_sample_greedy(root_logits, logits, cand_tok, cand_len, gate=None):
         out["n_out"][b] = ab + 1
         out["flags"][b] = flags
     return out
+
+
+# ----------------------------------------------------------------------------------
+# KV commit and rollback over the paged pool  [SD6]
+#
+# Pool model: pages of `page` tokens, K pages [n_pages, Hkv, page, hd] and V pages
+# transposed [n_pages, Hkv, hd, page] (token_major gives the token-major view);
+# page_table[b, j] = pool page of tokens j*page .. j*page+page-1 of sequence b; a
+# free-page stack free_list[0 .. n_free) whose top is free_list[n_free - 1].
+
+def _pages_for(n_tokens: int, page: int) -> int:
+    return (n_tokens + page - 1) // page
+
+
+def kv_commit(k_pool, v_pool, page_table, prefix_len, free_list, n_free, k_cand, v_cand,
+              best, n_acc, W, D, page=16):
+    """Append each sequence's accepted rows to its paged KV cache.
+
+    Sequence b's accepted rows are rows (best[b], 0 .. a-1), a = n_acc[b] clipped to
+    [0, D], of the candidate K/V buffers ([B*W*D, Hkv, hd], row (b, i, o) at
+    b*W*D + i*D + o); they become tokens P .. P+a-1, P = prefix_len[b].  Pages
+    beyond the ones the prefix already holds are popped from the free stack, in
+    sequence order and, within a sequence, in page order.  Nothing happens for a
+    sequence with best < 0 or a = 0.  A sequence is skipped (nothing written, no
+    page taken) with FLAG_BAD_PAGE when P + a exceeds the page table, when P is out
+    of range or when a page it would write (its partly filled last page, or a popped
+    one) is not a pool page; with FLAG_POOL_EMPTY when the stack holds fewer pages
+    than it needs.  Returns copies: (k_pool, v_pool, page_table, prefix_len,
+    free_list, n_free, flags)."""
+    k_pool = np.array(k_pool, copy=True)
+    v_pool = np.array(v_pool, copy=True)
+    page_table = np.array(page_table, dtype=np.int32, copy=True)
+    prefix_len = np.array(prefix_len, dtype=np.int32, copy=True)
+    free_list = np.array(free_list, dtype=np.int32, copy=True)
+    n_free = int(n_free)
+    B, max_pages = page_table.shape
+    n_pages = k_pool.shape[0]
+    M = W * D
+    Kt, Vt = token_major(k_pool, "k"), token_major(v_pool, "v")   # views: writes land in the pools
+    flags = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        i = int(best[b])
+        a = min(max(int(n_acc[b]), 0), D)
+        if i < 0 or i >= W or a == 0:
+            continue
+        P = int(prefix_len[b])
+        if P < 0 or P + a > max_pages * page:
+            flags[b] |= FLAG_BAD_PAGE
+            continue
+        have = _pages_for(P, page)
+        need = _pages_for(P + a, page) - have
+        if P % page and not (0 <= page_table[b, have - 1] < n_pages):
+            flags[b] |= FLAG_BAD_PAGE
+            continue
+        if need > n_free:
+            flags[b] |= FLAG_POOL_EMPTY
+            continue
+        new = [int(free_list[n_free - 1 - k]) for k in range(need)]
+        if any(not (0 <= pg < n_pages) for pg in new):
+            flags[b] |= FLAG_BAD_PAGE
+            continue
+        n_free -= need
+        page_table[b, have:have + need] = new
+        for o in range(a):
+            pos = P + o
+            pg = page_table[b, pos // page]
+            Kt[pg, pos % page] = k_cand[b * M + i * D + o]
+            Vt[pg, pos % page] = v_cand[b * M + i * D + o]
+        prefix_len[b] = P + a
+    return k_pool, v_pool, page_table, prefix_len, free_list, n_free, flags
+
+
+def kv_truncate(page_table, prefix_len, new_len, free_list, n_free, n_pages, page=16):
+    """Roll sequences back to new_len[b] tokens: the pages past the ones new_len needs
+    return to the free stack (sequence order, ascending page index within a sequence,
+    so the last page pushed is the sequence's highest) and their page-table entries
+    become -1.  Token data is not touched.  A sequence is skipped with FLAG_BAD_PAGE
+    when new_len is outside [0, prefix_len[b]], when prefix_len is out of range or
+    when a page to free is not a pool page.  Returns copies: (page_table, prefix_len,
+    free_list, n_free, flags)."""
+    page_table = np.array(page_table, dtype=np.int32, copy=True)
+    prefix_len = np.array(prefix_len, dtype=np.int32, copy=True)
+    free_list = np.array(free_list, dtype=np.int32, copy=True)
+    n_free = int(n_free)
+    B, max_pages = page_table.shape
+    flags = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        P, L = int(prefix_len[b]), int(new_len[b])
+        if P < 0 or P > max_pages * page or L < 0 or L > P:
+            flags[b] |= FLAG_BAD_PAGE
+            continue
+        keep, have = _pages_for(L, page), _pages_for(P, page)
+        freed = [int(page_table[b, j]) for j in range(keep, have)]
+        if any(not (0 <= pg < n_pages) for pg in freed) or n_free + len(freed) > len(free_list):
+            flags[b] |= FLAG_BAD_PAGE
+            continue
+        for pg in freed:
+            free_list[n_free] = pg
+            n_free += 1
+        page_table[b, keep:have] = -1
+        prefix_len[b] = L
+    return page_table, prefix_len, free_list, n_free, flags
 
 
 # ----------------------------------------------------------------------------------

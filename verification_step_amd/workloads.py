@@ -366,3 +366,39 @@ def draft_probs_from_logits(rng, shape, sigma: float, block_rows: int = 64) -> n
         e = np.exp(z)
         out[s:s + m] = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
     return out
+
+
+def make_kv_case(seed: int, B: int, W: int, D: int, Hkv: int, hd: int, prefix, n_spare: int,
+                 max_pages: int, dtype: str = "bf16"):
+    """Inputs of a KV commit / rollback: a paged pool whose first pages hold the
+    sequences' prefixes (pages in random order), `n_spare` further pages on a free
+    stack (random order), candidate K/V rows and a random accepted candidate and run
+    length per sequence.  Model tensors are bf16 bits (uint16) or float32.
+
+    Arrays: k_pool [n_pages, Hkv, 16, hd], v_pool [n_pages, Hkv, hd, 16],
+    page_table int32 [B, max_pages] (-1 past the prefix), prefix_len int32 [B],
+    free_list int32 [n_pages] (the stack in its first n_free entries), n_free,
+    k_cand/v_cand [B*W*D, Hkv, hd], best int32 [B] (-1 = none), n_acc int32 [B]."""
+    rng = np.random.default_rng(seed)
+    prefix = np.asarray(prefix, dtype=np.int64)
+    used = [(int(p) + PAGE - 1) // PAGE for p in prefix]
+    n_pages = int(sum(used)) + int(n_spare)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    pt = np.full((B, max_pages), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        pt[b, :used[b]] = perm[k:k + used[b]]
+        k += used[b]
+    free = np.zeros(n_pages, dtype=np.int32)
+    free[:n_spare] = perm[k:]
+    if dtype == "bf16":
+        mk = lambda shp: f32_to_bf16_bits(rng.standard_normal(shp).astype(np.float32))
+    else:
+        mk = lambda shp: rng.standard_normal(shp).astype(np.float32)
+    M = W * D
+    return dict(
+        k_pool=mk((n_pages, Hkv, PAGE, hd)), v_pool=mk((n_pages, Hkv, hd, PAGE)),
+        page_table=pt, prefix_len=prefix.astype(np.int32), free_list=free,
+        n_free=int(n_spare), k_cand=mk((B * M, Hkv, hd)), v_cand=mk((B * M, Hkv, hd)),
+        best=rng.integers(-1, W, size=B).astype(np.int32),
+        n_acc=rng.integers(0, D + 1, size=B).astype(np.int32))

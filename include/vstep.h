@@ -73,7 +73,8 @@ enum {
     VS_FLAG_NO_CANDIDATE = 16,        /* gate closed or no candidate: one token from the root p */
     VS_FLAG_BAD_PAGE = 32,            /* page index outside the pool, or prefix_len out of range */
     VS_FLAG_BAD_CTX = 64,             /* context offsets outside [0, ctx_total] or decreasing */
-    VS_FLAG_BAD_TOKEN = 128           /* a tested candidate token id is outside [0, V): rejected */
+    VS_FLAG_BAD_TOKEN = 128,          /* a tested candidate token id is outside [0, V): rejected */
+    VS_FLAG_POOL_EMPTY = 256          /* kv commit: fewer free pages than a sequence needs */
 };
 
 int         vs_abi_version(void);
@@ -297,6 +298,55 @@ typedef struct {
 size_t vs_step_workspace_bytes(const vs_step_desc *desc);
 int vs_verify_step(const vs_step_desc *desc, const vs_step_io *io, void *workspace,
                    size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * KV commit and rollback over the paged cache [SD section 6: the KV blocks of rejected
+ * tokens go back to the paged pool at once, and none may leak].  The verify step
+ * reads the candidates' K/V from their own buffers and leaves the cache untouched;
+ * these calls then keep what was accepted.
+ *
+ * Cache model (as vs_verify_attention reads it): pages of 16 tokens, k_pool
+ * [n_pool_pages, Hkv, 16, head_dim], v_pool [n_pool_pages, Hkv, head_dim, 16];
+ * page_table int32 [B, max_pages], entry j = the pool page of tokens 16j .. 16j+15;
+ * prefix_len int32 [B] (the cache length of each sequence); a free-page stack:
+ * free_list int32 [n_pool_pages] (room for every page) whose first *n_free entries
+ * are the free pages, top of the stack = free_list[*n_free - 1]; n_free is one int32
+ * in device memory.  Page ids are taken and returned in a fixed order -- sequence
+ * order, then page order -- so they do not depend on scheduling.
+ * flags int32 [B] (may be NULL) is written whole: 0, VS_FLAG_POOL_EMPTY or
+ * VS_FLAG_BAD_PAGE for a sequence that was refused (and left untouched).
+ * At most 2048 sequences per call (VS_ERR_UNSUPPORTED beyond). */
+
+typedef struct {
+    int32_t B, W, D, Hkv, head_dim, page_size, max_pages, n_pool_pages;
+    int32_t dtype;            /* vs_dtype of k_cand/v_cand and the pools (element copy) */
+} vs_kv_desc;
+
+size_t vs_kv_workspace_bytes(const vs_kv_desc *desc);
+
+/* Commit: for each sequence b with best[b] in [0, W) and a = min(n_acc[b], D) > 0,
+ * rows (b, best[b], 0 .. a-1) of k_cand/v_cand ([B*W*D, Hkv, head_dim], the verify
+ * step's candidate layout) become tokens P .. P+a-1, P = prefix_len[b]; the pages it
+ * needs beyond ceil(P/16) are popped off the stack; prefix_len[b] becomes P + a.
+ * Refused with VS_FLAG_BAD_PAGE when P < 0 or P + a > 16*max_pages or when its
+ * partly filled last page or a page it would pop is not in [0, n_pool_pages); with
+ * VS_FLAG_POOL_EMPTY when the stack holds fewer pages than it needs (later
+ * sequences may still be served).  best and n_acc are the sampler's outputs. */
+int vs_kv_commit(const vs_kv_desc *desc, const void *k_cand, const void *v_cand,
+                 const int32_t *best, const int32_t *n_acc, void *k_pool, void *v_pool,
+                 int32_t *page_table, int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
+                 int32_t *flags, void *workspace, size_t ws_bytes, void *stream);
+
+/* Rollback: sequence b keeps its first new_len[b] tokens; the pages past
+ * ceil(new_len[b]/16) are pushed onto the stack in ascending page order and their
+ * page-table entries set to -1; prefix_len[b] = new_len[b].  Token data is not
+ * touched.  Refused with VS_FLAG_BAD_PAGE when new_len[b] is outside
+ * [0, prefix_len[b]], prefix_len[b] is out of range, a page to free is not a pool
+ * page, or the stack would overflow.  Only B, page_size, max_pages and n_pool_pages
+ * of the descriptor are read. */
+int vs_kv_truncate(const vs_kv_desc *desc, const int32_t *new_len, int32_t *page_table,
+                   int32_t *prefix_len, int32_t *free_list, int32_t *n_free, int32_t *flags,
+                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -644,8 +644,9 @@ def kv_commit(k_pool, v_pool, page_table, prefix_len, free_list, n_free, k_cand,
     sequence order and, within a sequence, in page order.  Nothing happens for a
     sequence with best < 0 or a = 0.  A sequence is skipped (nothing written, no
     page taken) with FLAG_BAD_PAGE when P + a exceeds the page table, when P is out
-    of range or when a page it would write (its partly filled last page, or a popped
-    one) is not a pool page; with FLAG_POOL_EMPTY when the stack holds fewer pages
+    of range, when a page it would write (its partly filled last page, or a popped
+    one) is not a pool page, or when n_free itself is outside [0, n_pages] (the
+    stack is then not read); with FLAG_POOL_EMPTY when the stack holds fewer pages
     than it needs.  Returns copies: (k_pool, v_pool, page_table, prefix_len,
     free_list, n_free, flags)."""
     k_pool = np.array(k_pool, copy=True)
@@ -659,13 +660,14 @@ def kv_commit(k_pool, v_pool, page_table, prefix_len, free_list, n_free, k_cand,
     M = W * D
     Kt, Vt = token_major(k_pool, "k"), token_major(v_pool, "v")   # views: writes land in the pools
     flags = np.zeros(B, dtype=np.int32)
+    stack_ok = 0 <= n_free <= n_pages
     for b in range(B):
         i = int(best[b])
         a = min(max(int(n_acc[b]), 0), D)
         if i < 0 or i >= W or a == 0:
             continue
         P = int(prefix_len[b])
-        if P < 0 or P + a > max_pages * page:
+        if not stack_ok or P < 0 or P + a > max_pages * page:
             flags[b] |= FLAG_BAD_PAGE
             continue
         have = _pages_for(P, page)
@@ -696,8 +698,9 @@ def kv_truncate(page_table, prefix_len, new_len, free_list, n_free, n_pages, pag
     return to the free stack (sequence order, ascending page index within a sequence,
     so the last page pushed is the sequence's highest) and their page-table entries
     become -1.  Token data is not touched.  A sequence is skipped with FLAG_BAD_PAGE
-    when new_len is outside [0, prefix_len[b]], when prefix_len is out of range or
-    when a page to free is not a pool page.  Returns copies: (page_table, prefix_len,
+    when new_len is outside [0, prefix_len[b]], when prefix_len is out of range,
+    when a page to free is not a pool page, when the stack would overflow, or (all
+    sequences) when n_free itself is outside [0, n_pages].  Returns copies: (page_table, prefix_len,
     free_list, n_free, flags)."""
     page_table = np.array(page_table, dtype=np.int32, copy=True)
     prefix_len = np.array(prefix_len, dtype=np.int32, copy=True)
@@ -705,14 +708,15 @@ def kv_truncate(page_table, prefix_len, new_len, free_list, n_free, n_pages, pag
     n_free = int(n_free)
     B, max_pages = page_table.shape
     flags = np.zeros(B, dtype=np.int32)
+    stack_ok = 0 <= n_free <= n_pages
     for b in range(B):
         P, L = int(prefix_len[b]), int(new_len[b])
-        if P < 0 or P > max_pages * page or L < 0 or L > P:
+        if not stack_ok or P < 0 or P > max_pages * page or L < 0 or L > P:
             flags[b] |= FLAG_BAD_PAGE
             continue
         keep, have = _pages_for(L, page), _pages_for(P, page)
         freed = [int(page_table[b, j]) for j in range(keep, have)]
-        if any(not (0 <= pg < n_pages) for pg in freed) or n_free + len(freed) > len(free_list):
+        if any(not (0 <= pg < n_pages) for pg in freed) or n_free + len(freed) > n_pages:
             flags[b] |= FLAG_BAD_PAGE
             continue
         for pg in freed:

@@ -61,6 +61,7 @@ def test_struct_layouts_match_header():
     assert C.sizeof(L.AttnDesc) == 44
     assert C.sizeof(L.HeadDesc) == 28
     assert C.sizeof(L.SampleDesc) == 24
+    assert C.sizeof(L.KvDesc) == 36
 
 
 def test_copy_match_validation(lib):
@@ -201,3 +202,31 @@ def test_step_validation(lib):
     assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 16, None) == -3
     d5 = L.StepDesc(**{**base, "accept_mode": 7})
     assert lib.vs_step_workspace_bytes(C.byref(d5)) == 0
+
+
+def test_kv_validation(lib):
+    fake = C.c_void_p(16)
+    ok = dict(B=4, W=4, D=20, Hkv=8, head_dim=128, page_size=16, max_pages=64, n_pool_pages=300,
+              dtype=1)
+    d = L.KvDesc(**ok)
+    assert lib.vs_kv_workspace_bytes(C.byref(d)) >= 4 * 3 * 4
+    args = [fake] * 11
+
+    def commit(desc, a=args, nbytes=1 << 20):
+        return lib.vs_kv_commit(C.byref(desc), *a, fake, nbytes, None)
+
+    assert commit(L.KvDesc(**{**ok, "page_size": 8})) == -2
+    assert commit(L.KvDesc(**{**ok, "B": 0})) == -1
+    assert commit(L.KvDesc(**{**ok, "B": 2049})) == -2
+    assert commit(L.KvDesc(**{**ok, "dtype": 5})) == -2
+    assert commit(L.KvDesc(**{**ok, "W": 0})) == -1
+    assert commit(d, nbytes=8) == -3
+    bad = list(args)
+    bad[9] = None                               # n_free
+    assert commit(d, bad) == -1
+    assert lib.vs_kv_workspace_bytes(C.byref(L.KvDesc(**{**ok, "max_pages": 0}))) == 0
+    # truncate reads only B, page_size, max_pages, n_pool_pages
+    tr = L.KvDesc(**{**ok, "W": 0, "D": 0, "Hkv": 0, "head_dim": 0, "dtype": 9})
+    assert lib.vs_kv_truncate(C.byref(tr), fake, fake, fake, fake, None, None, None) == -1
+    assert lib.vs_kv_truncate(C.byref(L.KvDesc(**{**ok, "page_size": 32})), *([fake] * 6),
+                              None) == -2

@@ -554,6 +554,144 @@ def test_reject_sample_greedy(B, W, D, V, T):
     assert (o["flags"] & oracle.FLAG_CDF_TIE).any() or (o["flags"] & oracle.FLAG_ACCEPT_TIE).any()
 
 
+# =============================================================================== KV commit
+
+def _kv_dev(A, dtype):
+    import torch
+    out = {}
+    for k, v in A.items():
+        if isinstance(v, np.ndarray):
+            t = torch.from_numpy(np.ascontiguousarray(v))
+            if dtype == "bf16" and v.dtype == np.uint16:
+                t = t.view(torch.bfloat16)
+            out[k] = t.cuda()
+    import torch as _t
+    out["n_free"] = _t.tensor([A["n_free"]], dtype=_t.int32, device="cuda")
+    return out
+
+
+def _kv_host(G):
+    import torch
+    out = {}
+    for k, t in G.items():
+        if t.dtype == torch.bfloat16:
+            out[k] = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            out[k] = t.cpu().numpy()
+    out["n_free"] = int(out["n_free"][0])
+    return out
+
+
+def _kv_check(G, A, flags_g, flags_o):
+    H = _kv_host(G)
+    assert np.array_equal(flags_g, flags_o)
+    for k in ("page_table", "prefix_len", "k_pool", "v_pool"):
+        assert np.array_equal(H[k], A[k]), k
+    assert H["n_free"] == A["n_free"]
+    nf = min(max(A["n_free"], 0), len(A["free_list"]))
+    assert np.array_equal(H["free_list"][:nf], A["free_list"][:nf])
+
+
+@pytest.mark.parametrize("dtype,Hkv,hd", [("bf16", 8, 128), ("f32", 2, 64)])
+def test_kv_commit_and_truncate_rounds(dtype, Hkv, hd):
+    """Rounds of commit (fresh candidates and accepted runs each round) and random
+    rollbacks: pools, page tables, lengths, the free stack and the flags equal the
+    oracle's bit for bit after every call."""
+    api = _api()
+    B, W, D = 7, 3, 9
+    A = wl.make_kv_case(3, B, W, D, Hkv, hd, [0, 1, 15, 16, 17, 40, 100], n_spare=30,
+                        max_pages=16, dtype=dtype)
+    G = _kv_dev(A, dtype)
+    rng = np.random.default_rng(12)
+    for rnd in range(5):
+        fresh = wl.make_kv_case(50 + rnd, B, W, D, Hkv, hd, [0] * B, 0, 16, dtype)
+        if rnd == 3:
+            # full runs against a stack cut down to one page: refusals
+            fresh["n_acc"][:] = D
+            A["n_free"] = 1
+            G["n_free"].fill_(1)
+        for k in ("k_cand", "v_cand", "best", "n_acc"):
+            A[k] = fresh[k]
+            G[k] = _kv_dev({k: fresh[k], "n_free": 0}, dtype)[k]
+        say("kv commit", dtype, rnd)
+        fg = api.kv_commit(G["k_cand"], G["v_cand"], G["best"], G["n_acc"], G["k_pool"],
+                           G["v_pool"], G["page_table"], G["prefix_len"], G["free_list"],
+                           G["n_free"], W, D)
+        k, v, pt, P, fl, nf, fo = oracle.kv_commit(
+            A["k_pool"], A["v_pool"], A["page_table"], A["prefix_len"], A["free_list"],
+            A["n_free"], A["k_cand"], A["v_cand"], A["best"], A["n_acc"], W, D)
+        A.update(k_pool=k, v_pool=v, page_table=pt, prefix_len=P, free_list=fl, n_free=nf)
+        _kv_check(G, A, tensor_np(fg), fo)
+        if rnd == 3:
+            assert (fo == oracle.FLAG_POOL_EMPTY).any()
+        cut = np.array([rng.integers(0, int(p) + 1) if rng.random() < 0.5 else int(p)
+                        for p in A["prefix_len"]], dtype=np.int32)
+        cut[0] = int(A["prefix_len"][0]) + 1    # above the length: refused
+        say("kv truncate", dtype, rnd)
+        fg = api.kv_truncate(to_dev(cut), G["page_table"], G["prefix_len"], G["free_list"],
+                             G["n_free"], A["k_pool"].shape[0])
+        pt, P, fl, nf, fo = oracle.kv_truncate(A["page_table"], A["prefix_len"], cut,
+                                               A["free_list"], A["n_free"], A["k_pool"].shape[0])
+        A.update(page_table=pt, prefix_len=P, free_list=fl, n_free=nf)
+        _kv_check(G, A, tensor_np(fg), fo)
+    assert (fo == oracle.FLAG_BAD_PAGE).sum() == 1
+
+
+def test_kv_bad_stack_count():
+    """A free-stack count outside [0, n_pool_pages] is not read from: every request is
+    refused, as in the oracle."""
+    api = _api()
+    B, W, D = 3, 2, 4
+    A = wl.make_kv_case(7, B, W, D, 2, 64, [3, 20, 0], n_spare=4, max_pages=6, dtype="f32")
+    A["best"][:] = [0, 1, 0]
+    A["n_acc"][:] = [4, 4, 0]
+    for nf in (-1, A["k_pool"].shape[0] + 1):
+        A2 = dict(A, n_free=nf)
+        G = _kv_dev(A2, "f32")
+        say("kv bad stack", nf)
+        fg = api.kv_commit(G["k_cand"], G["v_cand"], G["best"], G["n_acc"], G["k_pool"],
+                           G["v_pool"], G["page_table"], G["prefix_len"], G["free_list"],
+                           G["n_free"], W, D)
+        k, v, pt, P, fl, n2, fo = oracle.kv_commit(
+            A2["k_pool"], A2["v_pool"], A2["page_table"], A2["prefix_len"], A2["free_list"], nf,
+            A2["k_cand"], A2["v_cand"], A2["best"], A2["n_acc"], W, D)
+        _kv_check(G, dict(A2, k_pool=k, v_pool=v, page_table=pt, prefix_len=P, free_list=fl,
+                          n_free=n2), tensor_np(fg), fo)
+        fg = api.kv_truncate(to_dev(np.zeros(B, np.int32)), G["page_table"], G["prefix_len"],
+                             G["free_list"], G["n_free"], A["k_pool"].shape[0])
+        assert (tensor_np(fg) == oracle.FLAG_BAD_PAGE).all()
+        assert int(tensor_np(G["n_free"])[0]) == nf
+
+
+def test_kv_commit_ragged_batch_full_size():
+    """The batched ragged shape (32 sequences, 4 x 8 candidates, 8 KV heads of 128, 16-token
+    pages in random order, prefixes 512..2048): one commit of the accepted runs and one
+    rollback to the old lengths, against the oracle; the rollback restores the stack's
+    page set and the page tables."""
+    api = _api()
+    rng = np.random.default_rng(77)
+    B, W, D = 32, 4, 8
+    prefix = rng.integers(512, 2049, size=B)
+    A = wl.make_kv_case(8, B, W, D, 8, 128, prefix, n_spare=64, max_pages=160)
+    G = _kv_dev(A, "bf16")
+    say("kv commit ragged")
+    fg = api.kv_commit(G["k_cand"], G["v_cand"], G["best"], G["n_acc"], G["k_pool"], G["v_pool"],
+                       G["page_table"], G["prefix_len"], G["free_list"], G["n_free"], W, D)
+    k, v, pt, P, fl, nf, fo = oracle.kv_commit(
+        A["k_pool"], A["v_pool"], A["page_table"], A["prefix_len"], A["free_list"], A["n_free"],
+        A["k_cand"], A["v_cand"], A["best"], A["n_acc"], W, D)
+    C = dict(A, k_pool=k, v_pool=v, page_table=pt, prefix_len=P, free_list=fl, n_free=nf)
+    _kv_check(G, C, tensor_np(fg), fo)
+    say("kv truncate ragged")
+    fg = api.kv_truncate(to_dev(A["prefix_len"]), G["page_table"], G["prefix_len"],
+                         G["free_list"], G["n_free"], A["k_pool"].shape[0])
+    H = _kv_host(G)
+    assert not tensor_np(fg).any()
+    assert np.array_equal(H["page_table"], A["page_table"])
+    assert np.array_equal(H["prefix_len"], A["prefix_len"])
+    assert sorted(H["free_list"][:H["n_free"]]) == sorted(A["free_list"][:A["n_free"]])
+
+
 # =============================================================================== whole step
 
 def _step_inputs(case, T, external=None):

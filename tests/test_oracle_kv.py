@@ -155,3 +155,17 @@ def test_truncate_round_trip_and_bad_lengths():
     assert list(Z["prefix_len"]) == [0, 0, 23, 64]
     assert (Z["page_table"][:2] == -1).all()
     assert conserved(Z, A["k_pool"].shape[0])
+
+
+def test_bad_stack_count_refuses_everything():
+    B, W, D = 3, 2, 4
+    A = wl.make_kv_case(7, B, W, D, 1, 4, [3, 20, 0], n_spare=4, max_pages=6, dtype="f32")
+    A["best"][:] = [0, 1, 0]
+    A["n_acc"][:] = [4, 4, 0]
+    for nf in (-1, A["k_pool"].shape[0] + 1):
+        A2 = dict(A, n_free=nf)
+        C, flags = commit(A2, W, D)
+        assert flags.tolist() == [oracle.FLAG_BAD_PAGE, oracle.FLAG_BAD_PAGE, 0]
+        assert C["n_free"] == nf and np.array_equal(C["prefix_len"], A["prefix_len"])
+        R, flags = truncate(A2, np.zeros(B, np.int32))
+        assert (flags == oracle.FLAG_BAD_PAGE).all() and R["n_free"] == nf

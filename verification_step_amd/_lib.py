@@ -23,12 +23,14 @@ FLAG_NO_CANDIDATE = 16
 FLAG_BAD_PAGE = 32
 FLAG_BAD_CTX = 64
 FLAG_BAD_TOKEN = 128
+FLAG_POOL_EMPTY = 256
 
 EXPORTED = [
     "vs_abi_version", "vs_status_str", "vs_copy_match", "vs_probe_gate",
     "vs_attention_workspace_bytes", "vs_verify_attention", "vs_head_workspace_bytes",
     "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
     "vs_step_workspace_bytes", "vs_verify_step", "vs_packed_weight_bytes", "vs_pack_weight",
+    "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate",
 ]
 
 P = C.c_void_p
@@ -57,6 +59,11 @@ class StepDesc(C.Structure):
                 ("n_pool_pages", I32), ("d", I32), ("V", I32), ("dtype", I32),
                 ("scale", C.c_float), ("tau", C.c_float), ("temperature", C.c_float),
                 ("external_drafts", I32), ("ctx_total", C.c_int64), ("accept_mode", I32)]
+
+
+class KvDesc(C.Structure):
+    _fields_ = [("B", I32), ("W", I32), ("D", I32), ("Hkv", I32), ("head_dim", I32),
+                ("page_size", I32), ("max_pages", I32), ("n_pool_pages", I32), ("dtype", I32)]
 
 
 class StepIO(C.Structure):
@@ -105,6 +112,10 @@ def load(path: str = LIB_PATH):
     lib.vs_packed_weight_bytes.restype = C.c_size_t
     lib.vs_packed_weight_bytes.argtypes = [C.c_int, C.c_int]
     lib.vs_pack_weight.argtypes = [P, P, C.c_int, C.c_int, P]
+    lib.vs_kv_workspace_bytes.restype = C.c_size_t
+    lib.vs_kv_workspace_bytes.argtypes = [C.POINTER(KvDesc)]
+    lib.vs_kv_commit.argtypes = [C.POINTER(KvDesc)] + [P] * 12 + [C.c_size_t, P]
+    lib.vs_kv_truncate.argtypes = [C.POINTER(KvDesc)] + [P] * 7
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
             getattr(lib, fn).restype = C.c_int

@@ -266,6 +266,57 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
 
 # ---------------------------------------------------------------------------------
 
+def _kv_desc(k_pool, page_table, W: int, D: int):
+    """k_pool [n_pages, Hkv, 16, hd]."""
+    B, max_pages = page_table.shape
+    return L.KvDesc(B, W, D, k_pool.shape[1], k_pool.shape[3], 16, max_pages, k_pool.shape[0],
+                    _vs_dtype(k_pool))
+
+
+def kv_commit(k_cand, v_cand, best, n_acc, k_pool, v_pool, page_table, prefix_len, free_list,
+              n_free, W: int, D: int):
+    """Append each sequence's accepted candidate rows to its paged cache, in place (pools,
+    page_table, prefix_len, free_list, n_free).  Returns the per-sequence flags."""
+    lib = L.load()
+    for t, dt, n in ((best, torch.int32, "best"), (n_acc, torch.int32, "n_acc"),
+                     (page_table, torch.int32, "page_table"),
+                     (prefix_len, torch.int32, "prefix_len"), (free_list, torch.int32, "free_list"),
+                     (n_free, torch.int32, "n_free")):
+        _check(t, dt, n)
+    for t, n in ((k_cand, "k_cand"), (v_cand, "v_cand"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _check(t, k_pool.dtype, n)
+    desc = _kv_desc(k_pool, page_table, W, D)
+    flags = torch.empty(page_table.shape[0], dtype=torch.int32, device=page_table.device)
+    nbytes = lib.vs_kv_workspace_bytes(C.byref(desc))
+    if nbytes == 0:
+        raise VstepError(L.VS_ERR_INVALID_ARG, "kv_commit (descriptor rejected)")
+    ws = workspace(nbytes, page_table.device, "kv")
+    st = lib.vs_kv_commit(C.byref(desc), _ptr(k_cand), _ptr(v_cand), _ptr(best), _ptr(n_acc),
+                          _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(prefix_len),
+                          _ptr(free_list), _ptr(n_free), _ptr(flags), _ptr(ws), ws.numel(),
+                          _stream())
+    _raise(st, "kv_commit")
+    return flags
+
+
+def kv_truncate(new_len, page_table, prefix_len, free_list, n_free, n_pool_pages: int):
+    """Roll sequences back to new_len tokens, in place; freed pages go back on the stack.
+    Returns the per-sequence flags."""
+    lib = L.load()
+    for t, n in ((new_len, "new_len"), (page_table, "page_table"), (prefix_len, "prefix_len"),
+                 (free_list, "free_list"), (n_free, "n_free")):
+        _check(t, torch.int32, n)
+    B, max_pages = page_table.shape
+    desc = L.KvDesc(B, 1, 1, 1, 1, 16, max_pages, int(n_pool_pages), 0)
+    flags = torch.empty(B, dtype=torch.int32, device=page_table.device)
+    st = lib.vs_kv_truncate(C.byref(desc), _ptr(new_len), _ptr(page_table), _ptr(prefix_len),
+                            _ptr(free_list), _ptr(n_free), _ptr(flags), _stream())
+    _raise(st, "kv_truncate")
+    return flags
+
+
+# ---------------------------------------------------------------------------------
+
 class VerifyStep:
     """One verify step bound to fixed device buffers, so that repeated calls (timing,
     a decode loop) enqueue the step without any host-side allocation.  A 2-D bf16

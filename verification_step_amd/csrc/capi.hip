@@ -352,4 +352,51 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   return VS_OK;
 }
 
+static int check_kv(const vs_kv_desc *d, bool commit) {
+  if (!d) return VS_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->max_pages <= 0 || d->n_pool_pages <= 0) return VS_ERR_INVALID_ARG;
+  if (d->page_size != 16) return VS_ERR_UNSUPPORTED;
+  if (d->B > vs::kMaxSeqKv) return VS_ERR_UNSUPPORTED;
+  if ((int64_t)d->max_pages * 16 > (1 << 28)) return VS_ERR_UNSUPPORTED;
+  if (commit) {
+    if (d->W <= 0 || d->D <= 0 || d->Hkv <= 0 || d->head_dim <= 0) return VS_ERR_INVALID_ARG;
+    if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
+    if (d->dtype != VS_BF16 && d->dtype != VS_F32) return VS_ERR_UNSUPPORTED;
+  }
+  return VS_OK;
+}
+
+size_t vs_kv_workspace_bytes(const vs_kv_desc *d) {
+  if (check_kv(d, true) != VS_OK) return 0;
+  return vs::kv_workspace_bytes(d->B);
+}
+
+int vs_kv_commit(const vs_kv_desc *d, const void *k_cand, const void *v_cand, const int32_t *best,
+                 const int32_t *n_acc, void *k_pool, void *v_pool, int32_t *page_table,
+                 int32_t *prefix_len, int32_t *free_list, int32_t *n_free, int32_t *flags,
+                 void *workspace, size_t ws_bytes, void *stream) {
+  const int st = check_kv(d, true);
+  if (st != VS_OK) return st;
+  if (!k_cand || !v_cand || !best || !n_acc || !k_pool || !v_pool || !page_table ||
+      !prefix_len || !free_list || !n_free)
+    return VS_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < vs::kv_workspace_bytes(d->B)) return VS_ERR_WORKSPACE;
+  return hip_status(vs::launch_kv_commit(d->B, d->W, d->D, d->Hkv, d->head_dim, d->max_pages,
+                                         d->n_pool_pages, d->dtype == VS_BF16 ? 2 : 4, k_cand,
+                                         v_cand, best, n_acc, k_pool, v_pool, page_table,
+                                         prefix_len, free_list, n_free, flags, workspace,
+                                         S(stream)));
+}
+
+int vs_kv_truncate(const vs_kv_desc *d, const int32_t *new_len, int32_t *page_table,
+                   int32_t *prefix_len, int32_t *free_list, int32_t *n_free, int32_t *flags,
+                   void *stream) {
+  const int st = check_kv(d, false);
+  if (st != VS_OK) return st;
+  if (!new_len || !page_table || !prefix_len || !free_list || !n_free) return VS_ERR_INVALID_ARG;
+  return hip_status(vs::launch_kv_truncate(d->B, d->max_pages, d->n_pool_pages, new_len,
+                                           page_table, prefix_len, free_list, n_free, flags,
+                                           S(stream)));
+}
+
 }  // extern "C"

@@ -19,7 +19,8 @@ constexpr int kHeadVocabTile = 256;
 // flag bits (same values as the public header)
 enum : int {
   FLAG_PROBE_TIE = 1, FLAG_ACCEPT_TIE = 2, FLAG_CDF_TIE = 4, FLAG_DEGENERATE = 8,
-  FLAG_NO_CANDIDATE = 16, FLAG_BAD_PAGE = 32, FLAG_BAD_CTX = 64, FLAG_BAD_TOKEN = 128
+  FLAG_NO_CANDIDATE = 16, FLAG_BAD_PAGE = 32, FLAG_BAD_CTX = 64, FLAG_BAD_TOKEN = 128,
+  FLAG_POOL_EMPTY = 256
 };
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
@@ -194,5 +195,17 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
                           const double *u_acc = nullptr);
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
+
+// ---- KV commit and rollback (kv.hip)
+constexpr int kMaxSeqKv = 2048;   // sequences per call
+size_t kv_workspace_bytes(int B);
+hipError_t launch_kv_commit(int B, int W, int D, int Hkv, int hd, int max_pages, int n_pool_pages,
+                            int esz, const void *k_cand, const void *v_cand, const int32_t *best,
+                            const int32_t *n_acc, void *k_pool, void *v_pool, int32_t *page_table,
+                            int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
+                            int32_t *flags, void *ws, hipStream_t st);
+hipError_t launch_kv_truncate(int B, int max_pages, int n_pool_pages, const int32_t *new_len,
+                              int32_t *page_table, int32_t *prefix_len, int32_t *free_list,
+                              int32_t *n_free, int32_t *flags, hipStream_t st);
 
 }  // namespace vs

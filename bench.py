@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--accept", choices=["longest", "multi", "greedy"], default="longest",
                     help="longest verified run (default), lossless multi-candidate "
                          "acceptance (copy candidates as point-mass drafts) or greedy")
+    ap.add_argument("--commit", action="store_true",
+                    help="after each step, commit the accepted rows to the paged KV cache and "
+                         "roll back to the old lengths (times the decode loop's cache update)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -220,6 +223,23 @@ def main():
     I = upload(case)
     B, W, D, M = sh.B, sh.W, sh.D, sh.M
     draft, drafts = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else (None, None)
+    kv = None
+    if args.commit and not sh.external_drafts:
+        # room for a full accepted run per sequence: spare pool pages on a free stack and
+        # page-table columns past the longest prefix
+        extra_cols = (D + 15) // 16 + 1
+        n_spare = B * extra_cols
+        n0 = I["k_pool"].shape[0]
+        for name in ("k_pool", "v_pool"):
+            t = I[name]
+            I[name] = torch.cat([t, torch.zeros((n_spare,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                                device=dev)])
+        I["page_table"] = torch.cat([I["page_table"],
+                                     torch.full((B, extra_cols), -1, dtype=torch.int32,
+                                                device=dev)], dim=1).contiguous()
+        kv = dict(free=torch.arange(n0, n0 + n_spare, dtype=torch.int32, device=dev),
+                  n_free=torch.tensor([n_spare], dtype=torch.int32, device=dev),
+                  P0=I["prefix_len"].clone(), n_pages=n0 + n_spare)
     if args.accept == "multi" and not sh.external_drafts:
         I["q_draft"] = None                      # copy candidates judged as point masses
     if args.accept == "greedy":
@@ -252,11 +272,21 @@ def main():
         step.io.v_pool = vp.data_ptr()
         step.io.w_full = heads[k % len(heads)].data_ptr()
 
+    def commit(k):
+        kp, vp = pools[k % len(pools)]
+        o = step.out
+        api.kv_commit(I["k_cand"], I["v_cand"], o["best"], o["n_acc"], kp, vp, I["page_table"],
+                      I["prefix_len"], kv["free"], kv["n_free"], W, D)
+        api.kv_truncate(kv["P0"], I["page_table"], I["prefix_len"], kv["free"], kv["n_free"],
+                        kv["n_pages"])
+
     def run(k):
         bind(k)
         if draft is not None:
             draft()
         step()
+        if kv is not None:
+            commit(k)
 
     K, Wm = args.steps, args.warmup
     for k in range(Wm):
@@ -294,6 +324,19 @@ def main():
     torch.cuda.synchronize()
     step.use_events(None)
     ms_staged = t0.elapsed_time(t1) / K
+    commit_ms = None
+    if kv is not None:
+        # pass 3: the cache update alone (commit + rollback) after each step
+        tc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for k in range(K):
+            bind(Wm + k)
+            step()
+            tc[k][0].record()
+            commit(Wm + k)
+            tc[k][1].record()
+        torch.cuda.synchronize()
+        commit_ms = float(np.mean([a.elapsed_time(b) for a, b in tc]))
 
     names = ["retrieval_gate", "attention", "head_gemm", "lse_tests", "sampler"]
     stage_ms = {}
@@ -338,6 +381,8 @@ def main():
                         "without stage events, stages from a second pass with them"}
     if args.accept != "longest":
         config["accept"] = args.accept
+    if kv is not None:
+        config["commit"] = "accepted rows committed to the paged cache, then rolled back"
     if draft is not None:
         config.update({"draft_head": "low-rank r=%d, gamma=%d, probabilities into q"
                                      % (sh.rank, sh.gamma), "drafts": "external"})
@@ -367,6 +412,8 @@ def main():
                                                         af / MFMA_PEAK[dt_name]) / att_s},
         "accepted": [int(x) for x in out["n_acc"].cpu().tolist()][:4],
     }
+    if commit_ms is not None:
+        rec["kv_commit_rollback_us"] = commit_ms * 1e3
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, sh, drafts, accept=args.accept)
     print(json.dumps(rec), flush=True)

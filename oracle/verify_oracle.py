@@ -131,6 +131,47 @@ def copy_match(ctx: np.ndarray, ctx_off: np.ndarray, kappa: int, W: int, D: int)
                 n_found=n_found, flags=flags)
 
 
+def copy_labels(ctx: np.ndarray, ctx_off: np.ndarray, kappa: int = 5, labels_init=None):
+    """Copy-mode labels [SW "어떻게 동작하나"]: a token position is labelled Y = 1 when it
+    lies inside a verbatim run of at least kappa tokens that already appeared earlier
+    in the same context.
+
+    Readings: "earlier" means the earlier occurrence starts at a smaller position (it
+    may overlap the later one, as copy_match's occurrences may); every run of length
+    L >= kappa holds a kappa-gram at each of its offsets, each of which also occurs
+    earlier, so a position is labelled iff some kappa-gram window [s, s+kappa) that
+    covers it occurs at a start t < s.  Written that way here: R[s] marks a repeated
+    kappa-gram start, Y[p] = OR of R over the windows covering p.
+
+    The offsets must be non-decreasing with ctx_off[0] >= 0 and ctx_off[B] <= len(ctx);
+    otherwise every sequence gets FLAG_BAD_CTX and nothing is written.  Positions
+    outside [ctx_off[0], ctx_off[B]) keep labels_init (0 by default).  Returns
+    (labels uint8 [len(ctx)], flags int32 [B])."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    off = np.asarray(ctx_off, dtype=np.int64)
+    B = len(off) - 1
+    labels = (np.zeros(len(ctx), dtype=np.uint8) if labels_init is None
+              else np.array(labels_init, dtype=np.uint8, copy=True))
+    flags = np.zeros(B, dtype=np.int32)
+    if off[0] < 0 or off[B] > len(ctx) or (np.diff(off) < 0).any():
+        flags[:] = FLAG_BAD_CTX
+        return labels, flags
+    for b in range(B):
+        lo, hi = int(off[b]), int(off[b + 1])
+        first = {}
+        R = np.zeros(max(hi - lo, 0), dtype=bool)
+        for s in range(lo, hi - kappa + 1):
+            g = tuple(ctx[s:s + kappa])
+            if g in first:
+                R[s - lo] = True
+            else:
+                first[g] = s
+        for p in range(lo, hi):
+            s0, s1 = max(lo, p - kappa + 1), min(p, hi - kappa)
+            labels[p] = 1 if any(R[s - lo] for s in range(s0, s1 + 1)) else 0
+    return labels, flags
+
+
 # ----------------------------------------------------------------------------------
 # a2: probe gate  [SW, "어떻게 동작하나" (bias-free probe) and "무엇과 다른가" (dual gate)]
 

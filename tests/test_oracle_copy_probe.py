@@ -154,3 +154,67 @@ def test_forced_open_recipe_fires_probe():
         A = case.arrays
         r = oracle.probe_gate(oracle.as_f64(A["probe_h"], sh.dtype), A["probe_w"], sh.tau)
         assert (r["probe"] == 1).all()
+
+
+# ----------------------------------------------------------------- copy-mode labels
+
+def _labels_brute(ctx, lo, hi, kappa):
+    """The label rule word for word: every run [s, s+L) with L >= kappa that equals an
+    earlier run [t, t+L), t < s, labels its L positions."""
+    c = [int(x) for x in ctx[lo:hi]]
+    n = len(c)
+    y = [0] * n
+    for s in range(n):
+        for L in range(kappa, n - s + 1):
+            if any(c[t:t + L] == c[s:s + L] for t in range(s)):
+                for p in range(s, s + L):
+                    y[p] = 1
+    return y
+
+
+@pytest.mark.parametrize("seed,kappa", [(0, 5), (1, 5), (2, 3), (3, 1), (4, 7)])
+def test_copy_labels_match_the_rule_word_for_word(seed, kappa):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 40, size=5)
+    parts = []
+    for n in lens:
+        c = rng.integers(0, 4, size=n)            # small alphabet: many repeats
+        if n > 20 and rng.random() < 0.7:         # plant a longer verbatim repeat
+            a = int(rng.integers(0, n - 12))
+            c[n - 9:n - 1] = c[a:a + 8]
+        parts.append(c)
+    ctx = np.concatenate(parts).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    y, flags = oracle.copy_labels(ctx, off, kappa)
+    assert not flags.any()
+    for b in range(5):
+        assert y[off[b]:off[b + 1]].tolist() == _labels_brute(ctx, off[b], off[b + 1], kappa)
+
+
+def test_copy_labels_examples():
+    #          0  1  2  3  4  5  6  7  8  9 10 11
+    ctx = np.array([1, 2, 3, 4, 5, 9, 1, 2, 3, 4, 5, 8], np.int32)
+    y, _ = oracle.copy_labels(ctx, np.array([0, 12]), 5)
+    assert y.tolist() == [0] * 6 + [1] * 5 + [0]
+    # a run of one token: the 5-gram at 1 repeats the one at 0 (overlapping occurrence)
+    y, _ = oracle.copy_labels(np.full(8, 7, np.int32), np.array([0, 8]), 5)
+    assert y.tolist() == [0] + [1] * 7
+    # four tokens repeated are not enough; the same 5-gram in another sequence does not count
+    y, _ = oracle.copy_labels(np.array([1, 2, 3, 4, 0, 1, 2, 3, 4, 6, 1, 2, 3, 4, 5, 1, 2, 3, 4, 5],
+                                       np.int32), np.array([0, 10, 20]), 5)
+    assert y.tolist() == [0] * 15 + [1] * 5
+    y, _ = oracle.copy_labels(np.array([1, 2, 3, 4, 5, 1, 2, 3, 4, 5], np.int32),
+                              np.array([0, 5, 10]), 5)
+    assert not y.any()
+
+
+def test_copy_labels_bad_offsets_write_nothing():
+    ctx = np.arange(20, dtype=np.int32) % 3
+    init = np.full(20, 9, np.uint8)
+    for off in ([0, 12, 8, 20], [-1, 10, 20], [0, 10, 21]):
+        y, flags = oracle.copy_labels(ctx, np.array(off), 2, init)
+        assert (flags == oracle.FLAG_BAD_CTX).all() and (y == 9).all()
+    # positions outside the sequences keep their value
+    y, flags = oracle.copy_labels(ctx, np.array([3, 10, 15]), 2, init)
+    assert not flags.any() and (y[:3] == 9).all() and (y[15:] == 9).all()
+    assert set(y[3:15].tolist()) <= {0, 1}

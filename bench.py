@@ -172,6 +172,53 @@ def slimspec_drafts(api, sh, case, I, dev):
     return draft, (tok, np.array([[sh.D]], dtype=np.int32))
 
 
+def run_labels(args, api, wl, dev):
+    """Copy-mode labels over one long context (Zipf ids, 5% of positions in planted
+    5..40-token repeats): tokens labelled per second, the oracle timed on the same
+    context."""
+    import numpy as np
+    import torch
+    import oracle
+    n = args.label_tokens
+    ctx, _, _ = wl.make_context(np.random.default_rng(11), np.random.default_rng(12), n, 128256,
+                                0.05, (5, 40), 4, 20, 5, False)
+    off = np.array([0, n], dtype=np.int32)
+    c, o = torch.from_numpy(ctx).to(dev), torch.from_numpy(off).to(dev)
+    labels = torch.zeros(n, dtype=torch.uint8, device=dev)
+    K, Wm = args.steps, args.warmup
+    for _ in range(Wm):
+        api.copy_labels(c, o, 5, labels)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(K):
+        api.copy_labels(c, o, 5, labels)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    alg = 5.0 * n                      # 4 B of token id read + 1 B of label written per position
+    rec = {"metric": "copy_labels_tokens_per_s", "value": n / (ms * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+           "data": "synthetic",
+           "config": {"workload": "copy_labels_long_context", "tokens": n, "kappa": 5,
+                      "context": "Zipf s=1.1 over 128256 ids, 5% planted 5..40-token repeats"},
+           "roofline": {"bound": "hbm", "achieved": alg / (ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "labels_{init,insert,query,mark}_kernel (whole call)",
+                        "algorithmic_bytes": alg},
+           "labelled_fraction": float(labels.float().mean().item())}
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        oracle.copy_labels(ctx, off, 5)
+        dt = time.perf_counter() - t
+        rec["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle", "sample": "the same %d-token context, one "
+                               "call, %.1f s" % (n, dt)}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +234,10 @@ def main():
     ap.add_argument("--commit", action="store_true",
                     help="after each step, commit the accepted rows to the paged KV cache and "
                          "roll back to the old lengths (times the decode loop's cache update)")
+    ap.add_argument("--labels", action="store_true",
+                    help="time the copy-mode label kernel over one long Zipf context instead "
+                         "of the verify step")
+    ap.add_argument("--label-tokens", type=int, default=1 << 20)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -213,6 +264,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": 1 << 30, "copies": args.copy_calib}))
+        return
+
+    if args.labels:
+        run_labels(args, api, wl, dev)
         return
 
     cfg, n_kv, n_head = WORKLOADS[args.workload]

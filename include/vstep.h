@@ -300,6 +300,24 @@ int vs_verify_step(const vs_step_desc *desc, const vs_step_io *io, void *workspa
                    size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Copy-mode labels [SW "어떻게 동작하나"]: labels[p] = 1 when position p lies inside a
+ * verbatim run of at least kappa tokens that already appeared earlier in the same
+ * context (the earlier occurrence starts earlier; it may overlap), else 0.
+ * Equivalently: some kappa-gram window [s, s+kappa) covering p also occurs at a start
+ * t < s of the same sequence.  The training labels of the copy-intent probe.
+ *   ctx int32 [ctx_total] (token ids, compared for equality only), ctx_off int32 [B+1]
+ *   (sequence b = ctx[ctx_off[b] .. ctx_off[b+1])), labels uint8 [ctx_total],
+ *   flags int32 [B] or NULL.
+ * The offsets must be non-decreasing with ctx_off[0] >= 0 and ctx_off[B] <= ctx_total,
+ * else every sequence gets VS_FLAG_BAD_CTX and no label is written; labels outside
+ * [ctx_off[0], ctx_off[B]) are never written.  1 <= kappa <= 16; ctx_total < 2^31
+ * (VS_ERR_UNSUPPORTED beyond). */
+size_t vs_copy_labels_workspace_bytes(int64_t ctx_total);
+int vs_copy_labels(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B,
+                   int kappa, uint8_t *labels, int32_t *flags, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * KV commit and rollback over the paged cache [SD section 6: the KV blocks of rejected
  * tokens go back to the paged pool at once, and none may leak].  The verify step
  * reads the candidates' K/V from their own buffers and leaves the cache untouched;

@@ -230,3 +230,15 @@ def test_kv_validation(lib):
     assert lib.vs_kv_truncate(C.byref(tr), fake, fake, fake, fake, None, None, None) == -1
     assert lib.vs_kv_truncate(C.byref(L.KvDesc(**{**ok, "page_size": 32})), *([fake] * 6),
                               None) == -2
+
+
+def test_copy_labels_validation(lib):
+    fake = C.c_void_p(16)
+    nb = lib.vs_copy_labels_workspace_bytes(1000)
+    assert nb >= 2048 * 12 + 1000
+    assert lib.vs_copy_labels_workspace_bytes(-1) == 0
+    assert lib.vs_copy_labels(fake, 1000, None, 2, 5, fake, None, fake, nb, None) == -1
+    assert lib.vs_copy_labels(fake, 1000, fake, 2, 0, fake, None, fake, nb, None) == -2
+    assert lib.vs_copy_labels(fake, 1000, fake, 2, 17, fake, None, fake, nb, None) == -2
+    assert lib.vs_copy_labels(fake, 1000, fake, 2, 5, fake, None, fake, nb - 1, None) == -3
+    assert lib.vs_copy_labels(fake, 1 << 31, fake, 2, 5, fake, None, fake, 1 << 40, None) == -2

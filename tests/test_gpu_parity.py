@@ -554,6 +554,72 @@ def test_reject_sample_greedy(B, W, D, V, T):
     assert (o["flags"] & oracle.FLAG_CDF_TIE).any() or (o["flags"] & oracle.FLAG_ACCEPT_TIE).any()
 
 
+# =============================================================================== copy labels
+
+@pytest.mark.parametrize("kappa", [1, 3, 5, 7, 16])
+def test_copy_labels_random(kappa):
+    """Small-alphabet contexts with planted repeats (empty, shorter-than-kappa and long
+    sequences, and a buffer with room before and after the sequences): every label
+    equal to the oracle's, untouched positions keep their value."""
+    api = _api()
+    rng = np.random.default_rng(kappa)
+    lens = rng.integers(0, 700, size=23)
+    lens[[0, 5]] = 0
+    lens[7] = max(kappa - 1, 0)
+    parts = []
+    for n in lens:
+        c = rng.integers(0, {1: 500, 3: 8, 5: 3, 7: 3, 16: 2}[kappa], size=n)
+        for _ in range(int(n) // 60):
+            L = int(rng.integers(kappa, 3 * kappa + 2))
+            if n > 2 * L:
+                a, d = sorted(rng.choice(n - L, size=2, replace=False))
+                c[d:d + L] = c[a:a + L]
+        parts.append(c)
+    body = np.concatenate(parts).astype(np.int32)
+    ctx = np.concatenate([np.full(17, 1, np.int32), body, np.full(9, 1, np.int32)])
+    off = (17 + np.concatenate([[0], np.cumsum(lens)])).astype(np.int32)
+    init = np.full(len(ctx), 7, np.uint8)
+    say("copy labels", kappa)
+    y, f = api.copy_labels(to_dev(ctx), to_dev(off), kappa, to_dev(init))
+    yo, fo = oracle.copy_labels(ctx, off, kappa, init)
+    assert np.array_equal(tensor_np(f), fo)
+    assert np.array_equal(tensor_np(y), yo)
+    assert 0.05 < yo[17:-9].mean() < 0.95
+
+
+def test_copy_labels_bad_offsets():
+    api = _api()
+    ctx = (np.arange(300) % 7).astype(np.int32)
+    init = np.full(300, 7, np.uint8)
+    for off in ([0, 120, 80, 300], [-3, 100, 300], [0, 100, 301]):
+        say("copy labels bad offsets", off)
+        y, f = api.copy_labels(to_dev(ctx), to_dev(np.array(off, np.int32)), 5, to_dev(init))
+        assert (tensor_np(f) == oracle.FLAG_BAD_CTX).all()
+        assert (tensor_np(y) == 7).all()
+
+
+@pytest.mark.parametrize("name", ["ragged", "llama70b", "long"])
+def test_copy_labels_full_contexts(name):
+    """The workloads' own contexts: 32 Zipf contexts of 512..8192 tokens with 5% planted
+    repeats, one of 16,384 with 5..60-token plants, and one of 262,144 tokens."""
+    api = _api()
+    if name == "long":
+        rng = np.random.default_rng(3)
+        ctx, _, _ = wl.make_context(rng, np.random.default_rng(4), 1 << 18, 128256, 0.05,
+                                    (5, 40), 4, 20, 5, False)
+        off = np.array([0, len(ctx)], np.int32)
+    else:
+        sh, seed = (wl.config(5), 5000) if name == "ragged" else (wl.config(4), 4000)
+        case = get_case(("labels", name), lambda: wl.make_case(sh, seed, with_head=False))
+        ctx, off = case.arrays["ctx"], case.arrays["ctx_off"]
+    say("copy labels", name, len(ctx))
+    y, f = api.copy_labels(to_dev(ctx), to_dev(off), 5)
+    yo, fo = oracle.copy_labels(ctx, off, 5)
+    assert not tensor_np(f).any() and not fo.any()
+    assert np.array_equal(tensor_np(y), yo)
+    assert 0.02 < yo.mean() < 0.5
+
+
 # =============================================================================== KV commit
 
 def _kv_dev(A, dtype):

@@ -31,6 +31,7 @@ EXPORTED = [
     "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
     "vs_step_workspace_bytes", "vs_verify_step", "vs_packed_weight_bytes", "vs_pack_weight",
     "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate",
+    "vs_copy_labels_workspace_bytes", "vs_copy_labels",
 ]
 
 P = C.c_void_p
@@ -116,6 +117,9 @@ def load(path: str = LIB_PATH):
     lib.vs_kv_workspace_bytes.argtypes = [C.POINTER(KvDesc)]
     lib.vs_kv_commit.argtypes = [C.POINTER(KvDesc)] + [P] * 12 + [C.c_size_t, P]
     lib.vs_kv_truncate.argtypes = [C.POINTER(KvDesc)] + [P] * 7
+    lib.vs_copy_labels_workspace_bytes.restype = C.c_size_t
+    lib.vs_copy_labels_workspace_bytes.argtypes = [C.c_int64]
+    lib.vs_copy_labels.argtypes = [P, C.c_int64, P, C.c_int, C.c_int, P, P, P, C.c_size_t, P]
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
             getattr(lib, fn).restype = C.c_int

@@ -99,6 +99,28 @@ def copy_match(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int, W: int, D: 
     return out
 
 
+def copy_labels(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int = 5, labels=None):
+    """Copy-mode labels of every context position (uint8, 1 = inside a verbatim run of
+    >= kappa tokens seen earlier in the same sequence).  Returns (labels, flags);
+    `labels` may be given (positions outside the sequences keep their values)."""
+    lib = L.load()
+    _check(ctx, torch.int32, "ctx")
+    _check(ctx_off, torch.int32, "ctx_off")
+    B = ctx_off.numel() - 1
+    dev = ctx_off.device
+    total = ctx.numel()
+    if labels is None:
+        labels = torch.zeros(total, dtype=torch.uint8, device=dev)
+    _check(labels, torch.uint8, "labels")
+    flags = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = lib.vs_copy_labels_workspace_bytes(total)
+    ws = workspace(nbytes, dev, "labels")
+    st = lib.vs_copy_labels(_ptr(ctx), total, _ptr(ctx_off), B, kappa, _ptr(labels), _ptr(flags),
+                            _ptr(ws), ws.numel(), _stream())
+    _raise(st, "copy_labels")
+    return labels, flags
+
+
 def probe_gate(h: torch.Tensor, w: torch.Tensor, tau: float, n_found: Optional[torch.Tensor] = None):
     lib = L.load()
     if h.dtype not in (torch.bfloat16, torch.float32):

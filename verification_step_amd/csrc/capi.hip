@@ -352,6 +352,22 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   return VS_OK;
 }
 
+size_t vs_copy_labels_workspace_bytes(int64_t ctx_total) {
+  if (ctx_total < 0 || ctx_total >= INT32_MAX) return 0;
+  return vs::labels_workspace_bytes(ctx_total);
+}
+
+int vs_copy_labels(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off, int B,
+                   int kappa, uint8_t *labels, int32_t *flags, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  if (!ctx_off || (ctx_total > 0 && (!ctx || !labels)) || B <= 0 || ctx_total < 0)
+    return VS_ERR_INVALID_ARG;
+  if (kappa < 1 || kappa > 16 || ctx_total >= INT32_MAX) return VS_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < vs::labels_workspace_bytes(ctx_total)) return VS_ERR_WORKSPACE;
+  return hip_status(vs::launch_copy_labels(ctx, ctx_total, ctx_off, B, kappa, labels, flags,
+                                           workspace, S(stream)));
+}
+
 static int check_kv(const vs_kv_desc *d, bool commit) {
   if (!d) return VS_ERR_INVALID_ARG;
   if (d->B <= 0 || d->max_pages <= 0 || d->n_pool_pages <= 0) return VS_ERR_INVALID_ARG;

@@ -196,6 +196,12 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 
+// ---- copy-mode labels (labels.hip)
+size_t labels_workspace_bytes(int64_t total);
+hipError_t launch_copy_labels(const int32_t *ctx, int64_t total, const int32_t *ctx_off, int B,
+                              int kappa, uint8_t *labels, int32_t *flags, void *ws,
+                              hipStream_t st);
+
 // ---- KV commit and rollback (kv.hip)
 constexpr int kMaxSeqKv = 2048;   // sequences per call
 size_t kv_workspace_bytes(int B);

@@ -10,5 +10,5 @@ from .verify_oracle import (  # noqa: F401
     bf16_bits_to_f64, round_f64_to_bf16, as_f64,
     copy_match, copy_labels, probe_gate, verify_attention, lm_head_full, lm_head_lowrank,
     head_softmax, reject_sample, reject_sample_multi, reject_sample_greedy, verify_step,
-    kv_commit, kv_truncate, gather_prefix, token_major,
+    kv_commit, kv_truncate, gather_prefix, token_major, draft_sample, rho_tps,
 )

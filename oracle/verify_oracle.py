@@ -333,6 +333,31 @@ def _draw(r: np.ndarray, u: float):
     return k, tie, margin
 
 
+def draft_sample(q: np.ndarray, u: np.ndarray):
+    """Draft tokens drawn from the drafter's distributions [SD section 2: each draft
+    token is sampled from the draft model's q; SL: q = softmax of the low-rank head's
+    logits]: row r gives _draw(q[r], u[r]) -- inverse CDF over ascending ids of the
+    stored fp32 probabilities (not renormalised; S is their sum).  Returns (tok int32
+    [rows], flags int32 [rows]: FLAG_CDF_TIE on a near tie)."""
+    q = np.asarray(q, dtype=np.float32)
+    rows = q.shape[0]
+    tok = np.zeros(rows, dtype=np.int32)
+    flags = np.zeros(rows, dtype=np.int32)
+    for r in range(rows):
+        k, tie, _ = _draw(q[r].astype(np.float64), float(u[r]))
+        tok[r] = k
+        flags[r] = FLAG_CDF_TIE if tie else 0
+    return tok, flags
+
+
+def rho_tps(nu: float, rho_tau: float, kappa: float) -> float:
+    """End-to-end speed-up of a faster draft head [SL, "이론적 프레임워크"]:
+    rho_TPS = rho_tau * (1 + kappa) / (1 + nu * kappa), with nu = new head time /
+    full head time, rho_tau = acceptance-length ratio, kappa = full head time / time
+    of the rest of the drafting pipeline."""
+    return rho_tau * (1.0 + kappa) / (1.0 + nu * kappa)
+
+
 def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
                   temperature: float = 1.0, gate=None):
     """Leviathan/Chen acceptance over W independent candidate chains, keeping the

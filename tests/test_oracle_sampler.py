@@ -572,3 +572,38 @@ def test_greedy_no_candidate_and_bad_token():
     assert g["acc_per_cand"][0].tolist() == [3, 1]
     assert g["flags"][0] == oracle.FLAG_BAD_TOKEN
     assert g["out_tok"][0].tolist() == [3, 0, 0, 0]
+
+
+# ----------------------------------------------------------------- draft sampling, rho_TPS
+
+def test_draft_sample_worked_cases():
+    q = np.array([[0.0, 0.5, 0.0, 0.5]] * 4, np.float32)
+    tok, flags = oracle.draft_sample(q, np.array([0.25, 0.75, 0.0, 0.4999]))
+    assert tok.tolist() == [1, 3, 1, 1]
+    assert flags.tolist() == [0, 0, oracle.FLAG_CDF_TIE, 0]      # u = 0 sits on the first step
+    # exactly on a step: flagged
+    tok, flags = oracle.draft_sample(q[:1], np.array([0.5]))
+    assert tok[0] == 3 and flags[0] == oracle.FLAG_CDF_TIE
+
+
+def test_draft_sample_law_on_a_stratified_grid():
+    """With u on the grid (k + 1/2)/N, token frequencies equal q / sum(q) within 1/N."""
+    rng = np.random.default_rng(2)
+    V, N = 37, 20000
+    q = rng.dirichlet(np.ones(V) * 0.3).astype(np.float32)
+    q[[3, 17]] = 0.0
+    u = (np.arange(N) + 0.5) / N
+    tok, _ = oracle.draft_sample(np.tile(q, (N, 1)), u)
+    freq = np.bincount(tok, minlength=V) / N
+    p = q.astype(np.float64) / q.astype(np.float64).sum()
+    assert np.abs(freq - p).max() <= 1.0 / N + 1e-12
+    assert freq[3] == 0 and freq[17] == 0
+
+
+def test_rho_tps_special_cases():
+    assert oracle.rho_tps(1.0, 0.97, 3.0) == pytest.approx(0.97)        # same head: acceptance only
+    assert oracle.rho_tps(0.2, 0.99, 0.0) == pytest.approx(0.99)        # head costs nothing
+    assert oracle.rho_tps(0.0, 1.0, 2.5) == pytest.approx(3.5)          # free head: 1 + kappa
+    assert oracle.rho_tps(0.25, 1.0, 1.0) == pytest.approx(2.0 / 1.25)
+    v = [oracle.rho_tps(nu, 0.99, 1.5) for nu in (0.1, 0.3, 0.6, 1.0)]
+    assert all(a > b for a, b in zip(v, v[1:]))

@@ -13,7 +13,8 @@ between 2 copies of the head, so that no step is served from the 256 MB Infinity
 Cache left warm by the last.
 
 Other workloads (--workload): tiny (fp32, V=512), slimspec (the low-rank draft head
-r=512 writing q for 7 drafts, then a W=1, D=7 verify step of those drafts), llama70b
+r=512 writing q for 7 drafts, the draft tokens drawn from q, then a W=1, D=7 verify
+step of those drafts), llama70b
 (d=8192, 64/8 heads, prefix 16384, W=8, D=20) and ragged (32 sequences, prefixes
 U[512, 8192], randomly ordered pages, W=4, D=8, point-mass drafts).
 
@@ -73,10 +74,11 @@ def upload(case):
     return out
 
 
-def cpu_baseline(case, shape, drafts=None, min_seconds=10.0, accept="longest"):
+def cpu_baseline(case, shape, min_seconds=10.0, accept="longest"):
     """The CPU oracle, as it stands, on full steps of the same inputs, repeated until at
     least `min_seconds` of CPU work have been timed.  With external drafts a step is the
-    oracle's low-rank draft head followed by its verify step over the given drafts."""
+    oracle's low-rank draft head, its draft sampling and its verify step over those
+    drafts."""
     import numpy as np
     import oracle
     threads = None
@@ -100,6 +102,8 @@ def cpu_baseline(case, shape, drafts=None, min_seconds=10.0, accept="longest"):
                                              A["w_up"])
             A2 = dict(A)
             A2["q_draft"] = oracle.head_softmax(z, l).astype(np.float32)
+            tok, _ = oracle.draft_sample(A2["q_draft"], A["u_draft"][0, 0, :sh.D])
+            drafts = (tok.reshape(1, 1, sh.D), np.array([[sh.D]], dtype=np.int32))
             oracle.verify_step(A2, sh, drafts=drafts, accept=accept)
         else:
             oracle.verify_step(A, sh, accept=accept)
@@ -107,7 +111,7 @@ def cpu_baseline(case, shape, drafts=None, min_seconds=10.0, accept="longest"):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    what = ("low-rank draft head (r=%d) + " % sh.rank) if sh.external_drafts else \
+    what = ("low-rank draft head (r=%d), draft sampling + " % sh.rank) if sh.external_drafts else \
         "retrieval, probe, "
     return {"value": n / dt, "unit": "verify steps/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d full %s verify steps (%sattention over %d prefix keys in all, "
@@ -149,27 +153,63 @@ MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense bf16 MFMA; fp32 vector (
 
 
 def slimspec_drafts(api, sh, case, I, dev):
-    """The SlimSpec side of the workload: the low-rank draft head, bound so that it
-    writes its probabilities straight into the verify step's q input, and the draft
-    tokens sampled once from them by inverse CDF (the drafter's job, not timed)."""
+    """The SlimSpec side of the workload, on the GPU in every step: the low-rank draft
+    head, bound so that it writes its probabilities straight into the verify step's q
+    input, then the draft tokens drawn from them by inverse CDF straight into the
+    step's candidate buffer."""
     import numpy as np
     import torch
     A = case.arrays
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
     qbuf = torch.empty((sh.M, sh.V), dtype=torch.float32, device=dev)
-    draft = api.LmHead(bf(A["draft_h"]), w_down=bf(A["w_down"]), w_up=bf(A["w_up"]),
-                       write_probs=True, probs=qbuf)
-    draft()
-    q = qbuf.double().cpu().numpy()
-    tok = np.zeros((1, 1, sh.D), dtype=np.int32)
-    for o in range(sh.D):
-        c = np.cumsum(q[o])
-        tok[0, 0, o] = min(int(np.searchsorted(c, A["u_draft"][0, 0, o] * c[-1], "right")),
-                           sh.V - 1)
+    head = api.LmHead(bf(A["draft_h"]), w_down=bf(A["w_down"]), w_up=bf(A["w_up"]),
+                      write_probs=True, probs=qbuf)
+    u = torch.from_numpy(np.ascontiguousarray(A["u_draft"][0, 0, :sh.D])).to(dev)
+    tok = torch.empty((1, 1, sh.D), dtype=torch.int32, device=dev)
+    dflags = torch.empty(sh.D, dtype=torch.int32, device=dev)
+    tok_flat = tok.view(-1)
+
+    def draft():
+        head()
+        api.draft_sample(qbuf, u, tok_flat, dflags)
+
     I["q_draft"] = qbuf
-    I["cand_tok"] = torch.from_numpy(tok).to(dev)
+    I["cand_tok"] = tok
     I["cand_len"] = torch.full((1, 1), sh.D, dtype=torch.int32, device=dev)
-    return draft, (tok, np.array([[sh.D]], dtype=np.int32))
+    return draft
+
+
+def draft_head_tradeoff(api, sh, case, step, dev, K, Wm):
+    """nu = low-rank draft head time / full-vocabulary draft head time on the same gamma
+    draft states, both measured here, and SlimSpec's rho_TPS for it at the pages'
+    rho_tau = 0.99 (r = d/8) over a range of kappa (full head time / rest of the
+    drafting pipeline, which has no stand-in here)."""
+    import numpy as np
+    import torch
+    A = case.arrays
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    h = bf(A["draft_h"])
+    heads = {"full": api.LmHead(h, w_full=step.w_packed, V=sh.V, write_probs=True),
+             "lowrank": api.LmHead(h, w_down=bf(A["w_down"]), w_up=bf(A["w_up"]),
+                                   write_probs=True)}
+    t = {}
+    for name, hd in heads.items():
+        for _ in range(Wm):
+            hd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            hd()
+        e1.record()
+        torch.cuda.synchronize()
+        t[name] = e0.elapsed_time(e1) / K * 1e3
+    nu = t["lowrank"] / t["full"]
+    return {"t_full_head_us": t["full"], "t_lowrank_head_us": t["lowrank"], "nu": nu,
+            "rho_tau": 0.99,
+            "rho_tps": {str(k): api.rho_tps(nu, 0.99, k) for k in (0.25, 0.5, 1.0, 2.0)},
+            "note": "heads with probabilities on gamma=%d rows, r=%d; the same head weights "
+                    "serve as the full draft head" % (sh.gamma, sh.rank)}
 
 
 def run_labels(args, api, wl, dev):
@@ -277,7 +317,7 @@ def main():
     case = wl.make_case(sh, wl.CONFIG_SEED[cfg], "measure")
     I = upload(case)
     B, W, D, M = sh.B, sh.W, sh.D, sh.M
-    draft, drafts = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else (None, None)
+    draft = slimspec_drafts(api, sh, case, I, dev) if sh.external_drafts else None
     kv = None
     if args.commit and not sh.external_drafts:
         # room for a full accepted run per sequence: spare pool pages on a free stack and
@@ -292,8 +332,9 @@ def main():
         I["page_table"] = torch.cat([I["page_table"],
                                      torch.full((B, extra_cols), -1, dtype=torch.int32,
                                                 device=dev)], dim=1).contiguous()
-        kv = dict(free=torch.arange(n0, n0 + n_spare, dtype=torch.int32, device=dev),
-                  n_free=torch.tensor([n_spare], dtype=torch.int32, device=dev),
+        free = torch.zeros(n0 + n_spare, dtype=torch.int32, device=dev)   # room for every page
+        free[:n_spare] = torch.arange(n0, n0 + n_spare, dtype=torch.int32, device=dev)
+        kv = dict(free=free, n_free=torch.tensor([n_spare], dtype=torch.int32, device=dev),
                   P0=I["prefix_len"].clone(), n_pages=n0 + n_spare)
     if args.accept == "multi" and not sh.external_drafts:
         I["q_draft"] = None                      # copy candidates judged as point masses
@@ -396,8 +437,8 @@ def main():
     names = ["retrieval_gate", "attention", "head_gemm", "lse_tests", "sampler"]
     stage_ms = {}
     if draft is not None:
-        stage_ms["draft_head_lowrank"] = float(np.mean([ev_d[k].elapsed_time(ev[k][0])
-                                                        for k in range(K)]))
+        stage_ms["draft_head_lowrank_and_sampling"] = float(
+            np.mean([ev_d[k].elapsed_time(ev[k][0]) for k in range(K)]))
     for i, n in enumerate(names):
         stage_ms[n] = float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)]))
 
@@ -440,7 +481,8 @@ def main():
         config["commit"] = "accepted rows committed to the paged cache, then rolled back"
     if draft is not None:
         config.update({"draft_head": "low-rank r=%d, gamma=%d, probabilities into q"
-                                     % (sh.rank, sh.gamma), "drafts": "external"})
+                                     % (sh.rank, sh.gamma),
+                       "drafts": "drawn on the GPU from q by inverse CDF in every step"})
     rec = {
         "metric": METRIC,
         "value": steps_per_s,
@@ -469,8 +511,10 @@ def main():
     }
     if commit_ms is not None:
         rec["kv_commit_rollback_us"] = commit_ms * 1e3
+    if draft is not None:
+        rec["slimspec_tradeoff"] = draft_head_tradeoff(api, sh, case, step, dev, K, Wm)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(case, sh, drafts, accept=args.accept)
+        rec["cpu_baseline"] = cpu_baseline(case, sh, accept=args.accept)
     print(json.dumps(rec), flush=True)
 
 

@@ -237,6 +237,18 @@ int vs_reject_sample(const vs_sample_desc *desc, const float *root_logits,
                      void *workspace, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Draft tokens [SD section 2: each draft token is sampled from the draft model's q]
+ * from stored draft probabilities, e.g. the low-rank head's (vs_lm_head with
+ * write_probs): tok[r] = min{k : C_k > u[r] * S} over the running sum C of q[r, 0..V)
+ * in ascending id order, S its total (the probabilities are not renormalised); sums
+ * in fp64.  A draw within 1e-8 * S of a CDF step raises VS_FLAG_CDF_TIE in flags[r].
+ *   q fp32 [rows, V]; u fp64 [rows] in [0, 1); tok int32 [rows]; flags int32 [rows]
+ *   or NULL.  V <= 524288 (VS_ERR_UNSUPPORTED beyond). */
+size_t vs_draft_sample_workspace_bytes(int rows, int V);
+int vs_draft_sample(const float *q, int rows, int V, const double *u, int32_t *tok,
+                    int32_t *flags, void *workspace, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * The whole verify step, enqueued on one stream with no host synchronisation:
  *   copy_match + probe_gate (one fused launch; skipped when external_drafts != 0, in
  *   which case cand_tok/cand_len are INPUTS from a neural drafter and the gate is open)

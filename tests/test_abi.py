@@ -242,3 +242,42 @@ def test_copy_labels_validation(lib):
     assert lib.vs_copy_labels(fake, 1000, fake, 2, 17, fake, None, fake, nb, None) == -2
     assert lib.vs_copy_labels(fake, 1000, fake, 2, 5, fake, None, fake, nb - 1, None) == -3
     assert lib.vs_copy_labels(fake, 1 << 31, fake, 2, 5, fake, None, fake, 1 << 40, None) == -2
+
+
+def test_draft_sample_validation(lib):
+    fake = C.c_void_p(16)
+    nb = lib.vs_draft_sample_workspace_bytes(7, 128256)
+    assert nb >= 7 * 63 * 257 * 8
+    assert lib.vs_draft_sample_workspace_bytes(7, 1 << 20) == 0
+    assert lib.vs_draft_sample(None, 7, 1000, fake, fake, None, fake, nb, None) == -1
+    assert lib.vs_draft_sample(fake, 7, 1 << 20, fake, fake, None, fake, 1 << 40, None) == -2
+    assert lib.vs_draft_sample(fake, 7, 128256, fake, fake, None, fake, nb - 1, None) == -3
+
+
+def test_rho_tps_matches_the_oracle():
+    import oracle
+    from verification_step_amd import api
+    for nu in (0.0, 0.2, 0.5, 1.0):
+        for k in (0.0, 0.3, 1.0, 4.0):
+            assert api.rho_tps(nu, 0.99, k) == oracle.rho_tps(nu, 0.99, k)
+
+
+def test_binding_rejects_inconsistent_shapes(lib):
+    """The binding stops tensors whose sizes disagree with the launch sizes on the host
+    (meta tensors: no device needed)."""
+    import torch
+    from verification_step_amd import api
+    m = lambda *s: torch.empty(*s, device="meta", dtype=torch.bfloat16)
+    packed = torch.empty(lib.vs_packed_weight_bytes(1000, 64) // 2, device="meta",
+                         dtype=torch.bfloat16)
+    api.head_weight_sizes(lib, True, 64, 1000, 0, packed, None, None)
+    api.head_weight_sizes(lib, True, 64, 1000, 0, m(1000, 64), None, None)
+    for bad in (torch.empty(packed.numel() - 8, device="meta", dtype=torch.bfloat16),
+                m(1000, 32)):
+        with pytest.raises(ValueError):
+            api.head_weight_sizes(lib, True, 64, 1000, 0, bad, None, None)
+    # the flat packed full weight of a Llama-8B head is not a [V, d] tensor for V=7
+    with pytest.raises(ValueError):
+        api.head_weight_sizes(lib, True, 4096, 7, 0, packed, None, None)
+    with pytest.raises(ValueError):
+        api._expect(m(3, 4), (3, 5), "x")

@@ -554,6 +554,49 @@ def test_reject_sample_greedy(B, W, D, V, T):
     assert (o["flags"] & oracle.FLAG_CDF_TIE).any() or (o["flags"] & oracle.FLAG_ACCEPT_TIE).any()
 
 
+# =============================================================================== draft tokens
+
+@pytest.mark.parametrize("rows,V", [(64, 1000), (33, 3001), (16, 128256)])
+def test_draft_sample(rows, V):
+    """Draft tokens by inverse CDF of stored probabilities, against the oracle on the same
+    fp32 rows (zero-probability ids included); near ties flagged on either side are
+    left out."""
+    api = _api()
+    rng = np.random.default_rng(V)
+    q = wl.draft_probs_from_logits(rng, (rows, V), 2.0)
+    q[:, rng.choice(V, size=V // 5, replace=False)] = 0.0
+    u = rng.random(rows)
+    say("draft sample", rows, V)
+    tok, f = api.draft_sample(to_dev(q), to_dev(u))
+    to, fo = oracle.draft_sample(q, u)
+    tg, fg = tensor_np(tok), tensor_np(f)
+    ok = (fg | fo) == 0
+    assert ok.sum() >= rows - 1
+    assert np.array_equal(tg[ok], to[ok])
+    assert (q[np.arange(rows), tg] > 0).all()
+
+
+def test_draft_sample_slimspec_pipeline():
+    """The SlimSpec draft side on the GPU: the low-rank head's probabilities, then the
+    draft tokens drawn from them.  Each token's CDF interval under those probabilities
+    (summed in fp64 on the host) holds u * S."""
+    api = _api()
+    sh = wl.config(3)
+    case = get_case(("slim",), lambda: wl.make_case(sh, 3000, with_head=False, with_q=False))
+    A = case.arrays
+    say("slimspec draft pipeline")
+    _, _, pr = api.lm_head(to_dev(A["draft_h"], True), w_down=to_dev(A["w_down"], True),
+                           w_up=to_dev(A["w_up"], True), write_probs=True)
+    u = A["u_draft"][0, 0, :sh.D]
+    tok, f = api.draft_sample(pr, to_dev(u))
+    q = tensor_np(pr).astype(np.float64)
+    for r, k in enumerate(tensor_np(tok)):
+        c = np.cumsum(q[r])
+        x = u[r] * c[-1]
+        lo = c[k - 1] if k > 0 else 0.0
+        assert q[r, k] > 0 and lo - 1e-9 * c[-1] <= x < c[k] + 1e-9 * c[-1]
+
+
 # =============================================================================== copy labels
 
 @pytest.mark.parametrize("kappa", [1, 3, 5, 7, 16])

@@ -32,6 +32,7 @@ EXPORTED = [
     "vs_step_workspace_bytes", "vs_verify_step", "vs_packed_weight_bytes", "vs_pack_weight",
     "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate",
     "vs_copy_labels_workspace_bytes", "vs_copy_labels",
+    "vs_draft_sample_workspace_bytes", "vs_draft_sample",
 ]
 
 P = C.c_void_p
@@ -120,6 +121,9 @@ def load(path: str = LIB_PATH):
     lib.vs_copy_labels_workspace_bytes.restype = C.c_size_t
     lib.vs_copy_labels_workspace_bytes.argtypes = [C.c_int64]
     lib.vs_copy_labels.argtypes = [P, C.c_int64, P, C.c_int, C.c_int, P, P, P, C.c_size_t, P]
+    lib.vs_draft_sample_workspace_bytes.restype = C.c_size_t
+    lib.vs_draft_sample_workspace_bytes.argtypes = [C.c_int, C.c_int]
+    lib.vs_draft_sample.argtypes = [P, C.c_int, C.c_int, P, P, P, P, C.c_size_t, P]
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
             getattr(lib, fn).restype = C.c_int

@@ -45,6 +45,28 @@ def _check(t, dtype, name, device=None):
     return t
 
 
+def _expect(t, shape, name):
+    """Raise unless tensor t (if given) has exactly `shape`: every launch reads the sizes
+    it is given, so inconsistent tensors must stop here, on the host."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def head_weight_sizes(lib, bf16: bool, d: int, V: int, rank: int, w_full, w_down, w_up):
+    """Check each given head weight against the size the kernels read: [V, d] (full),
+    [rank, d] and [V, rank] (low rank), as 2-D tensors or as flat packed bf16 tensors
+    of vs_packed_weight_bytes(rows, cols) bytes."""
+    for t, n, k, name in ((w_full, V, d, "w_full"), (w_down, rank, d, "w_down"),
+                          (w_up, V, rank, "w_up")):
+        if t is None:
+            continue
+        if t.dim() == 2:
+            _expect(t, (n, k), name)
+        elif not bf16 or t.numel() * 2 != lib.vs_packed_weight_bytes(n, k):
+            raise ValueError(f"{name}: {t.numel()} values is not the packed size of "
+                             f"[{n}, {k}]")
+
+
 def _vs_dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return L.VS_BF16
@@ -99,6 +121,36 @@ def copy_match(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int, W: int, D: 
     return out
 
 
+def rho_tps(nu: float, rho_tau: float, kappa: float) -> float:
+    """SlimSpec's acceptance-cost model ("SlimSpec: Low-Rank Draft LM-Head ...",
+    gist.science, "이론적 프레임워크"): the end-to-end speed-up of a draft head that
+    takes nu times the full head's time and keeps rho_tau of the acceptance length,
+    when the full head takes kappa times the rest of the drafting pipeline."""
+    return rho_tau * (1.0 + kappa) / (1.0 + nu * kappa)
+
+
+def draft_sample(q: torch.Tensor, u: torch.Tensor, tok=None, flags=None):
+    """Draft tokens by inverse CDF of stored probability rows q [rows, V] (fp32) with
+    uniforms u [rows] (fp64).  Returns (tok int32 [rows], flags int32 [rows]); tok and
+    flags may be given (bound buffers, no allocation but the cached workspace)."""
+    lib = L.load()
+    _check(q, torch.float32, "q")
+    _check(u, torch.float64, "u")
+    rows, V = q.shape
+    _expect(u, (rows,), "u")
+    _expect(tok, (rows,), "tok")
+    _expect(flags, (rows,), "flags")
+    dev = q.device
+    tok = torch.empty(rows, dtype=torch.int32, device=dev) if tok is None else tok
+    flags = torch.empty(rows, dtype=torch.int32, device=dev) if flags is None else flags
+    nbytes = lib.vs_draft_sample_workspace_bytes(rows, V)
+    ws = workspace(nbytes, dev, "draft")
+    st = lib.vs_draft_sample(_ptr(q), rows, V, _ptr(u), _ptr(tok), _ptr(flags), _ptr(ws),
+                             ws.numel(), _stream())
+    _raise(st, "draft_sample")
+    return tok, flags
+
+
 def copy_labels(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int = 5, labels=None):
     """Copy-mode labels of every context position (uint8, 1 = inside a verbatim run of
     >= kappa tokens seen earlier in the same sequence).  Returns (labels, flags);
@@ -112,6 +164,7 @@ def copy_labels(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int = 5, labels
     if labels is None:
         labels = torch.zeros(total, dtype=torch.uint8, device=dev)
     _check(labels, torch.uint8, "labels")
+    _expect(labels, (total,), "labels")
     flags = torch.empty(B, dtype=torch.int32, device=dev)
     nbytes = lib.vs_copy_labels_workspace_bytes(total)
     ws = workspace(nbytes, dev, "labels")
@@ -157,6 +210,12 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, 
     Hkv = k_cand.shape[1]
     if BM != B * W * D:
         raise ValueError("q rows must equal B*W*D")
+    _expect(k_cand, (BM, Hkv, hd), "k_cand")
+    _expect(v_cand, (BM, Hkv, hd), "v_cand")
+    _expect(k_pool, (k_pool.shape[0], Hkv, 16, hd), "k_pool")
+    _expect(v_pool, (k_pool.shape[0], Hkv, hd, 16), "v_pool")
+    _expect(page_table, (B, page_table.shape[1]), "page_table")
+    _expect(out, q.shape, "out")
     desc = attn_desc(B, W, D, Hq, Hkv, hd, page_table.shape[1], k_pool.shape[0], _vs_dtype(q),
                      scale)
     if out is None:
@@ -202,10 +261,15 @@ class LmHead:
         for name, t in (("w_full", w_full), ("w_down", w_down), ("w_up", w_up)):
             _check(t, dt, name)
         M, d = h.shape
+        flat = [t for t in (w_full, w_down, w_up) if t is not None and t.dim() != 2]
+        if flat and (V is None or (w_down is not None and rank is None)):
+            raise ValueError("lm_head: packed (flat) weights need V, and rank for the "
+                             "low-rank head")
         if rank is None:
             rank = 0 if w_down is None else w_down.shape[0]
         if V is None:
             V = (w_full if rank == 0 else w_up).shape[0]
+        head_weight_sizes(self.lib, dt == torch.bfloat16, d, V, rank, w_full, w_down, w_up)
         if dt == torch.bfloat16:
             w_full = pack_weight(w_full) if (w_full is not None and w_full.dim() == 2) else w_full
             w_down = pack_weight(w_down) if (w_down is not None and w_down.dim() == 2) else w_down
@@ -267,6 +331,11 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
     _check(gate, torch.int32, "gate")
     B, W, D = cand_tok.shape
     V = root_logits.shape[1]
+    M = B * W * D
+    for t, shp, n in ((root_logits, (B, V), "root_logits"), (logits, (M, V), "logits"),
+                      (row_lse, (M,), "row_lse"), (q, (M, V), "q"), (cand_len, (B, W), "cand_len"),
+                      (u_acc, (B, W, D), "u_acc"), (u_res, (B, W), "u_res"), (gate, (B,), "gate")):
+        _expect(t, shp, n)
     dev = root_logits.device
     desc = L.SampleDesc(B, W, D, V, float(temperature), _accept_mode(accept))
     out = dict(n_acc=torch.empty(B, dtype=torch.int32, device=dev),
@@ -308,6 +377,12 @@ def kv_commit(k_cand, v_cand, best, n_acc, k_pool, v_pool, page_table, prefix_le
     for t, n in ((k_cand, "k_cand"), (v_cand, "v_cand"), (k_pool, "k_pool"), (v_pool, "v_pool")):
         _check(t, k_pool.dtype, n)
     desc = _kv_desc(k_pool, page_table, W, D)
+    B, n_pages, Hkv, hd = page_table.shape[0], k_pool.shape[0], k_pool.shape[1], k_pool.shape[3]
+    for t, shp, n in ((k_cand, (B * W * D, Hkv, hd), "k_cand"), (v_cand, (B * W * D, Hkv, hd), "v_cand"),
+                      (k_pool, (n_pages, Hkv, 16, hd), "k_pool"), (v_pool, (n_pages, Hkv, hd, 16), "v_pool"),
+                      (best, (B,), "best"), (n_acc, (B,), "n_acc"), (prefix_len, (B,), "prefix_len"),
+                      (free_list, (n_pages,), "free_list"), (n_free, (1,), "n_free")):
+        _expect(t, shp, n)
     flags = torch.empty(page_table.shape[0], dtype=torch.int32, device=page_table.device)
     nbytes = lib.vs_kv_workspace_bytes(C.byref(desc))
     if nbytes == 0:
@@ -329,6 +404,9 @@ def kv_truncate(new_len, page_table, prefix_len, free_list, n_free, n_pool_pages
                  (free_list, "free_list"), (n_free, "n_free")):
         _check(t, torch.int32, n)
     B, max_pages = page_table.shape
+    for t, shp, n in ((new_len, (B,), "new_len"), (prefix_len, (B,), "prefix_len"),
+                      (free_list, (int(n_pool_pages),), "free_list"), (n_free, (1,), "n_free")):
+        _expect(t, shp, n)
     desc = L.KvDesc(B, 1, 1, 1, 1, 16, max_pages, int(n_pool_pages), 0)
     flags = torch.empty(B, dtype=torch.int32, device=page_table.device)
     st = lib.vs_kv_truncate(C.byref(desc), _ptr(new_len), _ptr(page_table), _ptr(prefix_len),
@@ -338,6 +416,34 @@ def kv_truncate(new_len, page_table, prefix_len, free_list, n_free, n_pool_pages
 
 
 # ---------------------------------------------------------------------------------
+
+def step_shapes(lib, I: dict, B, W, D, Hq, Hkv, hd, V, external_drafts, accept):
+    """Check every input of a verify step against the sizes its launches read."""
+    M = B * W * D
+    d = Hq * hd
+    _expect(I["q"], (M, Hq, hd), "q")
+    for n in ("k_cand", "v_cand"):
+        _expect(I[n], (M, Hkv, hd), n)
+    n_pages = I["k_pool"].shape[0]
+    _expect(I["k_pool"], (n_pages, Hkv, 16, hd), "k_pool")
+    _expect(I["v_pool"], (n_pages, Hkv, hd, 16), "v_pool")
+    _expect(I["page_table"], (B, I["page_table"].shape[1]), "page_table")
+    _expect(I["prefix_len"], (B,), "prefix_len")
+    _expect(I["root_logits"], (B, V), "root_logits")
+    _expect(I.get("q_draft"), (M, V), "q_draft")
+    _expect(I.get("u_acc"), (B, W, D), "u_acc")
+    _expect(I.get("u_res"), (B, W), "u_res")
+    head_weight_sizes(lib, I["w_full"].dtype == torch.bfloat16, d, V, 0, I["w_full"], None, None)
+    if external_drafts:
+        _expect(I["cand_tok"], (B, W, D), "cand_tok")
+        _expect(I["cand_len"], (B, W), "cand_len")
+    else:
+        _expect(I["ctx_off"], (B + 1,), "ctx_off")
+        _expect(I["probe_h"], (B, d), "probe_h")
+        _expect(I["probe_w"], (d,), "probe_w")
+    if accept != "greedy" and (I.get("u_acc") is None or I.get("u_res") is None):
+        raise ValueError("verify_step: u_acc and u_res are required unless accept='greedy'")
+
 
 class VerifyStep:
     """One verify step bound to fixed device buffers, so that repeated calls (timing,
@@ -354,6 +460,7 @@ class VerifyStep:
                  accept: str = "longest"):
         self.lib = L.load()
         I = dict(inputs)
+        step_shapes(self.lib, I, B, W, D, Hq, Hkv, hd, V, external_drafts, accept)
         if I["w_full"].dtype == torch.bfloat16 and I["w_full"].dim() == 2:
             I["w_full"] = pack_weight(I["w_full"])
         self.w_packed = I["w_full"]

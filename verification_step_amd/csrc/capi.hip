@@ -352,6 +352,19 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   return VS_OK;
 }
 
+size_t vs_draft_sample_workspace_bytes(int rows, int V) {
+  if (rows <= 0 || V <= 0 || V > kMaxVocabSampler) return 0;
+  return vs::draft_workspace_bytes(rows, V);
+}
+
+int vs_draft_sample(const float *q, int rows, int V, const double *u, int32_t *tok,
+                    int32_t *flags, void *workspace, size_t ws_bytes, void *stream) {
+  if (!q || !u || !tok || rows <= 0 || V <= 0) return VS_ERR_INVALID_ARG;
+  if (V > kMaxVocabSampler) return VS_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < vs::draft_workspace_bytes(rows, V)) return VS_ERR_WORKSPACE;
+  return hip_status(vs::launch_draft_sample(q, rows, V, u, tok, flags, workspace, S(stream)));
+}
+
 size_t vs_copy_labels_workspace_bytes(int64_t ctx_total) {
   if (ctx_total < 0 || ctx_total >= INT32_MAX) return 0;
   return vs::labels_workspace_bytes(ctx_total);

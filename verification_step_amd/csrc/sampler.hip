@@ -853,7 +853,138 @@ root_stats_kernel(const float *root_logits, int B, int V, float inv_t, float2 *s
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Draft tokens: row r of stored draft probabilities q (fp32, as the low-rank head
+// writes them) gives the id k = min{k : C_k > u_r * S} of its running sum C over
+// ascending ids, S = C_{V-1} -- the sampler's inverse-CDF draw with the same chunk
+// structure: per-chunk and per-thread fp64 sums, then one workgroup per row scans the
+// chunk sums, the owner chunk's thread sums and one thread's 8 ids.
+struct DraftArgs {
+  const float *q;
+  const double *u;
+  int rows, V, nch;
+  int32_t *tok, *flags;
+  double *chunk_sums;    // [rows][nch]
+  double *thread_sums;   // [rows][nch][kST]
+};
+
+__device__ __forceinline__ void draft_vals(const DraftArgs &a, int r, int k0, double *w) {
+  const float *row = a.q + (int64_t)r * a.V;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) w[j] = (k0 + j < a.V) ? (double)row[k0 + j] : 0.0;
+}
+
+__global__ void __launch_bounds__(kST)
+draft_sums_kernel(DraftArgs a) {
+  __shared__ double red[kST / 64];
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  double w[kPer];
+  draft_vals(a, r, c * kChunk + tid * kPer, w);
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) s += w[j];
+  a.thread_sums[((int64_t)r * a.nch + c) * kST + tid] = s;
+  s = warp_sum(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) a.chunk_sums[(int64_t)r * a.nch + c] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void __launch_bounds__(kST)
+draft_draw_kernel(DraftArgs a) {
+  __shared__ SampShared sh;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const double cs = (tid < a.nch) ? a.chunk_sums[(int64_t)r * a.nch + tid] : 0.0;
+  double S = cs, unused = 0.0;
+  block_sum2(sh, S, unused);
+  const double xs = a.u[r] * S;
+  const double incl = block_incl_scan(sh, cs);
+  if (tid == 0) {
+    sh.owner = INT_MAX;
+    sh.last_pos = -1;
+    sh.tstar = INT_MAX;
+    sh.flags = 0;
+  }
+  __syncthreads();
+  if (tid < a.nch && cs > 0.0) {
+    if (incl > xs) atomicMin(&sh.owner, tid);
+    atomicMax(&sh.last_pos, tid);
+  }
+  __syncthreads();
+  if (tid == 0 && sh.owner == INT_MAX) {
+    // rounding left u*S at or past the total (or a row without mass): last chunk with mass
+    sh.owner = sh.last_pos >= 0 ? sh.last_pos : a.nch - 1;
+    sh.flags = FLAG_CDF_TIE;
+  }
+  __syncthreads();
+  if (tid == sh.owner) sh.excl = incl - cs;
+  __syncthreads();
+  const int owner = sh.owner;
+  const double tv = a.thread_sums[((int64_t)r * a.nch + owner) * kST + tid];
+  const double tincl = block_incl_scan(sh, tv);
+  const double texcl = sh.excl + (tincl - tv);
+  if (tv > 0.0 && sh.excl + tincl > xs) atomicMin(&sh.tstar, tid);
+  __syncthreads();
+  if (tid == sh.tstar || (sh.tstar == INT_MAX && tid == 0)) {
+    int f = sh.flags;
+    int yy = -1;
+    if (sh.tstar != INT_MAX) {
+      double w[kPer];
+      const int k0 = owner * kChunk + tid * kPer;
+      draft_vals(a, r, k0, w);
+      double run = texcl, lo = 0.0, hi = 0.0;
+      int last_w = -1;
+      for (int j = 0; j < kPer; ++j) {
+        const double prev = run;
+        run += w[j];
+        if (w[j] > 0.0) last_w = k0 + j;
+        if (yy < 0 && w[j] > 0.0 && run > xs) {
+          yy = k0 + j;
+          lo = prev;
+          hi = run;
+        }
+      }
+      if (yy >= 0 && (fabs(xs - lo) < 1e-8 * S || fabs(hi - xs) < 1e-8 * S)) f |= FLAG_CDF_TIE;
+      if (yy < 0) {
+        yy = last_w;
+        f |= FLAG_CDF_TIE;
+      }
+    }
+    if (yy < 0) {
+      yy = min(a.V, (owner + 1) * kChunk) - 1;
+      f |= FLAG_CDF_TIE;
+    }
+    a.tok[r] = yy;
+    if (a.flags) a.flags[r] = f;
+  }
+}
+
 }  // namespace
+
+size_t draft_workspace_bytes(int rows, int V) {
+  const int nch = (V + kChunk - 1) / kChunk;
+  return ((((size_t)rows * nch * sizeof(double)) + 255) & ~(size_t)255) +
+         (((size_t)rows * nch * kST * sizeof(double) + 255) & ~(size_t)255);
+}
+
+hipError_t launch_draft_sample(const float *q, int rows, int V, const double *u, int32_t *tok,
+                               int32_t *flags, void *ws, hipStream_t st) {
+  DraftArgs a;
+  a.q = q;
+  a.u = u;
+  a.rows = rows;
+  a.V = V;
+  a.nch = (V + kChunk - 1) / kChunk;
+  a.tok = tok;
+  a.flags = flags;
+  a.chunk_sums = (double *)ws;
+  a.thread_sums = (double *)((char *)ws + ((((size_t)rows * a.nch * sizeof(double)) + 255) &
+                                           ~(size_t)255));
+  hipLaunchKernelGGL(draft_sums_kernel, dim3(a.nch, rows), dim3(kST), 0, st, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL(draft_draw_kernel, dim3(rows), dim3(kST), 0, st, a);
+  return hipGetLastError();
+}
 
 SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats) {
   SampleWs w;

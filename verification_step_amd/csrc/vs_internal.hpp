@@ -196,6 +196,11 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
 
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t st);
 
+// ---- draft tokens by inverse CDF of stored probability rows (sampler.hip)
+size_t draft_workspace_bytes(int rows, int V);
+hipError_t launch_draft_sample(const float *q, int rows, int V, const double *u, int32_t *tok,
+                               int32_t *flags, void *ws, hipStream_t st);
+
 // ---- copy-mode labels (labels.hip)
 size_t labels_workspace_bytes(int64_t total);
 hipError_t launch_copy_labels(const int32_t *ctx, int64_t total, const int32_t *ctx_off, int B,

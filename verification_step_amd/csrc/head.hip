@@ -248,7 +248,14 @@ __device__ __forceinline__ void dma16_h(const void *g, bf16_t *lds_dst) {
 template <int MT, int NG>
 __global__ void __launch_bounds__(kThreads * NG, 2)
 head_lds_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16_t Hs[2][MT * 16 * kHC];
+  // the H double buffer; after the K loop the same LDS stages each wave's logits tile
+  // (16 rows x 64 columns, rows padded to kStRow floats) for whole-segment stores
+  constexpr int kHsBuf = MT * 16 * kHC;
+  constexpr int kStRow = 68;
+  constexpr int kStageF = 4 * NG * 16 * kStRow;
+  constexpr int kHsAll = (4 * kHsBuf >= 4 * kStageF) ? 2 * kHsBuf : 2 * kStageF;
+  __shared__ __attribute__((aligned(1024))) bf16_t Hs_all[kHsAll];
+  bf16_t(*Hs)[kHsBuf] = reinterpret_cast<bf16_t(*)[kHsBuf]>(Hs_all);
   __shared__ float2 red[4 * NG][MT * 16];
 
   const int tid = threadIdx.x;
@@ -336,26 +343,58 @@ head_lds_kernel(GemmArgs a) {
   }
   static_assert(kHC / 32 == kRingL, "one ring turn per H chunk");
 
-  // ---- epilogue: logits + tile statistics (as the streaming kernel)
+  // ---- epilogue: logits + tile statistics.  With one or two row blocks (the weight
+  // stream dominates) each row tile goes through LDS: a wave writes its 16 x 64
+  // fragment, then stores 4 rows x 256 contiguous bytes per instruction -- whole cache
+  // lines, written non-temporally (the sampler reads one of these rows back, later).
+  // With more row blocks (matrix-bound shapes) the fragments are stored directly.
+  const bool staged = a.n_mblocks <= 2;
+  float *stg = reinterpret_cast<float *>(Hs_all) + wv * 16 * kStRow;
+  if (staged) __syncthreads();   // every wave is done reading H
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = mbase + mt * 16 + l16;
     float vmax = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kVT; ++v) {
       const int n0 = vbase + v * 16 + 4 * lg;
-      if (m < a.M) {
-        float *op = a.out + (int64_t)m * a.N + n0;
-        if (n0 + 3 < a.N) {
-          *(f32x4 *)op = acc[v][mt];
-        } else {
-          for (int j = 0; j < 4; ++j)
-            if (n0 + j < a.N) op[j] = acc[v][mt][j];
+      if (staged) {
+        *(f32x4 *)&stg[l16 * kStRow + v * 16 + 4 * lg] = acc[v][mt];
+      } else {
+        const int m = mbase + mt * 16 + l16;
+        if (m < a.M) {
+          float *op = a.out + (int64_t)m * a.N + n0;
+          if (n0 + 3 < a.N) {
+            *(f32x4 *)op = acc[v][mt];
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (n0 + j < a.N) op[j] = acc[v][mt][j];
+          }
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (n0 + j < a.N) vmax = fmaxf(vmax, acc[v][mt][j] * a.inv_t);
+    }
+    if (staged) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int c = 4 * (lane & 15);
+        const int m = mbase + mt * 16 + r;
+        const int n = vbase + c;
+        if (m < a.M && n < a.N) {
+          const f32x4 val = *(const f32x4 *)&stg[r * kStRow + c];
+          float *op = a.out + (int64_t)m * a.N + n;
+          if (n + 3 < a.N && ((a.N & 3) == 0)) {
+            __builtin_nontemporal_store(val, (f32x4 *)op);
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (n + j < a.N) op[j] = val[j];
+          }
+        }
+      }
+      __syncthreads();
     }
     if (a.stats == nullptr) continue;
     vmax = fmaxf(vmax, __shfl_xor(vmax, 16));

@@ -516,7 +516,8 @@ def _greedy_case(rng, B, W, D, V):
         j = int(rng.integers(0, V))
         logits[r, j] = logits[r, k]                 # exact tie, possibly in another tile
     logits[5] = 0.25                                 # all equal: argmax is token 0
-    root[3, :] = root[3, int(np.argmax(root[3]))]
+    t = min(3, B - 1)
+    root[t, :] = root[t, int(np.argmax(root[t]))]
     cand = rng.integers(0, V, size=(B, W, D)).astype(np.int32)
     for b in range(B):
         for i in range(W):
@@ -552,6 +553,75 @@ def test_reject_sample_greedy(B, W, D, V, T):
             (tensor_np(g[k]) != o[k]).reshape(B, -1).any(axis=1))[0][:5])
     assert (o["n_acc"] >= 3).sum() > B // 4
     assert (o["flags"] & oracle.FLAG_CDF_TIE).any() or (o["flags"] & oracle.FLAG_ACCEPT_TIE).any()
+
+
+# =============================================================================== limits
+
+def test_limits_max_rows_per_sequence():
+    """W*D = 1024 draft rows per sequence (the largest the ABI takes): retrieval with 32
+    candidates x 32 tokens, attention of 4096 query rows per KV head, and the sampler
+    (longest run and greedy) over 1024 rows, each against the oracle."""
+    api = _api()
+    rng = np.random.default_rng(99)
+    # retrieval: a context made of many repeats of the trailing 5-gram
+    W, D, kappa = 32, 32, 5
+    base = rng.integers(0, 50, size=2000).astype(np.int32)
+    key = base[-kappa:]
+    for j in rng.choice(np.arange(10, 1900), size=60, replace=False):
+        base[j:j + kappa] = key
+    off = np.array([0, len(base)], np.int32)
+    say("limits copy_match")
+    g = api.copy_match(to_dev(base), to_dev(off), kappa, W, D)
+    o = oracle.copy_match(base, off, kappa, W, D)
+    for k in ("cand_tok", "cand_len", "cand_pos", "n_found", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), k
+    assert o["n_found"][0] == W
+    # attention: 1 sequence x 1024 rows, 2 KV heads of 4 query heads, prefix 200
+    sh = small_shape(B=1, W=16, D=64, Hq=8, Hkv=2, P=(200,), V=600)
+    case = get_case(("limits", "attn"),
+                    lambda: wl.make_case(sh, 77, with_head=False, with_q=False))
+    say("limits attention")
+    ga, gf = _run_attention(case)
+    _, o_r, of = _oracle_attention(case)
+    assert np.array_equal(gf, of)
+    assert rel_err(ga, o_r) <= TOL
+    # sampler over 1024 rows (longest run and greedy)
+    B, W, D, V = 2, 32, 32, 3000
+    root, logits, cand, clen, gate = _greedy_case(rng, B, W, D, V)
+    gate[:] = 1
+    clen[0] = D
+    lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    say("limits sampler")
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), to_dev(ua), to_dev(ur), 1.0)
+    o = oracle.reject_sample(root, logits, None, cand, clen, ua, ur, 1.0)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    assert n_cmp >= 1
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), None, None, 1.0, accept="greedy")
+    o = oracle.reject_sample_greedy(root, logits, cand, clen)
+    for k in ("n_acc", "best", "out_tok", "n_out", "acc_per_cand", "flags"):
+        assert np.array_equal(tensor_np(g[k]), o[k]), k
+
+
+def test_limits_multi_lds_bound():
+    """Multi-candidate acceptance at the largest LDS footprint it takes (W = 8, D = 50:
+    401 x 8 + 400 doubles), against the oracle."""
+    api = _api()
+    rng = np.random.default_rng(5)
+    B, W, D, V = 6, 8, 50, 2000
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    lse = scipy.special.logsumexp(logits.astype(np.float64), axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    say("limits multi")
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), None, to_dev(cand),
+                          to_dev(clen), to_dev(ua), to_dev(ur), 1.0, accept="multi")
+    o = oracle.reject_sample_multi(root, logits, None, cand, clen, ua, ur, 1.0)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    assert n_exc <= 1 and n_cmp >= B - 1
 
 
 # =============================================================================== draft tokens

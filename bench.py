@@ -274,6 +274,9 @@ def main():
     ap.add_argument("--commit", action="store_true",
                     help="after each step, commit the accepted rows to the paged KV cache and "
                          "roll back to the old lengths (times the decode loop's cache update)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the K steps as HIP graph replays (one graph per KV "
+                         "buffer / head copy binding, captured after the warmup)")
     ap.add_argument("--labels", action="store_true",
                     help="time the copy-mode label kernel over one long Zipf context instead "
                          "of the verify step")
@@ -402,6 +405,26 @@ def main():
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / K
 
+    ms_graph = None
+    if args.graph:
+        # one graph per binding (KV buffer, head copy), each a whole step as captured
+        period = int(np.lcm(len(pools), len(heads)))
+        graphs = []
+        for k in range(period):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                run(k)
+            graphs.append(gr)
+        for k in range(Wm):
+            graphs[k % period].replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for k in range(K):
+            graphs[(Wm + k) % period].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_graph = t0.elapsed_time(t1) / K
+
     # pass 2: the same K steps with stage events (6 per step, made beforehand; one more
     # before the draft head where there is one)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
@@ -511,6 +534,8 @@ def main():
     }
     if commit_ms is not None:
         rec["kv_commit_rollback_us"] = commit_ms * 1e3
+    if ms_graph is not None:
+        rec["ms_per_step_graph_replay"] = ms_graph
     if draft is not None:
         rec["slimspec_tradeoff"] = draft_head_tradeoff(api, sh, case, step, dev, K, Wm)
     if not args.no_cpu_baseline:

@@ -30,7 +30,9 @@
 // sums the residual weights of its own vocabulary chunk with coalesced loads.  The
 // draw then adds the chunk sums in chunk order, finds the chunk holding u*S, finds
 // the thread range holding it with an ordered block scan of that chunk's per-thread
-// sums and writes the outputs.  Two ways to reach the draw:
+// sums (recomputed from the logits by the drawing workgroup: the same arithmetic in the
+// same order gives the same bits, and the owning thread then holds its ids' weights)
+// and writes the outputs.  Two ways to reach the draw:
 //   * fused: the last workgroup of the sequence to finish (atomic counter in the
 //     workspace, reset afterwards) does it.  Each workgroup then publishes its sums
 //     with a device-scope release, which writes back its XCD's L2; with a few dozen
@@ -417,7 +419,6 @@ struct SampArgs {
   int flags_accumulate;
   int32_t *attn_flags;   // [B] or null: flags raised by attention, folded and reset here
   double2 *chunk_sums;   // [B][nch]: (residual-or-bonus weight sum, target p sum)
-  double2 *thread_sums;  // [B][nch][kST]: the same over each thread's kPer ids
   uint32_t *counters;    // [B]
 };
 
@@ -705,10 +706,6 @@ sampler_kernel(SampArgs a) {
         sp += pk[j];
       }
     }
-    double2 *ts = a.thread_sums + ((int64_t)b * a.nch + c) * kST;
-    // every thread's sums reach memory before the barriers of block_sum2; thread 0's
-    // device-scope release below (or the end of the kernel) publishes them
-    ts[tid] = make_double2(sr, sp);
     block_sum2(sh, sr, sp);
     if constexpr (PHASE == SAMP_SUMS) {
       if (tid == 0) a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
@@ -761,10 +758,13 @@ sampler_kernel(SampArgs a) {
   __syncthreads();
   const int owner = sh.owner;
   const bool use_p = sh.mode == MODE_TARGET;
-  // the owner chunk's thread sums (kept by its workgroup) in id order: the thread
-  // whose range holds u*S
-  const double2 tsum2 = a.thread_sums[((int64_t)b * a.nch + owner) * kST + tid];
-  const double tv = use_p ? tsum2.y : tsum2.x;
+  // the owner chunk's per-thread sums, recomputed (same arithmetic, same order as its
+  // workgroup's): the thread whose range holds u*S
+  double pk[kPer], rk[kPer];
+  weights(owner * kChunk + tid * kPer, pk, rk);
+  double tv = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) tv += use_p ? pk[j] : rk[j];
   const double tincl = block_incl_scan(sh, tv);
   const double texcl = sh.excl + (tincl - tv);
   if (tv > 0.0 && sh.excl + tincl > xs) atomicMin(&sh.tstar, tid);
@@ -775,9 +775,6 @@ sampler_kernel(SampArgs a) {
     int f = sh.flags;
     int yy = -1;
     if (sh.tstar != INT_MAX) {
-      // the owning thread recomputes its kPer weights (same arithmetic, same order)
-      double pk[kPer], rk[kPer];
-      weights(owner * kChunk + tid * kPer, pk, rk);
       double run = texcl;
       double lo = 0.0, hi = 0.0;
       int last_w = -1;
@@ -865,7 +862,6 @@ struct DraftArgs {
   int rows, V, nch;
   int32_t *tok, *flags;
   double *chunk_sums;    // [rows][nch]
-  double *thread_sums;   // [rows][nch][kST]
 };
 
 __device__ __forceinline__ void draft_vals(const DraftArgs &a, int r, int k0, double *w) {
@@ -883,7 +879,6 @@ draft_sums_kernel(DraftArgs a) {
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) s += w[j];
-  a.thread_sums[((int64_t)r * a.nch + c) * kST + tid] = s;
   s = warp_sum(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
@@ -920,7 +915,13 @@ draft_draw_kernel(DraftArgs a) {
   if (tid == sh.owner) sh.excl = incl - cs;
   __syncthreads();
   const int owner = sh.owner;
-  const double tv = a.thread_sums[((int64_t)r * a.nch + owner) * kST + tid];
+  // the owner chunk's per-thread sums, recomputed in the sums kernel's order
+  double w[kPer];
+  const int k0 = owner * kChunk + tid * kPer;
+  draft_vals(a, r, k0, w);
+  double tv = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) tv += w[j];
   const double tincl = block_incl_scan(sh, tv);
   const double texcl = sh.excl + (tincl - tv);
   if (tv > 0.0 && sh.excl + tincl > xs) atomicMin(&sh.tstar, tid);
@@ -929,9 +930,6 @@ draft_draw_kernel(DraftArgs a) {
     int f = sh.flags;
     int yy = -1;
     if (sh.tstar != INT_MAX) {
-      double w[kPer];
-      const int k0 = owner * kChunk + tid * kPer;
-      draft_vals(a, r, k0, w);
       double run = texcl, lo = 0.0, hi = 0.0;
       int last_w = -1;
       for (int j = 0; j < kPer; ++j) {
@@ -963,8 +961,7 @@ draft_draw_kernel(DraftArgs a) {
 
 size_t draft_workspace_bytes(int rows, int V) {
   const int nch = (V + kChunk - 1) / kChunk;
-  return ((((size_t)rows * nch * sizeof(double)) + 255) & ~(size_t)255) +
-         (((size_t)rows * nch * kST * sizeof(double) + 255) & ~(size_t)255);
+  return (((size_t)rows * nch * sizeof(double)) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_draft_sample(const float *q, int rows, int V, const double *u, int32_t *tok,
@@ -978,8 +975,6 @@ hipError_t launch_draft_sample(const float *q, int rows, int V, const double *u,
   a.tok = tok;
   a.flags = flags;
   a.chunk_sums = (double *)ws;
-  a.thread_sums = (double *)((char *)ws + ((((size_t)rows * a.nch * sizeof(double)) + 255) &
-                                           ~(size_t)255));
   hipLaunchKernelGGL(draft_sums_kernel, dim3(a.nch, rows), dim3(kST), 0, st, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL(draft_draw_kernel, dim3(rows), dim3(kST), 0, st, a);
@@ -1004,8 +999,6 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats) {
   off += ((size_t)B * W * D + 255) & ~(size_t)255;
   w.attn_flags = (int32_t *)(p + off);
   off += ((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255;
-  w.thread_sums = (double2 *)(p + off);
-  off += ((size_t)B * nch * kST * sizeof(double2) + 255) & ~(size_t)255;
   w.pv = (double *)(p + off);
   off += ((size_t)B * (W * D + 1) * W * sizeof(double) + 255) & ~(size_t)255;
   w.amax = (int32_t *)(p + off);
@@ -1136,7 +1129,6 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   a.flags_accumulate = flags_accumulate;
   a.attn_flags = attn_flags;
   a.chunk_sums = ws.chunk_sums;
-  a.thread_sums = ws.thread_sums;
   a.counters = ws.counters;
   // fused while the workgroups number about one per CU or fewer (measured: B = 1 at
   // V = 128256 is faster fused, B = 32 far faster in two launches)

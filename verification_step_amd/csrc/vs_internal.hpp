@@ -153,7 +153,6 @@ struct SampleWs {
   double *root_lse;     // [B]
   uint8_t *code;        // [B][W][D] acceptance codes
   int32_t *attn_flags;  // [B] flags raised by attention inside the step, zero between calls
-  double2 *thread_sums; // [B][n_chunks][256] per-thread weight sums of the sampler
   double *pv;           // [B][W*D+1][W] multi-candidate acceptance: p of each candidate token
   int32_t *amax;        // [B*W*D + B] greedy: argmax of every verify row, then the root rows
   uint8_t *amax_tie;    // [B*W*D + B] greedy: near tie between the two largest logits

@@ -276,6 +276,30 @@ def test_head_full(M, d, V, dtype, T):
     assert np.abs(tensor_np(lse) - l).max() < 1e-5
 
 
+def test_head_full_llama70b_size_sampled():
+    """The full head at the Llama-70B shape (M = 160 rows, d = 8192, V = 128,256; two row
+    blocks per vocabulary tile): 4,096 sampled vocabulary rows against the oracle's
+    fp64 product, and every row's normaliser against the logsumexp of the kernel's own
+    logits (a property at any size)."""
+    import torch
+    api = _api()
+    M, d, V = 160, 8192, 128256
+    rng = np.random.default_rng(70)
+    h = wl.f32_to_bf16_bits((rng.standard_normal((M, d)) * 0.05).astype(np.float32))
+    w = np.empty((V, d), dtype=np.uint16)
+    for i in range(0, V, 8192):
+        n = min(8192, V - i)
+        w[i:i + n] = wl.f32_to_bf16_bits((rng.standard_normal((n, d)) / np.sqrt(d)).astype(np.float32))
+    say("head 70b size")
+    lg, lse, _ = api.lm_head(to_dev(h, True), w_full=to_dev(w, True))
+    rows = np.sort(rng.choice(V, 4096, replace=False))
+    g = tensor_np(lg)
+    z = oracle.as_f64(h, "bf16") @ oracle.bf16_bits_to_f64(w[rows]).T
+    assert rel_err(g[:, rows], z) <= TOL
+    own = torch.logsumexp(lg.double(), dim=1).cpu().numpy()
+    assert np.abs(tensor_np(lse) - own).max() < 1e-6
+
+
 @pytest.mark.parametrize("M,d,r,V", [(7, 256, 64, 1000), (5, 512, 32, 3000)])
 def test_head_lowrank_small(M, d, r, V):
     api = _api()

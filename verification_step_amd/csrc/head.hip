@@ -325,14 +325,21 @@ head_lds_kernel(GemmArgs a) {
       const int ss = c * (kHC / 32) + u;
       // ring slot of step ss is ss % kRingL; kHC/32 == kRingL keeps it static
       if (ss + kPDL < nsteps) load_w((u + kPDL) % kRingL, ss + kPDL);
+      // all of this step's H fragments are read first, then the products: one LDS
+      // latency per step instead of one per pair of row tiles
+      bf16x8 hf[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = mt * 16 + l16;
         const int pch = (4 * u + lg) ^ (row & 15);
-        const bf16x8 hf = *(const bf16x8 *)&Hs[buf][row * kHC + 8 * pch];
-#pragma unroll
-        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wr[u][v], hf, acc[v][mt]);
+        hf[mt] = *(const bf16x8 *)&Hs[buf][row * kHC + 8 * pch];
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wr[u][v], hf[mt], acc[v][mt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);        // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, MT * kVT, 0);  // then the products
     }
     if (c + 1 < nchunks) {
       // everything up to this chunk's H transfers: only the W loads issued after them

@@ -286,7 +286,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: there is no multi-GPU path "
               "(the verify step of one batch runs on one MI355X)", file=sys.stderr)
         sys.exit(2)
 

@@ -483,8 +483,8 @@ def reject_sample(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
 def reject_sample_multi(root_logits, logits, q, cand_tok, cand_len, u_acc, u_res,
                         temperature: float = 1.0, gate=None):
     """Lossless acceptance over W candidates: recursive residual across the sibling
-    candidates at each depth (the survey's next item N1; built from section 3's
-    single-draft rule and its residual).
+    candidates at each depth (built from [SD] section 3's single-draft rule and its
+    residual).
 
     Depth a starts from the target distribution P of the reference row: the root for
     a = 0, else row (ref, a-1), ref being the smallest surviving candidate.  The

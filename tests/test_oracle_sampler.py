@@ -277,7 +277,7 @@ def test_ties_choose_smallest_candidate_and_bad_token_rejects():
 
 
 # ----------------------------------------------------------------- lossless multi-candidate
-# (the survey's next item N1: recursive residual across sibling candidates)
+# (recursive residual across sibling candidates)
 
 def run_multi(root_p, rows_p, q, toks, lens, u_acc, u_res, W, D):
     V = len(root_p)

@@ -258,9 +258,10 @@ int vs_draft_sample(const float *q, int rows, int V, const double *u, int32_t *t
  * and after each of the 5 stages (retrieval+gate, attention, head GEMM, normalisers
  * and acceptance tests, sampler) -- for timing only.
  * aux_stream, fork_event, join_event: NULL, or a second stream (default priority)
- * and two events owned by the caller.  Then retrieval + gate, which nothing before
- * the acceptance tests reads, run on aux_stream concurrently with attention and the
- * head: fork_event is recorded on `stream` and waited for on aux_stream before the
+ * and two events owned by the caller.  Then retrieval + gate, when they have a launch
+ * of their own (bf16 attention with fewer than four waves per row block; otherwise
+ * they ride in the attention launch), run on aux_stream concurrently with attention
+ * and the head: fork_event is recorded on `stream` and waited for on aux_stream before the
  * retrieval; join_event is recorded on aux_stream after it and waited for on
  * `stream` before the tests.  Stage event 1 then follows event 0 directly (the
  * retrieval is off the main stream). */

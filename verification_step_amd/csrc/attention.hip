@@ -568,16 +568,23 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// The copy path's gate can ride in front: the first n_gate workgroups retrieve and gate
+// one sequence each.
 template <int HD>
 __global__ void __launch_bounds__(256)
 attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const float *k_pool,
                 const float *v_pool, const int32_t *page_table, const int32_t *prefix_len,
                 float *out, int32_t *flags, int B, int W, int D, int Hq, int Hkv, int max_pages,
-                int n_pool_pages, float scale) {
+                int n_pool_pages, float scale, int n_gate, GateArgs gate) {
   static_assert(HD <= 64, "one output element per lane");
+  if ((int)blockIdx.x < n_gate) {
+    __shared__ GateShared<256> gsh;
+    gate_wg<256>(gate, blockIdx.x, gsh);
+    return;
+  }
   const int M = W * D;
   const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t task = (int64_t)((int)blockIdx.x - n_gate) * 4 + (threadIdx.x >> 6);
   if (task >= (int64_t)B * M * Hq) return;     // uniform per wave
   const int hq = (int)(task % Hq);
   const int r = (int)((task / Hq) % M);
@@ -646,7 +653,7 @@ __global__ void zero_i32_kernel(int32_t *p, int n) {
 }  // namespace
 
 bool attn_fuses_gate(int B, int W, int D, int Hq, int Hkv, int max_pages, int dtype) {
-  return dtype == 1 && attn_plan(B, W, D, Hq, Hkv, max_pages, kPage).nw >= 4;
+  return dtype == 0 || (dtype == 1 && attn_plan(B, W, D, Hq, Hkv, max_pages, kPage).nw >= 4);
 }
 
 AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page) {
@@ -705,12 +712,14 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   const int M = W * D;
   if (dtype == 0) {
     const int64_t n = (int64_t)B * M * Hq;    // one wave each, four per workgroup
-    const int blocks = (int)((n + 3) / 4);
+    const int n_gate = gate != nullptr ? B : 0;
+    const int blocks = (int)((n + 3) / 4) + n_gate;
+    const GateArgs ga = gate != nullptr ? *gate : GateArgs{};
 #define VS_F32_ATTN(HDV)                                                                       \
   hipLaunchKernelGGL(attn_f32_kernel<HDV>, dim3(blocks), dim3(256), 0, st, (const float *)q,   \
                      (const float *)k_cand, (const float *)v_cand, (const float *)k_pool,      \
                      (const float *)v_pool, page_table, prefix_len, (float *)out, flags, B, W, \
-                     D, Hq, Hkv, max_pages, n_pool_pages, scale)
+                     D, Hq, Hkv, max_pages, n_pool_pages, scale, n_gate, ga)
     if (hd == 16) VS_F32_ATTN(16);
     else if (hd == 32) VS_F32_ATTN(32);
     else VS_F32_ATTN(64);

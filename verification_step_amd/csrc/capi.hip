@@ -292,10 +292,10 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
   hipError_t e;
   if (!mark(0)) return VS_ERR_HIP;
-  // 1. copy retrieval + probe gate.  When the attention row blocks have four or more
-  //    waves, its B workgroups ride in the attention launch (step 2) and run beside
-  //    the attention workgroups; otherwise one launch of its own, on the auxiliary
-  //    stream when given.  It is the first writer of io->flags; attention reports
+  // 1. copy retrieval + probe gate.  With fp32 attention, or bf16 attention whose row
+  //    blocks have four or more waves, its B workgroups ride in the attention launch
+  //    (step 2) and run beside the attention workgroups; otherwise one launch of its
+  //    own, on the auxiliary stream when given.  It is the first writer of io->flags; attention reports
   //    into the workspace (sw.attn_flags), which the sampler folds in, so the two never
   //    race.
   const bool copy_path = !d->external_drafts;

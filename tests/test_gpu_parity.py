@@ -924,7 +924,7 @@ def _check_step(case, g, o, external=False):
     return n_cmp, n_exc
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "llama8b", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "small", "llama8b", "llama70b", "ragged"])
 def test_verify_step_end_to_end(name):
     api = _api()
     if name == "tiny":
@@ -933,6 +933,8 @@ def test_verify_step_end_to_end(name):
         sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
     elif name == "llama8b":
         sh, seed = wl.config(2), 2000
+    elif name == "llama70b":
+        sh, seed = wl.config(4), 4000
     else:
         sh, seed = wl.config(5), 5000
     case = get_case(("step", name), lambda: wl.make_case(sh, seed))

@@ -244,12 +244,19 @@ __device__ __forceinline__ void dma16_h(const void *g, bf16_t *lds_dst) {
                : "memory", "m0");
 }
 
-// NG vocabulary tiles (of 4 waves each) share one workgroup and one staging of H.
-template <int MT, int NG>
+// A workgroup of 4*NG waves shares one staging of H.  Each wave streams VT 16-row
+// strips of W: with VT = 4 a vocabulary tile (256 rows of W) takes 4 waves and the
+// workgroup holds NG tiles; with VT = 2 it takes 8 waves, which halves the register
+// tile per row so that up to 12 row tiles (192 rows) fit in one row block and each
+// strip of W is streamed once instead of once per row block.
+template <int MT, int NG, int VT = kVT>
 __global__ void __launch_bounds__(kThreads * NG, 2)
 head_lds_kernel(GemmArgs a) {
+  constexpr int kWPT = kHeadVocabTile / (VT * 16);   // waves per vocabulary tile
+  constexpr int kTPW = 4 * NG / kWPT;                 // vocabulary tiles per workgroup
+  static_assert(kTPW >= 1 && kTPW * kWPT == 4 * NG, "waves split evenly over tiles");
   // the H double buffer; after the K loop the same LDS stages each wave's logits tile
-  // (16 rows x 64 columns, rows padded to kStRow floats) for whole-segment stores
+  // (16 rows x 16 VT columns, rows padded to kStRow floats) for whole-segment stores
   constexpr int kHsBuf = MT * 16 * kHC;
   constexpr int kStRow = 68;
   constexpr int kStageF = 4 * NG * 16 * kStRow;
@@ -261,34 +268,34 @@ head_lds_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int grp = wv >> 2;          // vocabulary tile of this wave within the workgroup
-  const int wq = wv & 3;            // wave within the tile
+  const int grp = wv / kWPT;        // vocabulary tile of this wave within the workgroup
+  const int wq = wv % kWPT;         // wave within the tile
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
-  const int nblocks = ((n_vt + NG - 1) / NG) * a.n_mblocks;
+  const int nblocks = ((n_vt + kTPW - 1) / kTPW) * a.n_mblocks;
   const int bid = xcd_remap(blockIdx.x, nblocks);
   const int mb = bid % a.n_mblocks;
-  const int vt = (bid / a.n_mblocks) * NG + grp;
+  const int vt = (bid / a.n_mblocks) * kTPW + grp;
   const bool tile_ok = vt < n_vt;
-  const int vbase = vt * kHeadVocabTile + wq * (kVT * 16);
+  const int vbase = vt * kHeadVocabTile + wq * (VT * 16);
   const int mbase = mb * MT * 16;
   const int nsteps = a.K / 32;
   const int nchunks = a.K / kHC;
 
   const int n_strips = (a.N + 15) / 16;
-  const bf16_t *wp[kVT];
+  const bf16_t *wp[VT];
 #pragma unroll
-  for (int v = 0; v < kVT; ++v) {
+  for (int v = 0; v < VT; ++v) {
     int t = vbase / 16 + v;
     t = t < n_strips ? t : n_strips - 1;
     wp[v] = a.w + ((int64_t)t * nsteps * 64 + lane) * 8;
   }
   constexpr int kPDL = 3, kRingL = kPDL + 1;   // W steps in flight; one ring turn per chunk
-  bf16x8 wr[kRingL][kVT];
+  bf16x8 wr[kRingL][VT];
   auto load_w = [&](int slot, int s) {
 #pragma unroll
-    for (int v = 0; v < kVT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 512 * s);
+    for (int v = 0; v < VT; ++v) wr[slot][v] = *(const bf16x8 *)(wp[v] + 512 * s);
   };
   // H chunk c: MT*16 rows x 128 columns = MT*4 transfers of 1 KB (4 rows each); wave
   // wv issues transfers wv, wv+4*NG, ...
@@ -306,9 +313,9 @@ head_lds_kernel(GemmArgs a) {
     }
   };
 
-  f32x4 acc[kVT][MT];
+  f32x4 acc[VT][MT];
 #pragma unroll
-  for (int v = 0; v < kVT; ++v)
+  for (int v = 0; v < VT; ++v)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[v][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -337,24 +344,25 @@ head_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int v = 0; v < kVT; ++v) acc[v][mt] = mfma16x16x32(wr[u][v], hf[mt], acc[v][mt]);
-      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);        // the LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, MT * kVT, 0);  // then the products
+        for (int v = 0; v < VT; ++v) acc[v][mt] = mfma16x16x32(wr[u][v], hf[mt], acc[v][mt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);       // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, MT * VT, 0);  // then the products
     }
     if (c + 1 < nchunks) {
       // everything up to this chunk's H transfers: only the W loads issued after them
-      // (kHC/32 steps x kVT) may still be in flight
-      __builtin_amdgcn_s_waitcnt(0x0F70 | ((kHC / 32) * kVT & 15) | ((((kHC / 32) * kVT) >> 4) << 14));
+      // (kHC/32 steps x VT) may still be in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((kHC / 32) * VT & 15) | ((((kHC / 32) * VT) >> 4) << 14));
       __syncthreads();
     }
   }
   static_assert(kHC / 32 == kRingL, "one ring turn per H chunk");
 
   // ---- epilogue: logits + tile statistics.  With one or two row blocks (the weight
-  // stream dominates) each row tile goes through LDS: a wave writes its 16 x 64
-  // fragment, then stores 4 rows x 256 contiguous bytes per instruction -- whole cache
-  // lines, written non-temporally (the sampler reads one of these rows back, later).
-  // With more row blocks (matrix-bound shapes) the fragments are stored directly.
+  // stream dominates) each row tile goes through LDS: a wave writes its 16 x (16 VT)
+  // fragment, then stores it as whole rows of 64 VT contiguous bytes (4 rows per
+  // instruction at VT = 4, 8 at VT = 2) -- whole cache lines, written non-temporally
+  // (the sampler reads one of these rows back, later).  With more row blocks
+  // (matrix-bound shapes) the fragments are stored directly.
   const bool staged = a.n_mblocks <= 2;
   float *stg = reinterpret_cast<float *>(Hs_all) + wv * 16 * kStRow;
   if (staged) __syncthreads();   // every wave is done reading H
@@ -362,7 +370,7 @@ head_lds_kernel(GemmArgs a) {
   for (int mt = 0; mt < MT; ++mt) {
     float vmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kVT; ++v) {
+    for (int v = 0; v < VT; ++v) {
       const int n0 = vbase + v * 16 + 4 * lg;
       if (staged) {
         *(f32x4 *)&stg[l16 * kStRow + v * 16 + 4 * lg] = acc[v][mt];
@@ -384,10 +392,12 @@ head_lds_kernel(GemmArgs a) {
     }
     if (staged) {
       __syncthreads();
+      constexpr int kLPR = 4 * VT;     // lanes per fragment row, 4 floats each
+      constexpr int kRPI = 64 / kLPR;  // fragment rows per store instruction
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + (lane >> 4);
-        const int c = 4 * (lane & 15);
+      for (int i = 0; i < 16 / kRPI; ++i) {
+        const int r = kRPI * i + lane / kLPR;
+        const int c = 4 * (lane % kLPR);
         const int m = mbase + mt * 16 + r;
         const int n = vbase + c;
         if (m < a.M && n < a.N) {
@@ -408,7 +418,7 @@ head_lds_kernel(GemmArgs a) {
     vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
     float vs = 0.f;
 #pragma unroll
-    for (int v = 0; v < kVT; ++v) {
+    for (int v = 0; v < VT; ++v) {
       const int n0 = vbase + v * 16 + 4 * lg;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -420,7 +430,7 @@ head_lds_kernel(GemmArgs a) {
   }
   if (a.stats == nullptr) return;
   if (a.root != nullptr && mb == 0 && tile_ok) {
-    for (int b = wq; b < a.B_root; b += 4) {
+    for (int b = wq; b < a.B_root; b += kWPT) {
       const float *row = a.root + (int64_t)b * a.N;
       float x[kHeadVocabTile / 64];
       float mx = -INFINITY;
@@ -441,15 +451,18 @@ head_lds_kernel(GemmArgs a) {
   }
   __syncthreads();
   if (!tile_ok) return;
-  for (int r = tid & (kThreads - 1); r < MT * 16; r += kThreads) {
+  constexpr int kTT = kThreads * NG / kTPW;   // threads per vocabulary tile
+  static_assert(kTT == 64 * kWPT, "a tile's threads are its waves");
+  for (int r = tid % kTT; r < MT * 16; r += kTT) {
     const int m = mbase + r;
     if (m >= a.M) continue;
+    const float2 *rw = &red[kWPT * grp][r];
     float mx = -INFINITY;
-    for (int w2 = 0; w2 < 4; ++w2) mx = fmaxf(mx, red[4 * grp + w2][r].x);
+    for (int w2 = 0; w2 < kWPT; ++w2) mx = fmaxf(mx, rw[w2 * MT * 16].x);
     float sm = 0.f;
-    for (int w2 = 0; w2 < 4; ++w2)
-      if (red[4 * grp + w2][r].x != -INFINITY)
-        sm += red[4 * grp + w2][r].y * expf(red[4 * grp + w2][r].x - mx);
+    for (int w2 = 0; w2 < kWPT; ++w2)
+      if (rw[w2 * MT * 16].x != -INFINITY)
+        sm += rw[w2 * MT * 16].y * expf(rw[w2 * MT * 16].x - mx);
     a.stats[(int64_t)m * n_vt + vt] = make_float2(mx, sm);
   }
 }
@@ -572,6 +585,20 @@ hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
     // CU instead of twice, which measured faster at every M tried (7, 32, 80)
     const char *ngv = getenv("VSTEP_HEAD_NG");
     const int ng = ngv ? atoi(ngv) : 2;
+    // 9..12 row tiles: one row block of 8 waves x 2 strips per vocabulary tile, so W is
+    // streamed once (two row blocks of 4 strips per wave would each stream it)
+    const int tiles = (a.M + 15) / 16;
+    const char *tallv = getenv("VSTEP_HEAD_TALL");
+    if (ng == 2 && tiles > 8 && tiles <= 12 && !(tallv && atoi(tallv) == 0)) {
+      a.n_mblocks = 1;
+      switch (tiles) {
+        case 9: hipLaunchKernelGGL((head_lds_kernel<9, 2, 2>), dim3(n_vt), dim3(2 * kThreads), 0, st, a); break;
+        case 10: hipLaunchKernelGGL((head_lds_kernel<10, 2, 2>), dim3(n_vt), dim3(2 * kThreads), 0, st, a); break;
+        case 11: hipLaunchKernelGGL((head_lds_kernel<11, 2, 2>), dim3(n_vt), dim3(2 * kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL((head_lds_kernel<12, 2, 2>), dim3(n_vt), dim3(2 * kThreads), 0, st, a); break;
+      }
+      return hipGetLastError();
+    }
 #define VS_LDS_CASE(MTV)                                                                  \
   case MTV:                                                                               \
     if (ng == 2)                                                                          \

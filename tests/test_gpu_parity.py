@@ -265,7 +265,7 @@ def test_pack_weight_layout():
     (37, 256, 1000, "bf16", 1.0), (100, 512, 2000, "bf16", 0.7), (8, 64, 512, "f32", 1.0),
     (160, 1024, 777, "bf16", 1.0), (1024, 256, 300, "bf16", 1.0), (200, 512, 1500, "bf16", 1.0),
     (192, 384, 900, "bf16", 0.8), (160, 8192, 2100, "bf16", 1.0), (144, 256, 1000, "bf16", 1.0),
-    (176, 128, 513, "bf16", 1.2)])
+    (176, 128, 513, "bf16", 1.2), (13, 300, 700, "f32", 0.9), (40, 512, 1000, "f32", 1.0)])
 def test_head_full(M, d, V, dtype, T):
     api = _api()
     h, ws = _head_case(M, d, V, dtype, seed=M + V)
@@ -301,16 +301,18 @@ def test_head_full_llama70b_size_sampled():
     assert np.abs(tensor_np(lse) - own).max() < 1e-6
 
 
-@pytest.mark.parametrize("M,d,r,V", [(7, 256, 64, 1000), (5, 512, 32, 3000)])
-def test_head_lowrank_small(M, d, r, V):
+@pytest.mark.parametrize("M,d,r,V,dtype", [(7, 256, 64, 1000, "bf16"), (5, 512, 32, 3000, "bf16"),
+                                           (9, 130, 21, 600, "f32")])
+def test_head_lowrank_small(M, d, r, V, dtype):
     api = _api()
-    h, ws = _head_case(M, d, V, "bf16", rank=r, seed=r)
-    say("head lowrank", M, d, r, V)
-    lg, lse, pr = api.lm_head(to_dev(h, True), w_down=to_dev(ws["w_down"], True),
-                              w_up=to_dev(ws["w_up"], True), write_probs=True)
-    z, l, _ = oracle.lm_head_lowrank(oracle.as_f64(h, "bf16"), ws["w_down"], ws["w_up"], 1.0,
-                                     "bf16")
-    assert rel_err(tensor_np(lg), z) <= TOL
+    bf = dtype == "bf16"
+    h, ws = _head_case(M, d, V, dtype, rank=r, seed=r)
+    say("head lowrank", M, d, r, V, dtype)
+    lg, lse, pr = api.lm_head(to_dev(h, bf), w_down=to_dev(ws["w_down"], bf),
+                              w_up=to_dev(ws["w_up"], bf), write_probs=True)
+    z, l, _ = oracle.lm_head_lowrank(oracle.as_f64(h, dtype), ws["w_down"], ws["w_up"], 1.0,
+                                     dtype)
+    assert rel_err(tensor_np(lg), z) <= (TOL if bf else 1e-5)
     assert np.abs(tensor_np(lse) - l).max() < 1e-5
     p = oracle.head_softmax(z, l)
     assert rel_err(tensor_np(pr), p) <= TOL

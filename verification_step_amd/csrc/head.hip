@@ -519,31 +519,136 @@ gemm_f32_kernel(const float *A, const float *B, float *out, int M, int N, int K)
   out[gid] = s;
 }
 
-// Tile statistics [rows][n_vt] of stored logits (fp32 path): max and sum of
-// exp(x - max) over one 256-wide vocabulary tile, by wave shuffles and 4 LDS slots.
+// fp32 head in one launch: a workgroup takes one 256-wide vocabulary tile (one column
+// per thread) for kF32Rows rows of H, staged through LDS in chunks of kF32KC columns.
+// Each logit is a k-ordered fmaf chain; then the tile statistics of those rows (max,
+// then sum exp(x - max), by wave shuffles and one LDS slot per wave), and, in row
+// block 0, the same statistics of the root rows (one wave per row, four ids per lane).
+constexpr int kF32Rows = 8;
+constexpr int kF32KC = 256;
+
 __global__ void __launch_bounds__(kThreads)
-tile_stats_kernel(const float *logits, float2 *stats, int M, int N, float inv_t) {
-  static_assert(kThreads == 256 && kHeadVocabTile == 256, "one logit per thread");
+head_f32_kernel(const float *H, const float *W, float *out, float2 *stats, const float *root,
+                float2 *root_stats, int M, int N, int K, int B_root, float inv_t) {
+  static_assert(kThreads == 256 && kHeadVocabTile == 256, "one column per thread");
+  __shared__ float hs[kF32Rows][kF32KC];
+  __shared__ float wmax[kF32Rows][4], wsum[kF32Rows][4];
   const int vt = blockIdx.x;
-  const int m = blockIdx.y;
   const int n_vt = gridDim.x;
-  const int wv = threadIdx.x >> 6;
-  __shared__ float wred[2][4];
-  const int n = vt * kHeadVocabTile + threadIdx.x;
+  const int m0 = blockIdx.y * kF32Rows;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int n = vt * kHeadVocabTile + tid;
   const bool ok = n < N;
-  const float x = ok ? logits[(int64_t)m * N + n] * inv_t : -INFINITY;
-  float v = x;
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) wred[0][wv] = v;
-  __syncthreads();
-  const float mx = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
-  float e = ok ? expf(x - mx) : 0.f;
-  for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
-  if ((threadIdx.x & 63) == 0) wred[1][wv] = e;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    stats[(int64_t)m * n_vt + vt] =
-        make_float2(mx, (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]));
+  const float *wrow = W + (int64_t)(ok ? n : N - 1) * K;
+  const bool vec = ((K & 3) == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
+
+  float acc[kF32Rows];
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r) acc[r] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += kF32KC) {
+    const int kc = min(kF32KC, K - k0);
+    // the chunk's first 64 columns of the W row, issued before the H staging so that
+    // the two loads overlap
+    float4 w4[16];
+    if (vec && kc >= 64) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) w4[q] = *reinterpret_cast<const float4 *>(wrow + k0 + 4 * q);
+    }
+    __syncthreads();   // the previous chunk has been consumed
+    constexpr int kPerT = kF32Rows * kF32KC / kThreads;
+    float hv[kPerT];
+#pragma unroll
+    for (int it = 0; it < kPerT; ++it) {   // all loads first, then the LDS writes
+      const int r = (tid + it * kThreads) / kF32KC, k = (tid + it * kThreads) % kF32KC;
+      hv[it] = (m0 + r < M && k < kc) ? H[(int64_t)(m0 + r) * K + k0 + k] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < kPerT; ++it)
+      hs[(tid + it * kThreads) / kF32KC][(tid + it * kThreads) % kF32KC] = hv[it];
+    __syncthreads();
+    int k = 0;
+    if (vec) {
+      // 64 columns of the W row in flight at once, then their products in k order
+      for (; k + 64 <= kc; k += 64) {
+        if (k > 0) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) w4[q] = *reinterpret_cast<const float4 *>(wrow + k0 + k + 4 * q);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the 16 loads ahead of their uses
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const float wk[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < kF32Rows; ++r) acc[r] = fmaf(hs[r][k + 4 * q + j], wk[j], acc[r]);
+        }
+      }
+      for (; k + 4 <= kc; k += 4) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(wrow + k0 + k);
+        const float wk[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < kF32Rows; ++r) acc[r] = fmaf(hs[r][k + j], wk[j], acc[r]);
+      }
+    }
+#pragma unroll 8
+    for (; k < kc; ++k) {
+      const float w = wrow[k0 + k];
+#pragma unroll
+      for (int r = 0; r < kF32Rows; ++r) acc[r] = fmaf(hs[r][k], w, acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kF32Rows; ++r)
+    if (ok && m0 + r < M) out[(int64_t)(m0 + r) * N + n] = acc[r];
+
+  if (stats != nullptr) {
+    float x[kF32Rows];
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r) {
+      x[r] = ok ? acc[r] * inv_t : -INFINITY;
+      float v = x[r];
+      for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+      if (lane == 0) wmax[r][wv] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kF32Rows; ++r) {
+      const float mx = fmaxf(fmaxf(wmax[r][0], wmax[r][1]), fmaxf(wmax[r][2], wmax[r][3]));
+      float e = ok ? expf(x[r] - mx) : 0.f;
+      for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o);
+      if (lane == 0) wsum[r][wv] = e;
+    }
+    __syncthreads();
+    if (tid < kF32Rows && m0 + tid < M) {
+      const float mx = fmaxf(fmaxf(wmax[tid][0], wmax[tid][1]), fmaxf(wmax[tid][2], wmax[tid][3]));
+      stats[(int64_t)(m0 + tid) * n_vt + vt] =
+          make_float2(mx, (wsum[tid][0] + wsum[tid][1]) + (wsum[tid][2] + wsum[tid][3]));
+    }
+  }
+  if (root == nullptr || root_stats == nullptr || blockIdx.y != 0) return;
+  for (int b = wv; b < B_root; b += 4) {
+    const float *row = root + (int64_t)b * N;
+    float x[kHeadVocabTile / 64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kHeadVocabTile / 64; ++j) {
+      const int k = vt * kHeadVocabTile + j * 64 + lane;
+      x[j] = (k < N) ? row[k] * inv_t : -INFINITY;
+      mx = fmaxf(mx, x[j]);
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < kHeadVocabTile / 64; ++j)
+      if (x[j] != -INFINITY) sm += expf(x[j] - mx);
+    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+    if (lane == 0) root_stats[(int64_t)b * n_vt + vt] = make_float2(mx, sm);
+  }
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -735,17 +840,12 @@ hipError_t launch_head_gemm(int M, int d, int V, int rank, int dtype, float temp
     K = rank;
   }
   const float *Bm = (const float *)(rank > 0 ? w_up : w_full);
-  const int64_t n = (int64_t)M * V;
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, A, Bm, logits, M, V, K);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int n_vt = (V + kHeadVocabTile - 1) / kHeadVocabTile;
-  hipLaunchKernelGGL(tile_stats_kernel, dim3(n_vt, M), dim3(kThreads), 0, st, logits, ws.stats,
-                     M, V, inv_t);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (root_logits && root_stats) return launch_root_stats(root_logits, B_root, V, temperature,
-                                                          root_stats, st);
-  return hipSuccess;
+  const bool with_root = root_logits != nullptr && root_stats != nullptr;
+  hipLaunchKernelGGL(head_f32_kernel, dim3(n_vt, (M + kF32Rows - 1) / kF32Rows), dim3(kThreads),
+                     0, st, A, Bm, logits, ws.stats, with_root ? root_logits : nullptr,
+                     with_root ? root_stats : nullptr, M, V, K, B_root, inv_t);
+  return hipGetLastError();
 }
 
 hipError_t launch_head_finish(int M, int V, float temperature, const float *logits,

@@ -712,21 +712,35 @@ sampler_kernel(SampArgs a) {
       return;
     } else {
       if (tid == 0) {
-        a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
-        __threadfence();
-        const uint32_t old = atomicAdd(&a.counters[b], 1u);
+        // Publication without a device-wide fence (which writes back the whole L2 of
+        // this XCD, with the head's logits in it, and took about 6 us): the sums go out
+        // as agent-scope stores, written through to where every XCD reads them; the
+        // wait for their completion orders them before the counter increment.  The
+        // last workgroup reads them with agent-scope loads issued after its increment
+        // has returned.
+        uint64_t *cp = reinterpret_cast<uint64_t *>(a.chunk_sums + (int64_t)b * a.nch + c);
+        __hip_atomic_store(cp, (uint64_t)__double_as_longlong(sr), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cp + 1, (uint64_t)__double_as_longlong(sp), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t old = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
         sh.is_last = (old == (uint32_t)(a.nch - 1));
       }
       __syncthreads();
       if (!sh.is_last) return;
-      __threadfence();
     }
   }
 
   // ---- last workgroup of the sequence: total, owner chunk, owner thread, draw
   // chunk k's sums on thread k (nch <= kST)
   double2 cs = make_double2(0.0, 0.0);
-  if (tid < a.nch) cs = a.chunk_sums[(int64_t)b * a.nch + tid];
+  if (tid < a.nch) {
+    const uint64_t *cp = reinterpret_cast<const uint64_t *>(a.chunk_sums + (int64_t)b * a.nch + tid);
+    cs.x = __longlong_as_double((long long)__hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    cs.y = __longlong_as_double((long long)__hip_atomic_load(cp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
   double Sx = cs.x, Sy = cs.y;
   block_sum2(sh, Sx, Sy);
   const bool use_target = !(Sx > 0.0);

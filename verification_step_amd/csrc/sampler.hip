@@ -695,6 +695,7 @@ sampler_kernel(SampArgs a) {
 
   // ---- this chunk's sums: thread t owns the kPer consecutive ids c*kChunk + t*kPer ..
   //      (vector loads; 8 KB contiguous per chunk); its sums are kept for the draw
+  double2 own = make_double2(0.0, 0.0);   // this workgroup's chunk sums (fused, nch == 1)
   if constexpr (PHASE != SAMP_DRAW) {
     double sr = 0.0, sp = 0.0;
     {
@@ -710,6 +711,8 @@ sampler_kernel(SampArgs a) {
     if constexpr (PHASE == SAMP_SUMS) {
       if (tid == 0) a.chunk_sums[(int64_t)b * a.nch + c] = make_double2(sr, sp);
       return;
+    } else if (a.nch == 1) {
+      own = make_double2(sr, sp);   // the sequence's only workgroup: its sums are the totals
     } else {
       if (tid == 0) {
         // Publication without a device-wide fence (which writes back the whole L2 of
@@ -736,7 +739,9 @@ sampler_kernel(SampArgs a) {
   // ---- last workgroup of the sequence: total, owner chunk, owner thread, draw
   // chunk k's sums on thread k (nch <= kST)
   double2 cs = make_double2(0.0, 0.0);
-  if (tid < a.nch) {
+  if (PHASE == SAMP_FUSED && a.nch == 1) {
+    if (tid == 0) cs = own;
+  } else if (tid < a.nch) {
     const uint64_t *cp = reinterpret_cast<const uint64_t *>(a.chunk_sums + (int64_t)b * a.nch + tid);
     cs.x = __longlong_as_double((long long)__hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     cs.y = __longlong_as_double((long long)__hip_atomic_load(cp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));

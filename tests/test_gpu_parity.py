@@ -265,7 +265,9 @@ def test_pack_weight_layout():
     (37, 256, 1000, "bf16", 1.0), (100, 512, 2000, "bf16", 0.7), (8, 64, 512, "f32", 1.0),
     (160, 1024, 777, "bf16", 1.0), (1024, 256, 300, "bf16", 1.0), (200, 512, 1500, "bf16", 1.0),
     (192, 384, 900, "bf16", 0.8), (160, 8192, 2100, "bf16", 1.0), (144, 256, 1000, "bf16", 1.0),
-    (176, 128, 513, "bf16", 1.2), (13, 300, 700, "f32", 0.9), (40, 512, 1000, "f32", 1.0)])
+    (176, 128, 513, "bf16", 1.2), (13, 300, 700, "f32", 0.9), (40, 512, 1000, "f32", 1.0),
+    (640, 256, 700, "bf16", 1.0), (480, 128, 513, "bf16", 0.9), (448, 256, 1000, "bf16", 1.0),
+    (400, 384, 300, "bf16", 1.0)])
 def test_head_full(M, d, V, dtype, T):
     api = _api()
     h, ws = _head_case(M, d, V, dtype, seed=M + V)

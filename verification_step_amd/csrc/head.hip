@@ -299,17 +299,24 @@ head_lds_kernel(GemmArgs a) {
   };
   // H chunk c: MT*16 rows x 128 columns = MT*4 transfers of 1 KB (4 rows each); wave
   // wv issues transfers wv, wv+4*NG, ...
+  // (32-bit element offsets of each transfer, computed once: H has M*K < 2^31 elements)
   const bf16_t *hbase = (const bf16_t *)a.h;
+  constexpr int kHT = (MT + NG - 1) / NG;   // transfers per wave per chunk
+  uint32_t hofs[kHT];
+#pragma unroll
+  for (int ii = 0; ii < kHT; ++ii) {
+    const int row = 4 * (wv + 4 * NG * ii) + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    int m = mbase + row;
+    m = m < a.M ? m : a.M - 1;
+    hofs[ii] = (uint32_t)m * (uint32_t)a.K + 8 * ch;
+  }
   auto issue_h = [&](int c, int buf) {
 #pragma unroll
-    for (int ii = 0; ii < (MT + NG - 1) / NG; ++ii) {
+    for (int ii = 0; ii < kHT; ++ii) {
       const int i = wv + 4 * NG * ii;
       if (i >= MT * 4) break;
-      const int row = 4 * i + (lane >> 4);
-      const int ch = (lane & 15) ^ (row & 15);
-      int m = mbase + row;
-      m = m < a.M ? m : a.M - 1;
-      dma16_h(hbase + (int64_t)m * a.K + c * kHC + 8 * ch, &Hs[buf][i * 512]);
+      dma16_h(hbase + hofs[ii] + c * kHC, &Hs[buf][i * 512]);
     }
   };
 
@@ -451,8 +458,7 @@ head_lds_kernel(GemmArgs a) {
   }
   __syncthreads();
   if (!tile_ok) return;
-  constexpr int kTT = kThreads * NG / kTPW;   // threads per vocabulary tile
-  static_assert(kTT == 64 * kWPT, "a tile's threads are its waves");
+  constexpr int kTT = 64 * kWPT;   // threads of one vocabulary tile (its waves)
   for (int r = tid % kTT; r < MT * 16; r += kTT) {
     const int m = mbase + r;
     if (m >= a.M) continue;
@@ -685,7 +691,9 @@ hipError_t launch_stream(GemmArgs a, bool split, int ksplit, hipStream_t st) {
   const int mt = pick_mt(a.M, &a.n_mblocks);
   const int n_vt = (a.N + kHeadVocabTile - 1) / kHeadVocabTile;
   const dim3 grid(n_vt * a.n_mblocks, ksplit);
-  if (!split && ksplit == 1 && a.K % kHC == 0 && getenv("VSTEP_HEAD_STREAM") == nullptr) {
+  // the LDS-staged kernels address H with 32-bit element offsets
+  const bool h32 = (int64_t)a.M * a.K <= (int64_t)INT32_MAX;
+  if (!split && ksplit == 1 && a.K % kHC == 0 && h32 && getenv("VSTEP_HEAD_STREAM") == nullptr) {
     // two vocabulary tiles per workgroup (one workgroup per CU): H is staged once per
     // CU instead of twice, which measured faster at every M tried (7, 32, 80)
     const char *ngv = getenv("VSTEP_HEAD_NG");

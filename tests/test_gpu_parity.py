@@ -279,6 +279,29 @@ def test_head_full(M, d, V, dtype, T):
     assert np.abs(tensor_np(lse) - l).max() < 1e-5
 
 
+@pytest.mark.parametrize("env,M,d,V", [
+    ("VSTEP_HEAD_STREAM=1", 80, 512, 1000),    # register-streaming kernel (the large-H path)
+    ("VSTEP_HEAD_STREAM=1", 300, 256, 700),    # ... over several row blocks
+    ("", 50, 160, 900),                        # d not a multiple of 128: streaming kernel
+    ("VSTEP_HEAD_NG=1", 80, 512, 1000),        # one vocabulary tile per workgroup
+    ("VSTEP_HEAD_TALL=0", 160, 256, 777),      # 160 rows as two row blocks
+])
+def test_head_kernel_variants(env, M, d, V, monkeypatch):
+    """Every head kernel the launcher can choose, against the oracle: the streaming
+    kernel (taken for d % 128 != 0 and for H of 2^31 elements or more) and the tuning
+    variants."""
+    api = _api()
+    if env:
+        k, v = env.split("=")
+        monkeypatch.setenv(k, v)
+    h, ws = _head_case(M, d, V, "bf16", seed=M + d)
+    say("head variant", env or "default", M, d, V)
+    lg, lse, _ = api.lm_head(to_dev(h, True), w_full=to_dev(ws["w_full"], True), temperature=0.9)
+    z, l = oracle.lm_head_full(oracle.as_f64(h, "bf16"), ws["w_full"], 0.9, "bf16")
+    assert rel_err(tensor_np(lg), z) <= TOL
+    assert np.abs(tensor_np(lse) - l).max() < 1e-5
+
+
 def test_head_full_llama70b_size_sampled():
     """The full head at the Llama-70B shape (M = 160 rows, d = 8192, V = 128,256; two row
     blocks per vocabulary tile): 4,096 sampled vocabulary rows against the oracle's

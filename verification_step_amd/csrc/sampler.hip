@@ -716,11 +716,11 @@ sampler_kernel(SampArgs a) {
     } else {
       if (tid == 0) {
         // Publication without a device-wide fence (which writes back the whole L2 of
-        // this XCD, with the head's logits in it, and took about 6 us): the sums go out
-        // as agent-scope stores, written through to where every XCD reads them; the
-        // wait for their completion orders them before the counter increment.  The
-        // last workgroup reads them with agent-scope loads issued after its increment
-        // has returned.
+        // this XCD, with the head's logits in it; with thousands of workgroups those
+        // write-backs queue behind each other): the sums go out as agent-scope stores,
+        // written through to where every XCD reads them; the wait for their completion
+        // orders them before the counter increment.  The last workgroup reads them
+        // with agent-scope loads issued after its increment has returned.
         uint64_t *cp = reinterpret_cast<uint64_t *>(a.chunk_sums + (int64_t)b * a.nch + c);
         __hip_atomic_store(cp, (uint64_t)__double_as_longlong(sr), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

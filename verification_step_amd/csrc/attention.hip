@@ -667,7 +667,8 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   // when the KV head has fewer row tiles
   static const int kNW[] = {1, 2, 4, 5, 8};
   p.nw = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
-  // key splits: about 512 workgroups, at least 256 keys per split (at most 1,024 in a batch)
+  // key splits: about 512 workgroups, at least 256 keys per split (128 for one-wave
+  // row blocks), at most 1,024 in a batch
   const int max_keys = max_pages * page;
   int split_keys = 0;
   // tuning override "nw,split_keys" (values <= 0 keep the heuristic's choice)
@@ -683,19 +684,22 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   p.n_rb = (tiles + p.nw - 1) / p.nw;
   if (split_keys == 0) {
     const int groups = B * Hkv * p.n_rb;
+    // one-wave workgroups leave room for many more per CU: their splits may be as
+    // short as the 4-block ring (128 keys)
+    const int min_keys = p.nw == 1 ? 128 : 256;
     if (B == 1) {
       // one sequence: all its splits are equally long, so one round of about 512
       // equal workgroups (two per CU; the candidates' short splits fill in behind)
       const int want = groups < 512 ? 512 / groups : 1;
       int sk = (max_keys + want - 1) / want;
       sk = ((sk + kKB - 1) / kKB) * kKB;
-      split_keys = sk < 256 ? 256 : sk;
+      split_keys = sk < min_keys ? min_keys : sk;
     } else {
       // a batch may be ragged: short splits keep the workgroups even
       const int want = (512 + groups - 1) / groups;
       int sk = (max_keys + want - 1) / want;
       sk = ((sk + kKB - 1) / kKB) * kKB;
-      split_keys = sk < 256 ? 256 : (sk > 1024 ? 1024 : sk);
+      split_keys = sk < min_keys ? min_keys : (sk > 1024 ? 1024 : sk);
     }
   }
   if (split_keys > kMaxSplitPages * kPage) split_keys = kMaxSplitPages * kPage;

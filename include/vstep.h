@@ -16,7 +16,8 @@
  * Conventions (every entry point):
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *     never allocates or frees memory and keeps no state between calls other than
- *     its loaded code object.
+ *     its loaded code object (which includes the fixed scratch area that only
+ *     vs_verify_step_noalloc uses, and the per-device address of it that call looks up).
  *   - Every call only ENQUEUES work on `stream` (a hipStream_t; NULL = the default
  *     stream) and returns at once; outputs are valid after the stream is synchronised.
  *   - The return value reports host-side validation (checked before anything is
@@ -311,6 +312,26 @@ typedef struct {
 size_t vs_step_workspace_bytes(const vs_step_desc *desc);
 int vs_verify_step(const vs_step_desc *desc, const vs_step_io *io, void *workspace,
                    size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * The verify step without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same descriptor, pointers,
+ * outputs, flags and results as vs_verify_step; the workspace is instead a fixed
+ * scratch area of VS_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which
+ * that GPU holds from the library's load until the process ends.
+ *   - A request whose vs_step_workspace_bytes(desc) exceeds VS_NOALLOC_SCRATCH_BYTES
+ *     returns VS_ERR_UNSUPPORTED before anything is enqueued.
+ *   - `stream` must belong to the current device (else VS_ERR_INVALID_ARG); NULL is
+ *     the current device's default stream.
+ *   - The call makes no hipMalloc, hipFree, hipMemset or other allocating call.  It
+ *     enqueues one small fill kernel first that clears the scratch words that must
+ *     start at zero (the scratch keeps whatever the previous call on that GPU left).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in time on
+ *     one GPU (different streams, or different host threads) race and must be
+ *     serialised by the caller. */
+#define VS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int vs_verify_step_noalloc(const vs_step_desc *desc, const vs_step_io *io, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Copy-mode labels [SW "어떻게 동작하나"]: labels[p] = 1 when position p lies inside a

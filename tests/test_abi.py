@@ -204,6 +204,27 @@ def test_step_validation(lib):
     assert lib.vs_step_workspace_bytes(C.byref(d5)) == 0
 
 
+def test_step_noalloc_validation(lib):
+    """The no-allocation step validates like the workspace step and refuses, before any
+    device call, a request whose workspace would exceed the fixed scratch area."""
+    base = dict(B=1, W=4, D=20, kappa=5, Hq=32, Hkv=8, head_dim=128, page_size=16, max_pages=256,
+                n_pool_pages=256, d=4096, V=128256, dtype=1, scale=0.0, tau=0.4, temperature=1.0,
+                external_drafts=0, ctx_total=4096)
+    d = L.StepDesc(**base)
+    assert 0 < lib.vs_step_workspace_bytes(C.byref(d)) <= L.VS_NOALLOC_SCRATCH_BYTES
+    assert lib.vs_verify_step_noalloc(C.byref(d), None, None) == -1
+    io = L.StepIO()
+    for f in io._fields_:
+        if f[0] != "stage_events":
+            setattr(io, f[0], 16)
+    d2 = L.StepDesc(**{**base, "d": 4000})
+    assert lib.vs_verify_step_noalloc(C.byref(d2), C.byref(io), None) == -1
+    # 32 sequences of up to 32768 prefix tokens: far beyond the scratch area
+    big = L.StepDesc(**{**base, "B": 32, "max_pages": 2048, "n_pool_pages": 65536})
+    assert lib.vs_step_workspace_bytes(C.byref(big)) > L.VS_NOALLOC_SCRATCH_BYTES
+    assert lib.vs_verify_step_noalloc(C.byref(big), C.byref(io), None) == -2
+
+
 def test_kv_validation(lib):
     fake = C.c_void_p(16)
     ok = dict(B=4, W=4, D=20, Hkv=8, head_dim=128, page_size=16, max_pages=64, n_pool_pages=300,

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libvstep.so")
 VS_OK, VS_ERR_INVALID_ARG, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE, VS_ERR_HIP = 0, -1, -2, -3, -4
 VS_F32, VS_BF16 = 0, 1
 VS_ACCEPT_LONGEST, VS_ACCEPT_MULTI, VS_ACCEPT_GREEDY = 0, 1, 2
+VS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 FLAG_PROBE_TIE = 1
 FLAG_ACCEPT_TIE = 2
@@ -29,7 +30,8 @@ EXPORTED = [
     "vs_abi_version", "vs_status_str", "vs_copy_match", "vs_probe_gate",
     "vs_attention_workspace_bytes", "vs_verify_attention", "vs_head_workspace_bytes",
     "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
-    "vs_step_workspace_bytes", "vs_verify_step", "vs_packed_weight_bytes", "vs_pack_weight",
+    "vs_step_workspace_bytes", "vs_verify_step", "vs_verify_step_noalloc",
+    "vs_packed_weight_bytes", "vs_pack_weight",
     "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate",
     "vs_copy_labels_workspace_bytes", "vs_copy_labels",
     "vs_draft_sample_workspace_bytes", "vs_draft_sample",
@@ -111,6 +113,7 @@ def load(path: str = LIB_PATH):
     lib.vs_step_workspace_bytes.restype = C.c_size_t
     lib.vs_step_workspace_bytes.argtypes = [C.POINTER(StepDesc)]
     lib.vs_verify_step.argtypes = [C.POINTER(StepDesc), C.POINTER(StepIO), P, C.c_size_t, P]
+    lib.vs_verify_step_noalloc.argtypes = [C.POINTER(StepDesc), C.POINTER(StepIO), P]
     lib.vs_packed_weight_bytes.restype = C.c_size_t
     lib.vs_packed_weight_bytes.argtypes = [C.c_int, C.c_int]
     lib.vs_pack_weight.argtypes = [P, P, C.c_int, C.c_int, P]

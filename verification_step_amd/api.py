@@ -457,7 +457,7 @@ class VerifyStep:
     def __init__(self, inputs: dict, B: int, W: int, D: int, Hq: int, Hkv: int, hd: int,
                  V: int, tau: float = 0.4, temperature: float = 1.0, kappa: int = 5,
                  external_drafts: bool = False, scale: float = 0.0, overlap: bool = False,
-                 accept: str = "longest"):
+                 accept: str = "longest", noalloc: bool = False):
         self.lib = L.load()
         I = dict(inputs)
         step_shapes(self.lib, I, B, W, D, Hq, Hkv, hd, V, external_drafts, accept)
@@ -495,7 +495,9 @@ class VerifyStep:
         nbytes = self.lib.vs_step_workspace_bytes(C.byref(self.desc))
         if nbytes == 0:
             raise VstepError(L.VS_ERR_INVALID_ARG, "verify_step (descriptor rejected)")
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        # noalloc: the library's fixed scratch area replaces the workspace
+        self.noalloc = bool(noalloc)
+        self.ws = None if self.noalloc else torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.io = L.StepIO()
         self.bind(I)
         if overlap and not external_drafts:
@@ -538,6 +540,10 @@ class VerifyStep:
         self.io.stage_events = ptr
 
     def __call__(self):
+        if self.noalloc:
+            st = self.lib.vs_verify_step_noalloc(C.byref(self.desc), C.byref(self.io), _stream())
+            _raise(st, "verify_step_noalloc")
+            return self.out
         st = self.lib.vs_verify_step(C.byref(self.desc), C.byref(self.io), _ptr(self.ws),
                                      self.ws.numel(), _stream())
         _raise(st, "verify_step")

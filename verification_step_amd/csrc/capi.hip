@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr int kMaxRows = 1024;      // W*D per sequence
@@ -90,6 +92,39 @@ StepLayout step_layout(const vs_step_desc *d) {
   const size_t s = vs::sample_workspace_bytes(d->B, d->W, d->D, d->V);
   L.total = align256(L.sample + s);
   return L;
+}
+
+// ---- fixed scratch area of vs_verify_step_noalloc (no allocation on the call path)
+// One array per GPU, a file-scope device global: the HIP runtime places a copy on
+// every device the library's code object is loaded on, and keeps it until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host that name is
+// only a stand-in for the symbol): the device address of each GPU's copy is looked up
+// once with hipGetSymbolAddress, with that GPU current, and kept in scratch_dev.
+constexpr size_t kScratchBytes = VS_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *scratch_dev[kMaxScratchDevices];
+std::mutex scratch_mu;
+
+// The scratch address on the device of `stream` (which must be the current device).
+int scratch_for_stream(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return VS_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return VS_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return VS_ERR_HIP;
+    if (sdev != dev) return VS_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return VS_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return VS_OK;
 }
 
 }  // namespace
@@ -258,8 +293,8 @@ size_t vs_step_workspace_bytes(const vs_step_desc *d) {
   return step_layout(d).total;
 }
 
-int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
-                   size_t ws_bytes, void *stream) {
+static int verify_step_impl(const vs_step_desc *d, const vs_step_io *io, void *workspace,
+                            size_t ws_bytes, void *stream, bool clear_counters) {
   int st = check_step(d);
   if (st != VS_OK) return st;
   if (!io) return VS_ERR_INVALID_ARG;
@@ -291,6 +326,13 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
   const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
   const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
   hipError_t e;
+  if (clear_counters) {
+    // a shared scratch area holds whatever the last call left there: the words that
+    // must start at zero (sampler counters, attention flags) are cleared by a kernel
+    e = vs::launch_zero_i32((int32_t *)sw.counters, d->B, s);
+    if (e == hipSuccess) e = vs::launch_zero_i32(sw.attn_flags, d->B, s);
+    if (e != hipSuccess) return VS_ERR_HIP;
+  }
   if (!mark(0)) return VS_ERR_HIP;
   // 1. copy retrieval + probe gate.  With fp32 attention, or bf16 attention whose row
   //    blocks have four or more waves, its B workgroups ride in the attention launch
@@ -350,6 +392,22 @@ int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
                          d->external_drafts ? 0 : 1, sw, s, sw.attn_flags, rule, io->u_acc);
   if (e != hipSuccess || !mark(5)) return VS_ERR_HIP;
   return VS_OK;
+}
+
+int vs_verify_step(const vs_step_desc *d, const vs_step_io *io, void *workspace,
+                   size_t ws_bytes, void *stream) {
+  return verify_step_impl(d, io, workspace, ws_bytes, stream, false);
+}
+
+int vs_verify_step_noalloc(const vs_step_desc *d, const vs_step_io *io, void *stream) {
+  const int st = check_step(d);
+  if (st != VS_OK) return st;
+  if (!io) return VS_ERR_INVALID_ARG;
+  if (step_layout(d).total > kScratchBytes) return VS_ERR_UNSUPPORTED;
+  void *ptr = nullptr;
+  const int sst = scratch_for_stream(S(stream), &ptr);
+  if (sst != VS_OK) return sst;
+  return verify_step_impl(d, io, ptr, kScratchBytes, stream, true);
 }
 
 size_t vs_draft_sample_workspace_bytes(int rows, int V) {

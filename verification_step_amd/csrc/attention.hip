@@ -317,6 +317,30 @@ attn_mfma_kernel(AttnArgs a) {
     return S;
   };
 
+  // V^T fragments of a prefix block that is not full: the values of keys past the
+  // prefix or on a bad page set to zero.  Their probabilities are zero already, but a
+  // page tail may hold anything (a NaN or an infinity times zero would reach O).
+  auto mask_v = [&](bf16x8 *vf, int kb) {
+    const int pl = (kb - k_begin) >> 4;
+    const bool pv0 = pages[pl] >= 0;
+    const bool pv1 = (kb + 16 < k_end) && pages[pl + 1] >= 0;
+    if (pv0 && pv1 && kb + kKB <= k_end) return;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bool pok = ks == 0 ? pv0 : pv1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 w = __builtin_bit_cast(u32x4, vf[2 * t + ks]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = kb + 16 * ks + 8 * h + 2 * e;   // keys of this word's two values
+          w[e] &= ((pok && k0 < k_end) ? 0x0000ffffu : 0u) | ((pok && k0 + 1 < k_end) ? 0xffff0000u : 0u);
+        }
+        vf[2 * t + ks] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
+
   // masking and the running maximum of one block's scores (may rescale O and l)
   auto softmax_max = [&](f32x16 &S, int kb) {
     // block validity, uniform over the workgroup: a block of 32 in-range keys on two
@@ -438,6 +462,7 @@ attn_mfma_kernel(AttnArgs a) {
       bf16x8 kf[8], vf[8];
       load_k(more ? (j + 1) & 3 : j & 3, kf);
       load_v(j & 3, vf);
+      mask_v(vf, kb);
       softmax_max(S_cur, kb);
       f32x16 S_next = qk_mma(kf);     // harmless recomputation on the last block
       softmax_pv(S_cur, vf);

@@ -34,9 +34,10 @@
 // same order gives the same bits, and the owning thread then holds its ids' weights)
 // and writes the outputs.  Two ways to reach the draw:
 //   * fused: the last workgroup of the sequence to finish (atomic counter in the
-//     workspace, reset afterwards) does it.  Each workgroup then publishes its sums
-//     with a device-scope release, which writes back its XCD's L2; with a few dozen
-//     workgroups that is cheap;
+//     workspace, reset afterwards) does it.  Each workgroup publishes its sums with
+//     agent-scope atomic stores followed by an agent-scope acquire-release increment of
+//     the counter (the release writes back its XCD's L2); with a few dozen workgroups
+//     that is cheap;
 //   * two launches: the chunk sums kernel ends, and a second kernel of one workgroup
 //     per sequence draws.  With thousands of workgroups (large batches) the releases
 //     of the fused form queue up behind each other and this is faster.
@@ -715,19 +716,18 @@ sampler_kernel(SampArgs a) {
       own = make_double2(sr, sp);   // the sequence's only workgroup: its sums are the totals
     } else {
       if (tid == 0) {
-        // Publication without a device-wide fence (which writes back the whole L2 of
-        // this XCD, with the head's logits in it; with thousands of workgroups those
-        // write-backs queue behind each other): the sums go out as agent-scope stores,
-        // written through to where every XCD reads them; the wait for their completion
-        // orders them before the counter increment.  The last workgroup reads them
-        // with agent-scope loads issued after its increment has returned.
+        // Publication: the sums are agent-scope atomic stores, and the counter increment
+        // is an agent-scope acquire-release read-modify-write.  Its release half orders
+        // this workgroup's sums before the increment; its acquire half, in the
+        // workgroup that reads the final count, orders every other workgroup's sums
+        // before the loads that follow.  (Only the few dozen workgroups of a small batch
+        // take this path; large batches draw in a second launch.)
         uint64_t *cp = reinterpret_cast<uint64_t *>(a.chunk_sums + (int64_t)b * a.nch + c);
         __hip_atomic_store(cp, (uint64_t)__double_as_longlong(sr), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(cp + 1, (uint64_t)__double_as_longlong(sp), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const uint32_t old = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED,
+        const uint32_t old = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_ACQ_REL,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         sh.is_last = (old == (uint32_t)(a.nch - 1));
       }

@@ -44,6 +44,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_llama8b_traffic.json")
 HEAD_SRC = os.path.join(ROOT, "verification_step_amd", "csrc", "head.hip")
 
 
+
+def rho_tps(nu: float, rho_tau: float, kappa: float) -> float:
+    """SlimSpec's acceptance-cost model ("SlimSpec: Low-Rank Draft LM-Head ...",
+    gist.science, "이론적 프레임워크"): the end-to-end speed-up of a draft head that
+    takes nu times the full head's time and keeps rho_tau of the acceptance length,
+    when the full head takes kappa times the rest of the drafting pipeline.  Reported
+    beside the measured nu; the verify path itself never evaluates it."""
+    return rho_tau * (1.0 + kappa) / (1.0 + nu * kappa)
+
 def head_bytes(M, d, V, esz=2):
     """Algorithmic bytes of one full-head launch: W + H (esz bytes each) + fp32 logits."""
     return V * d * esz + M * d * esz + M * V * 4
@@ -118,8 +127,104 @@ def cpu_baseline(case, shape, min_seconds=10.0, accept="longest"):
                       "%dx%d head over %d rows, sampler) on the same inputs, fp64 "
                       "NumPy/BLAS; %.1f s" % (n, sh.name, what, int(sum(sh.P)), sh.V, sh.d,
                                               sh.B * sh.M, dt),
-            "seconds_per_step": dt / n,
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds_per_step": dt / n, **host_info()}
+
+
+def measure_peaks(lib, dev):
+    """What this GPU sustains, timed with HIP events on the current stream: a 1 GiB
+    read stream (16-byte vector loads, eight in flight per thread, over 1,024, 4,096 and
+    16,384 workgroups) and back-to-back MFMA 32x32x16 bf16 products on register operands
+    (two workgroups of four waves per CU).  Best of five launches each, after two
+    warm-ups."""
+    import ctypes as C
+    import torch
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    fsink = torch.zeros(4096, dtype=torch.float32, device=dev)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_wg_mfma, iters = 2 * n_cu, 2000
+
+    def best(launch):
+        for _ in range(2):
+            launch()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    def rd(n_wg):
+        def go():
+            assert lib.vs_measure_read(C.c_void_p(buf.data_ptr()), nbytes,
+                                       C.c_void_p(sink.data_ptr()), n_wg, stream) == 0
+        return go
+
+    def mm():
+        assert lib.vs_measure_mfma(n_wg_mfma, iters, C.c_void_p(fsink.data_ptr()), stream) == 0
+
+    t_rd = min(best(rd(n)) for n in (1024, 4096, 16384))
+    t_mm = best(mm)
+    flops = n_wg_mfma * 4 * iters * 8 * 32768.0
+    del buf
+    return {"read_stream_GBs": nbytes / t_rd / 1e9, "mfma_bf16_TFLOPs": flops / t_mm / 1e12,
+            "how": "1 GiB read once per launch (1,024 / 4,096 / 16,384 workgroups, 16-byte "
+                   "loads, eight in flight per thread); %d "
+                   "workgroups x 4 waves x %d x 8 independent MFMA 32x32x16 bf16; best of 5 "
+                   "event-timed launches" % (n_wg_mfma, iters), "cus": n_cu}
+
+
+def host_info():
+    """The host the oracle baseline runs on: CPU model, cores the process may use,
+    os.cpu_count() and the BLAS thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = max((i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"),
+                   default=None)
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count(), "blas_threads": blas}
+
+
+def trace_summary(path):
+    """Markdown table of a rocprofv3 kernel trace (run_kernel_trace.csv): calls, mean,
+    median, p10, p90, min and max duration per kernel, in microseconds."""
+    import csv
+    import numpy as np
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("KernelName") or row.get("Name")
+            t0 = int(row.get("Start_Timestamp") or row.get("BeginNs"))
+            t1 = int(row.get("End_Timestamp") or row.get("EndNs"))
+            durs.setdefault(name, []).append((t1 - t0) / 1e3)
+    lines = ["| kernel | calls | mean | median | p10 | p90 | min | max |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        d = np.asarray(d)
+        short = name.replace("(anonymous namespace)::", "")
+        short = short.split("(")[0] if short.startswith("vs::") or short.startswith("void vs::") else short[:60]
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+            short, len(d), d.mean(), np.median(d), np.percentile(d, 10), np.percentile(d, 90),
+            d.min(), d.max()))
+    return "\n".join(lines)
 
 
 def traffic_entry():
@@ -207,7 +312,7 @@ def draft_head_tradeoff(api, sh, case, step, dev, K, Wm):
     nu = t["lowrank"] / t["full"]
     return {"t_full_head_us": t["full"], "t_lowrank_head_us": t["lowrank"], "nu": nu,
             "rho_tau": 0.99,
-            "rho_tps": {str(k): api.rho_tps(nu, 0.99, k) for k in (0.25, 0.5, 1.0, 2.0)},
+            "rho_tps": {str(k): rho_tps(nu, 0.99, k) for k in (0.25, 0.5, 1.0, 2.0)},
             "note": "heads with probabilities on gamma=%d rows, r=%d; the same head weights "
                     "serve as the full draft head" % (sh.gamma, sh.rank)}
 
@@ -262,7 +367,7 @@ def run_labels(args, api, wl, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=list(WORKLOADS), default="llama8b")
     ap.add_argument("--kv-buffers", type=int, default=0, help="0: the workload's default")
@@ -283,7 +388,16 @@ def main():
     ap.add_argument("--label-tokens", type=int, default=1 << 20)
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the read-stream and MFMA ceilings measured on this GPU")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print a markdown summary (mean, median, p10, p90) of a rocprofv3 "
+                         "kernel trace and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: there is no multi-GPU path "
@@ -312,6 +426,8 @@ def main():
     if args.labels:
         run_labels(args, api, wl, dev)
         return
+
+    peaks = None if args.no_peaks else measure_peaks(_lib.load(), dev)
 
     cfg, n_kv, n_head = WORKLOADS[args.workload]
     n_kv = args.kv_buffers or n_kv
@@ -481,6 +597,11 @@ def main():
                 "achieved": hf / head_s / 1e12, "peak": MFMA_PEAK[dt_name] / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if peaks is not None:
+        roof["peak_measured"] = (peaks["read_stream_GBs"] if roof["bound"] == "hbm"
+                                 else peaks["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else None)
+        if roof["peak_measured"]:
+            roof["frac_measured"] = roof["achieved"] / roof["peak_measured"]
     roof["traffic"] = traffic_entry() if args.workload == "llama8b" else None
     kname = "vs::head_lds_kernel" if dt_name == "bf16" else "vs::gemm_f32_kernel"
     roof.update({"kernel": kname + " (full LM head GEMM + tile statistics), M=%d" % MR,
@@ -532,6 +653,12 @@ def main():
                                                         af / MFMA_PEAK[dt_name]) / att_s},
         "accepted": [int(x) for x in out["n_acc"].cpu().tolist()][:4],
     }
+    if peaks is not None:
+        rec["peaks_measured"] = peaks
+        ar = rec["attention_roofline"]
+        t_hbm_m = ab / (peaks["read_stream_GBs"] * 1e9)
+        t_mm_m = af / (peaks["mfma_bf16_TFLOPs"] * 1e12) if dt_name == "bf16" else 0.0
+        ar["frac_of_max_measured_bound"] = max(t_hbm_m, t_mm_m) / att_s
     if commit_ms is not None:
         rec["kv_commit_rollback_us"] = commit_ms * 1e3
     if ms_graph is not None:

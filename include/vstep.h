@@ -389,6 +389,16 @@ int vs_kv_commit(const vs_kv_desc *desc, const void *k_cand, const void *v_cand,
                  int32_t *page_table, int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
                  int32_t *flags, void *workspace, size_t ws_bytes, void *stream);
 
+/* Token-major K/V into the pages above (data movement only).  k_src, v_src [n_tokens,
+ * Hkv, head_dim] of dtype are a cache in token order: a contiguous cache [P, Hkv, hd]
+ * (n_tokens = P), or token-major pages [n_pages, 16, Hkv, hd] (n_tokens = 16 n_pages;
+ * the same bytes).  Writes k_pool [ceil(n_tokens/16), Hkv, 16, hd] and v_pool
+ * [ceil(n_tokens/16), Hkv, hd, 16]; page p holds tokens 16p .. 16p+15 (positions past
+ * n_tokens are zero), so the identity page table (entry j = j) serves the contiguous
+ * cache.  k_pool/v_pool must not overlap the sources.  head_dim <= 256. */
+int vs_kv_pack_pages(const void *k_src, const void *v_src, int64_t n_tokens, int Hkv,
+                     int head_dim, int dtype, void *k_pool, void *v_pool, void *stream);
+
 /* Rollback: sequence b keeps its first new_len[b] tokens; the pages past
  * ceil(new_len[b]/16) are pushed onto the stack in ascending page order and their
  * page-table entries set to -1; prefix_len[b] = new_len[b].  Token data is not

@@ -23,7 +23,9 @@ def lib():
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    inc = os.path.dirname(HEADER)
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                  if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(vs_[a-z_]+)\s*\(", src)))
 
@@ -275,12 +277,26 @@ def test_draft_sample_validation(lib):
     assert lib.vs_draft_sample(fake, 7, 128256, fake, fake, None, fake, nb - 1, None) == -3
 
 
-def test_rho_tps_matches_the_oracle():
+def test_bench_rho_tps_matches_the_oracle():
+    import bench
     import oracle
+    for nu in (0.05, 0.19, 0.5, 1.0):
+        for k in (0.25, 1.0, 4.0):
+            assert bench.rho_tps(nu, 0.99, k) == oracle.rho_tps(nu, 0.99, k)
+
+
+def test_binding_computes_nothing():
+    """The binding only marshals: no arithmetic helper of the method lives in it."""
     from verification_step_amd import api
-    for nu in (0.0, 0.2, 0.5, 1.0):
-        for k in (0.0, 0.3, 1.0, 4.0):
-            assert api.rho_tps(nu, 0.99, k) == oracle.rho_tps(nu, 0.99, k)
+    assert not hasattr(api, "rho_tps")
+
+
+def test_kv_pack_validation(lib):
+    fake = C.c_void_p(16)
+    assert lib.vs_kv_pack_pages(None, fake, 100, 8, 128, 1, fake, fake, None) == -1
+    assert lib.vs_kv_pack_pages(fake, fake, 0, 8, 128, 1, fake, fake, None) == -1
+    assert lib.vs_kv_pack_pages(fake, fake, 100, 8, 128, 7, fake, fake, None) == -2
+    assert lib.vs_kv_pack_pages(fake, fake, 100, 8, 512, 1, fake, fake, None) == -2
 
 
 def test_binding_rejects_inconsistent_shapes(lib):

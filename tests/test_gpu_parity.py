@@ -925,6 +925,52 @@ def test_kv_commit_and_truncate_rounds(dtype, Hkv, hd):
     assert (fo == oracle.FLAG_BAD_PAGE).sum() == 1
 
 
+@pytest.mark.parametrize("dtype,P", [("bf16", 300), ("bf16", 4096), ("f32", 77)])
+def test_kv_pack_token_major(dtype, P):
+    """A contiguous token-major cache [P, Hkv, hd] packed into the verify step's pages
+    equals the same data rearranged on the host (bit for bit, zero tail), and verify
+    attention over it with the identity page table matches the oracle on that data."""
+    import torch
+    api = _api()
+    Hkv, hd = (8, 128) if dtype == "bf16" else (2, 64)
+    Hq = 4 * Hkv
+    rng = np.random.default_rng(31 + P)
+    if dtype == "bf16":
+        k_tm = wl.f32_to_bf16_bits(rng.standard_normal((P, Hkv, hd)).astype(np.float32))
+        v_tm = wl.f32_to_bf16_bits(rng.standard_normal((P, Hkv, hd)).astype(np.float32))
+    else:
+        k_tm = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
+        v_tm = rng.standard_normal((P, Hkv, hd)).astype(np.float32)
+    n_pages = (P + 15) // 16
+    pad = np.zeros((n_pages * 16 - P, Hkv, hd), dtype=k_tm.dtype)
+    kp = np.concatenate([k_tm, pad]).reshape(n_pages, 16, Hkv, hd)
+    vp = np.concatenate([v_tm, pad]).reshape(n_pages, 16, Hkv, hd)
+    k_ref = np.ascontiguousarray(kp.transpose(0, 2, 1, 3))     # [page, head, 16, hd]
+    v_ref = np.ascontiguousarray(vp.transpose(0, 2, 3, 1))     # [page, head, hd, 16]
+    bf = dtype == "bf16"
+    say("kv pack token-major", dtype, P)
+    gk, gv = api.kv_pack_pages(to_dev(k_tm, bf16=bf), to_dev(v_tm, bf16=bf))
+    torch.cuda.synchronize()
+    as_bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16) if bf else t.cpu().numpy()
+    assert np.array_equal(as_bits(gk), k_ref) and np.array_equal(as_bits(gv), v_ref)
+    # attention over the packed cache (identity page table) against the oracle
+    W, D = 2, 5
+    M = W * D
+    mk = (lambda sh_: wl.f32_to_bf16_bits(rng.standard_normal(sh_).astype(np.float32))) if bf else \
+        (lambda sh_: rng.standard_normal(sh_).astype(np.float32))
+    q, kc, vc = mk((M, Hq, hd)), mk((M, Hkv, hd)), mk((M, Hkv, hd))
+    pt = np.arange(n_pages, dtype=np.int32)[None, :]
+    pl = np.array([P], dtype=np.int32)
+    out, fl = api.verify_attention(to_dev(q, bf16=bf), to_dev(kc, bf16=bf), to_dev(vc, bf16=bf),
+                                   gk, gv, to_dev(pt), to_dev(pl), W, D)
+    f = lambda x: oracle.as_f64(x, dtype)
+    _, o_r, _ = oracle.verify_attention(f(q), f(kc), f(vc), f(k_ref), f(v_ref), pt, pl, 1, W, D,
+                                        Hq, Hkv, out_dtype=dtype)
+    err = rel_err(tensor_np(out), o_r)
+    print(f"rel_err={err:.3e}")
+    assert err <= (TOL if bf else 1e-5)
+
+
 def test_kv_bad_stack_count():
     """A free-stack count outside [0, n_pool_pages] is not read from: every request is
     refused, as in the oracle."""

@@ -32,9 +32,10 @@ EXPORTED = [
     "vs_lm_head", "vs_sample_workspace_bytes", "vs_reject_sample",
     "vs_step_workspace_bytes", "vs_verify_step", "vs_verify_step_noalloc",
     "vs_packed_weight_bytes", "vs_pack_weight",
-    "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate",
+    "vs_kv_workspace_bytes", "vs_kv_commit", "vs_kv_truncate", "vs_kv_pack_pages",
     "vs_copy_labels_workspace_bytes", "vs_copy_labels",
     "vs_draft_sample_workspace_bytes", "vs_draft_sample",
+    "vs_measure_read", "vs_measure_mfma",
 ]
 
 P = C.c_void_p
@@ -121,12 +122,15 @@ def load(path: str = LIB_PATH):
     lib.vs_kv_workspace_bytes.argtypes = [C.POINTER(KvDesc)]
     lib.vs_kv_commit.argtypes = [C.POINTER(KvDesc)] + [P] * 12 + [C.c_size_t, P]
     lib.vs_kv_truncate.argtypes = [C.POINTER(KvDesc)] + [P] * 7
+    lib.vs_kv_pack_pages.argtypes = [P, P, C.c_int64, C.c_int, C.c_int, C.c_int, P, P, P]
     lib.vs_copy_labels_workspace_bytes.restype = C.c_size_t
     lib.vs_copy_labels_workspace_bytes.argtypes = [C.c_int64]
     lib.vs_copy_labels.argtypes = [P, C.c_int64, P, C.c_int, C.c_int, P, P, P, C.c_size_t, P]
     lib.vs_draft_sample_workspace_bytes.restype = C.c_size_t
     lib.vs_draft_sample_workspace_bytes.argtypes = [C.c_int, C.c_int]
     lib.vs_draft_sample.argtypes = [P, C.c_int, C.c_int, P, P, P, P, C.c_size_t, P]
+    lib.vs_measure_read.argtypes = [P, C.c_size_t, P, C.c_int, P]
+    lib.vs_measure_mfma.argtypes = [C.c_int, C.c_int, P, P]
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):
             getattr(lib, fn).restype = C.c_int

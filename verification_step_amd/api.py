@@ -121,14 +121,6 @@ def copy_match(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int, W: int, D: 
     return out
 
 
-def rho_tps(nu: float, rho_tau: float, kappa: float) -> float:
-    """SlimSpec's acceptance-cost model ("SlimSpec: Low-Rank Draft LM-Head ...",
-    gist.science, "이론적 프레임워크"): the end-to-end speed-up of a draft head that
-    takes nu times the full head's time and keeps rho_tau of the acceptance length,
-    when the full head takes kappa times the rest of the drafting pipeline."""
-    return rho_tau * (1.0 + kappa) / (1.0 + nu * kappa)
-
-
 def draft_sample(q: torch.Tensor, u: torch.Tensor, tok=None, flags=None):
     """Draft tokens by inverse CDF of stored probability rows q [rows, V] (fp32) with
     uniforms u [rows] (fp64).  Returns (tok int32 [rows], flags int32 [rows]); tok and
@@ -149,6 +141,33 @@ def draft_sample(q: torch.Tensor, u: torch.Tensor, tok=None, flags=None):
                              ws.numel(), _stream())
     _raise(st, "draft_sample")
     return tok, flags
+
+
+def kv_pack_pages(k_src: torch.Tensor, v_src: torch.Tensor, k_pool=None, v_pool=None):
+    """Token-major K/V [n_tokens, Hkv, hd] (a contiguous cache, or token-major pages of
+    16 tokens flattened) into the verify step's pages: returns (k_pool [n_pages, Hkv, 16,
+    hd], v_pool [n_pages, Hkv, hd, 16]), n_pages = ceil(n_tokens / 16), positions past
+    n_tokens zero.  k_pool/v_pool may be given (bound buffers)."""
+    lib = L.load()
+    if k_src.dim() != 3 or v_src.shape != k_src.shape:
+        raise ValueError("k_src and v_src must both be [n_tokens, Hkv, hd]")
+    _check(k_src, k_src.dtype, "k_src")
+    _check(v_src, k_src.dtype, "v_src")
+    n, Hkv, hd = k_src.shape
+    n_pages = (n + 15) // 16
+    dev = k_src.device
+    if k_pool is None:
+        k_pool = torch.empty((n_pages, Hkv, 16, hd), dtype=k_src.dtype, device=dev)
+    if v_pool is None:
+        v_pool = torch.empty((n_pages, Hkv, hd, 16), dtype=k_src.dtype, device=dev)
+    _check(k_pool, k_src.dtype, "k_pool")
+    _check(v_pool, k_src.dtype, "v_pool")
+    _expect(k_pool, (n_pages, Hkv, 16, hd), "k_pool")
+    _expect(v_pool, (n_pages, Hkv, hd, 16), "v_pool")
+    st = lib.vs_kv_pack_pages(_ptr(k_src), _ptr(v_src), n, Hkv, hd, _vs_dtype(k_src),
+                              _ptr(k_pool), _ptr(v_pool), _stream())
+    _raise(st, "kv_pack_pages")
+    return k_pool, v_pool
 
 
 def copy_labels(ctx: torch.Tensor, ctx_off: torch.Tensor, kappa: int = 5, labels=None):

@@ -21,7 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libvstep.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["gate.hip", "attention.hip", "head.hip", "sampler.hip", "kv.hip", "labels.hip", "capi.hip"]
+SOURCES = ["gate.hip", "attention.hip", "head.hip", "sampler.hip", "kv.hip", "labels.hip", "peaks.hip",
+           "capi.hip"]
 # per-source flags: the attention scores are never NaN (masked keys are -inf), so its
 # max trees need no NaN canonicalisation (plain v_max3 instead of quieting each input)
 EXTRA = {"attention.hip": ["-fno-honor-nans"]}

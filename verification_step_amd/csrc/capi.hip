@@ -2,6 +2,7 @@
 // sizing and the verify-step orchestration.  See include/vstep.h for the contract.
 
 #include "../../include/vstep.h"
+#include "../../include/vstep_measure.h"
 #include "vs_internal.hpp"
 
 #include <math.h>
@@ -473,6 +474,26 @@ int vs_kv_commit(const vs_kv_desc *d, const void *k_cand, const void *v_cand, co
                                          v_cand, best, n_acc, k_pool, v_pool, page_table,
                                          prefix_len, free_list, n_free, flags, workspace,
                                          S(stream)));
+}
+
+int vs_measure_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg, void *stream) {
+  if (!buf || !sink || bytes < 16 || n_wg <= 0) return VS_ERR_INVALID_ARG;
+  return hip_status(vs::launch_peak_read(buf, bytes, sink, n_wg, S(stream)));
+}
+
+int vs_measure_mfma(int n_wg, int iters, float *sink, void *stream) {
+  if (!sink || n_wg <= 0 || iters <= 0) return VS_ERR_INVALID_ARG;
+  return hip_status(vs::launch_peak_mfma(n_wg, iters, sink, S(stream)));
+}
+
+int vs_kv_pack_pages(const void *k_src, const void *v_src, int64_t n_tokens, int Hkv,
+                     int head_dim, int dtype, void *k_pool, void *v_pool, void *stream) {
+  if (!k_src || !v_src || !k_pool || !v_pool) return VS_ERR_INVALID_ARG;
+  if (n_tokens <= 0 || Hkv <= 0 || head_dim <= 0) return VS_ERR_INVALID_ARG;
+  if (dtype != VS_BF16 && dtype != VS_F32) return VS_ERR_UNSUPPORTED;
+  if (head_dim > 256 || (n_tokens + 15) / 16 > INT32_MAX || Hkv > 65535) return VS_ERR_UNSUPPORTED;
+  return hip_status(vs::launch_kv_pack(k_src, v_src, n_tokens, Hkv, head_dim,
+                                       dtype == VS_BF16 ? 2 : 4, k_pool, v_pool, S(stream)));
 }
 
 int vs_kv_truncate(const vs_kv_desc *d, const int32_t *new_len, int32_t *page_table,

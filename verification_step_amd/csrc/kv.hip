@@ -276,4 +276,55 @@ hipError_t launch_kv_truncate(int B, int max_pages, int n_pool_pages, const int3
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Token-major K/V (the layout a cache written token by token has: [tokens][kv head][hd],
+// pages of 16 tokens one after another) into the pages the verify step reads: K
+// [page][kv head][16][hd] and V [page][kv head][hd][16].  One workgroup per (page, kv
+// head); V goes through LDS to be transposed.  Positions at or past n_tokens in the last
+// page are written as zero.
+namespace {
+template <typename T>
+__global__ void __launch_bounds__(kKT)
+kv_pack_kernel(const T *k_src, const T *v_src, int64_t n_tokens, int Hkv, int hd, T *k_pool,
+               T *v_pool) {
+  extern __shared__ unsigned char pack_lds[];
+  T *tile = reinterpret_cast<T *>(pack_lds);   // [16][hd]
+  const int64_t pg = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int n = kPg * hd;
+  T *kd = k_pool + (pg * Hkv + kvh) * (int64_t)n;
+  for (int i = tid; i < n; i += kKT) {
+    const int t = i / hd, e = i % hd;
+    const int64_t tok = pg * kPg + t;
+    const T kv = tok < n_tokens ? k_src[(tok * Hkv + kvh) * hd + e] : T(0);
+    kd[i] = kv;                                   // K keeps the token-major order of a page
+    tile[i] = tok < n_tokens ? v_src[(tok * Hkv + kvh) * hd + e] : T(0);
+  }
+  __syncthreads();
+  T *vd = v_pool + (pg * Hkv + kvh) * (int64_t)n;
+  for (int i = tid; i < n; i += kKT) {
+    const int e = i / kPg, t = i % kPg;
+    vd[i] = tile[t * hd + e];                     // V^T: the 16 tokens of one coordinate
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_pack(const void *k_src, const void *v_src, int64_t n_tokens, int Hkv, int hd,
+                          int esz, void *k_pool, void *v_pool, hipStream_t st) {
+  const int64_t n_pages = (n_tokens + kPg - 1) / kPg;
+  if (n_pages <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_pages, (unsigned)Hkv);
+  const size_t lds = (size_t)kPg * hd * esz;
+  if (esz == 2)
+    hipLaunchKernelGGL(kv_pack_kernel<uint16_t>, grid, dim3(kKT), lds, st, (const uint16_t *)k_src,
+                       (const uint16_t *)v_src, n_tokens, Hkv, hd, (uint16_t *)k_pool,
+                       (uint16_t *)v_pool);
+  else
+    hipLaunchKernelGGL(kv_pack_kernel<float>, grid, dim3(kKT), lds, st, (const float *)k_src,
+                       (const float *)v_src, n_tokens, Hkv, hd, (float *)k_pool, (float *)v_pool);
+  return hipGetLastError();
+}
+
 }  // namespace vs

@@ -206,6 +206,11 @@ hipError_t launch_copy_labels(const int32_t *ctx, int64_t total, const int32_t *
                               int kappa, uint8_t *labels, int32_t *flags, void *ws,
                               hipStream_t st);
 
+// ---- measured ceilings (peaks.hip)
+hipError_t launch_peak_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg,
+                            hipStream_t st);
+hipError_t launch_peak_mfma(int n_wg, int iters, float *sink, hipStream_t st);
+
 // ---- KV commit and rollback (kv.hip)
 constexpr int kMaxSeqKv = 2048;   // sequences per call
 size_t kv_workspace_bytes(int B);
@@ -214,6 +219,9 @@ hipError_t launch_kv_commit(int B, int W, int D, int Hkv, int hd, int max_pages,
                             const int32_t *n_acc, void *k_pool, void *v_pool, int32_t *page_table,
                             int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
                             int32_t *flags, void *ws, hipStream_t st);
+// token-major K/V [n_tokens][Hkv][hd] -> the verify step's pages (esz: 2 bf16, 4 fp32)
+hipError_t launch_kv_pack(const void *k_src, const void *v_src, int64_t n_tokens, int Hkv, int hd,
+                          int esz, void *k_pool, void *v_pool, hipStream_t st);
 hipError_t launch_kv_truncate(int B, int max_pages, int n_pool_pages, const int32_t *new_len,
                               int32_t *page_table, int32_t *prefix_len, int32_t *free_list,
                               int32_t *n_free, int32_t *flags, hipStream_t st);

@@ -100,8 +100,6 @@ def cpu_baseline(case, shape, min_seconds=10.0, accept="longest"):
     if not threads:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     A = case.arrays
-    if accept == "multi" and not shape.external_drafts:
-        A = {k: v for k, v in A.items() if k != "q_draft"}     # copy drafts: point masses
     sh = shape
     n = 0
     t0 = time.perf_counter()
@@ -375,7 +373,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--accept", choices=["longest", "multi", "greedy"], default="longest",
                     help="longest verified run (default), lossless multi-candidate "
-                         "acceptance (copy candidates as point-mass drafts) or greedy")
+                         "acceptance (over the workload's own drafts: dense q where it has "
+                         "one, point masses for copy drafts) or greedy")
     ap.add_argument("--commit", action="store_true",
                     help="after each step, commit the accepted rows to the paged KV cache and "
                          "roll back to the old lengths (times the decode loop's cache update)")
@@ -455,8 +454,6 @@ def main():
         free[:n_spare] = torch.arange(n0, n0 + n_spare, dtype=torch.int32, device=dev)
         kv = dict(free=free, n_free=torch.tensor([n_spare], dtype=torch.int32, device=dev),
                   P0=I["prefix_len"].clone(), n_pages=n0 + n_spare)
-    if args.accept == "multi" and not sh.external_drafts:
-        I["q_draft"] = None                      # copy candidates judged as point masses
     if args.accept == "greedy":
         for k in ("q_draft", "u_acc", "u_res"):  # argmax tests: nothing random is read
             I[k] = None

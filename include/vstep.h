@@ -203,15 +203,18 @@ int vs_lm_head(const vs_head_desc *desc, const void *h, const void *w_full,
  * root for a = 0, else row (b, ref, a-1), ref = the smallest surviving candidate
  * (all candidates with cand_len >= 1 survive at a = 0).  The survivors with
  * cand_len > a are tried in index order: with p' the current residual (initially p),
- * candidate i's token x is accepted iff u_acc[b,i,a] < p'(x); a rejection sets
- * p' <- normalise(max(0, p' - point mass on x)).  An accepted x is emitted and the
+ * candidate i's token x is accepted iff u_acc[b,i,a] * Q_i(x) < p'(x) with Q_i the
+ * draft row q[b, i, a] (the point mass on x when q == NULL); a rejection sets
+ * p' <- normalise(max(0, p' - Q_i)) over the whole vocabulary (a removal that would
+ * leave no mass is skipped and flagged DEGENERATE).  An accepted x is emitted and the
  * survivors become the tried candidates whose token at depth a is x.  If all are
  * rejected, one token is drawn from p' with u_res[b, last candidate tried]; if no
  * survivor has a token at depth a, a bonus token is drawn from p with
  * u_res[b, ref].  Outputs as above with best = the final reference candidate and
  * acc_per_cand[b,i] = the length of candidate i's common prefix with the accepted
- * tokens.  Copy drafts only (q == NULL) when W > 1 (else VS_ERR_UNSUPPORTED), at
- * most 64 candidates and (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); with
+ * tokens.  At most 64 candidates (else VS_ERR_UNSUPPORTED).  Copy drafts also need
+ * (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); dense drafts with W > 1 run
+ * one workgroup per sequence over fp64 residual rows kept in the workspace.  With
  * W == 1 the rule is the single-chain rule above, which is what runs.
  *
  * accept_mode VS_ACCEPT_GREEDY: greedy verification, the temperature -> 0 limit of

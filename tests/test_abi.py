@@ -140,17 +140,22 @@ def test_sample_validation(lib):
     bad = list(args)
     bad[0] = None
     assert lib.vs_reject_sample(C.byref(d), *bad, None, 0, None) == -1
-    # accept modes: unknown (3) -> invalid; multi with dense drafts (q given) and W > 1, more
-    # than 64 candidates, or too many p values for LDS -> unsupported; multi with W == 1
-    # takes dense drafts (single-chain rule) and gets as far as the workspace check
+    # accept modes: unknown (3) -> invalid; multi with more than 64 candidates, or copy
+    # drafts (q NULL) with too many p values for LDS -> unsupported; multi with dense
+    # drafts (any W) gets as far as the workspace check, whose size holds two fp64
+    # residual rows per sequence
     def samp(W, D, mode, q=fake):
         a = list(args)
         a[3] = q
         return lib.vs_reject_sample(C.byref(L.SampleDesc(2, W, D, 1000, 1.0, mode)), *a, None,
                                     0, None)
     assert samp(4, 20, 3) == -1
-    assert samp(4, 20, L.VS_ACCEPT_MULTI) == -2
+    assert samp(4, 20, L.VS_ACCEPT_MULTI) == -3
+    assert samp(65, 1, L.VS_ACCEPT_MULTI) == -2
+    assert samp(16, 40, L.VS_ACCEPT_MULTI) == -3             # dense: no LDS bound on W*D
     assert samp(4, 20, L.VS_ACCEPT_MULTI, q=None) == -3
+    assert (lib.vs_sample_workspace_bytes(C.byref(L.SampleDesc(2, 4, 20, 1000, 1.0, 1)))
+            >= 2 * 2 * 1000 * 8)
     assert samp(65, 1, L.VS_ACCEPT_MULTI, q=None) == -2
     assert samp(16, 40, L.VS_ACCEPT_MULTI, q=None) == -2     # (640+1)*16 + 640 > 4096
     assert samp(8, 20, L.VS_ACCEPT_MULTI, q=None) == -3      # (160+1)*8 + 160 fits
@@ -196,10 +201,11 @@ def test_step_validation(lib):
     assert lib.vs_verify_step(C.byref(d2), C.byref(io), fake, 1 << 40, None) == -1
     d3 = L.StepDesc(**{**base, "kappa": 20})
     assert lib.vs_verify_step(C.byref(d3), C.byref(io), fake, 1 << 40, None) == -2
-    # multi-candidate acceptance takes copy drafts only: q_draft must be null
+    # multi-candidate acceptance takes dense drafts (q_draft given) and copy drafts alike;
+    # both get as far as the workspace check
     d4 = L.StepDesc(**{**base, "accept_mode": L.VS_ACCEPT_MULTI})
     assert lib.vs_step_workspace_bytes(C.byref(d4)) > 0
-    assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 1 << 40, None) == -2
+    assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 16, None) == -3
     io.q_draft = None
     assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 16, None) == -3
     d5 = L.StepDesc(**{**base, "accept_mode": 7})

@@ -550,6 +550,41 @@ def test_reject_sample_multi(B, W, D, V, T):
     assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
 
 
+@pytest.mark.parametrize("B,W,D,V,T", [(48, 4, 6, 1000, 1.0), (16, 8, 20, 3000, 0.8),
+                                       (6, 2, 5, 128256, 1.0)])
+def test_reject_sample_multi_dense(B, W, D, V, T):
+    """Lossless multi-candidate acceptance with dense draft distributions (each
+    rejection removes the sibling's whole q row from the residual) against the
+    oracle's rule, up to the full vocabulary."""
+    api = _api()
+    rng = np.random.default_rng(53 + W + V)
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    clen[0] = 0
+    M = W * D
+    # draft distributions favouring the same hot tokens, less sharply than the target
+    ql = rng.standard_normal((B * M, V))
+    ql[:, 1:3] += 6.0
+    ql -= ql.max(axis=1, keepdims=True)
+    q = np.exp(ql)
+    q = (q / q.sum(axis=1, keepdims=True)).astype(np.float32)
+    lse = scipy.special.logsumexp(logits.astype(np.float64) / T, axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    gate = np.ones(B, dtype=np.int32)
+    gate[1] = 0
+    say("reject_sample multi dense", B, W, D, V, T)
+    g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), to_dev(q), to_dev(cand),
+                          to_dev(clen), to_dev(ua), to_dev(ur), T, to_dev(gate), accept="multi")
+    o = oracle.reject_sample_multi(root, logits, q, cand, clen, ua, ur, T, gate)
+    n_cmp, n_exc = compare_sampler(g, o, B)
+    print(f"compared {n_cmp}/{B}, excluded {n_exc}; n_acc {o['n_acc'].tolist()[:12]}")
+    assert n_exc <= max(1, B // 16) and n_cmp >= B - max(1, B // 16)
+    # chains that accepted tokens, and chains that ended on a rejection
+    ln = clen.max(axis=1)
+    assert (o["n_acc"][2:] >= 1).any() and (o["n_acc"][2:] < ln[2:]).any()
+    assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
+
+
 @pytest.mark.parametrize("mode", ["0", "1"])
 def test_reject_sample_multi_launch_modes(mode, monkeypatch):
     """Multi-candidate acceptance through both ways to reach the draw, with more
@@ -1134,6 +1169,27 @@ def test_verify_step_multi(name):
     o = oracle.verify_step(A, sh, accept="multi")
     n_cmp, n_exc = _check_step(case, g, o)
     _assert_compared(f"step multi {name}", sh.B, n_cmp, n_exc, gpu=g)
+
+
+@pytest.mark.parametrize("name", ["small", "llama8b"])
+def test_verify_step_multi_dense(name):
+    """The whole step with multi-candidate acceptance over the workload's own dense
+    draft distributions (N(0, 2^2) draft logits at V = 128,256 for the Llama-8B shape)."""
+    api = _api()
+    if name == "small":
+        sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
+    else:
+        sh, seed = wl.config(2), 2000
+    case = get_case(("step", name), lambda: wl.make_case(sh, seed))
+    I = _step_inputs(case, sh.temperature)
+    say("verify_step multi dense", name)
+    step = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa,
+                          accept="multi")
+    g = step()
+    o = oracle.verify_step(case.arrays, sh, accept="multi")
+    n_cmp, n_exc = _check_step(case, g, o)
+    _assert_compared(f"step multi dense {name}", sh.B, n_cmp, n_exc, o["sample"], g)
 
 
 @pytest.mark.parametrize("name", ["small", "llama8b", "ragged"])

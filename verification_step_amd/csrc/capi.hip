@@ -62,8 +62,7 @@ int check_sample(const vs_sample_desc *d) {
   if (d->accept_mode != VS_ACCEPT_LONGEST && d->accept_mode != VS_ACCEPT_MULTI &&
       d->accept_mode != VS_ACCEPT_GREEDY)
     return VS_ERR_INVALID_ARG;
-  if (d->accept_mode == VS_ACCEPT_MULTI && d->W > 1 && !vs::sampler_multi_fits(d->W, d->D))
-    return VS_ERR_UNSUPPORTED;
+  if (d->accept_mode == VS_ACCEPT_MULTI && d->W > 64) return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 
@@ -248,7 +247,8 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
   if (!root_logits || !logits || !row_lse || !cand_tok || !cand_len ||
       (!greedy && (!u_acc || !u_res)) || !n_acc || !best || !out_tok || !n_out || !acc_per_cand)
     return VS_ERR_INVALID_ARG;
-  if (rule == 1 && q) return VS_ERR_UNSUPPORTED;
+  // copy drafts (point masses) walk the chain in LDS, within its bound
+  if (rule == 1 && !q && !vs::sampler_multi_fits(d->W, d->D)) return VS_ERR_UNSUPPORTED;
   const size_t need = vs_sample_workspace_bytes(d);
   if (!workspace || ws_bytes < need) return VS_ERR_WORKSPACE;
   const vs::SampleWs sw = vs::sample_ws(workspace, d->B, d->W, d->D, d->V, greedy);
@@ -314,7 +314,7 @@ static int verify_step_impl(const vs_step_desc *d, const vs_step_io *io, void *w
       return VS_ERR_INVALID_ARG;
   }
   if (io->aux_stream && (!io->fork_event || !io->join_event)) return VS_ERR_INVALID_ARG;
-  if (rule == 1 && io->q_draft) return VS_ERR_UNSUPPORTED;
+  if (rule == 1 && !io->q_draft && !vs::sampler_multi_fits(d->W, d->D)) return VS_ERR_UNSUPPORTED;
   const StepLayout L = step_layout(d);
   if (!workspace || ws_bytes < L.total) return VS_ERR_WORKSPACE;
   hipStream_t s = S(stream);

@@ -1024,6 +1024,10 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats) {
   off += ((size_t)B * (W * D + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   w.amax_tie = (uint8_t *)(p + off);
   off += ((size_t)B * (W * D + 1) + 255) & ~(size_t)255;
+  // lossless multi-candidate acceptance with dense drafts: two fp64 residual rows per
+  // sequence
+  w.resid = (double *)(p + off);
+  off += ((size_t)B * 2 * V * sizeof(double) + 255) & ~(size_t)255;
   w.row_stats = nullptr;
   if (row_stats) {
     w.row_stats = (float2 *)(p + off);
@@ -1070,6 +1074,331 @@ hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *l
   a.row_lse = lse;
   hipLaunchKernelGGL(lse_tests_kernel, dim3(rows), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Lossless multi-candidate acceptance with dense drafts (accept mode MULTI, q given).
+// The single-draft rule and its residual (rejection-sampling blog, section 3) applied
+// across the sibling candidates at each depth: with the current residual p' (the
+// target p of the reference row at first), sibling i is kept iff u * Q_i(x_i) <
+// p'(x_i) / sum p', and a rejection sets p' <- max(0, p' / sum p' - Q_i) over the whole
+// vocabulary.  Every step needs the residual's total, so the chain runs in one
+// workgroup of kDT threads per sequence: the residual lives in the workspace (two fp64
+// rows per sequence, written alternately), and each pass over the vocabulary goes in
+// chunks of kDT * 8 consecutive ids (thread t: ids 8t .. 8t+7 of the chunk), summed in
+// a fixed order.  The draw is the inverse CDF over ascending ids, as everywhere.
+constexpr int kDT = 1024;
+constexpr int kDPer = 8;
+constexpr int kDChunk = kDT * kDPer;
+constexpr int kMaxDChunks = 64;            // V <= 524,288
+
+struct DenseShared {
+  double red[kDT / 64];
+  double csum[kMaxDChunks];
+  int lens[kMaxWMulti];
+  double ures[kMaxWMulti];
+  int tok[kMaxRows];
+  double uacc[kMaxRows];
+  double rlse[kMaxRows];
+  int acc[kMaxRows];
+  int surv[kMaxWMulti], sib[kMaxWMulti];
+  int flags, owner, tstar, y;
+  double excl;
+};
+
+struct DenseArgs {
+  int B, W, D, V;
+  double inv_t;
+  const float *root_logits, *logits, *q;
+  const double *row_lse, *root_lse;
+  const int32_t *cand_tok, *cand_len, *gate;
+  const double *u_acc, *u_res;
+  double *resid;          // [B][2][V]
+  int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
+  int flags_accumulate;
+  int32_t *attn_flags;
+};
+
+// fixed-order block sum over kDT threads (every thread receives the total)
+__device__ double dense_sum(DenseShared &sh, double v) {
+  const int tid = threadIdx.x;
+  v = warp_sum(v);
+  if ((tid & 63) == 0) sh.red[tid >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kDT / 64; ++w) t += sh.red[w];
+  __syncthreads();
+  return t;
+}
+
+__device__ double dense_incl_scan(DenseShared &sh, double v) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) sh.red[wv] = v;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wv; ++w) base += sh.red[w];
+  __syncthreads();
+  return base + v;
+}
+
+__global__ void __launch_bounds__(kDT)
+multi_dense_kernel(DenseArgs a) {
+  __shared__ DenseShared sh;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int W = a.W, D = a.D, V = a.V, M = W * D;
+  const int nch = (V + kDChunk - 1) / kDChunk;
+  const bool open = (a.gate == nullptr) || a.gate[b] != 0;
+  for (int i = tid; i < W; i += kDT) {
+    int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
+    sh.lens[i] = ln < 0 ? 0 : (ln > D ? D : ln);
+    sh.ures[i] = a.u_res[(int64_t)b * W + i];
+  }
+  for (int k = tid; k < M; k += kDT) {
+    sh.tok[k] = a.cand_tok[(int64_t)b * M + k];
+    sh.uacc[k] = a.u_acc[(int64_t)b * M + k];
+    sh.rlse[k] = a.row_lse[(int64_t)b * M + k];
+  }
+  if (tid == 0) sh.flags = 0;
+  __syncthreads();
+  double *rbuf[2] = {a.resid + (int64_t)b * 2 * V, a.resid + ((int64_t)b * 2 + 1) * V};
+
+  // the distribution a pass reads: p of row prow (kind 0), or the residual in rbuf[cur]
+  // (kind 1); lse of that row
+  const float *zrow = nullptr;
+  double lse = 0.0;
+  int kind = 0, cur = 0;
+  auto weight = [&](int k) -> double {
+    if (k >= V) return 0.0;
+    if (kind == 0) return exp((double)zrow[k] * a.inv_t - lse);
+    return rbuf[cur][k];
+  };
+  // total of the current distribution over the vocabulary (fixed order)
+  auto total = [&]() -> double {
+    double t = 0.0;
+    for (int c = 0; c < nch; ++c) {
+      double v = 0.0;
+      const int k0 = c * kDChunk + tid * kDPer;
+#pragma unroll
+      for (int j = 0; j < kDPer; ++j) v += weight(k0 + j);
+      t += dense_sum(sh, v);
+    }
+    return t;
+  };
+  auto set_row = [&](int prow) {
+    kind = 0;
+    zrow = prow < 0 ? a.root_logits + (int64_t)b * V : a.logits + ((int64_t)b * M + prow) * V;
+    lse = prow < 0 ? a.root_lse[b] : sh.rlse[prow];
+  };
+  // inverse-CDF draw from the current distribution with uniform u (ties flagged)
+  auto draw = [&](double u) -> int {
+    for (int c = 0; c < nch; ++c) {
+      double v = 0.0;
+      const int k0 = c * kDChunk + tid * kDPer;
+#pragma unroll
+      for (int j = 0; j < kDPer; ++j) v += weight(k0 + j);
+      v = dense_sum(sh, v);
+      if (tid == 0) sh.csum[c] = v;
+    }
+    __syncthreads();
+    double S = 0.0;
+    for (int c = 0; c < nch; ++c) S += sh.csum[c];
+    const double xs = u * S;
+    if (tid == 0) {
+      // the chunk holding u*S (the last chunk with weight if rounding leaves u*S past)
+      double run = 0.0;
+      int own = -1, last = nch - 1;
+      for (int c = 0; c < nch; ++c) {
+        if (sh.csum[c] > 0.0) last = c;
+        if (own < 0 && sh.csum[c] > 0.0 && run + sh.csum[c] > xs) own = c;
+        if (own < 0) run += sh.csum[c];
+      }
+      if (own < 0) {
+        own = last;
+        run = 0.0;
+        for (int c = 0; c < last; ++c) run += sh.csum[c];
+      }
+      sh.owner = own;
+      sh.excl = run;
+      sh.tstar = INT_MAX;
+    }
+    __syncthreads();
+    const int k0 = sh.owner * kDChunk + tid * kDPer;
+    double w[kDPer], tv = 0.0;
+#pragma unroll
+    for (int j = 0; j < kDPer; ++j) {
+      w[j] = weight(k0 + j);
+      tv += w[j];
+    }
+    const double incl = dense_incl_scan(sh, tv);
+    const double texcl = sh.excl + (incl - tv);
+    if (tv > 0.0 && sh.excl + incl > xs) atomicMin(&sh.tstar, tid);
+    __syncthreads();
+    if (tid == sh.tstar || (sh.tstar == INT_MAX && tid == 0)) {
+      int yy = -1, last_w = -1;
+      double run = texcl, lo = 0.0, hi = 0.0;
+      if (sh.tstar != INT_MAX) {
+        for (int j = 0; j < kDPer; ++j) {
+          if (w[j] <= 0.0) continue;
+          last_w = k0 + j;
+          if (run + w[j] > xs) {
+            yy = k0 + j;
+            lo = run;
+            hi = run + w[j];
+            break;
+          }
+          run += w[j];
+        }
+        if (yy < 0) {
+          yy = last_w;
+          lo = run;
+          hi = run;
+        }
+      } else {
+        yy = V - 1;
+        lo = hi = S;
+      }
+      if (fmin(fabs(xs - lo), fabs(hi - xs)) < 1e-8 * S) atomicOr(&sh.flags, FLAG_CDF_TIE);
+      sh.y = yy;
+    }
+    __syncthreads();
+    return sh.y;
+  };
+
+  if (tid == 0) {
+    int n = 0;
+    for (int i = 0; i < W; ++i)
+      if (sh.lens[i] >= 1) sh.surv[n++] = i;
+  }
+  __syncthreads();
+  int ns = 0;   // survivors (every thread keeps the same count)
+  for (int i = 0; i < W; ++i) ns += sh.lens[i] >= 1;
+  int depth = 0, y = -1, best = -1;
+  if (ns == 0) {
+    set_row(-1);
+    y = draw(sh.ures[0]);
+    if (tid == 0) atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
+  } else {
+    while (true) {
+      const int ref = sh.surv[0];
+      set_row(depth == 0 ? -1 : ref * D + depth - 1);
+      int nsib = 0;
+      for (int k = 0; k < ns; ++k)
+        if (sh.lens[sh.surv[k]] > depth) {
+          if (tid == 0) sh.sib[nsib] = sh.surv[k];
+          ++nsib;
+        }
+      __syncthreads();
+      if (nsib == 0) {
+        y = draw(sh.ures[ref]);
+        break;
+      }
+      // a target row sums to one up to the rounding of its lse, which moves p' by about
+      // 1e-7 relative: close enough for the acceptance tests, whose tie band is 1e-4;
+      // its exact total is taken only before the first rejection builds a residual
+      double S = 1.0;
+      bool exact = false;
+      int accepted = -1, last = sh.sib[0];
+      for (int k = 0; k < nsib; ++k) {
+        const int i = sh.sib[k];
+        last = i;
+        const int x = sh.tok[i * D + depth];
+        const float *qrow = a.q + ((int64_t)b * M + i * D + depth) * V;
+        const bool valid = x >= 0 && x < V;
+        const double pp = valid ? weight(x) / S : 0.0;
+        const double Qx = valid ? (double)qrow[x] : 1.0;
+        const double lhs = sh.uacc[i * D + depth] * Qx;
+        if (tid == 0) {
+          int f = 0;
+          if (!valid) f |= FLAG_BAD_TOKEN;
+          if (fabs(lhs - pp) < 1e-4 * fmax(pp, lhs)) f |= FLAG_ACCEPT_TIE;
+          if (f) atomicOr(&sh.flags, f);
+        }
+        if (lhs < pp) {
+          accepted = x;
+          break;
+        }
+        // rejected: p' <- max(0, p' / S - Q_i) into the residual row not being read
+        if (!exact) {
+          S = total();
+          exact = true;
+        }
+        const int nxt = (kind == 1) ? (cur ^ 1) : 0;
+        double *dst = rbuf[nxt];
+        double part = 0.0;
+        for (int c = 0; c < nch; ++c) {
+          const int k0 = c * kDChunk + tid * kDPer;
+          double v = 0.0;
+          if (k0 < V) {
+#pragma unroll
+            for (int j = 0; j < kDPer; ++j) {
+              const int kk = k0 + j;
+              if (kk < V) {
+                const double r = fmax(0.0, weight(kk) / S - (double)qrow[kk]);
+                dst[kk] = r;
+                v += r;
+              }
+            }
+          }
+          part += dense_sum(sh, v);
+        }
+        if (part > 0.0) {
+          cur = nxt;
+          kind = 1;
+          S = part;   // exact: summed in the same pass that wrote the row
+        } else if (tid == 0) {
+          atomicOr(&sh.flags, FLAG_DEGENERATE);   // no mass left: p' is kept
+        }
+        __syncthreads();   // the new residual row is complete before it is read
+      }
+      if (accepted < 0) {
+        y = draw(sh.ures[last]);
+        break;
+      }
+      if (tid == 0) {
+        sh.acc[depth] = accepted;
+        int n2 = 0;
+        for (int k = 0; k < nsib; ++k)
+          if (sh.tok[sh.sib[k] * D + depth] == accepted) sh.surv[n2++] = sh.sib[k];
+      }
+      __syncthreads();
+      int n2 = 0;
+      for (int k = 0; k < nsib; ++k) n2 += sh.tok[sh.sib[k] * D + depth] == accepted;
+      ns = n2;
+      ++depth;
+    }
+    best = sh.surv[0];
+  }
+  // ---- outputs
+  int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
+  for (int o = tid; o <= D; o += kDT) ot[o] = (o < depth) ? sh.acc[o] : (o == depth ? y : -1);
+  for (int i = tid; i < W; i += kDT) {
+    int k = 0;
+    const int lim = min(sh.lens[i], depth);
+    while (k < lim && sh.tok[i * D + k] == sh.acc[k]) ++k;
+    a.acc_per_cand[(int64_t)b * W + i] = k;
+  }
+  if (tid == 0) {
+    a.n_acc[b] = depth;
+    a.best[b] = best;
+    a.n_out[b] = depth + 1;
+    int f = sh.flags;
+    if (a.attn_flags) {
+      f |= a.attn_flags[b];
+      a.attn_flags[b] = 0;
+    }
+    if (a.flags) {
+      if (a.flags_accumulate) atomicOr(&a.flags[b], f);
+      else a.flags[b] = f;
+    }
+  }
 }
 
 hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
@@ -1156,6 +1485,37 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
   if (rule == 2) {
     // greedy: no vocabulary sweep, one workgroup per sequence
     hipLaunchKernelGGL((sampler_kernel<SAMP_DRAW, RULE_GREEDY>), dim3(1, B), dim3(kST), 0, st, a);
+    return hipGetLastError();
+  }
+  if (multi && q != nullptr) {
+    // dense drafts: the residual chain over the whole vocabulary, one workgroup per
+    // sequence
+    DenseArgs d{};
+    d.B = B;
+    d.W = W;
+    d.D = D;
+    d.V = V;
+    d.inv_t = a.inv_t;
+    d.root_logits = root_logits;
+    d.logits = logits;
+    d.q = q;
+    d.row_lse = row_lse;
+    d.root_lse = ws.root_lse;
+    d.cand_tok = cand_tok;
+    d.cand_len = cand_len;
+    d.gate = gate;
+    d.u_acc = u_acc;
+    d.u_res = u_res;
+    d.resid = ws.resid;
+    d.n_acc = n_acc;
+    d.best = best;
+    d.out_tok = out_tok;
+    d.n_out = n_out;
+    d.acc_per_cand = acc_per_cand;
+    d.flags = flags;
+    d.flags_accumulate = flags_accumulate;
+    d.attn_flags = attn_flags;
+    hipLaunchKernelGGL(multi_dense_kernel, dim3(B), dim3(kDT), 0, st, d);
     return hipGetLastError();
   }
   if (multi) {

@@ -156,6 +156,7 @@ struct SampleWs {
   double *pv;           // [B][W*D+1][W] multi-candidate acceptance: p of each candidate token
   int32_t *amax;        // [B*W*D + B] greedy: argmax of every verify row, then the root rows
   uint8_t *amax_tie;    // [B*W*D + B] greedy: near tie between the two largest logits
+  double *resid;        // [B][2][V] multi-candidate acceptance with dense drafts: residual rows
   float2 *row_stats;    // [B*W*D][n_vt] tile statistics of given logits (greedy, standalone)
   size_t bytes;
 };

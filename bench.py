@@ -369,6 +369,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=list(WORKLOADS), default="llama8b")
     ap.add_argument("--kv-buffers", type=int, default=0, help="0: the workload's default")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="attention layers per step, in one launch over one shared block "
+                         "table (per-layer synthetic q, candidate K/V and pools; the head "
+                         "reads the last layer)")
     ap.add_argument("--head-copies", type=int, default=0, help="0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--accept", choices=["longest", "multi", "greedy"], default="longest",
@@ -457,6 +461,20 @@ def main():
     if args.accept == "greedy":
         for k in ("q_draft", "u_acc", "u_res"):  # argmax tests: nothing random is read
             I[k] = None
+    n_layers = max(1, args.layers)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    if n_layers > 1:
+        # layer 0 is the seeded case; the other layers are N(0, 1) tensors made on the
+        # device; every layer reads its own pools through the one page table.  The KV of
+        # a step is then n_layers one-layer caches: two such sets alternate between
+        # steps (more for few layers), so the KV read per step is never the last step's
+        n_kv = args.kv_buffers or max(2, 32 // n_layers)
+        for k in ("q", "k_cand", "v_cand", "k_pool", "v_pool"):
+            t = I[k]
+            rest = torch.randn((n_layers - 1,) + tuple(t.shape), generator=g, device=dev)
+            I[k] = torch.cat([t.unsqueeze(0), rest.to(t.dtype)]).contiguous()
+            del rest
     step = api.VerifyStep(I, B=B, W=W, D=D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V, tau=sh.tau,
                           temperature=sh.temperature, kappa=sh.kappa,
                           external_drafts=sh.external_drafts, accept=args.accept)
@@ -464,8 +482,6 @@ def main():
     esz = I["q"].element_size()
 
     # distinct KV buffers (layers) and head copies; buffer 0 / copy 0 are the seeded inputs
-    g = torch.Generator(device=dev)
-    g.manual_seed(1234)
     pools = [(I["k_pool"], I["v_pool"])]
     for _ in range(n_kv - 1):
         pools.append((torch.randn(I["k_pool"].shape, generator=g, device=dev).to(mdt),
@@ -605,15 +621,15 @@ def main():
                  "algorithmic_bytes": hb, "algorithmic_flops": hf,
                  "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mm * 1e6})
     sum_p = int(sum(sh.P))
-    ab = attn_bytes(B, M, sh.Hq, sh.Hkv, sh.hd, sum_p, esz)
-    af = attn_flops(B, W, D, sh.Hq, sh.hd, sum_p)
+    ab = attn_bytes(B, M, sh.Hq, sh.Hkv, sh.hd, sum_p, esz) * n_layers
+    af = attn_flops(B, W, D, sh.Hq, sh.hd, sum_p) * n_layers
     att_s = stage_ms["attention"] * 1e-3
     out = step.out
     config = {"workload": WORKLOAD_NAMES[args.workload], "B": B, "W": W, "D": D,
               "prefix": sh.P[0] if B == 1 else {"sum": sum_p, "min": min(sh.P),
                                                 "max": max(sh.P)},
               "d": sh.d, "Hq": sh.Hq, "Hkv": sh.Hkv, "head_dim": sh.hd, "V": sh.V,
-              "kv_buffers": len(pools), "head_copies": len(heads),
+              "kv_buffers": len(pools), "head_copies": len(heads), "layers": n_layers,
               "timing": "hip events on the step stream, no graph; value from a pass "
                         "without stage events, stages from a second pass with them"}
     if args.accept != "longest":
@@ -662,7 +678,8 @@ def main():
         rec["ms_per_step_graph_replay"] = ms_graph
     if draft is not None:
         rec["slimspec_tradeoff"] = draft_head_tradeoff(api, sh, case, step, dev, K, Wm)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and n_layers == 1:
+        # (the oracle's step is one layer: no CPU figure for a layered step)
         rec["cpu_baseline"] = cpu_baseline(case, sh, accept=args.accept)
     print(json.dumps(rec), flush=True)
 

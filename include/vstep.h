@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VS_ABI_VERSION 3
+#define VS_ABI_VERSION 4
 
 typedef enum {
     VS_OK = 0,
@@ -130,11 +130,18 @@ int vs_probe_gate(const void *h, int h_dtype, const float *w, int B, int d, floa
  *   flags         int32 [B] out or NULL (VS_FLAG_BAD_PAGE: keys of a bad page are skipped)
  * Supported: VS_BF16 with head_dim 128 (MFMA path); VS_F32 with head_dim 16, 32 or 64.
  * page_size must be 16; max_pages > 0 requires n_pool_pages >= 1.  scale <= 0 selects
- * 1/sqrt(head_dim).  Accumulation in fp32. */
+ * 1/sqrt(head_dim).  Accumulation in fp32.
+ * Layers [SD section 6: one paged cache per layer, the same block table for all]:
+ * n_layers = L >= 1 (0 reads as 1) runs L independent layers in one launch.  q,
+ * k_cand, v_cand, k_pool, v_pool and out are then L copies of the shapes above,
+ * stacked (layer l at l times the one-layer size); page_table and prefix_len are
+ * shared (a page id names the same slot in every layer's pool); flags are as for one
+ * layer.  L <= 1024 and at most 2^30 workgroups (VS_ERR_UNSUPPORTED beyond). */
 typedef struct {
     int32_t B, W, D, Hq, Hkv, head_dim, page_size, max_pages, n_pool_pages;
     int32_t dtype;          /* vs_dtype */
     float scale;
+    int32_t n_layers;       /* 0 or 1: one layer */
 } vs_attn_desc;
 
 size_t vs_attention_workspace_bytes(const vs_attn_desc *desc);
@@ -281,6 +288,9 @@ typedef struct {
     int64_t ctx_total;
     int32_t accept_mode;      /* vs_accept_mode of the sampler (same limits as vs_reject_sample;
                                  greedy: u_acc, u_res and q_draft are not read) */
+    int32_t n_layers;         /* attention layers (0 or 1: one): q, k_cand, v_cand, the
+                                 pools and attn_out stacked as for vs_verify_attention;
+                                 the head reads the last layer's output */
 } vs_step_desc;
 
 typedef struct {
@@ -302,7 +312,7 @@ typedef struct {
     int32_t *cand_pos, *n_found;            /* may be NULL when external_drafts */
     float *score; int32_t *gate;            /* may be NULL when external_drafts */
     /* stage outputs */
-    void *attn_out;                         /* [B*W*D, Hq, hd] dtype */
+    void *attn_out;                         /* [n_layers][B*W*D, Hq, hd] dtype */
     float *logits;                          /* [B*W*D, V] */
     double *row_lse;                        /* [B*W*D] */
     int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand;
@@ -375,6 +385,7 @@ int vs_copy_labels(const int32_t *ctx, int64_t ctx_total, const int32_t *ctx_off
 typedef struct {
     int32_t B, W, D, Hkv, head_dim, page_size, max_pages, n_pool_pages;
     int32_t dtype;            /* vs_dtype of k_cand/v_cand and the pools (element copy) */
+    int32_t n_layers;         /* commit: layers (0 or 1: one; stacked as for attention) */
 } vs_kv_desc;
 
 size_t vs_kv_workspace_bytes(const vs_kv_desc *desc);
@@ -383,6 +394,9 @@ size_t vs_kv_workspace_bytes(const vs_kv_desc *desc);
  * rows (b, best[b], 0 .. a-1) of k_cand/v_cand ([B*W*D, Hkv, head_dim], the verify
  * step's candidate layout) become tokens P .. P+a-1, P = prefix_len[b]; the pages it
  * needs beyond ceil(P/16) are popped off the stack; prefix_len[b] becomes P + a.
+ * With n_layers = L > 1, k_cand/v_cand and the pools are L stacked layers (as for
+ * vs_verify_attention) and the same rows of every layer go to the same page slots:
+ * the pages are taken once, for all layers (L <= 65535).
  * Refused with VS_FLAG_BAD_PAGE when P < 0 or P + a > 16*max_pages or when its
  * partly filled last page or a page it would pop is not in [0, n_pool_pages); with
  * VS_FLAG_POOL_EMPTY when the stack holds fewer pages than it needs (later
@@ -408,7 +422,8 @@ int vs_kv_pack_pages(const void *k_src, const void *v_src, int64_t n_tokens, int
  * touched.  Refused with VS_FLAG_BAD_PAGE when new_len[b] is outside
  * [0, prefix_len[b]], prefix_len[b] is out of range, a page to free is not a pool
  * page, or the stack would overflow.  Only B, page_size, max_pages and n_pool_pages
- * of the descriptor are read. */
+ * of the descriptor are read: the page table is shared by all layers, so one call
+ * rolls back every layer's cache. */
 int vs_kv_truncate(const vs_kv_desc *desc, const int32_t *new_len, int32_t *page_table,
                    int32_t *prefix_len, int32_t *free_list, int32_t *n_free, int32_t *flags,
                    void *stream);

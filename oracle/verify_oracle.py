@@ -269,6 +269,26 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len,
     return O, round_stage(O, out_dtype), flags
 
 
+def verify_attention_layers(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len,
+                            B, W, D, Hq, Hkv, scale=None, page=16, out_dtype="bf16"):
+    """The verify attention of L layers of one model [SW, "무엇과 다른가"; SD6: a paged
+    cache per layer].  Reading: every layer keeps its own cache in pages, and the
+    block table -- which page holds which 16 positions of a sequence, and how long the
+    sequence is -- is the same for all layers, since every layer stores the same
+    positions.  So layer l is verify_attention on that layer's queries, candidate
+    keys/values and pools (each array here has a leading layer axis) with the common
+    page_table and prefix_len.  Returns (O exact [L, ...], O rounded, flags [B]: the
+    OR over layers, which all see the same table)."""
+    L = q.shape[0]
+    res = [verify_attention(q[l], k_cand[l], v_cand[l], k_pool[l], v_pool[l], page_table,
+                            prefix_len, B, W, D, Hq, Hkv, scale, page, out_dtype)
+           for l in range(L)]
+    flags = np.zeros(B, dtype=np.int32)
+    for r in res:
+        flags |= r[2]
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res]), flags
+
+
 # ----------------------------------------------------------------------------------
 # a4/a5: vocabulary projection  [SL, "방법론 / 아키텍처"]; softmax rows [SD, section 3]
 
@@ -757,6 +777,29 @@ def kv_commit(k_pool, v_pool, page_table, prefix_len, free_list, n_free, k_cand,
             Vt[pg, pos % page] = v_cand[b * M + i * D + o]
         prefix_len[b] = P + a
     return k_pool, v_pool, page_table, prefix_len, free_list, n_free, flags
+
+
+def kv_commit_layers(k_pools, v_pools, page_table, prefix_len, free_list, n_free, k_cands,
+                     v_cands, best, n_acc, W, D, page=16):
+    """kv_commit for L layers that share one block table [SD6].  Reading: the decision
+    which pages a sequence takes is made once (it depends only on the table, the
+    lengths and the free stack), and every layer's accepted rows are then written at
+    the same (page, slot) of that layer's pool.  Equivalently: kv_commit applied to
+    each layer alone from the same table and stack gives the same new table, lengths,
+    stack and flags for every layer, and the layers' pools.  Arrays with a leading
+    layer axis: k_pools/v_pools [L, n_pages, ...], k_cands/v_cands [L, B*W*D, Hkv, hd].
+    Returns copies: (k_pools, v_pools, page_table, prefix_len, free_list, n_free,
+    flags)."""
+    L = k_pools.shape[0]
+    ks, vs = [], []
+    res = None
+    for l in range(L):
+        r = kv_commit(k_pools[l], v_pools[l], page_table, prefix_len, free_list, n_free,
+                      k_cands[l], v_cands[l], best, n_acc, W, D, page)
+        ks.append(r[0])
+        vs.append(r[1])
+        res = r
+    return (np.stack(ks), np.stack(vs)) + tuple(res[2:])
 
 
 def kv_truncate(page_table, prefix_len, new_len, free_list, n_free, n_pages, page=16):

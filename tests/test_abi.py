@@ -48,22 +48,58 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vs_abi_version() == 3
+    assert lib.vs_abi_version() == 4
     assert lib.vs_status_str(0) == b"ok"
     assert b"workspace" in lib.vs_status_str(-3)
     assert lib.vs_status_str(99) == b"unknown status"
 
 
 def test_struct_layouts_match_header():
-    # int32 fields, int64 ctx_total at its natural alignment, int32 accept_mode, padding
+    # int32 fields, int64 ctx_total at its natural alignment, int32 accept_mode and
+    # n_layers in what was the tail padding
     assert C.sizeof(L.StepDesc) == 88
     assert L.StepDesc.ctx_total.offset == 72
     assert L.StepDesc.accept_mode.offset == 80
+    assert L.StepDesc.n_layers.offset == 84
     assert C.sizeof(L.StepIO) == 35 * 8
-    assert C.sizeof(L.AttnDesc) == 44
+    assert C.sizeof(L.AttnDesc) == 48
     assert C.sizeof(L.HeadDesc) == 28
     assert C.sizeof(L.SampleDesc) == 24
-    assert C.sizeof(L.KvDesc) == 36
+    assert C.sizeof(L.KvDesc) == 40
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    """Every descriptor's size and field offsets as the C compiler lays out the header
+    (gcc on this host) equal the binding's ctypes view."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    structs = {"vs_attn_desc": L.AttnDesc, "vs_head_desc": L.HeadDesc,
+               "vs_sample_desc": L.SampleDesc, "vs_step_desc": L.StepDesc,
+               "vs_step_io": L.StepIO, "vs_kv_desc": L.KvDesc}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "vstep.h"', 'int main(void){']
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in cls._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    seen = 0
+    for line in out:
+        if not line:
+            continue
+        cname, field, val = line.split()
+        cls = structs[cname]
+        want = C.sizeof(cls) if field == "size" else getattr(cls, field).offset
+        assert int(val) == want, (cname, field)
+        seen += 1
+    assert seen == sum(len(c._fields_) + 1 for c in structs.values())
 
 
 def test_copy_match_validation(lib):
@@ -103,8 +139,14 @@ def test_attention_validation(lib):
     assert call(W=0) == -1
     assert call(W=64, D=20) == -1            # more than 1024 rows per sequence
     assert call() == -3                      # workspace too small
+    assert call(n_layers=-1) == -1
+    assert call(n_layers=1025) == -2         # beyond the layer limit
+    assert call(n_layers=32) == -3           # 32 layers: valid, needs its workspace
     d = L.AttnDesc(**ok)
     assert lib.vs_attention_workspace_bytes(C.byref(d)) > 0
+    # one layer: n_layers 0 and 1 are the same request
+    d1 = L.AttnDesc(**{**ok, "n_layers": 1})
+    assert lib.vs_attention_workspace_bytes(C.byref(d1)) == lib.vs_attention_workspace_bytes(C.byref(d))
     assert lib.vs_verify_attention(C.byref(d), None, fake, fake, fake, fake, fake, fake, fake,
                                    None, fake, 1 << 30, None) == -1
 

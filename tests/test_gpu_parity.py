@@ -281,6 +281,73 @@ def test_attention_full_size(c):
     assert err <= TOL
 
 
+def _layers_dev(LI, bf16):
+    return {k: to_dev(v, bf16=bf16) for k, v in LI.items()}
+
+
+@pytest.mark.parametrize("shape,L,plan", [
+    (small_shape(), 3, ""),                                                  # split-K
+    (small_shape(B=3, P=(0, 16, 1000), W=2, D=5, Hq=16, Hkv=4), 2, "0,8192"),  # one split
+    (small_shape(B=1, P=(4096,), W=4, D=20, Hq=32, Hkv=8, d=4096), 4, ""),   # Llama-8B layers
+    (wl.config(1), 3, ""),                                                   # fp32 path
+], ids=["small_split", "one_split", "llama8b_4", "tiny_f32"])
+def test_attention_layers(shape, L, plan, monkeypatch):
+    """L layers in one launch, sharing the page table and prefix lengths: every layer
+    against the oracle's layered attention; layer 0 also bit-identical to a one-layer
+    call where both use the same plan (same splits)."""
+    api = _api()
+    case = wl.make_case(shape, 31, with_head=False, with_q=False)
+    LI = wl.layer_inputs(case, L, 77)
+    bf = shape.dtype == "bf16"
+    T = _layers_dev(LI, bf)
+    pt, plen = to_dev(case.arrays["page_table"]), to_dev(case.arrays["prefix_len"])
+    if plan:
+        monkeypatch.setenv("VSTEP_ATTN_PLAN", plan)
+    say("attention layers", shape.name, L, plan or "default")
+    out, fl = api.verify_attention(T["q"], T["k_cand"], T["v_cand"], T["k_pool"], T["v_pool"],
+                                   pt, plen, shape.W, shape.D)
+    g = tensor_np(out)
+    f = lambda k: oracle.as_f64(LI[k], shape.dtype)
+    O, o_r, of = oracle.verify_attention_layers(f("q"), f("k_cand"), f("v_cand"), f("k_pool"),
+                                                f("v_pool"), case.arrays["page_table"],
+                                                case.arrays["prefix_len"], shape.B, shape.W,
+                                                shape.D, shape.Hq, shape.Hkv, out_dtype=shape.dtype)
+    assert np.array_equal(tensor_np(fl), of)
+    errs = [rel_err(g[l], (o_r if bf else O)[l]) for l in range(L)]
+    print("rel_err per layer", ["%.2e" % e for e in errs])
+    assert max(errs) <= (TOL if bf else 1e-5)
+    if plan:
+        one, _ = api.verify_attention(T["q"][0], T["k_cand"][0], T["v_cand"][0], T["k_pool"][0],
+                                      T["v_pool"][0], pt, plen, shape.W, shape.D)
+        assert np.array_equal(tensor_np(one), g[0])
+
+
+def test_attention_layers_llama8b_32_sampled():
+    """The 32 layers of a Llama-8B-shaped step (prefix 4096) in one launch, in the
+    configuration the layered bench times; layers 0, 13 and 31 against the oracle."""
+    api = _api()
+    sh = small_shape(B=1, P=(4096,), W=4, D=20, Hq=32, Hkv=8, d=4096)
+    case = wl.make_case(sh, 2000, with_head=False, with_q=False)
+    L = 32
+    LI = wl.layer_inputs(case, L, 5)
+    T = _layers_dev(LI, True)
+    say("attention layers llama8b 32")
+    out, fl = api.verify_attention(T["q"], T["k_cand"], T["v_cand"], T["k_pool"], T["v_pool"],
+                                   to_dev(case.arrays["page_table"]),
+                                   to_dev(case.arrays["prefix_len"]), sh.W, sh.D)
+    g = tensor_np(out)
+    assert (tensor_np(fl) == 0).all()
+    for l in (0, 13, 31):
+        f = lambda k: oracle.as_f64(LI[k][l], "bf16")
+        _, o_r, _ = oracle.verify_attention(f("q"), f("k_cand"), f("v_cand"), f("k_pool"),
+                                            f("v_pool"), case.arrays["page_table"],
+                                            case.arrays["prefix_len"], sh.B, sh.W, sh.D, sh.Hq,
+                                            sh.Hkv, out_dtype="bf16")
+        err = rel_err(g[l], o_r)
+        print(f"layer {l}: rel_err={err:.3e}")
+        assert err <= TOL
+
+
 # =============================================================================== head
 
 def _head_case(M, d, V, dtype="bf16", rank=0, seed=0):
@@ -960,6 +1027,47 @@ def test_kv_commit_and_truncate_rounds(dtype, Hkv, hd):
     assert (fo == oracle.FLAG_BAD_PAGE).sum() == 1
 
 
+@pytest.mark.parametrize("dtype,L", [("bf16", 4), ("f32", 3)])
+def test_kv_commit_layers_then_truncate(dtype, L):
+    """One commit over L layer pools that share the page table: every layer's pool,
+    the table, lengths, stack and flags equal the oracle's bit for bit; then one
+    rollback (the table is shared, so one call rolls back every layer) and a second
+    commit into the pages it freed."""
+    import torch
+    api = _api()
+    B, W, D, Hkv, hd = 6, 3, 9, 2, 128 if dtype == "bf16" else 64
+    A = wl.make_kv_case(8, B, W, D, Hkv, hd, [0, 1, 15, 16, 40, 100], n_spare=24,
+                        max_pages=16, dtype=dtype)
+    rng = np.random.default_rng(3)
+    extra = lambda a: np.stack([a] + [wl._normal_model(rng, a.shape, 1.0, dtype)
+                                      for _ in range(L - 1)])
+    A["k_pool"], A["v_pool"] = extra(A["k_pool"]), extra(A["v_pool"])
+    for rnd in range(2):
+        fresh = wl.make_kv_case(60 + rnd, B, W, D, Hkv, hd, [0] * B, 0, 16, dtype)
+        A["k_cand"], A["v_cand"] = extra(fresh["k_cand"]), extra(fresh["v_cand"])
+        A["best"], A["n_acc"] = fresh["best"], fresh["n_acc"]
+        G = _kv_dev(A, dtype)
+        say("kv commit layers", dtype, L, rnd)
+        fg = api.kv_commit(G["k_cand"], G["v_cand"], G["best"], G["n_acc"], G["k_pool"],
+                           G["v_pool"], G["page_table"], G["prefix_len"], G["free_list"],
+                           G["n_free"], W, D)
+        k, v, pt, P, fl, nf, fo = oracle.kv_commit_layers(
+            A["k_pool"], A["v_pool"], A["page_table"], A["prefix_len"], A["free_list"],
+            A["n_free"], A["k_cand"], A["v_cand"], A["best"], A["n_acc"], W, D)
+        A.update(k_pool=k, v_pool=v, page_table=pt, prefix_len=P, free_list=fl, n_free=nf)
+        _kv_check(G, A, tensor_np(fg), fo)
+        assert (A["prefix_len"] > 0).any()
+        cut = (A["prefix_len"] // 2).astype(np.int32)
+        say("kv truncate layers", dtype, L, rnd)
+        fg = api.kv_truncate(to_dev(cut), G["page_table"], G["prefix_len"], G["free_list"],
+                             G["n_free"], A["k_pool"].shape[1])
+        pt, P, fl, nf, fo = oracle.kv_truncate(A["page_table"], A["prefix_len"], cut,
+                                               A["free_list"], A["n_free"], A["k_pool"].shape[1])
+        A.update(page_table=pt, prefix_len=P, free_list=fl, n_free=nf)
+        _kv_check(G, A, tensor_np(fg), fo)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype,P", [("bf16", 300), ("bf16", 4096), ("f32", 77)])
 def test_kv_pack_token_major(dtype, P):
     """A contiguous token-major cache [P, Hkv, hd] packed into the verify step's pages
@@ -1144,6 +1252,45 @@ def test_verify_step_end_to_end(name):
     o = oracle.verify_step(case.arrays, sh)
     n_cmp, n_exc = _check_step(case, g, o)
     _assert_compared(f"step {name}", sh.B, n_cmp, n_exc, o["sample"], g)
+
+
+@pytest.mark.parametrize("name,L", [("small", 3), ("llama8b", 32)])
+def test_verify_step_layers(name, L):
+    """A step whose attention covers L layers in one launch (shared block table): every
+    layer's output against the oracle (all of them for the small shape, three for
+    Llama-8B), and the head and sampler, which read the last layer, against the
+    oracle's step on a case whose attention tensors are that layer's."""
+    api = _api()
+    if name == "small":
+        sh, seed = small_shape(B=3, P=(300, 777, 64)), 11
+    else:
+        sh, seed = wl.config(2), 2000
+    case = get_case(("step", name), lambda: wl.make_case(sh, seed))
+    LI = wl.layer_inputs(case, L, 99)
+    I = _step_inputs(case, sh.temperature)
+    I.update(_layers_dev(LI, sh.dtype == "bf16"))
+    say("verify_step layers", name, L)
+    step = api.VerifyStep(I, B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V,
+                          tau=sh.tau, temperature=sh.temperature, kappa=sh.kappa)
+    g = step()
+    ga = tensor_np(g["attn_out"])
+    assert ga.shape[0] == L
+    for l in (range(L) if L <= 4 else (0, 13, L - 1)):
+        f = lambda k: oracle.as_f64(LI[k][l], sh.dtype)
+        _, o_r, _ = oracle.verify_attention(f("q"), f("k_cand"), f("v_cand"), f("k_pool"),
+                                            f("v_pool"), case.arrays["page_table"],
+                                            case.arrays["prefix_len"], sh.B, sh.W, sh.D, sh.Hq,
+                                            sh.Hkv, out_dtype=sh.dtype)
+        err = rel_err(ga[l], o_r)
+        print(f"layer {l}: rel_err={err:.3e}")
+        assert err <= TOL
+    last = wl.Case(shape=case.shape, variant=case.variant, seed=case.seed,
+                   arrays={**case.arrays, **{k: LI[k][L - 1] for k in LI}}, meta=case.meta)
+    o = oracle.verify_step(last.arrays, sh)
+    g_last = dict(g)
+    g_last["attn_out"] = g["attn_out"][L - 1]
+    n_cmp, n_exc = _check_step(last, g_last, o)
+    _assert_compared(f"step layers {name}", sh.B, n_cmp, n_exc, o["sample"], g)
 
 
 @pytest.mark.parametrize("name", ["small", "llama8b", "ragged"])

@@ -162,3 +162,55 @@ def test_bad_page_is_flagged_and_masked():
     pt[0, 1] = 999
     _, _, fl = oracle.verify_attention(q, kc, vc, kp, vp, pt, plen, 1, 1, 2, 1, 1)
     assert fl[0] & oracle.FLAG_BAD_PAGE
+
+
+def test_layers_share_the_block_table():
+    """Several layers over one block table [SD6: a paged cache per layer].  Layer 0 is
+    a random layer pinned per candidate against causal attention (library routine);
+    layer 1 has zero queries (mean of the visible values, read element by element
+    from its own pool through the common table); layer 2 has constant values (they
+    pass through); a page entry out of the pool is flagged once for the sequence
+    and masked in every layer."""
+    rng = np.random.default_rng(11)
+    B, W, D, Hq, Hkv, hd, P = 2, 2, 3, 4, 2, 8, (37, 20)
+    layers = [_rand_case(rng, B, W, D, Hq, Hkv, hd, P, shuffle=False) for _ in range(3)]
+    pt, plen = layers[0][5], layers[0][6]
+    q, kc, vc, kp, vp = (np.stack([L_[j] for L_ in layers]) for j in range(5))
+    q[1] = 0.0
+    c = rng.standard_normal(hd)
+    vc[2] = c
+    vp[2] = c[None, None, :, None]
+    O, _, fl = oracle.verify_attention_layers(q, kc, vc, kp, vp, pt, plen, B, W, D, Hq, Hkv,
+                                              out_dtype="f32")
+    assert O.shape == (3,) + q.shape[1:] and (fl == 0).all()
+    ref0 = causal_per_candidate(q[0], kc[0], vc[0], kp[0], vp[0], pt, plen, B, W, D, Hq, Hkv)
+    assert np.abs(O[0] - ref0).max() < 1e-12
+    M = W * D
+    g = Hq // Hkv
+    for b in range(B):
+        Vp = _contiguous_prefix(vp[1], pt, b, int(plen[b]), kind="v")
+        for i in range(W):
+            for o in range(D):
+                r = b * M + i * D + o
+                for hq in range(Hq):
+                    vis = np.concatenate([Vp[:, hq // g, :], vc[1, b * M + i * D:r + 1, hq // g, :]])
+                    assert np.abs(O[1, r, hq] - vis.mean(axis=0)).max() < 1e-13
+    assert np.abs(O[2] - c).max() < 1e-13
+    # a bad page entry: flagged, and the same keys are dropped in every layer
+    pt_bad = pt.copy()
+    pt_bad[0, 1] = 10 ** 6
+    Ob, _, fb = oracle.verify_attention_layers(q, kc, vc, kp, vp, pt_bad, plen, B, W, D, Hq,
+                                               Hkv, out_dtype="f32")
+    assert fb.tolist() == [oracle.FLAG_BAD_PAGE, 0]
+    for l in range(3):
+        keep = np.ones(int(plen[0]), dtype=bool)
+        keep[16:32] = False
+        Kp = _contiguous_prefix(kp[l], pt, 0, int(plen[0]), kind="k")[keep]
+        Vp = _contiguous_prefix(vp[l], pt, 0, int(plen[0]), kind="v")[keep]
+        r, hq = 2, 3                       # candidate 0, offset 2, query head 3
+        K = np.concatenate([Kp[:, hq // g], kc[l, 0:3, hq // g]])
+        Vv = np.concatenate([Vp[:, hq // g], vc[l, 0:3, hq // g]])
+        s = K @ q[l, r, hq] / np.sqrt(hd)
+        a = np.exp(s - s.max())
+        a /= a.sum()
+        assert np.abs(Ob[l, r, hq] - a @ Vv).max() < 1e-12

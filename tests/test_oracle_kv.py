@@ -169,3 +169,51 @@ def test_bad_stack_count_refuses_everything():
         assert C["n_free"] == nf and np.array_equal(C["prefix_len"], A["prefix_len"])
         R, flags = truncate(A2, np.zeros(B, np.int32))
         assert (flags == oracle.FLAG_BAD_PAGE).all() and R["n_free"] == nf
+
+
+def test_commit_layers_write_every_layer_at_the_same_slots():
+    """Layers sharing one block table [SD6]: one commit takes each sequence's pages
+    once, and every layer's accepted rows are found through the new table in that
+    layer's own pool (read element by element from the raw head-major layout), the
+    rows before them untouched and every other pool entry unchanged."""
+    B, W, D, Hkv, hd, L = 5, 3, 6, 2, 8, 3
+    base = wl.make_kv_case(21, B, W, D, Hkv, hd, [0, 15, 16, 17, 33], n_spare=20,
+                           max_pages=8, dtype="f32")
+    rng = np.random.default_rng(4)
+    kp = np.stack([base["k_pool"]] + [rng.standard_normal(base["k_pool"].shape).astype(np.float32)
+                                      for _ in range(L - 1)])
+    vp = np.stack([base["v_pool"]] + [rng.standard_normal(base["v_pool"].shape).astype(np.float32)
+                                      for _ in range(L - 1)])
+    kc = np.stack([base["k_cand"]] + [rng.standard_normal(base["k_cand"].shape).astype(np.float32)
+                                      for _ in range(L - 1)])
+    vc = np.stack([base["v_cand"]] + [rng.standard_normal(base["v_cand"].shape).astype(np.float32)
+                                      for _ in range(L - 1)])
+    k2, v2, pt, P, fl, nf, flags = oracle.kv_commit_layers(
+        kp, vp, base["page_table"], base["prefix_len"], base["free_list"], base["n_free"],
+        kc, vc, base["best"], base["n_acc"], W, D)
+    assert not flags.any()
+    written = np.zeros(kp.shape, dtype=bool)
+    written_v = np.zeros(vp.shape, dtype=bool)
+    for b in range(B):
+        P0, i, a = int(base["prefix_len"][b]), int(base["best"][b]), int(base["n_acc"][b])
+        a = a if i >= 0 else 0
+        assert int(P[b]) == P0 + a
+        # the table keeps its old pages and takes new ones only past them
+        old = (P0 + PAGE - 1) // PAGE
+        assert np.array_equal(pt[b, :old], base["page_table"][b, :old])
+        for o in range(a):
+            pos = P0 + o
+            pg, t = int(pt[b, pos // PAGE]), pos % PAGE
+            row = b * W * D + i * D + o
+            for l in range(L):
+                for h in range(Hkv):
+                    assert np.array_equal(k2[l, pg, h, t, :], kc[l, row, h])
+                    assert np.array_equal(v2[l, pg, h, :, t], vc[l, row, h])
+                    written[l, pg, h, t, :] = True
+                    written_v[l, pg, h, :, t] = True
+    assert np.array_equal(k2[~written], kp[~written])
+    assert np.array_equal(v2[~written_v], vp[~written_v])
+    # the pages taken are the ones a one-layer commit takes
+    one = oracle.kv_commit(kp[0], vp[0], base["page_table"], base["prefix_len"], base["free_list"],
+                           base["n_free"], kc[0], vc[0], base["best"], base["n_acc"], W, D)
+    assert np.array_equal(one[2], pt) and one[5] == nf

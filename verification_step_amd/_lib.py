@@ -40,12 +40,14 @@ EXPORTED = [
 
 P = C.c_void_p
 I32 = C.c_int32
+ABI_VERSION = 4      # VS_ABI_VERSION of the descriptor layouts below
 
 
 class AttnDesc(C.Structure):
     _fields_ = [("B", I32), ("W", I32), ("D", I32), ("Hq", I32), ("Hkv", I32),
                 ("head_dim", I32), ("page_size", I32), ("max_pages", I32),
-                ("n_pool_pages", I32), ("dtype", I32), ("scale", C.c_float)]
+                ("n_pool_pages", I32), ("dtype", I32), ("scale", C.c_float),
+                ("n_layers", I32)]
 
 
 class HeadDesc(C.Structure):
@@ -63,12 +65,14 @@ class StepDesc(C.Structure):
                 ("head_dim", I32), ("page_size", I32), ("max_pages", I32),
                 ("n_pool_pages", I32), ("d", I32), ("V", I32), ("dtype", I32),
                 ("scale", C.c_float), ("tau", C.c_float), ("temperature", C.c_float),
-                ("external_drafts", I32), ("ctx_total", C.c_int64), ("accept_mode", I32)]
+                ("external_drafts", I32), ("ctx_total", C.c_int64), ("accept_mode", I32),
+                ("n_layers", I32)]
 
 
 class KvDesc(C.Structure):
     _fields_ = [("B", I32), ("W", I32), ("D", I32), ("Hkv", I32), ("head_dim", I32),
-                ("page_size", I32), ("max_pages", I32), ("n_pool_pages", I32), ("dtype", I32)]
+                ("page_size", I32), ("max_pages", I32), ("n_pool_pages", I32), ("dtype", I32),
+                ("n_layers", I32)]
 
 
 class StepIO(C.Structure):
@@ -96,6 +100,9 @@ def load(path: str = LIB_PATH):
             "`python -m verification_step_amd.build` (hipcc, gfx950)")
     lib = C.CDLL(path)
     lib.vs_abi_version.restype = C.c_int
+    if lib.vs_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.vs_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     lib.vs_status_str.restype = C.c_char_p
     lib.vs_status_str.argtypes = [C.c_int]
     lib.vs_copy_match.argtypes = [P, C.c_int64, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P,

@@ -211,12 +211,15 @@ def probe_gate(h: torch.Tensor, w: torch.Tensor, tau: float, n_found: Optional[t
     return out
 
 
-def attn_desc(B, W, D, Hq, Hkv, hd, max_pages, n_pool_pages, dtype, scale=0.0):
-    return L.AttnDesc(B, W, D, Hq, Hkv, hd, 16, max_pages, n_pool_pages, dtype, scale)
+def attn_desc(B, W, D, Hq, Hkv, hd, max_pages, n_pool_pages, dtype, scale=0.0, n_layers=1):
+    return L.AttnDesc(B, W, D, Hq, Hkv, hd, 16, max_pages, n_pool_pages, dtype, scale, n_layers)
 
 
 def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, W: int, D: int,
                      scale: float = 0.0, out: Optional[torch.Tensor] = None):
+    """One layer: q [B*W*D, Hq, hd], k/v_cand [B*W*D, Hkv, hd], k_pool [n_pages, Hkv, 16,
+    hd], v_pool [n_pages, Hkv, hd, 16].  L layers in one launch: each of these with a
+    leading layer dimension (the page table and prefix lengths are shared)."""
     lib = L.load()
     dt = q.dtype
     for name, t in (("q", q), ("k_cand", k_cand), ("v_cand", v_cand), ("k_pool", k_pool),
@@ -224,25 +227,31 @@ def verify_attention(q, k_cand, v_cand, k_pool, v_pool, page_table, prefix_len, 
         _check(t, dt, name)
     _check(page_table, torch.int32, "page_table")
     _check(prefix_len, torch.int32, "prefix_len")
-    BM, Hq, hd = q.shape
+    layered = q.dim() == 4
+    n_layers = q.shape[0] if layered else 1
+    lead = (n_layers,) if layered else ()
+    BM, Hq, hd = q.shape[-3:]
     B = prefix_len.numel()
-    Hkv = k_cand.shape[1]
+    Hkv = k_cand.shape[-2]
+    n_pages = k_pool.shape[-4]
     if BM != B * W * D:
         raise ValueError("q rows must equal B*W*D")
-    _expect(k_cand, (BM, Hkv, hd), "k_cand")
-    _expect(v_cand, (BM, Hkv, hd), "v_cand")
-    _expect(k_pool, (k_pool.shape[0], Hkv, 16, hd), "k_pool")
-    _expect(v_pool, (k_pool.shape[0], Hkv, hd, 16), "v_pool")
+    _expect(k_cand, lead + (BM, Hkv, hd), "k_cand")
+    _expect(v_cand, lead + (BM, Hkv, hd), "v_cand")
+    _expect(k_pool, lead + (n_pages, Hkv, 16, hd), "k_pool")
+    _expect(v_pool, lead + (n_pages, Hkv, hd, 16), "v_pool")
     _expect(page_table, (B, page_table.shape[1]), "page_table")
     _expect(out, q.shape, "out")
-    desc = attn_desc(B, W, D, Hq, Hkv, hd, page_table.shape[1], k_pool.shape[0], _vs_dtype(q),
-                     scale)
+    desc = attn_desc(B, W, D, Hq, Hkv, hd, page_table.shape[1], n_pages, _vs_dtype(q),
+                     scale, n_layers)
     if out is None:
         out = torch.empty_like(q)
     flags = torch.empty(B, dtype=torch.int32, device=q.device)
     nbytes = lib.vs_attention_workspace_bytes(C.byref(desc))
+    if nbytes == 0 and _vs_dtype(q) == L.VS_BF16:
+        raise VstepError(L.VS_ERR_INVALID_ARG, "verify_attention (descriptor rejected)")
     ws = workspace(nbytes, q.device, "attention",
-                   (B, W, D, Hq, Hkv, hd, page_table.shape[1], k_pool.shape[0], _vs_dtype(q)))
+                   (B, W, D, Hq, Hkv, hd, page_table.shape[1], n_pages, _vs_dtype(q), n_layers))
     st = lib.vs_verify_attention(C.byref(desc), _ptr(q), _ptr(k_cand), _ptr(v_cand), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(page_table), _ptr(prefix_len), _ptr(out),
                                  _ptr(flags), _ptr(ws), ws.numel(), _stream())
@@ -377,16 +386,19 @@ def reject_sample(root_logits, logits, row_lse, q, cand_tok, cand_len, u_acc, u_
 # ---------------------------------------------------------------------------------
 
 def _kv_desc(k_pool, page_table, W: int, D: int):
-    """k_pool [n_pages, Hkv, 16, hd]."""
+    """k_pool [n_pages, Hkv, 16, hd], or [L, n_pages, Hkv, 16, hd] for L layers."""
     B, max_pages = page_table.shape
-    return L.KvDesc(B, W, D, k_pool.shape[1], k_pool.shape[3], 16, max_pages, k_pool.shape[0],
-                    _vs_dtype(k_pool))
+    n_layers = k_pool.shape[0] if k_pool.dim() == 5 else 1
+    return L.KvDesc(B, W, D, k_pool.shape[-3], k_pool.shape[-1], 16, max_pages,
+                    k_pool.shape[-4], _vs_dtype(k_pool), n_layers)
 
 
 def kv_commit(k_cand, v_cand, best, n_acc, k_pool, v_pool, page_table, prefix_len, free_list,
               n_free, W: int, D: int):
     """Append each sequence's accepted candidate rows to its paged cache, in place (pools,
-    page_table, prefix_len, free_list, n_free).  Returns the per-sequence flags."""
+    page_table, prefix_len, free_list, n_free).  Returns the per-sequence flags.  With a
+    leading layer dimension on k/v_cand and the pools, every layer's rows go to the same
+    page slots (pages taken once for all layers)."""
     lib = L.load()
     for t, dt, n in ((best, torch.int32, "best"), (n_acc, torch.int32, "n_acc"),
                      (page_table, torch.int32, "page_table"),
@@ -396,9 +408,12 @@ def kv_commit(k_cand, v_cand, best, n_acc, k_pool, v_pool, page_table, prefix_le
     for t, n in ((k_cand, "k_cand"), (v_cand, "v_cand"), (k_pool, "k_pool"), (v_pool, "v_pool")):
         _check(t, k_pool.dtype, n)
     desc = _kv_desc(k_pool, page_table, W, D)
-    B, n_pages, Hkv, hd = page_table.shape[0], k_pool.shape[0], k_pool.shape[1], k_pool.shape[3]
-    for t, shp, n in ((k_cand, (B * W * D, Hkv, hd), "k_cand"), (v_cand, (B * W * D, Hkv, hd), "v_cand"),
-                      (k_pool, (n_pages, Hkv, 16, hd), "k_pool"), (v_pool, (n_pages, Hkv, hd, 16), "v_pool"),
+    B, n_pages, Hkv, hd = page_table.shape[0], k_pool.shape[-4], k_pool.shape[-3], k_pool.shape[-1]
+    lead = (k_pool.shape[0],) if k_pool.dim() == 5 else ()
+    for t, shp, n in ((k_cand, lead + (B * W * D, Hkv, hd), "k_cand"),
+                      (v_cand, lead + (B * W * D, Hkv, hd), "v_cand"),
+                      (k_pool, lead + (n_pages, Hkv, 16, hd), "k_pool"),
+                      (v_pool, lead + (n_pages, Hkv, hd, 16), "v_pool"),
                       (best, (B,), "best"), (n_acc, (B,), "n_acc"), (prefix_len, (B,), "prefix_len"),
                       (free_list, (n_pages,), "free_list"), (n_free, (1,), "n_free")):
         _expect(t, shp, n)
@@ -426,7 +441,7 @@ def kv_truncate(new_len, page_table, prefix_len, free_list, n_free, n_pool_pages
     for t, shp, n in ((new_len, (B,), "new_len"), (prefix_len, (B,), "prefix_len"),
                       (free_list, (int(n_pool_pages),), "free_list"), (n_free, (1,), "n_free")):
         _expect(t, shp, n)
-    desc = L.KvDesc(B, 1, 1, 1, 1, 16, max_pages, int(n_pool_pages), 0)
+    desc = L.KvDesc(B, 1, 1, 1, 1, 16, max_pages, int(n_pool_pages), 0, 1)
     flags = torch.empty(B, dtype=torch.int32, device=page_table.device)
     st = lib.vs_kv_truncate(C.byref(desc), _ptr(new_len), _ptr(page_table), _ptr(prefix_len),
                             _ptr(free_list), _ptr(n_free), _ptr(flags), _stream())
@@ -437,15 +452,17 @@ def kv_truncate(new_len, page_table, prefix_len, free_list, n_free, n_pool_pages
 # ---------------------------------------------------------------------------------
 
 def step_shapes(lib, I: dict, B, W, D, Hq, Hkv, hd, V, external_drafts, accept):
-    """Check every input of a verify step against the sizes its launches read."""
+    """Check every input of a verify step against the sizes its launches read (q, k/v_cand
+    and the pools may carry a leading layer dimension)."""
     M = B * W * D
     d = Hq * hd
-    _expect(I["q"], (M, Hq, hd), "q")
+    lead = (I["q"].shape[0],) if I["q"].dim() == 4 else ()
+    _expect(I["q"], lead + (M, Hq, hd), "q")
     for n in ("k_cand", "v_cand"):
-        _expect(I[n], (M, Hkv, hd), n)
-    n_pages = I["k_pool"].shape[0]
-    _expect(I["k_pool"], (n_pages, Hkv, 16, hd), "k_pool")
-    _expect(I["v_pool"], (n_pages, Hkv, hd, 16), "v_pool")
+        _expect(I[n], lead + (M, Hkv, hd), n)
+    n_pages = I["k_pool"].shape[-4]
+    _expect(I["k_pool"], lead + (n_pages, Hkv, 16, hd), "k_pool")
+    _expect(I["v_pool"], lead + (n_pages, Hkv, hd, 16), "v_pool")
     _expect(I["page_table"], (B, I["page_table"].shape[1]), "page_table")
     _expect(I["prefix_len"], (B,), "prefix_len")
     _expect(I["root_logits"], (B, V), "root_logits")
@@ -489,11 +506,13 @@ class VerifyStep:
         self.inputs = I
         d = Hq * hd
         M = B * W * D
+        self.n_layers = I["q"].shape[0] if I["q"].dim() == 4 else 1
+        lead = (self.n_layers,) if I["q"].dim() == 4 else ()
         self.desc = L.StepDesc(B, W, D, kappa, Hq, Hkv, hd, 16, I["page_table"].shape[1],
-                               I["k_pool"].shape[0], d, V, _vs_dtype(I["q"]), float(scale),
+                               I["k_pool"].shape[-4], d, V, _vs_dtype(I["q"]), float(scale),
                                float(tau), float(temperature), int(external_drafts),
                                I["ctx"].numel() if not external_drafts else 0,
-                               _accept_mode(accept))
+                               _accept_mode(accept), self.n_layers)
         self.out = dict(
             cand_tok=I["cand_tok"] if external_drafts else torch.empty((B, W, D), dtype=torch.int32, device=dev),
             cand_len=I["cand_len"] if external_drafts else torch.empty((B, W), dtype=torch.int32, device=dev),
@@ -501,7 +520,7 @@ class VerifyStep:
             n_found=torch.empty(B, dtype=torch.int32, device=dev),
             score=torch.empty(B, dtype=torch.float32, device=dev),
             gate=torch.empty(B, dtype=torch.int32, device=dev),
-            attn_out=torch.empty((M, Hq, hd), dtype=dt, device=dev),
+            attn_out=torch.empty(lead + (M, Hq, hd), dtype=dt, device=dev),
             logits=torch.empty((M, V), dtype=torch.float32, device=dev),
             row_lse=torch.empty(M, dtype=torch.float64, device=dev),
             n_acc=torch.empty(B, dtype=torch.int32, device=dev),

@@ -24,7 +24,11 @@
 //     error at the bf16 rounding of O itself;
 //   * partial (max, sum, O) per split go to the workspace and a combine kernel
 //     merges them in a fixed order.
-// fp32 path (head_dim 16/32/64): one thread per (query row, head), plain loops.
+// Layers: one launch may cover L layers that share the page table and prefix lengths
+// (a page id names the same slot in every layer's pool); each layer has its own
+// queries, candidate keys/values, pools and output at a fixed stride, and the
+// workgroups of all layers form one grid.
+// fp32 path (head_dim 16/32/64): one wave per (layer, query row, head), plain loops.
 
 #include "gate_wg.hpp"
 #include "vs_internal.hpp"
@@ -64,10 +68,11 @@ struct AttnArgs {
   const bf16_t *q, *k_cand, *v_cand, *k_pool, *v_pool;
   const int32_t *page_table, *prefix_len;
   bf16_t *out;
-  float *part_o;   // [B*Hkv][n_rb][n_splits+1][rows_per_block][hd]
-  float *part_ml;  // [B*Hkv][n_rb][n_splits+1][rows_per_block][2]
+  float *part_o;   // [L*B*Hkv][n_rb][n_splits+1][rows_per_block][hd]
+  float *part_ml;  // [L*B*Hkv][n_rb][n_splits+1][rows_per_block][2]
   int32_t *flags;
-  int B, W, D, M, Hq, Hkv, g, max_pages, n_pool_pages;
+  int64_t q_ls, c_ls, p_ls;   // per-layer strides (elements) of q/out, k/v_cand, pools
+  int B, W, D, M, Hq, Hkv, g, max_pages, n_pool_pages, L;
   int rows_per_kv, n_rb, rows_per_block, split_keys, n_splits;
   float scale_log2;
   int n_gate;        // leading workgroups that run the copy path's gate (0: none)
@@ -161,22 +166,31 @@ attn_mfma_kernel(AttnArgs a) {
       return;
     }
   }
-  const int n_sp = a.n_splits + 1;
-  const int nblocks = a.n_rb * n_sp * a.B * a.Hkv;
+  // one prefix split: its workgroup also takes the candidates' keys (no partials)
+  const bool fold = a.n_splits == 1;
+  const int n_sp = fold ? 1 : a.n_splits + 1;
+  const int nblocks = a.n_rb * n_sp * a.B * a.Hkv * a.L;
   const int bid = xcd_remap((int)blockIdx.x - a.n_gate, nblocks);
   const int rb = bid % a.n_rb;
   const int s = (bid / a.n_rb) % n_sp;
-  const int z = bid / (a.n_rb * n_sp);
-  const int b = z / a.Hkv;
-  const int kvh = z % a.Hkv;
+  const int z = bid / (a.n_rb * n_sp);        // (layer, sequence, kv head)
+  const int zs = z % (a.B * a.Hkv);
+  const int layer = z / (a.B * a.Hkv);
+  const int b = zs / a.Hkv;
+  const int kvh = zs % a.Hkv;
+  const bf16_t *q_l = a.q + layer * a.q_ls;
+  const bf16_t *kc_l = a.k_cand + layer * a.c_ls;
+  const bf16_t *vc_l = a.v_cand + layer * a.c_ls;
+  const bf16_t *kp_l = a.k_pool + layer * a.p_ls;
+  const bf16_t *vp_l = a.v_pool + layer * a.p_ls;
 
   bool badP = false;
   const int P = clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
   const int n_pref = (P + a.split_keys - 1) / a.split_keys;
   const int n_active = n_pref + 1;
-  const bool is_cand = (s == a.n_splits);
-  if (!is_cand && s >= n_pref) return;
-  if (badP && is_cand && rb == 0 && kvh == 0 && tid == 0 && a.flags)
+  const bool is_cand = !fold && s == a.n_splits;
+  if (!is_cand && !fold && s >= n_pref) return;
+  if (badP && (is_cand || fold) && rb == 0 && kvh == 0 && layer == 0 && tid == 0 && a.flags)
     atomicOr(&a.flags[b], FLAG_BAD_PAGE);
 
   const int k_begin = is_cand ? 0 : s * a.split_keys;
@@ -190,7 +204,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int hq = kvh * a.g + (rok ? rr % a.g : 0);
   bf16x8 qf[8];
   {
-    const bf16_t *qp = a.q + (((int64_t)b * a.M + (rok ? mrow : 0)) * a.Hq + hq) * kHD + 8 * h;
+    const bf16_t *qp = q_l + (((int64_t)b * a.M + (rok ? mrow : 0)) * a.Hq + hq) * kHD + 8 * h;
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) qf[s8] = rok ? *(const bf16x8 *)(qp + 16 * s8) : bf16x8{};
   }
@@ -259,9 +273,9 @@ attn_mfma_kernel(AttnArgs a) {
       if (i >= kT) break;
       const int64_t run = ((i & 7) >> 2) ? run1 : run0;
       if (i < 8)
-        dma16(a.k_pool + run, voff[ii], kb_lds + slot * kSlotBytes + i * 1024);
+        dma16(kp_l + run, voff[ii], kb_lds + slot * kSlotBytes + i * 1024);
       else
-        dma16(a.v_pool + run, voff[ii], vb_lds + slot * kSlotBytes + (i - 8) * 1024);
+        dma16(vp_l + run, voff[ii], vb_lds + slot * kSlotBytes + (i - 8) * 1024);
     }
   };
   // candidate keys (row-major [B*M, Hkv, hd]): staged through registers, V transposed
@@ -270,10 +284,10 @@ attn_mfma_kernel(AttnArgs a) {
       const int key = cc >> 4, ch = cc & 15;
       const int pos = kb + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (pos < k_end) {
+      if (pos < a.M) {
         const int64_t off = (((int64_t)b * a.M + pos) * a.Hkv + kvh) * kHD + 8 * ch;
-        kv = *(const u32x4 *)(a.k_cand + off);
-        vv = *(const u32x4 *)(a.v_cand + off);
+        kv = *(const u32x4 *)(kc_l + off);
+        vv = *(const u32x4 *)(vc_l + off);
       }
       *(u32x4 *)&Kb[slot][key * kHD + 8 * (ch ^ (key & 15))] = kv;
       const bf16_t *ve = (const bf16_t *)&vv;
@@ -341,24 +355,25 @@ attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // masking and the running maximum of one block's scores (may rescale O and l)
-  auto softmax_max = [&](f32x16 &S, int kb) {
+  // masking and the running maximum of one block's scores (may rescale O and l);
+  // cand: a block of the candidates' own keys, else of the prefix
+  auto softmax_max = [&](f32x16 &S, int kb, bool cand) {
     // block validity, uniform over the workgroup: a block of 32 in-range keys on two
     // valid pages needs no per-key mask
     int pv0 = 1, pv1 = 1;
-    if (!is_cand) {
+    if (!cand) {
       const int pl = (kb - k_begin) >> 4;
       pv0 = pages[pl] >= 0;
       pv1 = (kb + 16 < k_end) ? (pages[pl + 1] >= 0) : 0;
     }
-    const bool full = !is_cand && pv0 && pv1 && (kb + kKB <= k_end);
+    const bool full = !cand && pv0 && pv1 && (kb + kKB <= k_end);
     if (!full) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kpos = kb + 16 * (j >> 3) + 8 * h + (j & 7);
         bool v;
-        if (is_cand)
-          v = kpos < k_end && mrow < a.M && kpos / a.D == mrow / a.D && kpos <= mrow;
+        if (cand)
+          v = kpos < a.M && mrow < a.M && kpos / a.D == mrow / a.D && kpos <= mrow;
         else
           v = (j < 8 ? pv0 : pv1) && kpos < k_end;
         S[j] = v ? S[j] : -INFINITY;
@@ -424,20 +439,21 @@ attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  if (is_cand) {
+  // a wave whose 32 rows all lie past the KV head's rows (the padding of the last row
+  // block) only moves its share of the blocks and keeps the barriers
+  const bool idle = rb * a.rows_per_block + wv * kTileRows >= a.rows_per_kv;
+  if (!is_cand && nblk > 0 && idle) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < nblk) issue_prefix(j, j);
+    wait_blocks(min(nblk - 1, 2));
+    __syncthreads();
     for (int j = 0; j < nblk; ++j) {
-      const int slot = j & 1;
-      const int kb = k_begin + j * kKB;
-      stage_cand(slot, kb);
+      wait_blocks(min(nblk - 1, j + 2) - (j + 1));
       __syncthreads();
-      bf16x8 kf[8], vf[8];
-      load_k(slot, kf);
-      load_v(slot, vf);
-      f32x16 S = qk_mma(kf);
-      softmax_max(S, kb);
-      softmax_pv(S, vf);
+      if (j + 3 < nblk) issue_prefix(j + 3, (j + 3) & 3);
     }
-  } else if (nblk > 0) {
+  } else if (!is_cand && nblk > 0) {
     // software pipeline over the ring: in iteration j block j+1's QK product is
     // interleaved with block j's softmax and PV product, and block j+3 is in flight
     static_assert(kNBuf == 4, "ring of four blocks");
@@ -463,7 +479,7 @@ attn_mfma_kernel(AttnArgs a) {
       load_k(more ? (j + 1) & 3 : j & 3, kf);
       load_v(j & 3, vf);
       mask_v(vf, kb);
-      softmax_max(S_cur, kb);
+      softmax_max(S_cur, kb, false);
       f32x16 S_next = qk_mma(kf);     // harmless recomputation on the last block
       softmax_pv(S_cur, vf);
       // issue order: QK products between the exponentials, PV products as P is ready
@@ -480,14 +496,33 @@ attn_mfma_kernel(AttnArgs a) {
       S_cur = S_next;
     }
   }
+  if (is_cand || fold) {
+    // the candidates' keys (after the prefix when folded: every wave is done reading
+    // the ring before it is restaged)
+    if (fold) __syncthreads();
+    const int nc = (a.M + kKB - 1) / kKB;
+    for (int j = 0; j < nc; ++j) {
+      const int slot = j & 1;
+      const int kb = j * kKB;
+      stage_cand(slot, kb);
+      __syncthreads();
+      if (idle) continue;
+      bf16x8 kf[8], vf[8];
+      load_k(slot, kf);
+      load_v(slot, vf);
+      f32x16 S = qk_mma(kf);
+      softmax_max(S, kb, true);
+      softmax_pv(S, vf);
+    }
+  }
 
   // ---- finish: the row's sum over both lane halves, then final output or partials
   const float l = sum_xor32(l_part);
   if (!rok) return;
   // O^T register j of tile t: head dim 32t + 8*(j/4) + 4h + j%4
-  if (n_active == 1) {
+  if (fold || n_active == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    bf16_t *op = a.out + (((int64_t)b * a.M + mrow) * a.Hq + hq) * kHD + 4 * h;
+    bf16_t *op = a.out + layer * a.q_ls + (((int64_t)b * a.M + mrow) * a.Hq + hq) * kHD + 4 * h;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -519,14 +554,15 @@ __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a) {
   const int n_sp = a.n_splits + 1;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total_rows = (int64_t)a.B * a.Hkv * a.n_rb * a.rows_per_block;
+  const int64_t total_rows = (int64_t)a.L * a.B * a.Hkv * a.n_rb * a.rows_per_block;
   const int64_t row = gid / 32;
   const int c4 = (int)(gid % 32) * 4;
   if (row >= total_rows) return;
   const int row_in_block = (int)(row % a.rows_per_block);
   const int rb = (int)((row / a.rows_per_block) % a.n_rb);
-  const int z = (int)(row / ((int64_t)a.rows_per_block * a.n_rb));
-  const int b = z / a.Hkv, kvh = z % a.Hkv;
+  const int z = (int)(row / ((int64_t)a.rows_per_block * a.n_rb));   // (layer, b, kv head)
+  const int layer = z / (a.B * a.Hkv);
+  const int b = (z / a.Hkv) % a.B, kvh = z % a.Hkv;
   const int rr = rb * a.rows_per_block + row_in_block;
   if (rr >= a.rows_per_kv) return;
   bool badP = false;
@@ -571,7 +607,7 @@ attn_combine_kernel(AttnArgs a) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int m = rr / a.g;
   const int hq = kvh * a.g + rr % a.g;
-  bf16_t *op = a.out + (((int64_t)b * a.M + m) * a.Hq + hq) * kHD + c4;
+  bf16_t *op = a.out + layer * a.q_ls + (((int64_t)b * a.M + m) * a.Hq + hq) * kHD + c4;
   *(uint2 *)op = make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv),
                             pack_bf16x2(acc[2] * inv, acc[3] * inv));
 }
@@ -600,7 +636,7 @@ __global__ void __launch_bounds__(256)
 attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const float *k_pool,
                 const float *v_pool, const int32_t *page_table, const int32_t *prefix_len,
                 float *out, int32_t *flags, int B, int W, int D, int Hq, int Hkv, int max_pages,
-                int n_pool_pages, float scale, int n_gate, GateArgs gate) {
+                int n_pool_pages, float scale, int n_gate, GateArgs gate, int L) {
   static_assert(HD <= 64, "one output element per lane");
   if ((int)blockIdx.x < n_gate) {
     __shared__ GateShared<256> gsh;
@@ -610,14 +646,26 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
   const int M = W * D;
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)((int)blockIdx.x - n_gate) * 4 + (threadIdx.x >> 6);
-  if (task >= (int64_t)B * M * Hq) return;     // uniform per wave
+  const int64_t per_layer = (int64_t)B * M * Hq;
+  if (task >= per_layer * L) return;     // uniform per wave
   const int hq = (int)(task % Hq);
   const int r = (int)((task / Hq) % M);
-  const int b = (int)(task / ((int64_t)Hq * M));
+  const int b = (int)((task / ((int64_t)Hq * M)) % B);
+  const int layer = (int)(task / per_layer);
+  {
+    const int64_t qs = per_layer * HD, cs = (int64_t)B * M * Hkv * HD;
+    const int64_t ps = (int64_t)n_pool_pages * Hkv * kPage * HD;
+    q += layer * qs;
+    out += layer * qs;
+    k_cand += layer * cs;
+    v_cand += layer * cs;
+    if (k_pool) k_pool += layer * ps;
+    if (v_pool) v_pool += layer * ps;
+  }
   const int kvh = hq / (Hq / Hkv);
   bool badP = false;
   const int P = clamp_prefix(prefix_len[b], max_pages * kPage, &badP);
-  if (badP && flags && r == 0 && hq == 0 && lane == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
+  if (badP && flags && r == 0 && hq == 0 && layer == 0 && lane == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
   float qv[HD], acc[HD];
   const float *qp = q + (((int64_t)b * M + r) * Hq + hq) * HD;
 #pragma unroll
@@ -634,7 +682,7 @@ attn_f32_kernel(const float *q, const float *k_cand, const float *v_cand, const 
     if (k < P) {
       const int pg = page_table[(int64_t)b * max_pages + k / kPage];
       if (pg < 0 || pg >= n_pool_pages) {
-        if (flags && (k % kPage) == 0 && hq == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
+        if (flags && (k % kPage) == 0 && hq == 0 && layer == 0) atomicOr(&flags[b], FLAG_BAD_PAGE);
         continue;
       }
       kp = k_pool + (((int64_t)pg * Hkv + kvh) * kPage + k % kPage) * HD;
@@ -678,10 +726,10 @@ __global__ void zero_i32_kernel(int32_t *p, int n) {
 }  // namespace
 
 bool attn_fuses_gate(int B, int W, int D, int Hq, int Hkv, int max_pages, int dtype) {
-  return dtype == 0 || (dtype == 1 && attn_plan(B, W, D, Hq, Hkv, max_pages, kPage).nw >= 4);
+  return dtype == 0 || (dtype == 1 && attn_plan(B, W, D, Hq, Hkv, max_pages, kPage, 1).nw >= 4);
 }
 
-AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page) {
+AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page, int L) {
   AttnPlan p{};
   const int M = W * D;
   const int g = Hq / Hkv;
@@ -708,7 +756,7 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   p.rows_per_block = p.nw * kTileRows;
   p.n_rb = (tiles + p.nw - 1) / p.nw;
   if (split_keys == 0) {
-    const int groups = B * Hkv * p.n_rb;
+    const int groups = L * B * Hkv * p.n_rb;
     // one-wave workgroups leave room for many more per CU: their splits may be as
     // short as the 4-block ring (128 keys)
     const int min_keys = p.nw == 1 ? 128 : 256;
@@ -734,12 +782,17 @@ AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page
   return p;
 }
 
+// partial slots of the split-K form (none when the one prefix split takes the candidates)
+static size_t attn_slots(const AttnPlan &p, int B, int Hkv, int L) {
+  if (p.n_splits == 1) return 0;
+  return (size_t)L * B * Hkv * p.n_rb * (p.n_splits + 1) * p.rows_per_block;
+}
+
 size_t attn_workspace_bytes(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages, int page,
-                            int dtype) {
+                            int dtype, int L) {
   if (dtype != 1) return 0;
-  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, page);
-  const size_t slots = (size_t)B * Hkv * p.n_rb * (p.n_splits + 1) * p.rows_per_block;
-  return slots * (size_t)(kHD + 2) * sizeof(float) + 256;
+  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, page, L);
+  return attn_slots(p, B, Hkv, L) * (size_t)(kHD + 2) * sizeof(float) + 256;
 }
 
 hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages,
@@ -747,10 +800,11 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
                             const void *k_cand, const void *v_cand, const void *k_pool,
                             const void *v_pool, const int32_t *page_table,
                             const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
-                            hipStream_t st, const GateArgs *gate) {
+                            hipStream_t st, const GateArgs *gate, int L) {
   const int M = W * D;
+  if (L < 1) return hipErrorInvalidValue;
   if (dtype == 0) {
-    const int64_t n = (int64_t)B * M * Hq;    // one wave each, four per workgroup
+    const int64_t n = (int64_t)L * B * M * Hq;    // one wave each, four per workgroup
     const int n_gate = gate != nullptr ? B : 0;
     const int blocks = (int)((n + 3) / 4) + n_gate;
     const GateArgs ga = gate != nullptr ? *gate : GateArgs{};
@@ -758,14 +812,15 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   hipLaunchKernelGGL(attn_f32_kernel<HDV>, dim3(blocks), dim3(256), 0, st, (const float *)q,   \
                      (const float *)k_cand, (const float *)v_cand, (const float *)k_pool,      \
                      (const float *)v_pool, page_table, prefix_len, (float *)out, flags, B, W, \
-                     D, Hq, Hkv, max_pages, n_pool_pages, scale, n_gate, ga)
+                     D, Hq, Hkv, max_pages, n_pool_pages, scale, n_gate, ga, L)
     if (hd == 16) VS_F32_ATTN(16);
     else if (hd == 32) VS_F32_ATTN(32);
     else VS_F32_ATTN(64);
 #undef VS_F32_ATTN
     return hipGetLastError();
   }
-  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, kPage);
+  const AttnPlan p = attn_plan(B, W, D, Hq, Hkv, max_pages, kPage, L);
+  const bool fold = p.n_splits == 1;
   AttnArgs a;
   a.q = (const bf16_t *)q;
   a.k_cand = (const bf16_t *)k_cand;
@@ -775,10 +830,14 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   a.page_table = page_table;
   a.prefix_len = prefix_len;
   a.out = (bf16_t *)out;
-  const size_t slots = (size_t)B * Hkv * p.n_rb * (p.n_splits + 1) * p.rows_per_block;
+  const size_t slots = attn_slots(p, B, Hkv, L);
   a.part_o = (float *)ws;
   a.part_ml = a.part_o + slots * kHD;
   a.flags = flags;
+  a.L = L;
+  a.q_ls = (int64_t)B * M * Hq * kHD;
+  a.c_ls = (int64_t)B * M * Hkv * kHD;
+  a.p_ls = (int64_t)n_pool_pages * Hkv * kPage * kHD;
   a.B = B;
   a.W = W;
   a.D = D;
@@ -800,7 +859,7 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
     a.n_gate = B;
     a.gate = *gate;
   }
-  const int nblocks = p.n_rb * (p.n_splits + 1) * B * Hkv;
+  const int nblocks = p.n_rb * (fold ? 1 : p.n_splits + 1) * B * Hkv * L;
   const dim3 grid(nblocks + a.n_gate), block(64 * p.nw);
   switch (p.nw) {
     case 1: hipLaunchKernelGGL((attn_mfma_kernel<1>), grid, block, 0, st, a); break;
@@ -811,8 +870,8 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)B * Hkv * p.n_rb * p.rows_per_block * 32;
+  if (e != hipSuccess || fold) return e;
+  const int64_t threads = (int64_t)L * B * Hkv * p.n_rb * p.rows_per_block * 32;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      st, a);
   return hipGetLastError();

@@ -20,6 +20,22 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? VS_OK : VS_ERR_HI
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxLayers = 1024;
+
+// layers of a descriptor: 0 reads as one; negative is invalid (returned as 0)
+inline int layers_of(int32_t n) { return n == 0 ? 1 : (n < 0 ? 0 : n); }
+
+// attention workgroups of one launch (prefix splits of the bf16 plan, or one wave per
+// row and head for fp32), for the grid-size limit
+int64_t attn_launch_groups(int B, int W, int D, int Hq, int Hkv, int max_pages, int dtype,
+                           int L) {
+  if (dtype == VS_BF16) {
+    const vs::AttnPlan p = vs::attn_plan(B, W, D, Hq, Hkv, max_pages, 16, L);
+    return (int64_t)p.n_rb * (p.n_splits + 1) * B * Hkv * L;
+  }
+  return ((int64_t)L * B * W * D * Hq + 3) / 4;
+}
+
 int check_attn(const vs_attn_desc *d) {
   if (!d) return VS_ERR_INVALID_ARG;
   if (d->B <= 0 || d->W <= 0 || d->D <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->head_dim <= 0 ||
@@ -38,6 +54,11 @@ int check_attn(const vs_attn_desc *d) {
     return VS_ERR_UNSUPPORTED;
   }
   if ((int64_t)d->max_pages * 16 > (1 << 28)) return VS_ERR_UNSUPPORTED;
+  const int L = layers_of(d->n_layers);
+  if (L < 1) return VS_ERR_INVALID_ARG;
+  if (L > kMaxLayers) return VS_ERR_UNSUPPORTED;
+  if (attn_launch_groups(d->B, d->W, d->D, d->Hq, d->Hkv, d->max_pages, d->dtype, L) > (1 << 30))
+    return VS_ERR_UNSUPPORTED;
   return VS_OK;
 }
 
@@ -85,7 +106,7 @@ StepLayout step_layout(const vs_step_desc *d) {
   StepLayout L;
   L.attn = 0;
   const size_t a = vs::attn_workspace_bytes(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim,
-                                            d->max_pages, 16, d->dtype);
+                                            d->max_pages, 16, d->dtype, layers_of(d->n_layers));
   L.head = align256(a);
   const size_t h = vs::head_workspace_bytes(d->B * d->W * d->D, d->d, d->V, 0, d->dtype);
   L.sample = align256(L.head + h);
@@ -169,7 +190,7 @@ int vs_probe_gate(const void *h, int h_dtype, const float *w, int B, int d, floa
 size_t vs_attention_workspace_bytes(const vs_attn_desc *d) {
   if (check_attn(d) != VS_OK) return 0;
   return vs::attn_workspace_bytes(d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->max_pages,
-                                  d->page_size, d->dtype);
+                                  d->page_size, d->dtype, layers_of(d->n_layers));
 }
 
 int vs_verify_attention(const vs_attn_desc *d, const void *q, const void *k_cand,
@@ -190,7 +211,7 @@ int vs_verify_attention(const vs_attn_desc *d, const void *q, const void *k_cand
                                          d->max_pages, d->n_pool_pages, d->dtype,
                                          attn_scale(d->scale, d->head_dim), q, k_cand, v_cand,
                                          k_pool, v_pool, page_table, prefix_len, out, flags,
-                                         workspace, S(stream)));
+                                         workspace, S(stream), nullptr, layers_of(d->n_layers)));
 }
 
 size_t vs_packed_weight_bytes(int N, int K) {
@@ -274,7 +295,7 @@ int vs_reject_sample(const vs_sample_desc *d, const float *root_logits, const fl
 static int check_step(const vs_step_desc *d) {
   if (!d) return VS_ERR_INVALID_ARG;
   vs_attn_desc ad = {d->B, d->W, d->D, d->Hq, d->Hkv, d->head_dim, d->page_size, d->max_pages,
-                     d->n_pool_pages, d->dtype, d->scale};
+                     d->n_pool_pages, d->dtype, d->scale, d->n_layers};
   int st = check_attn(&ad);
   if (st != VS_OK) return st;
   vs_head_desc hd = {d->B * d->W * d->D, d->d, d->V, 0, d->dtype, d->temperature, 0};
@@ -323,6 +344,7 @@ static int verify_step_impl(const vs_step_desc *d, const vs_step_io *io, void *w
     return ev == nullptr || hipEventRecord(ev[i], s) == hipSuccess;
   };
   const int M = d->B * d->W * d->D;
+  const int n_layers = layers_of(d->n_layers);
   char *ws = (char *)workspace;
   const vs::HeadWs hw = vs::head_ws(ws + L.head, M, d->V, 0);
   const vs::SampleWs sw = vs::sample_ws(ws + L.sample, d->B, d->W, d->D, d->V);
@@ -370,10 +392,13 @@ static int verify_step_impl(const vs_step_desc *d, const vs_step_io *io, void *w
                            d->n_pool_pages, d->dtype, attn_scale(d->scale, d->head_dim), io->q,
                            io->k_cand, io->v_cand, io->k_pool, io->v_pool, io->page_table,
                            io->prefix_len, io->attn_out, sw.attn_flags, ws + L.attn, s,
-                           fuse ? &ga : nullptr);
+                           fuse ? &ga : nullptr, n_layers);
   if (e != hipSuccess || !mark(2)) return VS_ERR_HIP;
-  // 3. head: GEMM + tile statistics (verify rows and root rows)
-  e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, io->attn_out, io->w_full,
+  // 3. head: GEMM + tile statistics (verify rows and root rows) over the last layer's
+  //    attention output
+  const char *head_in = (const char *)io->attn_out +
+                        (size_t)(n_layers - 1) * M * d->d * (d->dtype == VS_BF16 ? 2 : 4);
+  e = vs::launch_head_gemm(M, d->d, d->V, 0, d->dtype, d->temperature, head_in, io->w_full,
                            nullptr, nullptr, io->logits, hw, io->root_logits, d->B,
                            sw.root_stats, s);
   if (e != hipSuccess || !mark(3)) return VS_ERR_HIP;
@@ -450,6 +475,9 @@ static int check_kv(const vs_kv_desc *d, bool commit) {
     if (d->W <= 0 || d->D <= 0 || d->Hkv <= 0 || d->head_dim <= 0) return VS_ERR_INVALID_ARG;
     if ((int64_t)d->W * d->D > kMaxRows) return VS_ERR_INVALID_ARG;
     if (d->dtype != VS_BF16 && d->dtype != VS_F32) return VS_ERR_UNSUPPORTED;
+    const int L = layers_of(d->n_layers);
+    if (L < 1) return VS_ERR_INVALID_ARG;
+    if (L > 65535) return VS_ERR_UNSUPPORTED;
   }
   return VS_OK;
 }
@@ -473,7 +501,7 @@ int vs_kv_commit(const vs_kv_desc *d, const void *k_cand, const void *v_cand, co
                                          d->n_pool_pages, d->dtype == VS_BF16 ? 2 : 4, k_cand,
                                          v_cand, best, n_acc, k_pool, v_pool, page_table,
                                          prefix_len, free_list, n_free, flags, workspace,
-                                         S(stream)));
+                                         S(stream), layers_of(d->n_layers)));
 }
 
 int vs_measure_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg, void *stream) {

@@ -138,15 +138,21 @@ kv_commit_plan_kernel(CommitArgs a) {
   if (tid == 0) *a.n_free = sh.n_free1;
 }
 
-// One workgroup per (row o, sequence b): row (b, best, o) of the candidate K/V goes to
-// token P + o of the cache.  E = element type of the model tensors (bf16 bits or fp32).
+// One workgroup per (row o, sequence b, layer): row (b, best, o) of the layer's
+// candidate K/V goes to token P + o of the layer's pool (the page table is shared by
+// every layer).  E = element type of the model tensors (bf16 bits or fp32).
 template <typename E>
 __global__ void __launch_bounds__(kKT)
 kv_copy_kernel(const E *k_cand, const E *v_cand, E *k_pool, E *v_pool,
                const int32_t *page_table, const int32_t *plan, int W, int D, int Hkv, int hd,
-               int max_pages) {
+               int max_pages, int64_t cand_ls, int64_t pool_ls) {
   const int o = blockIdx.x;
   const int b = blockIdx.y;
+  const int64_t layer = blockIdx.z;
+  k_cand += layer * cand_ls;
+  v_cand += layer * cand_ls;
+  k_pool += layer * pool_ls;
+  v_pool += layer * pool_ls;
   const int32_t *pl = plan + 3 * b;
   if (o >= pl[1]) return;
   const int pos = pl[0] + o;
@@ -230,7 +236,8 @@ hipError_t launch_kv_commit(int B, int W, int D, int Hkv, int hd, int max_pages,
                             int esz, const void *k_cand, const void *v_cand, const int32_t *best,
                             const int32_t *n_acc, void *k_pool, void *v_pool, int32_t *page_table,
                             int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
-                            int32_t *flags, void *ws, hipStream_t st) {
+                            int32_t *flags, void *ws, hipStream_t st, int L) {
+  if (L < 1 || L > 65535) return hipErrorInvalidValue;
   CommitArgs a;
   a.B = B;
   a.W = W;
@@ -247,15 +254,19 @@ hipError_t launch_kv_commit(int B, int W, int D, int Hkv, int hd, int max_pages,
   a.plan = (int32_t *)ws;
   hipLaunchKernelGGL(kv_commit_plan_kernel, dim3(1), dim3(kKT), 0, st, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const dim3 grid(D, B);
+  const dim3 grid(D, B, L);
+  const int64_t cand_ls = (int64_t)B * W * D * Hkv * hd;
+  const int64_t pool_ls = (int64_t)n_pool_pages * Hkv * kPg * hd;
   if (esz == 2)
     hipLaunchKernelGGL(kv_copy_kernel<uint16_t>, grid, dim3(kKT), 0, st,
                        (const uint16_t *)k_cand, (const uint16_t *)v_cand, (uint16_t *)k_pool,
-                       (uint16_t *)v_pool, page_table, a.plan, W, D, Hkv, hd, max_pages);
+                       (uint16_t *)v_pool, page_table, a.plan, W, D, Hkv, hd, max_pages, cand_ls,
+                       pool_ls);
   else
     hipLaunchKernelGGL(kv_copy_kernel<uint32_t>, grid, dim3(kKT), 0, st,
                        (const uint32_t *)k_cand, (const uint32_t *)v_cand, (uint32_t *)k_pool,
-                       (uint32_t *)v_pool, page_table, a.plan, W, D, Hkv, hd, max_pages);
+                       (uint32_t *)v_pool, page_table, a.plan, W, D, Hkv, hd, max_pages, cand_ls,
+                       pool_ls);
   return hipGetLastError();
 }
 

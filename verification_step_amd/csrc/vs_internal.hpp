@@ -76,9 +76,10 @@ struct AttnPlan {
   int n_splits;     // prefix splits (a candidate split is added after them)
 };
 
-AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page);
+// L: layers covered by one launch (they share page table and prefix lengths)
+AttnPlan attn_plan(int B, int W, int D, int Hq, int Hkv, int max_pages, int page, int L);
 size_t attn_workspace_bytes(int B, int W, int D, int Hq, int Hkv, int hd, int max_pages, int page,
-                            int dtype);
+                            int dtype, int L);
 
 // Retrieval + probe of the copy path, one sequence per workgroup (gate_wg.hpp).
 struct GateArgs {
@@ -121,7 +122,7 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
                             const void *k_cand, const void *v_cand, const void *k_pool,
                             const void *v_pool, const int32_t *page_table,
                             const int32_t *prefix_len, void *out, int32_t *flags, void *ws,
-                            hipStream_t st, const GateArgs *gate = nullptr);
+                            hipStream_t st, const GateArgs *gate = nullptr, int L = 1);
 
 // Head workspace: per-tile (max, sumexp) statistics [rows][n_vt] and the low-rank
 // intermediate.
@@ -219,7 +220,7 @@ hipError_t launch_kv_commit(int B, int W, int D, int Hkv, int hd, int max_pages,
                             int esz, const void *k_cand, const void *v_cand, const int32_t *best,
                             const int32_t *n_acc, void *k_pool, void *v_pool, int32_t *page_table,
                             int32_t *prefix_len, int32_t *free_list, int32_t *n_free,
-                            int32_t *flags, void *ws, hipStream_t st);
+                            int32_t *flags, void *ws, hipStream_t st, int L = 1);
 // token-major K/V [n_tokens][Hkv][hd] -> the verify step's pages (esz: 2 bf16, 4 fp32)
 hipError_t launch_kv_pack(const void *k_src, const void *v_src, int64_t n_tokens, int Hkv, int hd,
                           int esz, void *k_pool, void *v_pool, hipStream_t st);

@@ -368,6 +368,24 @@ def draft_probs_from_logits(rng, shape, sigma: float, block_rows: int = 64) -> n
     return out
 
 
+LAYER_TENSORS = ("q", "k_cand", "v_cand", "k_pool", "v_pool")
+
+
+def layer_inputs(case: Case, n_layers: int, seed: int) -> dict:
+    """The attention tensors of a model with n_layers layers that share the case's block
+    table (page_table, prefix_len): q, k_cand, v_cand, k_pool and v_pool stacked on a
+    leading layer axis.  Layer 0 is the case's own; layers 1.. are fresh N(0, 1)
+    tensors of the same shapes and dtype, one generator stream per layer."""
+    sh = case.shape
+    kids = np.random.SeedSequence(seed).spawn(max(n_layers - 1, 0))
+    out = {k: [case.arrays[k]] for k in LAYER_TENSORS}
+    for kid in kids:
+        rng = np.random.default_rng(kid)
+        for k in LAYER_TENSORS:
+            out[k].append(_normal_model(rng, case.arrays[k].shape, 1.0, sh.dtype))
+    return {k: np.stack(v) for k, v in out.items()}
+
+
 def make_kv_case(seed: int, B: int, W: int, D: int, Hkv: int, hd: int, prefix, n_spare: int,
                  max_pages: int, dtype: str = "bf16"):
     """Inputs of a KV commit / rollback: a paged pool whose first pages hold the

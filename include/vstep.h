@@ -75,7 +75,10 @@ enum {
     VS_FLAG_BAD_PAGE = 32,            /* page index outside the pool, or prefix_len out of range */
     VS_FLAG_BAD_CTX = 64,             /* context offsets outside [0, ctx_total] or decreasing */
     VS_FLAG_BAD_TOKEN = 128,          /* a tested candidate token id is outside [0, V): rejected */
-    VS_FLAG_POOL_EMPTY = 256          /* kv commit: fewer free pages than a sequence needs */
+    VS_FLAG_POOL_EMPTY = 256,         /* kv commit: fewer free pages than a sequence needs */
+    VS_FLAG_SYNC_TIMEOUT = 512        /* multi with dense drafts: a wait for the sequence's other
+                                         workgroups gave up (cannot happen when the launch
+                                         succeeds; the outputs are then not valid) */
 };
 
 int         vs_abi_version(void);

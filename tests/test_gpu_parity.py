@@ -652,6 +652,40 @@ def test_reject_sample_multi_dense(B, W, D, V, T):
     assert (tensor_np(g["flags"])[:2] & oracle.FLAG_NO_CANDIDATE).all()
 
 
+def test_reject_sample_multi_dense_widths(monkeypatch):
+    """The dense chain gives the same bits whether a sequence's vocabulary passes are
+    shared by 1, 3 or 16 workgroups (each chunk's sum is formed the same way whatever
+    workgroup owns it), with several rejections per sequence at V = 128,256."""
+    api = _api()
+    rng = np.random.default_rng(808)
+    B, W, D, V, T = 5, 6, 3, 128256, 1.0
+    root, logits, cand, clen = _multi_case(rng, B, W, D, V)
+    M = W * D
+    ql = rng.standard_normal((B * M, V))
+    ql[:, 1:3] += 6.0
+    ql -= ql.max(axis=1, keepdims=True)
+    q = np.exp(ql)
+    q = (q / q.sum(axis=1, keepdims=True)).astype(np.float32)
+    lse = scipy.special.logsumexp(logits.astype(np.float64) / T, axis=1)
+    ua = rng.random((B, W, D))
+    ur = rng.random((B, W))
+    outs = []
+    for wg in ("1", "3", "16"):
+        monkeypatch.setenv("VSTEP_DENSE_WG", wg)
+        say("reject_sample multi dense widths", wg)
+        g = api.reject_sample(to_dev(root), to_dev(logits), to_dev(lse), to_dev(q), to_dev(cand),
+                              to_dev(clen), to_dev(ua), to_dev(ur), T, None, accept="multi")
+        outs.append({k: tensor_np(v) for k, v in g.items()})
+    for o in outs[1:]:
+        for k in outs[0]:
+            assert np.array_equal(o[k], outs[0][k]), k
+    orc = oracle.reject_sample_multi(root, logits, q, cand, clen, ua, ur, T, None)
+    n_cmp, n_exc = compare_sampler({k: to_dev(v) for k, v in outs[0].items()}, orc, B)
+    print(f"compared {n_cmp}/{B}, excluded {n_exc}; n_acc {orc['n_acc'].tolist()}")
+    assert n_cmp >= B - 1
+    assert not (outs[0]["flags"] & 512).any()      # no wait gave up
+
+
 @pytest.mark.parametrize("mode", ["0", "1"])
 def test_reject_sample_multi_launch_modes(mode, monkeypatch):
     """Multi-candidate acceptance through both ways to reach the draw, with more

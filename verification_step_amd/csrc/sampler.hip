@@ -47,6 +47,8 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 namespace vs {
 
 namespace {
@@ -55,6 +57,7 @@ constexpr int kST = 256;              // threads per workgroup
 constexpr int kPer = 8;               // vocabulary entries per thread per chunk
 constexpr int kChunk = kST * kPer;    // 2048
 constexpr int kMaxRows = 1024;
+constexpr int kMaxCChunks = 128;      // dense multi-candidate chain: 4,096-id chunks, V <= 524,288
 
 // Acceptance codes per draft position, written by the normaliser kernel and read by
 // the sampler.
@@ -1028,6 +1031,8 @@ SampleWs sample_ws(void *ws, int B, int W, int D, int V, bool row_stats) {
   // sequence
   w.resid = (double *)(p + off);
   off += ((size_t)B * 2 * V * sizeof(double) + 255) & ~(size_t)255;
+  w.dpart = (double *)(p + off);
+  off += ((size_t)B * 2 * kMaxCChunks * sizeof(double) + 255) & ~(size_t)255;
   w.row_stats = nullptr;
   if (row_stats) {
     w.row_stats = (float2 *)(p + off);
@@ -1082,24 +1087,48 @@ hipError_t launch_lse_from_stats(const float2 *stats, int rows, int V, double *l
 // across the sibling candidates at each depth: with the current residual p' (the
 // target p of the reference row at first), sibling i is kept iff u * Q_i(x_i) <
 // p'(x_i) / sum p', and a rejection sets p' <- max(0, p' / sum p' - Q_i) over the whole
-// vocabulary.  Every step needs the residual's total, so the chain runs in one
-// workgroup of kDT threads per sequence: the residual lives in the workspace (two fp64
-// rows per sequence, written alternately), and each pass over the vocabulary goes in
-// chunks of kDT * 8 consecutive ids (thread t: ids 8t .. 8t+7 of the chunk), summed in
-// a fixed order.  The draw is the inverse CDF over ascending ids, as everywhere.
-constexpr int kDT = 1024;
-constexpr int kDPer = 8;
-constexpr int kDChunk = kDT * kDPer;
-constexpr int kMaxDChunks = 64;            // V <= 524,288
+// vocabulary.  The chain itself is serial: every rejection needs the new residual's
+// total before the next sibling is tested.
+//
+// G workgroups per sequence share the vocabulary passes: the ids are cut into chunks of
+// kCChunk (thread t of a workgroup holds ids 8t .. 8t+7 of a chunk) and workgroup c of
+// the sequence owns chunks c, c+G, c+2G, ...  Every workgroup repeats the (cheap)
+// decisions of the chain; a pass over the vocabulary (the exact total of a target row,
+// a new residual, the sums of a draw) has each workgroup sum its own chunks in a fixed
+// order and publish the chunk sums, then a barrier of the sequence's G workgroups (a
+// counter in the workspace, agent-scope release on arrival and acquire while waiting),
+// after which every workgroup adds all chunk sums in chunk order -- the same total, bit
+// for bit, everywhere.  Residual rows live in the workspace (two fp64 rows per sequence,
+// written alternately); a workgroup only ever reads back its own chunks of them.  The
+// residual at a sibling's token, which may lie in another workgroup's chunk, is
+// replayed from the target row and the removals made so far at this depth -- the same
+// operations in the same order as the pass that stored it, so the same bits.  The draw
+// is the inverse CDF over ascending ids: the chunk holding u * S is found from the
+// chunk sums by every workgroup, and its owner scans it and writes the outputs.
+//
+// The G workgroups of a sequence must be resident together: with G > 1 the kernel goes
+// out as a cooperative launch (which fails rather than oversubscribe); G = 1 needs
+// nothing.  A wait gives up after kSpinLimit polls (FLAG_SYNC_TIMEOUT), so a kernel
+// always ends.
+constexpr int kCT = 512;
+constexpr int kCPer = 8;
+constexpr int kCChunk = kCT * kCPer;     // 4,096 ids
+constexpr int kMaxCoopWg = 32;           // workgroups per sequence
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kPvCache = 1024;           // p of the candidates' tokens, kept in LDS when it fits
 
 struct DenseShared {
-  double red[kDT / 64];
-  double csum[kMaxDChunks];
+  double red[kCT / 64];
+  double csum[kMaxCChunks];              // chunk sums of the last pass, all chunks
+  double hist_s[kMaxWMulti];             // removals at this depth: the total before each
+  int hist_q[kMaxWMulti];                // and the draft row it removed
   int lens[kMaxWMulti];
   double ures[kMaxWMulti];
   int tok[kMaxRows];
   double uacc[kMaxRows];
   double rlse[kMaxRows];
+  float qx[kMaxRows];                    // Q of each candidate token at its own depth
+  double pvc[kPvCache];                  // copy of pv when (W*D+1)*W fits
   int acc[kMaxRows];
   int surv[kMaxWMulti], sib[kMaxWMulti];
   int flags, owner, tstar, y;
@@ -1107,19 +1136,22 @@ struct DenseShared {
 };
 
 struct DenseArgs {
-  int B, W, D, V;
+  int B, W, D, V, G;
   double inv_t;
   const float *root_logits, *logits, *q;
   const double *row_lse, *root_lse;
+  const double *pv;       // [B][W*D+1][W] p of every candidate's token under each row
   const int32_t *cand_tok, *cand_len, *gate;
   const double *u_acc, *u_res;
   double *resid;          // [B][2][V]
+  double *part;           // [B][2][kMaxCChunks] published chunk sums (two pass parities)
+  uint32_t *bar;          // [B] barrier counters, zero between calls
   int32_t *n_acc, *best, *out_tok, *n_out, *acc_per_cand, *flags;
   int flags_accumulate;
   int32_t *attn_flags;
 };
 
-// fixed-order block sum over kDT threads (every thread receives the total)
+// fixed-order block sum over kCT threads (every thread receives the total)
 __device__ double dense_sum(DenseShared &sh, double v) {
   const int tid = threadIdx.x;
   v = warp_sum(v);
@@ -1127,7 +1159,7 @@ __device__ double dense_sum(DenseShared &sh, double v) {
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int w = 0; w < kDT / 64; ++w) t += sh.red[w];
+  for (int w = 0; w < kCT / 64; ++w) t += sh.red[w];
   __syncthreads();
   return t;
 }
@@ -1148,68 +1180,121 @@ __device__ double dense_incl_scan(DenseShared &sh, double v) {
   return base + v;
 }
 
-__global__ void __launch_bounds__(kDT)
+// (four waves per SIMD, i.e. at most 128 VGPRs: the runtime's occupancy check for a
+// cooperative launch finds no room for a 512-thread workgroup above that)
+__global__ void __launch_bounds__(kCT, 4)
 multi_dense_kernel(DenseArgs a) {
   __shared__ DenseShared sh;
-  const int b = blockIdx.x;
+  const int c0 = blockIdx.x;          // this workgroup's place among the sequence's G
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
+  const int G = a.G;
   const int W = a.W, D = a.D, V = a.V, M = W * D;
-  const int nch = (V + kDChunk - 1) / kDChunk;
+  const int nch = (V + kCChunk - 1) / kCChunk;
   const bool open = (a.gate == nullptr) || a.gate[b] != 0;
-  for (int i = tid; i < W; i += kDT) {
+  for (int i = tid; i < W; i += kCT) {
     int ln = open ? a.cand_len[(int64_t)b * W + i] : 0;
     sh.lens[i] = ln < 0 ? 0 : (ln > D ? D : ln);
     sh.ures[i] = a.u_res[(int64_t)b * W + i];
   }
-  for (int k = tid; k < M; k += kDT) {
-    sh.tok[k] = a.cand_tok[(int64_t)b * M + k];
+  // everything the acceptance tests read, loaded at once: an accepted depth then needs
+  // no memory access (p of the tokens comes from the normaliser pass, pv, formed there
+  // with the same arithmetic as p_at below)
+  const bool pv_lds = (M + 1) * W <= kPvCache;
+  for (int k = tid; k < M; k += kCT) {
+    const int x = a.cand_tok[(int64_t)b * M + k];
+    sh.tok[k] = x;
     sh.uacc[k] = a.u_acc[(int64_t)b * M + k];
     sh.rlse[k] = a.row_lse[(int64_t)b * M + k];
+    sh.qx[k] = (x >= 0 && x < V) ? a.q[((int64_t)b * M + k) * V + x] : 1.0f;
   }
+  if (pv_lds)
+    for (int k = tid; k < (M + 1) * W; k += kCT) sh.pvc[k] = a.pv[(int64_t)b * (M + 1) * W + k];
   if (tid == 0) sh.flags = 0;
   __syncthreads();
   double *rbuf[2] = {a.resid + (int64_t)b * 2 * V, a.resid + ((int64_t)b * 2 + 1) * V};
+  uint32_t *bar = a.bar + b;
+  double *part = a.part + (int64_t)b * 2 * kMaxCChunks;
+  int n_bar = 0, par = 0;
+
+  // barrier of the sequence's G workgroups, then every workgroup reads all chunk sums
+  // of the pass (published in parity `par`) into LDS and returns their total
+  auto sync_sums = [&]() -> double {
+    __syncthreads();
+    ++n_bar;
+    if (tid < 64) {
+      if (tid == 0) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t target = (uint32_t)n_bar * (uint32_t)G;
+      // poll with plain atomic loads, then one acquire (an acquiring load in the loop
+      // would invalidate this XCD's L2 on every poll, under the other workgroups' feet)
+      int spins = 0;
+      while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          if (tid == 0) atomicOr(&sh.flags, FLAG_SYNC_TIMEOUT);
+          break;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      for (int c = tid; c < nch; c += 64)
+        sh.csum[c] = __hip_atomic_load(part + par * kMaxCChunks + c, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    double S = 0.0;
+    for (int c = 0; c < nch; ++c) S += sh.csum[c];
+    par ^= 1;
+    return S;
+  };
+  auto publish = [&](int c, double v) {
+    if (tid == 0)
+      __hip_atomic_store(part + par * kMaxCChunks + c, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
 
   // the distribution a pass reads: p of row prow (kind 0), or the residual in rbuf[cur]
-  // (kind 1); lse of that row
+  // (kind 1, this workgroup's chunks only); lse of that row
   const float *zrow = nullptr;
   double lse = 0.0;
   int kind = 0, cur = 0;
+  auto p_at = [&](int k) -> double { return exp((double)zrow[k] * a.inv_t - lse); };
   auto weight = [&](int k) -> double {
     if (k >= V) return 0.0;
-    if (kind == 0) return exp((double)zrow[k] * a.inv_t - lse);
+    if (kind == 0) return p_at(k);
     return rbuf[cur][k];
-  };
-  // total of the current distribution over the vocabulary (fixed order)
-  auto total = [&]() -> double {
-    double t = 0.0;
-    for (int c = 0; c < nch; ++c) {
-      double v = 0.0;
-      const int k0 = c * kDChunk + tid * kDPer;
-#pragma unroll
-      for (int j = 0; j < kDPer; ++j) v += weight(k0 + j);
-      t += dense_sum(sh, v);
-    }
-    return t;
   };
   auto set_row = [&](int prow) {
     kind = 0;
     zrow = prow < 0 ? a.root_logits + (int64_t)b * V : a.logits + ((int64_t)b * M + prow) * V;
     lse = prow < 0 ? a.root_lse[b] : sh.rlse[prow];
   };
-  // inverse-CDF draw from the current distribution with uniform u (ties flagged)
-  auto draw = [&](double u) -> int {
-    for (int c = 0; c < nch; ++c) {
+  // chunk sums of the current distribution (this workgroup's chunks), then everyone's
+  auto sum_pass = [&]() -> double {
+    for (int c = c0; c < nch; c += G) {
+      const int k0 = c * kCChunk + tid * kCPer;
       double v = 0.0;
-      const int k0 = c * kDChunk + tid * kDPer;
 #pragma unroll
-      for (int j = 0; j < kDPer; ++j) v += weight(k0 + j);
-      v = dense_sum(sh, v);
-      if (tid == 0) sh.csum[c] = v;
+      for (int j = 0; j < kCPer; ++j) v += weight(k0 + j);
+      publish(c, dense_sum(sh, v));
     }
-    __syncthreads();
-    double S = 0.0;
-    for (int c = 0; c < nch; ++c) S += sh.csum[c];
+    return sync_sums();
+  };
+  // the current distribution at candidate j's token x, whichever workgroup owns it: the
+  // target row's p(x) followed by this depth's removals, as the passes that stored them
+  // computed it
+  int n_hist = 0, pvrow = M;
+  auto value_at = [&](int j0, int x) -> double {
+    const int idx = pvrow * W + j0;
+    double w = pv_lds ? sh.pvc[idx] : a.pv[(int64_t)b * (M + 1) * W + idx];
+    for (int j = 0; j < n_hist; ++j) {
+      const float *qr = a.q + ((int64_t)b * M + sh.hist_q[j]) * V;
+      w = fmax(0.0, w / sh.hist_s[j] - (double)qr[x]);
+    }
+    return w;
+  };
+  // inverse-CDF draw with uniform u from the distribution whose chunk sums are in
+  // sh.csum (total S); only the owner of the chunk holding u*S finds the token
+  auto draw = [&](double u, double S) -> int {
     const double xs = u * S;
     if (tid == 0) {
       // the chunk holding u*S (the last chunk with weight if rounding leaves u*S past)
@@ -1228,12 +1313,14 @@ multi_dense_kernel(DenseArgs a) {
       sh.owner = own;
       sh.excl = run;
       sh.tstar = INT_MAX;
+      sh.y = -1;
     }
     __syncthreads();
-    const int k0 = sh.owner * kDChunk + tid * kDPer;
-    double w[kDPer], tv = 0.0;
+    if (sh.owner % G != c0) return -1;
+    const int k0 = sh.owner * kCChunk + tid * kCPer;
+    double w[kCPer], tv = 0.0;
 #pragma unroll
-    for (int j = 0; j < kDPer; ++j) {
+    for (int j = 0; j < kCPer; ++j) {
       w[j] = weight(k0 + j);
       tv += w[j];
     }
@@ -1245,7 +1332,7 @@ multi_dense_kernel(DenseArgs a) {
       int yy = -1, last_w = -1;
       double run = texcl, lo = 0.0, hi = 0.0;
       if (sh.tstar != INT_MAX) {
-        for (int j = 0; j < kDPer; ++j) {
+        for (int j = 0; j < kCPer; ++j) {
           if (w[j] <= 0.0) continue;
           last_w = k0 + j;
           if (run + w[j] > xs) {
@@ -1283,12 +1370,14 @@ multi_dense_kernel(DenseArgs a) {
   int depth = 0, y = -1, best = -1;
   if (ns == 0) {
     set_row(-1);
-    y = draw(sh.ures[0]);
+    y = draw(sh.ures[0], sum_pass());
     if (tid == 0) atomicOr(&sh.flags, FLAG_NO_CANDIDATE);
   } else {
     while (true) {
       const int ref = sh.surv[0];
       set_row(depth == 0 ? -1 : ref * D + depth - 1);
+      pvrow = depth == 0 ? M : ref * D + depth - 1;
+      n_hist = 0;
       int nsib = 0;
       for (int k = 0; k < ns; ++k)
         if (sh.lens[sh.surv[k]] > depth) {
@@ -1297,7 +1386,7 @@ multi_dense_kernel(DenseArgs a) {
         }
       __syncthreads();
       if (nsib == 0) {
-        y = draw(sh.ures[ref]);
+        y = draw(sh.ures[ref], sum_pass());
         break;
       }
       // a target row sums to one up to the rounding of its lse, which moves p' by about
@@ -1305,15 +1394,17 @@ multi_dense_kernel(DenseArgs a) {
       // its exact total is taken only before the first rejection builds a residual
       double S = 1.0;
       bool exact = false;
+      bool sums_valid = false;   // sh.csum holds the current distribution's chunk sums
       int accepted = -1, last = sh.sib[0];
       for (int k = 0; k < nsib; ++k) {
         const int i = sh.sib[k];
         last = i;
         const int x = sh.tok[i * D + depth];
-        const float *qrow = a.q + ((int64_t)b * M + i * D + depth) * V;
+        const int qr = i * D + depth;
+        const float *qrow = a.q + ((int64_t)b * M + qr) * V;
         const bool valid = x >= 0 && x < V;
-        const double pp = valid ? weight(x) / S : 0.0;
-        const double Qx = valid ? (double)qrow[x] : 1.0;
+        const double pp = valid ? value_at(i, x) / S : 0.0;
+        const double Qx = valid ? (double)sh.qx[qr] : 1.0;
         const double lhs = sh.uacc[i * D + depth] * Qx;
         if (tid == 0) {
           int f = 0;
@@ -1327,39 +1418,57 @@ multi_dense_kernel(DenseArgs a) {
         }
         // rejected: p' <- max(0, p' / S - Q_i) into the residual row not being read
         if (!exact) {
-          S = total();
+          S = sum_pass();
           exact = true;
         }
         const int nxt = (kind == 1) ? (cur ^ 1) : 0;
         double *dst = rbuf[nxt];
-        double part = 0.0;
-        for (int c = 0; c < nch; ++c) {
-          const int k0 = c * kDChunk + tid * kDPer;
-          double v = 0.0;
-          if (k0 < V) {
+        for (int c = c0; c < nch; c += G) {
+          const int k0 = c * kCChunk + tid * kCPer;
+          // all loads first: the stores below may alias them as far as the compiler
+          // knows, and would otherwise serialise every load behind the previous store
+          double wv[kCPer];
+          float qv[kCPer];
 #pragma unroll
-            for (int j = 0; j < kDPer; ++j) {
-              const int kk = k0 + j;
-              if (kk < V) {
-                const double r = fmax(0.0, weight(kk) / S - (double)qrow[kk]);
-                dst[kk] = r;
-                v += r;
-              }
+          for (int j = 0; j < kCPer; ++j) {
+            const int kk = k0 + j;
+            wv[j] = weight(kk);
+            qv[j] = kk < V ? qrow[kk] : 0.0f;
+          }
+          double v = 0.0;
+#pragma unroll
+          for (int j = 0; j < kCPer; ++j) {
+            const int kk = k0 + j;
+            if (kk < V) {
+              const double r = fmax(0.0, wv[j] / S - (double)qv[j]);
+              dst[kk] = r;
+              v += r;
             }
           }
-          part += dense_sum(sh, v);
+          publish(c, dense_sum(sh, v));
         }
-        if (part > 0.0) {
+        const double part_s = sync_sums();
+        if (part_s > 0.0) {
+          if (tid == 0) {
+            sh.hist_s[n_hist] = S;
+            sh.hist_q[n_hist] = qr;
+          }
+          ++n_hist;
           cur = nxt;
           kind = 1;
-          S = part;   // exact: summed in the same pass that wrote the row
-        } else if (tid == 0) {
-          atomicOr(&sh.flags, FLAG_DEGENERATE);   // no mass left: p' is kept
+          S = part_s;   // exact: summed in the pass that wrote the row
+          sums_valid = true;
+        } else {
+          if (tid == 0) atomicOr(&sh.flags, FLAG_DEGENERATE);   // no mass left: p' is kept
+          sums_valid = false;
         }
-        __syncthreads();   // the new residual row is complete before it is read
+        __syncthreads();   // the row and the history are complete before they are read
       }
       if (accepted < 0) {
-        y = draw(sh.ures[last]);
+        // every sibling rejected: draw from p' (its chunk sums are the last pass's
+        // unless that removal was skipped)
+        const double Sd = sums_valid ? S : sum_pass();
+        y = draw(sh.ures[last], Sd);
         break;
       }
       if (tid == 0) {
@@ -1376,29 +1485,74 @@ multi_dense_kernel(DenseArgs a) {
     }
     best = sh.surv[0];
   }
-  // ---- outputs
-  int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
-  for (int o = tid; o <= D; o += kDT) ot[o] = (o < depth) ? sh.acc[o] : (o == depth ? y : -1);
-  for (int i = tid; i < W; i += kDT) {
-    int k = 0;
-    const int lim = min(sh.lens[i], depth);
-    while (k < lim && sh.tok[i * D + k] == sh.acc[k]) ++k;
-    a.acc_per_cand[(int64_t)b * W + i] = k;
+  // ---- outputs, from the workgroup that drew the token
+  if (y >= 0) {
+    int32_t *ot = a.out_tok + (int64_t)b * (D + 1);
+    for (int o = tid; o <= D; o += kCT) ot[o] = (o < depth) ? sh.acc[o] : (o == depth ? y : -1);
+    for (int i = tid; i < W; i += kCT) {
+      int k = 0;
+      const int lim = min(sh.lens[i], depth);
+      while (k < lim && sh.tok[i * D + k] == sh.acc[k]) ++k;
+      a.acc_per_cand[(int64_t)b * W + i] = k;
+    }
+    if (tid == 0) {
+      a.n_acc[b] = depth;
+      a.best[b] = best;
+      a.n_out[b] = depth + 1;
+      int f = sh.flags;
+      if (a.attn_flags) {
+        f |= a.attn_flags[b];
+        a.attn_flags[b] = 0;
+      }
+      if (a.flags) {
+        if (a.flags_accumulate) atomicOr(&a.flags[b], f);
+        else a.flags[b] = f;
+      }
+    }
   }
+  // the last workgroup of the sequence to leave puts the counter back to zero
   if (tid == 0) {
-    a.n_acc[b] = depth;
-    a.best[b] = best;
-    a.n_out[b] = depth + 1;
-    int f = sh.flags;
-    if (a.attn_flags) {
-      f |= a.attn_flags[b];
-      a.attn_flags[b] = 0;
-    }
-    if (a.flags) {
-      if (a.flags_accumulate) atomicOr(&a.flags[b], f);
-      else a.flags[b] = f;
+    const uint32_t old = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)(n_bar + 1) * (uint32_t)G - 1u)
+      __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Workgroups per sequence for the dense multi-candidate chain: up to kMaxCoopWg, no more
+// than the vocabulary has chunks, and all B*G of them resident at once (the device's
+// cooperative-launch support and the kernel's occupancy, looked up once per device).
+// VSTEP_DENSE_WG=n caps it (1: one workgroup per sequence, a plain launch).
+int dense_width(int B, int nch) {
+  static std::mutex mu;
+  static int cap[64], coop[64];
+  static bool known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+      int cus = 0, per_cu = 0, c = 0;
+      if (hipDeviceGetAttribute(&c, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) c = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, multi_dense_kernel, kCT, 0) !=
+          hipSuccess)
+        per_cu = 0;
+      cap[dev] = cus * per_cu;
+      coop[dev] = c;
+      known[dev] = true;
     }
   }
+  int g = kMaxCoopWg;
+  if (const char *e = getenv("VSTEP_DENSE_WG")) {
+    const int v = atoi(e);
+    if (v >= 1 && v < g) g = v;
+  }
+  g = g < nch ? g : nch;
+  if (!coop[dev] || B <= 0) return 1;
+  const int fit = cap[dev] / B;
+  g = g < fit ? g : fit;
+  return g < 1 ? 1 : g;
 }
 
 hipError_t launch_lse_tests(int B, int W, int D, int V, float temperature,
@@ -1488,8 +1642,8 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
     return hipGetLastError();
   }
   if (multi && q != nullptr) {
-    // dense drafts: the residual chain over the whole vocabulary, one workgroup per
-    // sequence
+    // dense drafts: the residual chain over the whole vocabulary, G workgroups per
+    // sequence (a cooperative launch when G > 1)
     DenseArgs d{};
     d.B = B;
     d.W = W;
@@ -1501,12 +1655,15 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
     d.q = q;
     d.row_lse = row_lse;
     d.root_lse = ws.root_lse;
+    d.pv = ws.pv;
     d.cand_tok = cand_tok;
     d.cand_len = cand_len;
     d.gate = gate;
     d.u_acc = u_acc;
     d.u_res = u_res;
     d.resid = ws.resid;
+    d.part = ws.dpart;
+    d.bar = ws.counters;
     d.n_acc = n_acc;
     d.best = best;
     d.out_tok = out_tok;
@@ -1515,7 +1672,19 @@ hipError_t launch_sampler(int B, int W, int D, int V, float temperature, const f
     d.flags = flags;
     d.flags_accumulate = flags_accumulate;
     d.attn_flags = attn_flags;
-    hipLaunchKernelGGL(multi_dense_kernel, dim3(B), dim3(kDT), 0, st, d);
+    d.G = dense_width(B, (V + kCChunk - 1) / kCChunk);
+    if (d.G == 1) {
+      hipLaunchKernelGGL(multi_dense_kernel, dim3(1, B), dim3(kCT), 0, st, d);
+      return hipGetLastError();
+    }
+    void *args[] = {&d};
+    if (hipLaunchCooperativeKernel((const void *)multi_dense_kernel, dim3(d.G, B), dim3(kCT), args,
+                                   0, st) == hipSuccess)
+      return hipSuccess;
+    // refused (the grid would not be resident at once): one workgroup per sequence
+    (void)hipGetLastError();
+    d.G = 1;
+    hipLaunchKernelGGL(multi_dense_kernel, dim3(1, B), dim3(kCT), 0, st, d);
     return hipGetLastError();
   }
   if (multi) {

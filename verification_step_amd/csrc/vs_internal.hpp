@@ -20,7 +20,7 @@ constexpr int kHeadVocabTile = 256;
 enum : int {
   FLAG_PROBE_TIE = 1, FLAG_ACCEPT_TIE = 2, FLAG_CDF_TIE = 4, FLAG_DEGENERATE = 8,
   FLAG_NO_CANDIDATE = 16, FLAG_BAD_PAGE = 32, FLAG_BAD_CTX = 64, FLAG_BAD_TOKEN = 128,
-  FLAG_POOL_EMPTY = 256
+  FLAG_POOL_EMPTY = 256, FLAG_SYNC_TIMEOUT = 512
 };
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
@@ -158,6 +158,7 @@ struct SampleWs {
   int32_t *amax;        // [B*W*D + B] greedy: argmax of every verify row, then the root rows
   uint8_t *amax_tie;    // [B*W*D + B] greedy: near tie between the two largest logits
   double *resid;        // [B][2][V] multi-candidate acceptance with dense drafts: residual rows
+  double *dpart;        // [B][2][128] and its published chunk sums
   float2 *row_stats;    // [B*W*D][n_vt] tile statistics of given logits (greedy, standalone)
   size_t bytes;
 };

@@ -223,8 +223,10 @@ int vs_lm_head(const vs_head_desc *desc, const void *h, const void *w_full,
  * u_res[b, ref].  Outputs as above with best = the final reference candidate and
  * acc_per_cand[b,i] = the length of candidate i's common prefix with the accepted
  * tokens.  At most 64 candidates (else VS_ERR_UNSUPPORTED).  Copy drafts also need
- * (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); dense drafts with W > 1 run
- * one workgroup per sequence over fp64 residual rows kept in the workspace.  With
+ * (W*D+1)*W + W*D <= 4096 (else VS_ERR_UNSUPPORTED); dense drafts with W > 1 keep
+ * fp64 residual rows in the workspace and share each sequence's vocabulary passes
+ * among up to 32 workgroups of a cooperative launch (one workgroup per sequence when
+ * the device or the grid does not allow one; the results are the same bits).  With
  * W == 1 the rule is the single-chain rule above, which is what runs.
  *
  * accept_mode VS_ACCEPT_GREEDY: greedy verification, the temperature -> 0 limit of

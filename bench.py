@@ -130,10 +130,11 @@ def cpu_baseline(case, shape, min_seconds=10.0, accept="longest"):
 
 def measure_peaks(lib, dev):
     """What this GPU sustains, timed with HIP events on the current stream: a 1 GiB
-    read stream (16-byte vector loads, eight in flight per thread, over 1,024, 4,096 and
-    16,384 workgroups) and back-to-back MFMA 32x32x16 bf16 products on register operands
-    (two workgroups of four waves per CU).  Best of five launches each, after two
-    warm-ups."""
+    read stream (16-byte vector loads, eight in flight per thread; grid-strided over
+    1,024, 4,096 and 16,384 workgroups, and one contiguous slice per workgroup over 1, 2,
+    4 and 8 workgroups per CU) and back-to-back MFMA 32x32x16 bf16 products on register
+    operands (two workgroups of four waves per CU).  Best of five launches each, after
+    two warm-ups; the read ceiling is the best pattern."""
     import ctypes as C
     import torch
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -157,22 +158,27 @@ def measure_peaks(lib, dev):
             times.append(e0.elapsed_time(e1) * 1e-3)
         return min(times)
 
-    def rd(n_wg):
+    def rd(n_wg, pattern):
         def go():
             assert lib.vs_measure_read(C.c_void_p(buf.data_ptr()), nbytes,
-                                       C.c_void_p(sink.data_ptr()), n_wg, stream) == 0
+                                       C.c_void_p(sink.data_ptr()), n_wg, pattern, stream) == 0
         return go
 
     def mm():
         assert lib.vs_measure_mfma(n_wg_mfma, iters, C.c_void_p(fsink.data_ptr()), stream) == 0
 
-    t_rd = min(best(rd(n)) for n in (1024, 4096, 16384))
+    t_strided = min(best(rd(n, 0)) for n in (1024, 4096, 16384))
+    t_slices = min(best(rd(n, 1)) for n in (n_cu, 2 * n_cu, 4 * n_cu, 8 * n_cu))
+    t_rd = min(t_strided, t_slices)
     t_mm = best(mm)
     flops = n_wg_mfma * 4 * iters * 8 * 32768.0
     del buf
     return {"read_stream_GBs": nbytes / t_rd / 1e9, "mfma_bf16_TFLOPs": flops / t_mm / 1e12,
-            "how": "1 GiB read once per launch (1,024 / 4,096 / 16,384 workgroups, 16-byte "
-                   "loads, eight in flight per thread); %d "
+            "read_grid_strided_GBs": nbytes / t_strided / 1e9,
+            "read_slice_per_workgroup_GBs": nbytes / t_slices / 1e9,
+            "how": "1 GiB read once per launch, 16-byte loads, eight in flight per thread, "
+                   "grid-strided (1,024 / 4,096 / 16,384 workgroups) or one contiguous slice "
+                   "per workgroup (1 / 2 / 4 / 8 per CU), the faster pattern; %d "
                    "workgroups x 4 waves x %d x 8 independent MFMA 32x32x16 bf16; best of 5 "
                    "event-timed launches" % (n_wg_mfma, iters), "cus": n_cu}
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VS_ABI_VERSION 4
+#define VS_ABI_VERSION 5
 
 typedef enum {
     VS_OK = 0,

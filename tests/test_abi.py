@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.vs_abi_version() == 4
+    assert lib.vs_abi_version() == 5
     assert lib.vs_status_str(0) == b"ok"
     assert b"workspace" in lib.vs_status_str(-3)
     assert lib.vs_status_str(99) == b"unknown status"
@@ -366,3 +366,14 @@ def test_binding_rejects_inconsistent_shapes(lib):
         api.head_weight_sizes(lib, True, 4096, 7, 0, packed, None, None)
     with pytest.raises(ValueError):
         api._expect(m(3, 4), (3, 5), "x")
+
+
+def test_measure_validation(lib):
+    fake = C.c_void_p(16)
+    assert lib.vs_measure_read(None, 1 << 20, fake, 64, 0, None) == -1
+    assert lib.vs_measure_read(fake, 8, fake, 64, 0, None) == -1          # under 16 bytes
+    assert lib.vs_measure_read(fake, 1 << 20, fake, 0, 0, None) == -1     # no workgroups
+    assert lib.vs_measure_read(fake, 1 << 20, fake, 64, 2, None) == -1    # no such pattern
+    assert lib.vs_measure_read(fake, 64, fake, 64, 1, None) == -1         # slices under 16 B
+    assert lib.vs_measure_mfma(0, 10, fake, None) == -1
+    assert lib.vs_measure_mfma(4, 0, fake, None) == -1

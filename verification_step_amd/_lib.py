@@ -40,7 +40,7 @@ EXPORTED = [
 
 P = C.c_void_p
 I32 = C.c_int32
-ABI_VERSION = 4      # VS_ABI_VERSION of the descriptor layouts below
+ABI_VERSION = 5      # VS_ABI_VERSION of the descriptor layouts below
 
 
 class AttnDesc(C.Structure):
@@ -136,7 +136,7 @@ def load(path: str = LIB_PATH):
     lib.vs_draft_sample_workspace_bytes.restype = C.c_size_t
     lib.vs_draft_sample_workspace_bytes.argtypes = [C.c_int, C.c_int]
     lib.vs_draft_sample.argtypes = [P, C.c_int, C.c_int, P, P, P, P, C.c_size_t, P]
-    lib.vs_measure_read.argtypes = [P, C.c_size_t, P, C.c_int, P]
+    lib.vs_measure_read.argtypes = [P, C.c_size_t, P, C.c_int, C.c_int, P]
     lib.vs_measure_mfma.argtypes = [C.c_int, C.c_int, P, P]
     for fn in EXPORTED:
         if fn not in ("vs_abi_version", "vs_status_str") and not fn.endswith("_bytes"):

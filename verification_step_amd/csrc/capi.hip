@@ -504,9 +504,12 @@ int vs_kv_commit(const vs_kv_desc *d, const void *k_cand, const void *v_cand, co
                                          S(stream), layers_of(d->n_layers)));
 }
 
-int vs_measure_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg, void *stream) {
-  if (!buf || !sink || bytes < 16 || n_wg <= 0) return VS_ERR_INVALID_ARG;
-  return hip_status(vs::launch_peak_read(buf, bytes, sink, n_wg, S(stream)));
+int vs_measure_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg, int pattern,
+                    void *stream) {
+  if (!buf || !sink || bytes < 16 || n_wg <= 0 || (pattern != 0 && pattern != 1))
+    return VS_ERR_INVALID_ARG;
+  if (pattern == 1 && bytes / 16 < (size_t)n_wg) return VS_ERR_INVALID_ARG;
+  return hip_status(vs::launch_peak_read(buf, bytes, sink, n_wg, pattern, S(stream)));
 }
 
 int vs_measure_mfma(int n_wg, int iters, float *sink, void *stream) {

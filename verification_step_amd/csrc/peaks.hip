@@ -1,7 +1,8 @@
 // Ceilings measured on the running GPU, so that kernel fractions can be stated against
 // what the part sustains as well as against its datasheet peaks:
 //   * read stream: every byte of a buffer read once with 16-byte vector loads, eight
-//     in flight per thread (no writes beyond one word per workgroup), grid-strided;
+//     in flight per thread (no writes beyond one word per workgroup), grid-strided or
+//     one contiguous slice per workgroup;
 //   * matrix rate: back-to-back MFMA 32x32x16 bf16 products on register operands, eight
 //     independent accumulators per wave, no memory traffic.
 // Neither is part of the verify step; they exist for its measurement.
@@ -29,6 +30,30 @@ peak_read_kernel(const u32x4 *buf, size_t n16, uint32_t *sink) {
   }
   for (; i < n16; i += stride) {
     const u32x4 a = __builtin_nontemporal_load(buf + i);
+    acc ^= a[0] ^ a[3];
+  }
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) atomicXor(&sink[blockIdx.x & 1023], acc);
+}
+
+// one contiguous slice per workgroup, read front to back (4 KB per step, eight steps
+// in flight)
+__global__ void __launch_bounds__(256)
+peak_read_slice_kernel(const u32x4 *buf, size_t n16, uint32_t *sink) {
+  const size_t per = n16 / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = (blockIdx.x + 1 == gridDim.x) ? n16 : lo + per;
+  uint32_t acc = 0;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = buf[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][u & 3];
+  }
+  for (; i < hi; i += 256) {
+    const u32x4 a = buf[i];
     acc ^= a[0] ^ a[3];
   }
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
@@ -64,9 +89,13 @@ peak_mfma_kernel(int iters, float *sink) {
 }  // namespace
 
 hipError_t launch_peak_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(peak_read_kernel, dim3(n_wg), dim3(256), 0, st, (const u32x4 *)buf,
-                     bytes / 16, sink);
+                            int pattern, hipStream_t st) {
+  if (pattern == 1)
+    hipLaunchKernelGGL(peak_read_slice_kernel, dim3(n_wg), dim3(256), 0, st,
+                       (const u32x4 *)buf, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(peak_read_kernel, dim3(n_wg), dim3(256), 0, st, (const u32x4 *)buf,
+                       bytes / 16, sink);
   return hipGetLastError();
 }
 

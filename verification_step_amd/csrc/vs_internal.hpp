@@ -211,7 +211,7 @@ hipError_t launch_copy_labels(const int32_t *ctx, int64_t total, const int32_t *
 
 // ---- measured ceilings (peaks.hip)
 hipError_t launch_peak_read(const void *buf, size_t bytes, uint32_t *sink, int n_wg,
-                            hipStream_t st);
+                            int pattern, hipStream_t st);
 hipError_t launch_peak_mfma(int n_wg, int iters, float *sink, hipStream_t st);
 
 // ---- KV commit and rollback (kv.hip)

@@ -252,6 +252,15 @@ def test_step_validation(lib):
     assert lib.vs_verify_step(C.byref(d4), C.byref(io), fake, 16, None) == -3
     d5 = L.StepDesc(**{**base, "accept_mode": 7})
     assert lib.vs_step_workspace_bytes(C.byref(d5)) == 0
+    # layers: negative is invalid, beyond 1,024 unsupported; 0 and 1 are one layer
+    assert lib.vs_step_workspace_bytes(C.byref(L.StepDesc(**{**base, "n_layers": -2}))) == 0
+    assert lib.vs_verify_step(C.byref(L.StepDesc(**{**base, "n_layers": -2})), C.byref(io), fake,
+                              1 << 40, None) == -1
+    assert lib.vs_verify_step(C.byref(L.StepDesc(**{**base, "n_layers": 2000})), C.byref(io), fake,
+                              1 << 40, None) == -2
+    one = lib.vs_step_workspace_bytes(C.byref(L.StepDesc(**{**base, "n_layers": 1})))
+    assert one == lib.vs_step_workspace_bytes(C.byref(d))
+    assert lib.vs_step_workspace_bytes(C.byref(L.StepDesc(**{**base, "n_layers": 32}))) > 0
 
 
 def test_step_noalloc_validation(lib):
@@ -285,6 +294,9 @@ def test_kv_validation(lib):
 
     def commit(desc, a=args, nbytes=1 << 20):
         return lib.vs_kv_commit(C.byref(desc), *a, fake, nbytes, None)
+
+    assert commit(L.KvDesc(**{**ok, "n_layers": -1})) == -1
+    assert commit(L.KvDesc(**{**ok, "n_layers": 70000})) == -2
 
     assert commit(L.KvDesc(**{**ok, "page_size": 8})) == -2
     assert commit(L.KvDesc(**{**ok, "B": 0})) == -1

@@ -17,12 +17,18 @@ def _inputs(case):
     return case_to_dev(case, keys)
 
 
-def _pair(api, case, accept="longest"):
+def _pair(api, case, accept="longest", layers=1):
     sh = case.shape
     I = _inputs(case)
+    if layers > 1:
+        from gpu_util import to_dev
+        for k, v in wl.layer_inputs(case, layers, 404).items():
+            I[k] = to_dev(v, bf16=sh.dtype == "bf16")
+    dense = accept == "multi_dense"
+    accept = "multi" if dense else accept
     kw = dict(B=sh.B, W=sh.W, D=sh.D, Hq=sh.Hq, Hkv=sh.Hkv, hd=sh.hd, V=sh.V, tau=sh.tau,
               temperature=sh.temperature, kappa=sh.kappa, accept=accept)
-    if accept == "multi":
+    if accept == "multi" and not dense:
         I["q_draft"] = None
     ref = api.VerifyStep(I, **kw)
     na = api.VerifyStep(I, noalloc=True, **kw)
@@ -44,11 +50,12 @@ def test_noalloc_matches_workspace_entry_point():
     big = wl.make_case(wl.Shape(name="small", dtype="bf16", B=3, W=3, D=7, Hq=8, Hkv=2, hd=128,
                                 d=1024, V=1000, P=(300, 777, 64), paged_random=True), 11)
     small = wl.make_case(wl.config(1), 1000)          # fp32, one sequence
-    cases = [("bf16 B=3", big, "longest"), ("fp32 tiny", small, "longest"),
-             ("bf16 B=3 multi", big, "multi"), ("fp32 tiny", small, "longest")]
-    for name, case, accept in cases:
-        say("noalloc vs workspace step:", name, accept)
-        ref, na = _pair(api, case, accept)
+    cases = [("bf16 B=3", big, "longest", 1), ("fp32 tiny", small, "longest", 1),
+             ("bf16 B=3 multi", big, "multi", 1), ("bf16 B=3 multi, dense drafts", big, "multi_dense", 1),
+             ("bf16 B=3, 3 layers", big, "longest", 3), ("fp32 tiny", small, "longest", 1)]
+    for name, case, accept, layers in cases:
+        say("noalloc vs workspace step:", name, accept, layers)
+        ref, na = _pair(api, case, accept, layers)
         r = {k: tensor_np(v).copy() for k, v in ref().items()}
         torch.cuda.synchronize()
         g = na()

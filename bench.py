@@ -183,6 +183,51 @@ def measure_peaks(lib, dev):
                    "event-timed launches" % (n_wg_mfma, iters), "cus": n_cu}
 
 
+def vendor_gemm_reference(api, dev, reps=20):
+    """The head's product beside the vendor GEMM on the same shapes: this library's
+    bound LM head (bf16 GEMM, fp32 logits, tile statistics and the row normalisers)
+    against torch.mm with an fp32 output (bf16 operands; hipBLASLt on ROCm), which
+    computes the product alone.  Two weight copies alternate so that the Infinity
+    Cache does not serve the weight; mean of `reps` event-timed calls after warm-up."""
+    import torch
+    out = []
+    V = 128256
+    for name, M, K in (("slimspec verify head", 7, 4096), ("llama8b", 80, 4096),
+                       ("llama70b", 160, 8192), ("ragged", 1024, 4096)):
+        g = torch.Generator(device=dev).manual_seed(M)
+        h = (torch.randn(M, K, device=dev, generator=g) * 0.05).to(torch.bfloat16)
+        Ws = [(torch.randn(V, K, device=dev, generator=g) / K ** 0.5).to(torch.bfloat16)
+              for _ in range(2)]
+        heads = [api.LmHead(h, w_full=w) for w in Ws]
+        Wt = [w.t() for w in Ws]
+
+        def timed(fn):
+            for i in range(4):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1000.0 / reps
+
+        ours = timed(lambda i: heads[i % 2]())
+        vendor = timed(lambda i: torch.mm(h, Wt[i % 2], out_dtype=torch.float32))
+        flops = 2.0 * M * K * V
+        out.append({"shape": name, "M": M, "K": K, "V": V, "ours_us": ours,
+                    "vendor_us": vendor, "ours_TFLOPs": flops / ours / 1e6,
+                    "vendor_TFLOPs": flops / vendor / 1e6})
+        del heads, Ws, Wt
+        torch.cuda.empty_cache()
+    return {"vendor_gemm_reference": out,
+            "how": "ours: vs_lm_head (GEMM + fp32 logits + tile statistics + normalisers); "
+                   "vendor: torch.mm(h, W^T, out_dtype=float32), the product only; "
+                   "bf16 operands, two weight copies alternating, mean of %d event-timed "
+                   "calls" % reps}
+
+
 def host_info():
     """The host the oracle baseline runs on: CPU model, cores the process may use,
     os.cpu_count() and the BLAS thread count."""
@@ -399,6 +444,8 @@ def main():
                     help="only run N plain copies of 1 GiB (counter calibration) and exit")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the read-stream and MFMA ceilings measured on this GPU")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the LM head beside the vendor GEMM on the four head shapes")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print a markdown summary (mean, median, p10, p90) of a rocprofv3 "
                          "kernel trace and exit (no GPU needed)")
@@ -434,6 +481,10 @@ def main():
 
     if args.labels:
         run_labels(args, api, wl, dev)
+        return
+
+    if args.vendor_gemm:
+        print(json.dumps(vendor_gemm_reference(api, dev)))
         return
 
     peaks = None if args.no_peaks else measure_peaks(_lib.load(), dev)

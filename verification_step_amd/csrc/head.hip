@@ -326,6 +326,18 @@ head_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[v][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the root row this wave folds into the tile statistics, loaded before the K loop (at
+  // most one root row per wave, and only where the accumulators leave registers free):
+  // the epilogue then waits on no load
+  constexpr bool kRootPre = MT * VT <= 24;
+  const bool root_pre = kRootPre && a.root != nullptr && mb == 0 && tile_ok && a.B_root <= kWPT;
+  float rx[kHeadVocabTile / 64];
+#pragma unroll
+  for (int j = 0; j < kHeadVocabTile / 64; ++j) {
+    const int k = vt * kHeadVocabTile + j * 64 + lane;
+    rx[j] = (root_pre && wq < a.B_root && k < a.N) ? a.root[(int64_t)wq * a.N + k] * a.inv_t : -INFINITY;
+  }
+
   issue_h(0, 0);
 #pragma unroll
   for (int p = 0; p < kPDL; ++p) load_w(p, p);
@@ -398,7 +410,10 @@ head_lds_kernel(GemmArgs a) {
         if (n0 + j < a.N) vmax = fmaxf(vmax, acc[v][mt][j] * a.inv_t);
     }
     if (staged) {
-      __syncthreads();
+      // each wave reads back only its own fragment: a wave-level sync suffices
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       constexpr int kLPR = 4 * VT;     // lanes per fragment row, 4 floats each
       constexpr int kRPI = 64 / kLPR;  // fragment rows per store instruction
 #pragma unroll
@@ -418,7 +433,9 @@ head_lds_kernel(GemmArgs a) {
           }
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     if (a.stats == nullptr) continue;
     vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
@@ -444,7 +461,7 @@ head_lds_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < kHeadVocabTile / 64; ++j) {
         const int k = vt * kHeadVocabTile + j * 64 + lane;
-        x[j] = (k < a.N) ? row[k] * a.inv_t : -INFINITY;
+        x[j] = root_pre ? rx[j] : ((k < a.N) ? row[k] * a.inv_t : -INFINITY);
         mx = fmaxf(mx, x[j]);
       }
       for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));

@@ -119,6 +119,27 @@ __device__ double lse_of_stats(const float2 *st, int n_vt, double *red) {
   return mx + log((red[0] + red[1]) + (red[2] + red[3]));
 }
 
+// lse_of_stats for n_vt <= 512 from the two entries t = tid and t = tid + 256 a thread
+// reads there, loaded beforehand by the caller: the same operations in the same order
+__device__ double lse_of_stats2(float2 a0, float2 a1, int n_vt, double *red) {
+  const int tid = threadIdx.x;
+  double mx = -INFINITY;
+  if (tid < n_vt) mx = fmax(mx, (double)a0.x);
+  if (tid + 256 < n_vt) mx = fmax(mx, (double)a1.x);
+  mx = warp_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  __syncthreads();
+  double sm = 0.0;
+  if (tid < n_vt && a0.x != -INFINITY) sm += (double)a0.y * exp((double)a0.x - mx);
+  if (tid + 256 < n_vt && a1.x != -INFINITY) sm += (double)a1.y * exp((double)a1.x - mx);
+  sm = warp_sum(sm);
+  if ((tid & 63) == 0) red[tid >> 6] = sm;
+  __syncthreads();
+  return mx + log((red[0] + red[1]) + (red[2] + red[3]));
+}
+
 struct PosIn {
   int x, len;
   double u, Q;
@@ -279,16 +300,26 @@ lse_tests_kernel(TestArgs a) {
     }
   }
   const int rrow = root ? -1 : r;
+  // this row's tile statistics first (up to 512 tiles: two per thread, in registers),
+  // so that the draft token's dependent loads overlap the reduction
+  const float2 *stp = root ? a.root_stats + (int64_t)b * a.n_vt
+                           : (a.row_stats != nullptr ? a.row_stats + (int64_t)r * a.n_vt : nullptr);
+  const bool pre = stp != nullptr && a.n_vt <= 512;
+  float2 s0 = make_float2(0.f, 0.f), s1 = make_float2(0.f, 0.f);
+  if (pre) {
+    if (tid < a.n_vt) s0 = stp[tid];
+    if (tid + 256 < a.n_vt) s1 = stp[tid + 256];
+  }
   PosIn first{-1, 0, 0.0, 1.0, 0.f};
   if (tid < npos) first = load_pos(a, b, rrow, root ? tid : i0, oo);
 
   double lse;
-  if (root) {
-    lse = lse_of_stats(a.root_stats + (int64_t)b * a.n_vt, a.n_vt, red);
-    if (tid == 0) a.root_lse[b] = lse;
-  } else if (a.row_stats != nullptr) {
-    lse = lse_of_stats(a.row_stats + (int64_t)r * a.n_vt, a.n_vt, red);
-    if (tid == 0) a.row_lse[r] = lse;
+  if (stp != nullptr) {
+    lse = pre ? lse_of_stats2(s0, s1, a.n_vt, red) : lse_of_stats(stp, a.n_vt, red);
+    if (tid == 0) {
+      if (root) a.root_lse[b] = lse;
+      else a.row_lse[r] = lse;
+    }
   } else {
     lse = a.row_lse[r];
   }

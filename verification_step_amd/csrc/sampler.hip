@@ -383,7 +383,7 @@ struct SampShared {
   int flags;
   int best, ab, mode, xpt, is_last, owner, last_pos, tstar;
   int64_t prow, qrow;
-  double lse, u, excl;
+  double lse, u, excl, tot, xs;
 };
 
 enum { MODE_ROOT = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_TARGET = 3 };
@@ -780,35 +780,74 @@ sampler_kernel(SampArgs a) {
     cs.x = __longlong_as_double((long long)__hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     cs.y = __longlong_as_double((long long)__hip_atomic_load(cp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   }
-  double Sx = cs.x, Sy = cs.y;
-  block_sum2(sh, Sx, Sy);
-  const bool use_target = !(Sx > 0.0);
-  const double S = use_target ? Sy : Sx;
-  const double xs = sh.u * S;
-  const double v = use_target ? cs.y : cs.x;
-  const double incl = block_incl_scan(sh, v);
+  double S, xs;
   // the owner chunk: first with weight whose inclusive sum passes u*S; if rounding
   // leaves u*S at or past the total, the last chunk with weight
-  if (tid == 0) {
-    sh.owner = INT_MAX;
-    sh.last_pos = -1;
-    sh.tstar = INT_MAX;
-    if (use_target) {
-      sh.mode = MODE_TARGET;
-      atomicOr(&sh.flags, FLAG_DEGENERATE);
+  if (a.nch <= 64) {
+    // the chunk sums lie in wave 0: its shuffles and ballots replace the block's
+    // reductions and scans (the other waves would add zeros: the same numbers)
+    if (tid < 64) {
+      const double Sx = warp_sum(cs.x), Sy = warp_sum(cs.y);
+      const bool use_target = !(Sx > 0.0);
+      const double St = use_target ? Sy : Sx;
+      const double xt = sh.u * St;
+      const double v = use_target ? cs.y : cs.x;
+      double incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(incl, off);
+        if (tid >= off) incl += y;
+      }
+      const bool has = tid < a.nch && v > 0.0;
+      const uint64_t passed = __ballot(has && incl > xt);
+      const uint64_t weighted = __ballot(has);
+      int own = passed ? __builtin_ctzll(passed) : (weighted ? 63 - __builtin_clzll(weighted) : a.nch - 1);
+      const double ex = __shfl(incl - v, own);
+      if (tid == 0) {
+        sh.owner = own;
+        sh.excl = ex;
+        sh.tot = St;
+        sh.xs = xt;
+        sh.tstar = INT_MAX;
+        if (use_target) {
+          sh.mode = MODE_TARGET;
+          atomicOr(&sh.flags, FLAG_DEGENERATE);
+        }
+        if (PHASE == SAMP_FUSED) a.counters[b] = 0u;   // ready for the next call on this workspace
+      }
     }
-    if (PHASE == SAMP_FUSED) a.counters[b] = 0u;   // ready for the next call on this workspace
+    __syncthreads();
+    S = sh.tot;
+    xs = sh.xs;
+  } else {
+    double Sx = cs.x, Sy = cs.y;
+    block_sum2(sh, Sx, Sy);
+    const bool use_target = !(Sx > 0.0);
+    S = use_target ? Sy : Sx;
+    xs = sh.u * S;
+    const double v = use_target ? cs.y : cs.x;
+    const double incl = block_incl_scan(sh, v);
+    if (tid == 0) {
+      sh.owner = INT_MAX;
+      sh.last_pos = -1;
+      sh.tstar = INT_MAX;
+      if (use_target) {
+        sh.mode = MODE_TARGET;
+        atomicOr(&sh.flags, FLAG_DEGENERATE);
+      }
+      if (PHASE == SAMP_FUSED) a.counters[b] = 0u;   // ready for the next call on this workspace
+    }
+    __syncthreads();
+    if (tid < a.nch && v > 0.0) {
+      if (incl > xs) atomicMin(&sh.owner, tid);
+      atomicMax(&sh.last_pos, tid);
+    }
+    __syncthreads();
+    if (sh.owner == INT_MAX && tid == 0) sh.owner = sh.last_pos >= 0 ? sh.last_pos : a.nch - 1;
+    __syncthreads();
+    if (tid == sh.owner) sh.excl = incl - v;
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid < a.nch && v > 0.0) {
-    if (incl > xs) atomicMin(&sh.owner, tid);
-    atomicMax(&sh.last_pos, tid);
-  }
-  __syncthreads();
-  if (sh.owner == INT_MAX && tid == 0) sh.owner = sh.last_pos >= 0 ? sh.last_pos : a.nch - 1;
-  __syncthreads();
-  if (tid == sh.owner) sh.excl = incl - v;
-  __syncthreads();
   const int owner = sh.owner;
   const bool use_p = sh.mode == MODE_TARGET;
   // the owner chunk's per-thread sums, recomputed (same arithmetic, same order as its

@@ -77,6 +77,7 @@ struct AttnArgs {
   float scale_log2;
   int n_gate;        // leading workgroups that run the copy path's gate (0: none)
   GateArgs gate;
+  int grp_map;
 };
 
 __device__ __forceinline__ int clamp_prefix(int P, int max_keys, bool *bad) {
@@ -169,11 +170,38 @@ attn_mfma_kernel(AttnArgs a) {
   // one prefix split: its workgroup also takes the candidates' keys (no partials)
   const bool fold = a.n_splits == 1;
   const int n_sp = fold ? 1 : a.n_splits + 1;
-  const int nblocks = a.n_rb * n_sp * a.B * a.Hkv * a.L;
-  const int bid = xcd_remap((int)blockIdx.x - a.n_gate, nblocks);
-  const int rb = bid % a.n_rb;
-  const int s = (bid / a.n_rb) % n_sp;
-  const int z = bid / (a.n_rb * n_sp);        // (layer, sequence, kv head)
+  // Workgroup -> (row block, split, (layer, sequence, kv head)).  Workgroups are dealt
+  // round-robin over the 8 XCDs; the row blocks of one split (which read the same K/V)
+  // sit on one XCD, and consecutive (split, group) pairs on consecutive XCDs, so that
+  // splits of uneven length -- ragged prefixes -- spread over every XCD.  Workgroup j
+  // (after the gate's) is row block (j/8) % n_rb of pair ((j/8) / n_rb) * 8 + j % 8;
+  // pairs past the last return at once.  One sequence (grp_map 1): pairs split-major
+  // (pair = z + groups * s), so that its short candidate splits are dispatched last,
+  // behind the prefix splits, when the grid outgrows one round; batches (grp_map 2):
+  // group-major (pair = s + splits * z).
+  int rb, s, z;
+  if (a.grp_map) {
+    const int n_z = a.B * a.Hkv * a.L;
+    const int n_pairs = n_sp * n_z;
+    const int j = (int)blockIdx.x - a.n_gate;
+    const int r = j >> 3;
+    const int pair = (r / a.n_rb) * 8 + (j & 7);
+    if (pair >= n_pairs) return;
+    rb = r % a.n_rb;
+    if (a.grp_map == 1) {
+      s = pair / n_z;
+      z = pair % n_z;
+    } else {
+      s = pair % n_sp;
+      z = pair / n_sp;
+    }
+  } else {
+    const int nblocks = a.n_rb * n_sp * a.B * a.Hkv * a.L;
+    const int bid = xcd_remap((int)blockIdx.x - a.n_gate, nblocks);
+    rb = bid % a.n_rb;
+    s = (bid / a.n_rb) % n_sp;
+    z = bid / (a.n_rb * n_sp);        // (layer, sequence, kv head)
+  }
   const int zs = z % (a.B * a.Hkv);
   const int layer = z / (a.B * a.Hkv);
   const int b = zs / a.Hkv;
@@ -859,7 +887,12 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
     a.n_gate = B;
     a.gate = *gate;
   }
-  const int nblocks = p.n_rb * (fold ? 1 : p.n_splits + 1) * B * Hkv * L;
+  const int n_pairs = (fold ? 1 : p.n_splits + 1) * B * Hkv * L;
+  {
+    const char *mv = getenv("VSTEP_ATTN_MAP");
+    a.grp_map = mv ? atoi(mv) : (B == 1 ? 1 : 2);
+  }
+  const int nblocks = a.grp_map ? 8 * p.n_rb * ((n_pairs + 7) / 8) : p.n_rb * n_pairs;
   const dim3 grid(nblocks + a.n_gate), block(64 * p.nw);
   switch (p.nw) {
     case 1: hipLaunchKernelGGL((attn_mfma_kernel<1>), grid, block, 0, st, a); break;

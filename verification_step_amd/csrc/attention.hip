@@ -178,8 +178,14 @@ attn_mfma_kernel(AttnArgs a) {
   // pairs past the last return at once.  One sequence (grp_map 1): pairs split-major
   // (pair = z + groups * s), so that its short candidate splits are dispatched last,
   // behind the prefix splits, when the grid outgrows one round; batches (grp_map 2):
-  // group-major (pair = s + splits * z).
+  // group-major (pair = s + splits * z); batches of up to 64 sequences (grp_map 3):
+  // longest first -- every full-length split of every sequence, then the partial
+  // splits by decreasing length, then the candidate splits, then the empty ones -- so
+  // that the grid's last round holds short work (the batch's prefix lengths live on the
+  // device: each wave ranks them itself, lane b holding sequence b).
   int rb, s, z;
+  int P_ranked = -1;
+  bool bad_ranked = false;
   if (a.grp_map) {
     const int n_z = a.B * a.Hkv * a.L;
     const int n_pairs = n_sp * n_z;
@@ -188,7 +194,45 @@ attn_mfma_kernel(AttnArgs a) {
     const int pair = (r / a.n_rb) * 8 + (j & 7);
     if (pair >= n_pairs) return;
     rb = r % a.n_rb;
-    if (a.grp_map == 1) {
+    if (a.grp_map == 3) {
+      const int G = a.Hkv * a.L;                  // groups of one sequence
+      bool bl = false;
+      const int Pl = lane < a.B ? clamp_prefix(a.prefix_len[lane], a.max_pages * kPage, &bl) : 0;
+      const int nfull = Pl / a.split_keys;        // its full-length splits
+      const int rem = Pl - nfull * a.split_keys;  // keys of its partial split (0: none)
+      int incl = nfull;                           // inclusive scan over the sequences
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int F = __builtin_amdgcn_readlane(incl, 63);
+      const int Pn = __popcll(__ballot(rem > 0));
+      const int u = pair / G, gi = pair % G;
+      int bs;
+      if (u < F) {
+        bs = __builtin_ctzll(__ballot(incl > u));
+        s = u - (__builtin_amdgcn_readlane(incl, bs) - __builtin_amdgcn_readlane(nfull, bs));
+      } else if (u < F + Pn) {
+        // rank among the partial splits: longer first, equal lengths by sequence
+        int rank = 0;
+#pragma unroll
+        for (int o = 0; o < 64; ++o) {
+          const int r2 = __builtin_amdgcn_readlane(rem, o);
+          rank += (r2 > rem || (r2 == rem && o < lane)) ? 1 : 0;
+        }
+        bs = __builtin_ctzll(__ballot(rem > 0 && rank == u - F));
+        s = __builtin_amdgcn_readlane(nfull, bs);
+      } else if (u < F + Pn + a.B) {
+        bs = u - F - Pn;
+        s = a.n_splits;
+      } else {
+        return;
+      }
+      z = (gi / a.Hkv) * (a.B * a.Hkv) + bs * a.Hkv + gi % a.Hkv;
+      P_ranked = __builtin_amdgcn_readlane(Pl, bs);
+      bad_ranked = __builtin_amdgcn_readlane(bl ? 1 : 0, bs) != 0;
+    } else if (a.grp_map == 1) {
       s = pair / n_z;
       z = pair % n_z;
     } else {
@@ -212,8 +256,8 @@ attn_mfma_kernel(AttnArgs a) {
   const bf16_t *kp_l = a.k_pool + layer * a.p_ls;
   const bf16_t *vp_l = a.v_pool + layer * a.p_ls;
 
-  bool badP = false;
-  const int P = clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
+  bool badP = bad_ranked;
+  const int P = P_ranked >= 0 ? P_ranked : clamp_prefix(a.prefix_len[b], a.max_pages * kPage, &badP);
   const int n_pref = (P + a.split_keys - 1) / a.split_keys;
   const int n_active = n_pref + 1;
   const bool is_cand = !fold && s == a.n_splits;
@@ -890,7 +934,11 @@ hipError_t launch_attention(int B, int W, int D, int Hq, int Hkv, int hd, int ma
   const int n_pairs = (fold ? 1 : p.n_splits + 1) * B * Hkv * L;
   {
     const char *mv = getenv("VSTEP_ATTN_MAP");
-    a.grp_map = mv ? atoi(mv) : (B == 1 ? 1 : 2);
+    a.grp_map = mv ? atoi(mv) : (B == 1 ? 1 : 3);
+    if (a.grp_map < 0 || a.grp_map > 3) a.grp_map = 2;
+    // the longest-first order ranks the sequences inside one wave; one split has no
+    // order to choose
+    if (a.grp_map == 3 && (B > 64 || fold)) a.grp_map = 2;
   }
   const int nblocks = a.grp_map ? 8 * p.n_rb * ((n_pairs + 7) / 8) : p.n_rb * n_pairs;
   const dim3 grid(nblocks + a.n_gate), block(64 * p.nw);

@@ -446,7 +446,10 @@ head_lds_kernel(GemmArgs a) {
       const int n0 = vbase + v * 16 + 4 * lg;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (n0 + j < a.N) vs += expf(acc[v][mt][j] * a.inv_t - vmax);
+        // the hardware exp2 of the log2(e)-scaled difference (one instruction where expf
+        // takes a range-reduction sequence); within an ulp or two, far inside the
+        // normaliser's tolerance
+        if (n0 + j < a.N) vs += __builtin_amdgcn_exp2f((acc[v][mt][j] * a.inv_t - vmax) * 1.4426950408889634f);
     }
     vs += __shfl_xor(vs, 16);
     vs += __shfl_xor(vs, 32);

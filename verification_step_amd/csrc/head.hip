@@ -385,76 +385,88 @@ head_lds_kernel(GemmArgs a) {
   const bool staged = a.n_mblocks <= 2;
   float *stg = reinterpret_cast<float *>(Hs_all) + wv * 16 * kStRow;
   if (staged) __syncthreads();   // every wave is done reading H
+  // WHOLE: the workgroup's rows and vocabulary columns all lie inside M x N (every
+  // tile but the last vocabulary tile and the last row block), so no bounds are tested
+  auto epilogue = [&](auto whole_tag) {
+    constexpr bool WHOLE = decltype(whole_tag)::value;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float vmax = -INFINITY;
+    for (int mt = 0; mt < MT; ++mt) {
+      float vmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < VT; ++v) {
-      const int n0 = vbase + v * 16 + 4 * lg;
+      for (int v = 0; v < VT; ++v) {
+        const int n0 = vbase + v * 16 + 4 * lg;
+        if (staged) {
+          *(f32x4 *)&stg[l16 * kStRow + v * 16 + 4 * lg] = acc[v][mt];
+        } else {
+          const int m = mbase + mt * 16 + l16;
+          if (WHOLE || m < a.M) {
+            float *op = a.out + (int64_t)m * a.N + n0;
+            if (WHOLE || n0 + 3 < a.N) {
+              *(f32x4 *)op = acc[v][mt];
+            } else {
+              for (int j = 0; j < 4; ++j)
+                if (n0 + j < a.N) op[j] = acc[v][mt][j];
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (WHOLE || n0 + j < a.N) vmax = fmaxf(vmax, acc[v][mt][j] * a.inv_t);
+      }
       if (staged) {
-        *(f32x4 *)&stg[l16 * kStRow + v * 16 + 4 * lg] = acc[v][mt];
-      } else {
-        const int m = mbase + mt * 16 + l16;
-        if (m < a.M) {
-          float *op = a.out + (int64_t)m * a.N + n0;
-          if (n0 + 3 < a.N) {
-            *(f32x4 *)op = acc[v][mt];
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (n0 + j < a.N) op[j] = acc[v][mt][j];
+        // each wave reads back only its own fragment: a wave-level sync suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int kLPR = 4 * VT;     // lanes per fragment row, 4 floats each
+        constexpr int kRPI = 64 / kLPR;  // fragment rows per store instruction
+#pragma unroll
+        for (int i = 0; i < 16 / kRPI; ++i) {
+          const int r = kRPI * i + lane / kLPR;
+          const int c = 4 * (lane % kLPR);
+          const int m = mbase + mt * 16 + r;
+          const int n = vbase + c;
+          if (WHOLE || (m < a.M && n < a.N)) {
+            const f32x4 val = *(const f32x4 *)&stg[r * kStRow + c];
+            float *op = a.out + (int64_t)m * a.N + n;
+            if (WHOLE || (n + 3 < a.N && ((a.N & 3) == 0))) {
+              __builtin_nontemporal_store(val, (f32x4 *)op);
+            } else {
+              for (int j = 0; j < 4; ++j)
+                if (n + j < a.N) op[j] = val[j];
+            }
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
+      if (a.stats == nullptr) continue;
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+      float vs = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + j < a.N) vmax = fmaxf(vmax, acc[v][mt][j] * a.inv_t);
-    }
-    if (staged) {
-      // each wave reads back only its own fragment: a wave-level sync suffices
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      constexpr int kLPR = 4 * VT;     // lanes per fragment row, 4 floats each
-      constexpr int kRPI = 64 / kLPR;  // fragment rows per store instruction
+      for (int v = 0; v < VT; ++v) {
+        const int n0 = vbase + v * 16 + 4 * lg;
 #pragma unroll
-      for (int i = 0; i < 16 / kRPI; ++i) {
-        const int r = kRPI * i + lane / kLPR;
-        const int c = 4 * (lane % kLPR);
-        const int m = mbase + mt * 16 + r;
-        const int n = vbase + c;
-        if (m < a.M && n < a.N) {
-          const f32x4 val = *(const f32x4 *)&stg[r * kStRow + c];
-          float *op = a.out + (int64_t)m * a.N + n;
-          if (n + 3 < a.N && ((a.N & 3) == 0)) {
-            __builtin_nontemporal_store(val, (f32x4 *)op);
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (n + j < a.N) op[j] = val[j];
-          }
-        }
+        for (int j = 0; j < 4; ++j)
+          // the hardware exp2 of the log2(e)-scaled difference (one instruction where
+          // expf takes a range-reduction sequence); within an ulp or two, far inside
+          // the normaliser's tolerance
+          if (WHOLE || n0 + j < a.N)
+            vs += __builtin_amdgcn_exp2f((acc[v][mt][j] * a.inv_t - vmax) * 1.4426950408889634f);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      vs += __shfl_xor(vs, 16);
+      vs += __shfl_xor(vs, 32);
+      if (lg == 0) red[wv][mt * 16 + l16] = make_float2(vmax, vs);
     }
-    if (a.stats == nullptr) continue;
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-    float vs = 0.f;
-#pragma unroll
-    for (int v = 0; v < VT; ++v) {
-      const int n0 = vbase + v * 16 + 4 * lg;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        // the hardware exp2 of the log2(e)-scaled difference (one instruction where expf
-        // takes a range-reduction sequence); within an ulp or two, far inside the
-        // normaliser's tolerance
-        if (n0 + j < a.N) vs += __builtin_amdgcn_exp2f((acc[v][mt][j] * a.inv_t - vmax) * 1.4426950408889634f);
-    }
-    vs += __shfl_xor(vs, 16);
-    vs += __shfl_xor(vs, 32);
-    if (lg == 0) red[wv][mt * 16 + l16] = make_float2(vmax, vs);
-  }
+  };
+  // (a.N & 3) == 0 keeps the whole-tile stores 16-byte aligned
+  const bool whole = mbase + MT * 16 <= a.M && (vt + 1) * kHeadVocabTile <= a.N && (a.N & 3) == 0;
+  if (whole)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
   if (a.stats == nullptr) return;
   if (a.root != nullptr && mb == 0 && tile_ok) {
     for (int b = wq; b < a.B_root; b += kWPT) {

@@ -197,6 +197,37 @@ def test_attention_repeatable(plan, monkeypatch):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_attention_batch_orders(B, monkeypatch):
+    """A batch of ragged prefixes (empty, one key, one key short of a split, exact
+    multiples of the split, the longest, two out of range) through every order of
+    workgroups to XCDs -- contiguous ranges, split-major, group-major and longest first
+    (taken up to 64 sequences; 65 fall back to group-major) -- gives the same bits,
+    matches the oracle, and flags the out-of-range lengths."""
+    api = _api()
+    rng = np.random.default_rng(B)
+    P = rng.integers(0, 2049, size=B)
+    P[:6] = [0, 1, 511, 512, 1024, 2048]
+    sh = small_shape(B=B, P=tuple(int(x) for x in P), W=2, D=3, Hq=4, Hkv=2, d=512)
+    case = wl.make_case(sh, 5 + B, with_head=False, with_q=False)
+    case.arrays["prefix_len"][7] = -5
+    case.arrays["prefix_len"][9] = 10 ** 6
+    outs = {}
+    for m in ("3", "2", "1", "0"):
+        monkeypatch.setenv("VSTEP_ATTN_MAP", m)
+        say("attention batch order", B, m)
+        outs[m] = _run_attention(case)
+    for m in ("2", "1", "0"):
+        assert np.array_equal(outs[m][0], outs["3"][0]), m
+        assert np.array_equal(outs[m][1], outs["3"][1]), m
+    _, o_r, of = _oracle_attention(case)
+    assert np.array_equal(outs["3"][1], of)
+    assert (of[[7, 9]] & oracle.FLAG_BAD_PAGE).all()
+    err = rel_err(outs["3"][0], o_r)
+    print(f"rel_err={err:.3e}")
+    assert err <= TOL
+
+
 def test_attention_nan_in_page_tails():
     """The unused tail of each sequence's last page holds NaN in K and V: the masked
     keys must not reach the output (a zero probability times NaN would)."""
